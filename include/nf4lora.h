@@ -1,0 +1,224 @@
+/*
+ * nf4lora.h - C ABI of the MI355X (gfx950) frozen-NF4-base LoRA linear and its
+ * blockwise weight-streaming pool.
+ *
+ * Sources (page title, section):
+ *   [api]      Poros API reference - "PorosTrainer.from_pretrained" (quantization
+ *              "nf4" = 4-bit NF4 QLoRA; lora_rank 16, lora_alpha 32; NF4 reaches
+ *              elementwise-exact resident parity), "patch_hf_model" Behavior
+ *              (frozen base; blocks of block_size layers; block manager with
+ *              cross-stream safety), "Determinism".
+ *   [consumer] "Poros on consumer GPUs" - "What you need besides VRAM" (the NF4
+ *              base lives in pinned host memory, transferred per block),
+ *              "OOM playbook" (block_size never affects parity).
+ *   [hn]       HN comment thread on streaming the frozen base (item 49166984),
+ *              main comment: the base is read, never written; it sits in host RAM
+ *              and streams into a small pool of pre-allocated device buffers,
+ *              prefetched one ahead on a dedicated stream.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument named for a tensor is a DEVICE pointer unless its
+ *     comment says host. The caller owns all tensors and both streams; the
+ *     library allocates no device memory in any entry point of this header.
+ *   - bf16 tensors are passed as uint16_t bit patterns; all matrices are
+ *     row-major and densely packed (leading dimension = number of columns).
+ *   - Streams are hipStream_t values passed as nf4_stream (NULL = the null
+ *     stream). Every compute call only enqueues work on the given stream and
+ *     returns; argument errors are detected on the host before anything is
+ *     enqueued and are reported synchronously.
+ *   - Return value: NF4_OK or a negative NF4_E_* code; nf4_last_error() then
+ *     describes the failure (with the offending sizes) for the calling thread.
+ *   - Results are deterministic: no atomics, fixed reduction orders, and launch
+ *     shapes chosen from the problem sizes alone, so a repeated call returns
+ *     bitwise-identical outputs ([api] "Determinism").
+ */
+#ifndef NF4LORA_H
+#define NF4LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NF4_OK 0
+#define NF4_E_ARG (-1)   /* null pointer, bad enum, bad rank */
+#define NF4_E_SHAPE (-2) /* sizes that the format or the kernels cannot take */
+#define NF4_E_OOM (-3)   /* a pool that does not fit the device slab given */
+#define NF4_E_HIP (-4)   /* a HIP runtime call failed */
+#define NF4_E_STATE (-5) /* pool call out of order (release without acquire, ...) */
+#define NF4_E_BUSY (-6)  /* no pool slot can be reused right now */
+
+#define NF4_BLOCK 64     /* elements per absmax block, along a row */
+#define NF4_MAX_RANK 64  /* largest LoRA rank r accepted */
+
+#define NF4_DTYPE_BF16 0
+#define NF4_DTYPE_F32 1
+
+typedef void* nf4_stream; /* a hipStream_t */
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* nf4_last_error(void);
+
+/* ABI version, bumped on any signature change. */
+int nf4_abi_version(void);
+
+/*
+ * The 16 NF4 levels the library uses, ascending, written to a HOST array.
+ * NF4 is QLoRA's 4-bit NormalFloat ([api] "PorosTrainer.from_pretrained",
+ * quantization "nf4"): 7 negative and 8 positive N(0,1) quantiles scaled to
+ * [-1, 1] plus an exact 0 (index 7). The library derives them itself at load
+ * time in extended precision and rounds each once to float32.
+ */
+int nf4_codebook(float levels_out[16]);
+
+/*
+ * Quantise a row-major [rows, cols] matrix to NF4 ([api] quantization "nf4";
+ * storage format of [consumer] "What you need besides VRAM").
+ *   w       device, rows*cols elements of in_dtype (NF4_DTYPE_BF16 or _F32), finite
+ *   codes   device, [rows][cols/2] bytes; element 2i of a row in the low nibble of
+ *           byte i, element 2i+1 in the high nibble
+ *   absmax  device, [rows][cols/64] float32; absmax of each run of 64 elements
+ * Each element gets the nearest level to RN32(w/absmax) (ties to the lower
+ * code); an all-zero block gets absmax 0 and code 7. cols % 64 != 0 -> NF4_E_SHAPE.
+ * rows == 0 is a no-op.
+ */
+int nf4_quantize(const void* w, int in_dtype, int64_t rows, int64_t cols,
+                 uint8_t* codes, float* absmax, nf4_stream stream);
+
+/*
+ * Dequantise to bf16: w[n][k] = RNbf(RN32(level[code] * absmax)) - the exact
+ * values every fused kernel below multiplies with.
+ *   codes [rows][cols/2], absmax [rows][cols/64] (device, as nf4_quantize writes)
+ *   w_bf16 device [rows][cols]
+ */
+int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int64_t cols,
+                   uint16_t* w_bf16, nf4_stream stream);
+
+/* Bytes of device workspace nf4_lora_linear_fwd needs for these sizes (may be 0). */
+size_t nf4_lora_linear_fwd_workspace(int64_t T, int64_t N, int64_t K, int r);
+
+/*
+ * Forward of the frozen-NF4-base LoRA linear ([api] "PorosTrainer.from_pretrained":
+ * NF4 base with rank-r LoRA; [hn]: the frozen base is only read):
+ *     u = x . A^T                          (fp32, saved for the backward)
+ *     y = RNbf( x . W^T + s . u . B^T ),   s = RN32(alpha / r), one rounding
+ * with W the dequantised base (never materialised: dequantised in registers
+ * and fed to bf16 MFMA with fp32 accumulation).
+ *   codes/absmax  device, the NF4 base W [N][K] (K % 64 == 0, N % 16 == 0)
+ *   x             device bf16 [T][K]
+ *   A             device bf16 [r][K];  B device bf16 [N][r]   (r in 0..NF4_MAX_RANK)
+ *   y             device bf16 [T][N]  (written)
+ *   u_save        device fp32 [T][r]  (written; may be NULL only when r == 0)
+ *   ws            device workspace of at least nf4_lora_linear_fwd_workspace()
+ *                 bytes, 256-byte aligned (NULL allowed when that size is 0);
+ *                 contents on entry are ignored
+ * r == 0 computes the base only (A, B, u_save may be NULL). T == 0 is a no-op.
+ * Device pointers must be 16-byte aligned.
+ */
+int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K,
+                        const uint16_t* x, int64_t T,
+                        const uint16_t* A, const uint16_t* B, int r, float alpha,
+                        uint16_t* y, float* u_save, void* ws, size_t ws_bytes, nf4_stream stream);
+
+/* Bytes of device workspace nf4_lora_linear_bwd needs for these sizes. */
+size_t nf4_lora_linear_bwd_workspace(int64_t T, int64_t N, int64_t K, int r);
+
+/*
+ * Backward of the same linear. The base is frozen ([api] "patch_hf_model"
+ * Behavior 3; [hn]): no gradient is ever formed for it.
+ *     g  = dY . B                          (fp32, in the workspace)
+ *     dX = RNbf( dY . W + s . g . A )      one rounding
+ *     dA = s . g^T . x                     fp32, overwritten (not accumulated)
+ *     dB = s . dY^T . u                    fp32, overwritten
+ *   x [T][K], u_save [T][r] (from the forward), dy [T][N]: device
+ *   dx  device bf16 [T][K], or NULL to skip dX
+ *   dA  device fp32 [r][K]; dB device fp32 [N][r] (may be NULL when r == 0)
+ *   ws  device workspace of at least nf4_lora_linear_bwd_workspace() bytes,
+ *       256-byte aligned; its contents on entry are ignored
+ * Shapes and r as in the forward.
+ */
+int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K,
+                        const uint16_t* x, const float* u_save, const uint16_t* dy, int64_t T,
+                        const uint16_t* A, const uint16_t* B, int r, float alpha,
+                        uint16_t* dx, float* dA, float* dB,
+                        void* ws, size_t ws_bytes, nf4_stream stream);
+
+/* ------------------------------------------------------------------ stream pool
+ * Blockwise residency of the frozen base ([hn] main comment; [api]
+ * "patch_hf_model" Behavior 5-6; [consumer] "What you need besides VRAM",
+ * "OOM playbook"): the NF4 base of block_size layers at a time lives in a
+ * pinned HOST slab; a pool of n_slots device slots (carved from one caller
+ * allocation) receives blocks by hipMemcpyAsync on a dedicated copy stream.
+ * A block is used on a compute stream between acquire and release; release
+ * records an event on that stream, and the copy that later reuses the slot
+ * waits on it, so reuse is ordered on the streams and never blocks the host.
+ * The bytes a kernel sees are the same whether the block is streamed or was
+ * copied once (resident), so streamed and resident results are bitwise equal.
+ * A pool is used from one host thread at a time.
+ */
+typedef struct nf4_pool nf4_pool;
+
+typedef struct {
+    const void* host; /* pinned host pointer (hipHostMalloc / pin_memory) */
+    size_t bytes;     /* bytes of this block; <= slot_bytes */
+} nf4_host_block;
+
+typedef struct {
+    uint64_t bytes_copied; /* H2D bytes issued */
+    uint64_t copies;       /* H2D copies issued */
+    uint64_t hits;         /* acquires that found the block already issued/resident */
+    uint64_t misses;       /* acquires that had to issue the copy themselves */
+    uint64_t evictions;    /* copies that reused a slot holding another block */
+} nf4_pool_stats;
+
+/*
+ * Create a pool over n_blocks host blocks and n_slots device slots.
+ *   blocks       HOST array of n_blocks descriptors (copied; the pinned slabs
+ *                must outlive the pool)
+ *   device_slab  device memory of at least n_slots * slot_bytes bytes; slot i
+ *                starts at device_slab + i * slot_bytes (slot_bytes % 256 == 0)
+ *   copy_stream  the dedicated stream for H2D copies (must not be NULL)
+ *   out          receives the pool handle
+ * NF4_E_OOM if some block is larger than slot_bytes (sizes in the message).
+ */
+int stream_pool_create(const nf4_host_block* blocks, int n_blocks, void* device_slab,
+                       size_t slot_bytes, int n_slots, nf4_stream copy_stream, nf4_pool** out);
+
+/*
+ * Issue the H2D copy of `block` on the copy stream if it is not already in a
+ * slot (no-op then). The victim slot is the least recently used slot not held
+ * between acquire and release; the copy first waits for that slot's last
+ * release. NF4_E_BUSY when every slot is held.
+ */
+int stream_pool_prefetch(nf4_pool* pool, int block);
+
+/*
+ * Make `block` usable on `compute`: issue its copy if it was not prefetched (a
+ * miss), make `compute` wait for the copy, mark the slot held and return its
+ * device address in *dev. NF4_E_STATE if the block is already held.
+ */
+int stream_pool_acquire(nf4_pool* pool, int block, nf4_stream compute, const void** dev);
+
+/*
+ * End the use of `block` on `compute`: record the slot's last-use event there.
+ * The slot stays valid (a later acquire of the same block is a hit) until a
+ * prefetch/acquire of another block reuses it. NF4_E_STATE if not held.
+ */
+int stream_pool_release(nf4_pool* pool, int block, nf4_stream compute);
+
+/* Counters since creation (HOST struct). */
+int stream_pool_stats(const nf4_pool* pool, nf4_pool_stats* out);
+
+/* Which block slot `slot` holds (-1 if none), for tests and tracing. */
+int stream_pool_slot_block(const nf4_pool* pool, int slot, int* block_out);
+
+/* Wait for the copy stream to drain, then free the pool's events and state. */
+int stream_pool_destroy(nf4_pool* pool);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4LORA_H */

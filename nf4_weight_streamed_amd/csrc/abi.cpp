@@ -1,0 +1,237 @@
+// C ABI of the NF4-LoRA library: argument validation, error reporting, the NF4
+// level table and the enqueue order of each linear's kernels.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/nf4lora.h"
+#include "common.h"
+
+namespace nf4 {
+
+namespace {
+
+thread_local std::string g_error;
+
+// Standard normal CDF and its inverse in x87 extended precision (64-bit
+// significand): the inverse by bisection on erfcl, which converges to the last
+// bit of the format. The levels only need about 1e-9 relative accuracy to round
+// to the same float32 values; this is far beyond that.
+long double normal_cdf(long double z) { return 0.5L * erfcl(-z / sqrtl(2.0L)); }
+
+long double normal_quantile(long double p) {
+    long double lo = -40.0L, hi = 40.0L;
+    for (int i = 0; i < 400 && lo < hi; ++i) {
+        const long double mid = 0.5L * (lo + hi);
+        if (mid == lo || mid == hi) break;
+        if (normal_cdf(mid) < p)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return 0.5L * (lo + hi);
+}
+
+// NF4 = QLoRA's 4-bit NormalFloat (Poros API reference, "PorosTrainer.from_pretrained",
+// quantization "nf4"): eight positive quantiles on a probability grid from
+// delta down to 1/2 (8 steps), seven negative ones on the same span in 7 steps,
+// each divided by the quantile at delta so the extremes are exactly -1 and +1,
+// plus an exact 0; delta = ((1 - 1/30) + (1 - 1/32)) / 2.
+Tables build_tables() {
+    Tables t{};
+    const long double delta = 0.5L * ((1.0L - 1.0L / 30.0L) + (1.0L - 1.0L / 32.0L));
+    const long double top = normal_quantile(delta);
+    long double lv[16];
+    int n = 0;
+    for (int i = 0; i <= 6; ++i) lv[n++] = -normal_quantile(delta - (delta - 0.5L) * i / 7.0L) / top;
+    lv[n++] = 0.0L;
+    for (int i = 7; i >= 0; --i) lv[n++] = normal_quantile(delta - (delta - 0.5L) * i / 8.0L) / top;
+    for (int j = 0; j < 16; ++j) t.level[j] = static_cast<float>(lv[j]);
+    t.level[0] = -1.0f;  // the extremes are exact by construction (q(delta)/q(delta))
+    t.level[15] = 1.0f;
+    for (int j = 0; j < 15; ++j) {
+        // midpoint of two float32 values is exact in double
+        const double mid = (double(t.level[j]) + double(t.level[j + 1])) * 0.5;
+        float c = static_cast<float>(mid);
+        if (double(c) <= mid) c = std::nextafter(c, 2.0f);
+        t.thresh[j] = c;
+    }
+    return t;
+}
+
+}  // namespace
+
+const Tables& tables() {
+    static const Tables t = build_tables();
+    return t;
+}
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+int check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(NF4_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return NF4_OK;
+}
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(NF4_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return NF4_OK;
+}
+
+int check_linear_common(const char* fn, const uint8_t* codes, const float* absmax, int64_t N, int64_t K, int64_t T,
+                        int r, float alpha) {
+    if (N <= 0 || K <= 0 || T < 0)
+        return fail(NF4_E_SHAPE, "%s: need N > 0, K > 0, T >= 0 (got N=%lld K=%lld T=%lld)", fn, (long long)N,
+                    (long long)K, (long long)T);
+    if (K % NF4_BLOCK != 0)
+        return fail(NF4_E_SHAPE, "%s: K=%lld is not a multiple of %d", fn, (long long)K, NF4_BLOCK);
+    if (N % 16 != 0) return fail(NF4_E_SHAPE, "%s: N=%lld is not a multiple of 16", fn, (long long)N);
+    if (N > (int64_t(1) << 30) || K > (int64_t(1) << 30) || T > (int64_t(1) << 30))
+        return fail(NF4_E_SHAPE, "%s: sizes beyond 2^30 (N=%lld K=%lld T=%lld)", fn, (long long)N, (long long)K,
+                    (long long)T);
+    if (r < 0 || r > NF4_MAX_RANK) return fail(NF4_E_ARG, "%s: rank r=%d outside 0..%d", fn, r, NF4_MAX_RANK);
+    if (!std::isfinite(alpha)) return fail(NF4_E_ARG, "%s: alpha is not finite", fn);
+    if (!codes || !absmax) return fail(NF4_E_ARG, "%s: codes/absmax must not be NULL", fn);
+    if (!aligned(codes, 16) || !aligned(absmax, 4))
+        return fail(NF4_E_ARG, "%s: codes must be 16-byte and absmax 4-byte aligned", fn);
+    return NF4_OK;
+}
+
+float lora_scale(float alpha, int r) { return r > 0 ? alpha / float(r) : 0.0f; }
+
+}  // namespace
+
+}  // namespace nf4
+
+using namespace nf4;
+
+extern "C" {
+
+const char* nf4_last_error(void) { return g_error.c_str(); }
+
+int nf4_abi_version(void) { return 1; }
+
+int nf4_codebook(float levels_out[16]) {
+    if (!levels_out) return fail(NF4_E_ARG, "nf4_codebook: NULL output");
+    for (int i = 0; i < 16; ++i) levels_out[i] = tables().level[i];
+    return NF4_OK;
+}
+
+int nf4_quantize(const void* w, int in_dtype, int64_t rows, int64_t cols, uint8_t* codes, float* absmax,
+                 nf4_stream stream) {
+    if (in_dtype != NF4_DTYPE_BF16 && in_dtype != NF4_DTYPE_F32)
+        return fail(NF4_E_ARG, "nf4_quantize: unknown in_dtype %d", in_dtype);
+    if (rows < 0 || cols <= 0 || cols % NF4_BLOCK != 0)
+        return fail(NF4_E_SHAPE, "nf4_quantize: need rows >= 0 and cols a positive multiple of %d (got %lld x %lld)",
+                    NF4_BLOCK, (long long)rows, (long long)cols);
+    if (rows == 0) return NF4_OK;
+    if (!w || !codes || !absmax) return fail(NF4_E_ARG, "nf4_quantize: NULL pointer");
+    if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(absmax, 4))
+        return fail(NF4_E_ARG, "nf4_quantize: w and codes must be 16-byte aligned, absmax 4-byte");
+    return hip_status(launch_quantize(w, in_dtype, rows, cols, codes, absmax, static_cast<hipStream_t>(stream)),
+                      "nf4_quantize");
+}
+
+int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int64_t cols, uint16_t* w_bf16,
+                   nf4_stream stream) {
+    if (rows < 0 || cols <= 0 || cols % NF4_BLOCK != 0)
+        return fail(NF4_E_SHAPE, "nf4_dequantize: need rows >= 0 and cols a positive multiple of %d (got %lld x %lld)",
+                    NF4_BLOCK, (long long)rows, (long long)cols);
+    if (rows == 0) return NF4_OK;
+    if (!codes || !absmax || !w_bf16) return fail(NF4_E_ARG, "nf4_dequantize: NULL pointer");
+    if (!aligned(codes, 4) || !aligned(w_bf16, 16) || !aligned(absmax, 4))
+        return fail(NF4_E_ARG, "nf4_dequantize: codes 4-byte, w 16-byte, absmax 4-byte alignment needed");
+    return hip_status(launch_dequantize(codes, absmax, rows, cols, w_bf16, static_cast<hipStream_t>(stream)),
+                      "nf4_dequantize");
+}
+
+size_t nf4_lora_linear_fwd_workspace(int64_t T, int64_t N, int64_t K, int r) {
+    if (T <= 0 || N <= 0 || K <= 0 || K % NF4_BLOCK != 0 || r < 0 || r > NF4_MAX_RANK) return 0;
+    return plan_fwd(T, N, K, r).ws_bytes;
+}
+
+int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, const uint16_t* x,
+                        int64_t T, const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* y,
+                        float* u_save, void* ws, size_t ws_bytes, nf4_stream stream) {
+    const char* fn = "nf4_lora_linear_fwd";
+    int st = check_linear_common(fn, codes, absmax, N, K, T, r, alpha);
+    if (st != NF4_OK) return st;
+    if (T == 0) return NF4_OK;
+    if (!x || !y) return fail(NF4_E_ARG, "%s: x/y must not be NULL", fn);
+    if (r > 0 && (!A || !B || !u_save)) return fail(NF4_E_ARG, "%s: r=%d needs A, B and u_save", fn, r);
+    if (!aligned(x, 16) || !aligned(y, 2) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || !aligned(u_save, 4))))
+        return fail(NF4_E_ARG, "%s: misaligned pointer (x and A need 16 bytes)", fn);
+    const FwdPlan p = plan_fwd(T, N, K, r);
+    if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned(ws, 256)))
+        return fail(NF4_E_ARG, "%s: workspace of %zu bytes (256-byte aligned) needed for T=%lld N=%lld K=%lld r=%d, got %zu",
+                    fn, p.ws_bytes, (long long)T, (long long)N, (long long)K, r, ws_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale = lora_scale(alpha, r);
+    if (r > 0) {
+        float* upart = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_upart);
+        st = hip_status(launch_lora_down(x, A, T, K, r, u_save, upart, p.down_splits, p.down_steps, s),
+                        "nf4_lora_linear_fwd (x.A^T)");
+        if (st != NF4_OK) return st;
+    }
+    return hip_status(launch_gemm_fwd(p, codes, absmax, x, u_save, B, T, N, K, r, scale, y, ws, s),
+                      "nf4_lora_linear_fwd (gemm)");
+}
+
+size_t nf4_lora_linear_bwd_workspace(int64_t T, int64_t N, int64_t K, int r) {
+    if (T <= 0 || N <= 0 || K <= 0 || K % NF4_BLOCK != 0 || r < 0 || r > NF4_MAX_RANK) return 0;
+    return plan_bwd(T, N, K, r).ws_bytes;
+}
+
+int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, const uint16_t* x,
+                        const float* u_save, const uint16_t* dy, int64_t T, const uint16_t* A, const uint16_t* B,
+                        int r, float alpha, uint16_t* dx, float* dA, float* dB, void* ws, size_t ws_bytes,
+                        nf4_stream stream) {
+    const char* fn = "nf4_lora_linear_bwd";
+    int st = check_linear_common(fn, codes, absmax, N, K, T, r, alpha);
+    if (st != NF4_OK) return st;
+    if (T == 0) return NF4_OK;
+    if (!dy) return fail(NF4_E_ARG, "%s: dy must not be NULL", fn);
+    if (r > 0 && (!x || !u_save || !A || !B || !dA || !dB))
+        return fail(NF4_E_ARG, "%s: r=%d needs x, u_save, A, B, dA and dB", fn, r);
+    if (!aligned(dy, 16) || (dx && !aligned(dx, 2)) ||
+        (r > 0 && (!aligned(x, 16) || !aligned(A, 2) || !aligned(B, 2) || !aligned(u_save, 4) || !aligned(dA, 4) ||
+                   !aligned(dB, 4))))
+        return fail(NF4_E_ARG, "%s: misaligned pointer (dy and x need 16 bytes)", fn);
+    const BwdPlan p = plan_bwd(T, N, K, r);
+    if (!ws || ws_bytes < p.ws_bytes || !aligned(ws, 256))
+        return fail(NF4_E_ARG, "%s: workspace of %zu bytes (256-byte aligned) needed for T=%lld N=%lld K=%lld r=%d, got %zu",
+                    fn, p.ws_bytes, (long long)T, (long long)N, (long long)K, r, ws_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale = lora_scale(alpha, r);
+    if (r > 0) {
+        st = hip_status(launch_lora_bwd_pre(p, dy, B, u_save, T, N, r, scale, dB, ws, s), "nf4_lora_linear_bwd (g, dB)");
+        if (st != NF4_OK) return st;
+    }
+    if (dx) {
+        st = hip_status(launch_gemm_bwd_dx(p, codes, absmax, dy, A, T, N, K, r, scale, dx, ws, s),
+                        "nf4_lora_linear_bwd (dX)");
+        if (st != NF4_OK) return st;
+    }
+    if (r > 0) {
+        st = hip_status(launch_lora_da(p, x, T, K, r, scale, dA, ws, s), "nf4_lora_linear_bwd (dA)");
+        if (st != NF4_OK) return st;
+    }
+    return NF4_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal declarations of the NF4-LoRA library (host + device). Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstddef>
+#include <cstdint>
+
+namespace nf4 {
+
+// Levels of the NF4 code (ascending) and the quantiser's decision thresholds:
+// thresh[j] is the smallest float32 strictly above the midpoint of level[j] and
+// level[j+1], so "v >= thresh[j]" is "v lies above that midpoint" for float32 v.
+struct Tables {
+    float level[16];
+    float thresh[15];
+};
+
+const Tables& tables();  // built once per process (abi.cpp)
+
+// Error plumbing (abi.cpp): record a message for nf4_last_error() and return code.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int check_launch(const char* what);  // NF4_OK, or NF4_E_HIP with the HIP error text
+
+// ---- kernel launchers (each returns hipError_t of the launch) ----
+hipError_t launch_quantize(const void* w, int in_dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                           float* absmax, hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int64_t cols,
+                             uint16_t* w, hipStream_t stream);
+
+#define NF4_MAX_RANK_BLOCKS 4  // r <= 16 * NF4_MAX_RANK_BLOCKS (= NF4_MAX_RANK)
+
+// Forward plan: how the kernels are split for a shape (a pure function of the shape,
+// so repeated calls - streamed or resident - launch identical grids).
+struct FwdPlan {
+    int bm, bn;           // GEMM workgroup tile (tokens x out features)
+    int splits;           // GEMM K splits (1 = fused epilogue in the GEMM)
+    int steps_per_split;  // 64-wide K steps per split
+    int down_splits;      // K splits of u = x.A^T (1 = written directly)
+    int down_steps;       // 32-wide K steps per split
+    size_t off_upart, off_ypart;  // workspace offsets (bytes)
+    size_t ws_bytes;
+};
+FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r);
+
+struct BwdPlan {
+    int bm, bn;            // dX tile (tokens x in features)
+    int splits;            // N (contraction) splits for dX
+    int steps_per_split;
+    int nslab;             // out-feature slabs of the LoRA pre-pass (partial g)
+    size_t off_g, off_gpart, off_dx;  // workspace offsets (bytes)
+    size_t ws_bytes;
+};
+BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r);
+
+hipError_t launch_lora_down(const uint16_t* x, const uint16_t* A, int64_t T, int64_t K, int r, float* u,
+                            float* upart, int splits, int steps_per_split, hipStream_t stream);
+hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* x,
+                           const float* u, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,
+                           uint16_t* y, void* ws, hipStream_t stream);
+hipError_t launch_lora_bwd_pre(const BwdPlan& p, const uint16_t* dy, const uint16_t* B, const float* u,
+                               int64_t T, int64_t N, int r, float s, float* dB, void* ws, hipStream_t stream);
+hipError_t launch_gemm_bwd_dx(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* dy,
+                              const uint16_t* A, int64_t T, int64_t N, int64_t K, int r, float s, uint16_t* dx,
+                              void* ws, hipStream_t stream);
+hipError_t launch_lora_da(const BwdPlan& p, const uint16_t* x, int64_t T, int64_t K, int r, float s, float* dA,
+                          void* ws, hipStream_t stream);
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+}  // namespace nf4

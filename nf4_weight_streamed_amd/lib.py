@@ -1,0 +1,281 @@
+"""ctypes binding of libnf4lora.so (include/nf4lora.h): argument marshalling only.
+
+Every computation runs in the HIP library; this module checks tensor
+placement/dtype/shape, allocates outputs with torch (device memory is the only
+thing torch provides here) and passes raw pointers plus the current stream.
+There is no fallback: if the library is missing, importing this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnf4lora.so")
+
+NF4_OK = 0
+NF4_E_ARG, NF4_E_SHAPE, NF4_E_OOM, NF4_E_HIP, NF4_E_STATE, NF4_E_BUSY = -1, -2, -3, -4, -5, -6
+NF4_BLOCK = 64
+NF4_MAX_RANK = 64
+NF4_DTYPE_BF16, NF4_DTYPE_F32 = 0, 1
+_CODE_NAMES = {-1: "NF4_E_ARG", -2: "NF4_E_SHAPE", -3: "NF4_E_OOM", -4: "NF4_E_HIP", -5: "NF4_E_STATE",
+               -6: "NF4_E_BUSY"}
+
+
+class Nf4Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODE_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class HostBlock(C.Structure):
+    _fields_ = [("host", C.c_void_p), ("bytes", C.c_size_t)]
+
+
+class PoolStats(C.Structure):
+    _fields_ = [("bytes_copied", C.c_uint64), ("copies", C.c_uint64), ("hits", C.c_uint64),
+                ("misses", C.c_uint64), ("evictions", C.c_uint64)]
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m nf4_weight_streamed_amd.build` "
+                           "(there is no fallback path)")
+    lib = C.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_size_t
+    sig = {
+        "nf4_last_error": (C.c_char_p, []),
+        "nf4_abi_version": (i32, []),
+        "nf4_codebook": (i32, [C.POINTER(C.c_float)]),
+        "nf4_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
+        "nf4_dequantize": (i32, [vp, vp, i64, i64, vp, vp]),
+        "nf4_lora_linear_fwd_workspace": (sz, [i64, i64, i64, i32]),
+        "nf4_lora_linear_fwd": (i32, [vp, vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "nf4_lora_linear_bwd_workspace": (sz, [i64, i64, i64, i32]),
+        "nf4_lora_linear_bwd": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
+        "stream_pool_create": (i32, [C.POINTER(HostBlock), i32, vp, sz, i32, vp, C.POINTER(vp)]),
+        "stream_pool_prefetch": (i32, [vp, i32]),
+        "stream_pool_acquire": (i32, [vp, i32, vp, C.POINTER(vp)]),
+        "stream_pool_release": (i32, [vp, i32, vp]),
+        "stream_pool_stats": (i32, [vp, C.POINTER(PoolStats)]),
+        "stream_pool_slot_block": (i32, [vp, i32, C.POINTER(i32)]),
+        "stream_pool_destroy": (i32, [vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def raw() -> C.CDLL:
+    """The loaded CDLL (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def last_error() -> str:
+    return _lib.nf4_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != NF4_OK:
+        raise Nf4Error(rc, last_error())
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t) -> C.c_void_p | None:
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def abi_version() -> int:
+    return _lib.nf4_abi_version()
+
+
+def codebook() -> list:
+    out = (C.c_float * 16)()
+    _check(_lib.nf4_codebook(out))
+    return list(out)
+
+
+def quantize(w: torch.Tensor, codes: torch.Tensor | None = None, absmax: torch.Tensor | None = None, stream=None):
+    """NF4-quantise a [N, K] bf16 or float32 device matrix -> (codes uint8 [N, K/2], absmax float32 [N, K/64])."""
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D")
+    n, k = w.shape
+    dtype = {torch.bfloat16: NF4_DTYPE_BF16, torch.float32: NF4_DTYPE_F32}.get(w.dtype)
+    if dtype is None:
+        raise TypeError("w must be bfloat16 or float32")
+    _need(w, "w", w.dtype, (n, k))
+    if codes is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    if absmax is None:
+        absmax = torch.empty((n, k // NF4_BLOCK), dtype=torch.float32, device=w.device)
+    _need(codes, "codes", torch.uint8, (n, k // 2))
+    _need(absmax, "absmax", torch.float32, (n, k // NF4_BLOCK))
+    _check(_lib.nf4_quantize(_ptr(w), dtype, n, k, _ptr(codes), _ptr(absmax), _stream(stream)))
+    return codes, absmax
+
+
+def dequantize(codes: torch.Tensor, absmax: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    n, kh = codes.shape
+    k = kh * 2
+    _need(codes, "codes", torch.uint8, (n, kh))
+    _need(absmax, "absmax", torch.float32, (n, k // NF4_BLOCK))
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=codes.device)
+    _need(out, "out", torch.bfloat16, (n, k))
+    _check(_lib.nf4_dequantize(_ptr(codes), _ptr(absmax), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def fwd_workspace_bytes(T: int, N: int, K: int, r: int) -> int:
+    return int(_lib.nf4_lora_linear_fwd_workspace(T, N, K, r))
+
+
+def bwd_workspace_bytes(T: int, N: int, K: int, r: int) -> int:
+    return int(_lib.nf4_lora_linear_bwd_workspace(T, N, K, r))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A 256-byte aligned device buffer of at least nbytes (torch's allocator aligns to 512)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def lora_linear_fwd(codes, absmax, x, A, B, alpha: float, y=None, u=None, ws=None, stream=None):
+    """y = RNbf(x.W^T + (alpha/r).(x.A^T).B^T), u = x.A^T. Returns (y, u)."""
+    n, kh = codes.shape
+    k = kh * 2
+    t = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(codes, "codes", torch.uint8, (n, kh))
+    _need(absmax, "absmax", torch.float32, (n, k // NF4_BLOCK))
+    _need(x, "x", torch.bfloat16, (t, k))
+    if r:
+        _need(A, "A", torch.bfloat16, (r, k))
+        _need(B, "B", torch.bfloat16, (n, r))
+    if y is None:
+        y = torch.empty((t, n), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, (t, n))
+    if r and u is None:
+        u = torch.empty((t, r), dtype=torch.float32, device=x.device)
+    if r:
+        _need(u, "u", torch.float32, (t, r))
+    need = fwd_workspace_bytes(t, n, k, r)
+    if ws is None and need:
+        ws = workspace(need, x.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.nf4_lora_linear_fwd(_ptr(codes), _ptr(absmax), n, k, _ptr(x), t, _ptr(A), _ptr(B), r,
+                                    float(alpha), _ptr(y), _ptr(u), _ptr(ws), ws_bytes, _stream(stream)))
+    return y, u
+
+
+def lora_linear_bwd(codes, absmax, x, u, dy, A, B, alpha: float, dx=None, dA=None, dB=None, ws=None,
+                    need_dx: bool = True, stream=None):
+    """Backward: returns (dx or None, dA, dB); no gradient of the frozen base exists."""
+    n, kh = codes.shape
+    k = kh * 2
+    t = dy.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(codes, "codes", torch.uint8, (n, kh))
+    _need(absmax, "absmax", torch.float32, (n, k // NF4_BLOCK))
+    _need(dy, "dy", torch.bfloat16, (t, n))
+    if r:
+        _need(x, "x", torch.bfloat16, (t, k))
+        _need(u, "u", torch.float32, (t, r))
+        _need(A, "A", torch.bfloat16, (r, k))
+        _need(B, "B", torch.bfloat16, (n, r))
+        if dA is None:
+            dA = torch.empty((r, k), dtype=torch.float32, device=dy.device)
+        if dB is None:
+            dB = torch.empty((n, r), dtype=torch.float32, device=dy.device)
+        _need(dA, "dA", torch.float32, (r, k))
+        _need(dB, "dB", torch.float32, (n, r))
+    if need_dx and dx is None:
+        dx = torch.empty((t, k), dtype=torch.bfloat16, device=dy.device)
+    if dx is not None:
+        _need(dx, "dx", torch.bfloat16, (t, k))
+    need = bwd_workspace_bytes(t, n, k, r)
+    if ws is None:
+        ws = workspace(need, dy.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.nf4_lora_linear_bwd(_ptr(codes), _ptr(absmax), n, k, _ptr(x), _ptr(u), _ptr(dy), t, _ptr(A),
+                                    _ptr(B), r, float(alpha), _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes,
+                                    _stream(stream)))
+    return dx, dA, dB
+
+
+class StreamPool:
+    """Thin handle over stream_pool_*: pinned host blocks -> device slots on a copy stream."""
+
+    def __init__(self, host_blocks, device_slab: torch.Tensor, slot_bytes: int, n_slots: int, copy_stream):
+        arr = (HostBlock * len(host_blocks))()
+        for i, hb in enumerate(host_blocks):
+            if hb.device.type != "cpu" or not hb.is_pinned():
+                raise ValueError(f"host block {i} must be pinned host memory")
+            arr[i].host = hb.data_ptr()
+            arr[i].bytes = hb.numel() * hb.element_size()
+        self._blocks = list(host_blocks)     # keep the slabs alive
+        self._slab = device_slab
+        self._copy = copy_stream
+        h = C.c_void_p()
+        _check(_lib.stream_pool_create(arr, len(host_blocks), _ptr(device_slab), slot_bytes, n_slots,
+                                       _stream(copy_stream), C.byref(h)))
+        self._h = h
+        self.slot_bytes = slot_bytes
+        self.n_slots = n_slots
+
+    def prefetch(self, block: int) -> None:
+        _check(_lib.stream_pool_prefetch(self._h, block))
+
+    def acquire(self, block: int, stream=None) -> int:
+        dev = C.c_void_p()
+        _check(_lib.stream_pool_acquire(self._h, block, _stream(stream), C.byref(dev)))
+        return dev.value
+
+    def release(self, block: int, stream=None) -> None:
+        _check(_lib.stream_pool_release(self._h, block, _stream(stream)))
+
+    def stats(self) -> dict:
+        s = PoolStats()
+        _check(_lib.stream_pool_stats(self._h, C.byref(s)))
+        return {f: getattr(s, f) for f, _ in PoolStats._fields_}
+
+    def slot_block(self, slot: int) -> int:
+        b = C.c_int()
+        _check(_lib.stream_pool_slot_block(self._h, slot, C.byref(b)))
+        return b.value
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _check(_lib.stream_pool_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,134 @@
+"""GPU NF4-LoRA linear (forward and backward) vs the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic_inputs as S
+from helpers import bits_of, check_bf16_output, check_f32_output, f32_of, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _prepare(lib, case, r):
+    """Quantise W on the oracle side (the oracle's codes are the GEMM's input)."""
+    w32 = O.bf16_bits_to_f64(case["W"]).astype(np.float32)
+    codes, absmax = O.quantize(w32)
+    wq = O.dequantize(codes, absmax)
+    dev = {
+        "codes": torch.from_numpy(codes).cuda(), "absmax": torch.from_numpy(absmax).cuda(),
+        "x": to_dev_bf16(case["x"]), "dY": to_dev_bf16(case["dY"]),
+        "A": to_dev_bf16(case["A"]) if r else None, "B": to_dev_bf16(case["B"]) if r else None,
+    }
+    return wq, dev
+
+
+def _run(lib, dev, alpha, need_dx=True):
+    y, u = lib.lora_linear_fwd(dev["codes"], dev["absmax"], dev["x"], dev["A"], dev["B"], alpha)
+    dx, da, db = lib.lora_linear_bwd(dev["codes"], dev["absmax"], dev["x"], u, dev["dY"], dev["A"], dev["B"],
+                                     alpha, need_dx=need_dx)
+    torch.cuda.synchronize()
+    return y, u, dx, da, db
+
+
+def _check_case(lib, t, n, k, r, alpha=32.0, seed=42, b_std=0.01):
+    case = S.linear_case(t, n, k, r=max(r, 1), seed=seed, b_std=b_std)
+    if r == 0:
+        case["A"] = np.zeros((0, k), np.uint16)
+        case["B"] = np.zeros((n, 0), np.uint16)
+    wq, dev = _prepare(lib, case, r)
+    y, u, dx, da, db = _run(lib, dev, alpha)
+    y_ref, u_ref = O.lora_linear_fwd(case["x"], wq, case["A"], case["B"], alpha)
+    dx_ref, da_ref, db_ref = O.lora_linear_bwd(case["x"], wq, case["A"], case["B"], alpha, case["dY"])
+    check_bf16_output(bits_of(y), y_ref, f"y {t}x{n}x{k} r{r}")
+    check_bf16_output(bits_of(dx), dx_ref, f"dX {t}x{n}x{k} r{r}")
+    if r:
+        check_f32_output(f32_of(u), u_ref, "u")
+        check_f32_output(f32_of(da), da_ref, "dA")
+        check_f32_output(f32_of(db), db_ref, "dB")
+    return y, dx, da, db
+
+
+def test_single_linear_workload(gpu_lib):
+    """in = out = 1024, 256 tokens, r = 16, alpha = 32: fwd + bwd (dX, dA, dB)."""
+    _check_case(gpu_lib, 256, 1024, 1024, 16)
+
+
+@pytest.mark.parametrize("t,n,k,r", [
+    (300, 400, 640, 16),     # several tiles and ragged tails in every dimension
+    (1, 128, 256, 16),       # one token
+    (17, 48, 64, 8),         # rank not a multiple of 16, one K block
+    (130, 272, 320, 48),     # rank 48
+    (64, 256, 1024, 64),     # maximum rank
+    (200, 512, 3584, 16),    # skinny N with split-K (k/v-like)
+    (96, 3584, 512, 16),     # long N, short K
+    (513, 160, 192, 16),     # T one past a tile boundary
+])
+def test_shapes(gpu_lib, t, n, k, r):
+    _check_case(gpu_lib, t, n, k, r)
+
+
+def test_base_only_rank0(gpu_lib):
+    _check_case(gpu_lib, 100, 256, 512, 0)
+
+
+def test_b_zero_equals_base_only(gpu_lib):
+    t, n, k = 130, 384, 512
+    case = S.linear_case(t, n, k)
+    case["B"] = np.zeros_like(case["B"])
+    wq, dev = _prepare(gpu_lib, case, 16)
+    y_lora, _ = gpu_lib.lora_linear_fwd(dev["codes"], dev["absmax"], dev["x"], dev["A"], dev["B"], 32.0)
+    y_base, _ = gpu_lib.lora_linear_fwd(dev["codes"], dev["absmax"], dev["x"], None, None, 32.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y_lora, y_base)
+
+
+def test_integer_exact_case(gpu_lib):
+    """Codes in {0, 7, 15} with absmax 2^e and small integers elsewhere: every
+    partial sum is exact in fp32, so the GPU output must be exactly the oracle's
+    value rounded once to bf16 (fp32 outputs must equal it exactly)."""
+    rng = np.random.default_rng(5)
+    t, n, k, r = 96, 160, 256, 16
+    codes = rng.choice([0, 7, 15], size=(n, k)).astype(np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    absmax = np.full((n, k // 64), 0.125, np.float32)
+    wq = O.dequantize(packed, absmax)
+    ints = lambda shape, lo, hi: S.to_bf16_bits(rng.integers(lo, hi + 1, size=shape).astype(np.float32))
+    x, a, b, dy = ints((t, k), -2, 2), ints((r, k), -1, 1), ints((n, r), -1, 1), ints((t, n), -2, 2)
+    alpha = 1.0 * r / 8.0                                                  # s = 0.125
+    dev = {"codes": torch.from_numpy(packed).cuda(), "absmax": torch.from_numpy(absmax).cuda(),
+           "x": to_dev_bf16(x), "dY": to_dev_bf16(dy), "A": to_dev_bf16(a), "B": to_dev_bf16(b)}
+    y, u, dx, da, db = _run(gpu_lib, dev, alpha)
+    y_ref, u_ref = O.lora_linear_fwd(x, wq, a, b, alpha)
+    dx_ref, da_ref, db_ref = O.lora_linear_bwd(x, wq, a, b, alpha, dy)
+    # every partial sum is exact in fp32, so the single rounding to bf16 is the only one
+    for ref in (y_ref, dx_ref, u_ref, da_ref, db_ref):
+        assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
+    assert np.array_equal(bits_of(y), O.f32_to_bf16_bits(y_ref.astype(np.float32)))
+    assert np.array_equal(bits_of(dx), O.f32_to_bf16_bits(dx_ref.astype(np.float32)))
+    assert np.array_equal(f32_of(u).astype(np.float64), u_ref)
+    assert np.array_equal(f32_of(da).astype(np.float64), da_ref)
+    assert np.array_equal(f32_of(db).astype(np.float64), db_ref)
+
+
+def test_repeat_is_bitwise_identical(gpu_lib):
+    case = S.linear_case(512, 3584, 3584, proj="q")
+    _, dev = _prepare(gpu_lib, case, 16)
+    a = _run(gpu_lib, dev, 32.0)
+    b = _run(gpu_lib, dev, 32.0)
+    for p, q in zip(a, b):
+        assert torch.equal(p, q)
+
+
+def test_dx_can_be_skipped(gpu_lib):
+    case = S.linear_case(64, 256, 256)
+    wq, dev = _prepare(gpu_lib, case, 16)
+    y, u = gpu_lib.lora_linear_fwd(dev["codes"], dev["absmax"], dev["x"], dev["A"], dev["B"], 32.0)
+    dx, da, db = gpu_lib.lora_linear_bwd(dev["codes"], dev["absmax"], dev["x"], u, dev["dY"], dev["A"], dev["B"],
+                                         32.0, need_dx=False)
+    torch.cuda.synchronize()
+    assert dx is None
+    _, da_ref, db_ref = O.lora_linear_bwd(case["x"], wq, case["A"], case["B"], 32.0, case["dY"])
+    check_f32_output(f32_of(da), da_ref, "dA")
+    check_f32_output(f32_of(db), db_ref, "dB")
