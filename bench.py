@@ -1,0 +1,242 @@
+"""Throughput of the NF4-LoRA linear hot path on one MI355X.
+
+A step is one forward + backward pass of every projection of one Qwen2.5-7B-
+shaped layer (q 3584x3584, k/v 512x3584, o 3584x3584, gate/up 18944x3584,
+down 3584x18944; N x K), 512 tokens, LoRA rank 16, alpha 32, fully resident:
+per projection the fused u = x.A^T + dequant-GEMM + LoRA forward, and the
+backward g/dB pre-pass + dequant-GEMM dX + dA. x is shared by q/k/v and by
+gate/up as in a real layer; dY is independent per projection. Inputs are
+seeded synthetic data; the NF4 base is quantised by the library before timing.
+
+Prints ONE JSON line (metric, value in tokens/s, TFLOP/s, the roofline of the
+dominant kernel measured with HIP events on its own stream, and the fp64 CPU
+oracle timed on a bounded sample of the same workload).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+T_TOKENS = 512
+RANK = 16
+ALPHA = 32.0
+HIDDEN, QW, KVW, INTER = 3584, 3584, 512, 18944
+PROJ = [("q", QW, HIDDEN, "x1"), ("k", KVW, HIDDEN, "x1"), ("v", KVW, HIDDEN, "x1"), ("o", HIDDEN, QW, "x2"),
+        ("gate", INTER, HIDDEN, "x3"), ("up", INTER, HIDDEN, "x3"), ("down", HIDDEN, INTER, "x4")]
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0
+METRIC = "NF4-LoRA linear fwd+bwd tokens/s & TFLOP/s; % of MFMA/HBM/PCIe roofline"
+
+
+def step_flops(t: int, r: int) -> float:
+    """Algorithmic FLOPs of one step: per projection 4TNK (base fwd + dX) + 6Tr(N+K) (LoRA)."""
+    return float(sum(4 * t * n * k + 6 * t * r * (n + k) for _, n, k, _ in PROJ))
+
+
+class HipEvents:
+    """hipEvent_t pairs through the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self):
+        self.hip = C.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self) -> int:
+        e = C.c_void_p()
+        assert self.hip.hipEventCreate(C.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        assert self.hip.hipEventSynchronize(C.c_void_p(b)) == 0
+        ms = C.c_float()
+        assert self.hip.hipEventElapsedTime(C.byref(ms), C.c_void_p(a), C.c_void_p(b)) == 0
+        return float(ms.value)
+
+    def destroy(self, e: int) -> None:
+        self.hip.hipEventDestroy(C.c_void_p(e))
+
+
+def build_layer(lib, torch, seed: int = 42):
+    """Synthetic layer on the GPU: W ~ N(0, 0.02) bf16 -> NF4; x, dY ~ N(0, 1); A ~ U(+-1/sqrt(K)); B ~ N(0, 0.01)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    dev = "cuda"
+    acts = {
+        "x1": torch.randn(T_TOKENS, HIDDEN, generator=g, device=dev).to(torch.bfloat16),
+        "x2": torch.randn(T_TOKENS, QW, generator=g, device=dev).to(torch.bfloat16),
+        "x3": torch.randn(T_TOKENS, HIDDEN, generator=g, device=dev).to(torch.bfloat16),
+        "x4": torch.randn(T_TOKENS, INTER, generator=g, device=dev).to(torch.bfloat16),
+    }
+    layer = {}
+    for name, n, k, xin in PROJ:
+        w = (torch.randn(n, k, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        codes, absmax = lib.quantize(w)
+        del w
+        a = ((torch.rand(RANK, k, generator=g, device=dev) * 2 - 1) / k ** 0.5).to(torch.bfloat16)
+        b = (torch.randn(n, RANK, generator=g, device=dev) * 0.01).to(torch.bfloat16)
+        p = {
+            "n": n, "k": k, "codes": codes, "absmax": absmax, "A": a, "B": b, "x": acts[xin],
+            "dy": torch.randn(T_TOKENS, n, generator=g, device=dev).to(torch.bfloat16),
+            "y": torch.empty(T_TOKENS, n, dtype=torch.bfloat16, device=dev),
+            "u": torch.empty(T_TOKENS, RANK, dtype=torch.float32, device=dev),
+            "dx": torch.empty(T_TOKENS, k, dtype=torch.bfloat16, device=dev),
+            "dA": torch.empty(RANK, k, dtype=torch.float32, device=dev),
+            "dB": torch.empty(n, RANK, dtype=torch.float32, device=dev),
+            "wsf": lib.workspace(lib.fwd_workspace_bytes(T_TOKENS, n, k, RANK)),
+            "wsb": lib.workspace(lib.bwd_workspace_bytes(T_TOKENS, n, k, RANK)),
+        }
+        layer[name] = p
+    torch.cuda.synchronize()
+    return layer
+
+
+def run_step(lib, layer, prof=None):
+    """Forward of all 7 projections, then backward in reverse order. `prof` =
+    (name, start, stop) records events around that projection's forward GEMM."""
+    for name, *_ in PROJ:
+        p = layer[name]
+        if prof is not None and prof[0] == name:
+            lib.profile_next_gemm(prof[1], prof[2])
+        lib.lora_linear_fwd(p["codes"], p["absmax"], p["x"], p["A"], p["B"], ALPHA, y=p["y"], u=p["u"], ws=p["wsf"])
+    for name, *_ in reversed(PROJ):
+        p = layer[name]
+        lib.lora_linear_bwd(p["codes"], p["absmax"], p["x"], p["u"], p["dy"], p["A"], p["B"], ALPHA, dx=p["dx"],
+                            dA=p["dA"], dB=p["dB"], ws=p["wsb"])
+
+
+def cpu_baseline(seconds_budget: float = 12.0) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    the q projection (3584 x 3584) of the layer with all 512 tokens - dequantise
+    + forward + backward - repeated for about `seconds_budget` seconds, scaled
+    to the whole layer by the algorithmic-FLOP ratio. Quantisation (load time)
+    is outside the timed region, as on the GPU."""
+    import numpy as np
+
+    import oracle as O
+    import synthetic_inputs as S
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = 1
+    n, k = QW, HIDDEN
+    case = S.linear_case(T_TOKENS, n, k, r=RANK, proj="q")
+    codes, absmax = O.quantize(S.bf16_bits_to_f32(case["W"]))
+    reps = 0
+    t0 = time.perf_counter()
+    while reps < 3 or time.perf_counter() - t0 < seconds_budget:
+        wq = O.dequantize(codes, absmax)
+        O.lora_linear_fwd(case["x"], wq, case["A"], case["B"], ALPHA)
+        O.lora_linear_bwd(case["x"], wq, case["A"], case["B"], ALPHA, case["dY"])
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
+    sample_flops = 4 * T_TOKENS * n * k + 6 * T_TOKENS * RANK * (n + k)
+    layer_seconds = dt * step_flops(T_TOKENS, RANK) / sample_flops
+    return {
+        "value": round(T_TOKENS / layer_seconds, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"q projection 3584x3584, 512 tokens, r16: dequantise + fwd + bwd in fp64 numpy, "
+                   f"{dt:.2f} s per pass (mean of {reps}); "
+                   f"scaled to the 7-projection layer by algorithmic FLOPs ({step_flops(T_TOKENS, RANK) / sample_flops:.2f}x)"),
+        "gflops": round(sample_flops / dt / 1e9, 3),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "
+              "how it would shard is described in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from nf4_weight_streamed_amd import lib
+
+    torch.cuda.set_device(0)
+    layer = build_layer(lib, torch)
+    ev = HipEvents()
+    for _ in range(args.warmup):
+        run_step(lib, layer)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronized on both sides; the gate forward
+    # GEMM of every step is bracketed by HIP events on the stream it runs on
+    starts = [ev.create() for _ in range(args.steps)]
+    stops = [ev.create() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(lib, layer, prof=("gate", starts[i], stops[i]))
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gemm_ms = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
+    for e in starts + stops:
+        ev.destroy(e)
+
+    ms = dt * 1000.0 / args.steps
+    tokens_per_s = T_TOKENS / (dt / args.steps)
+    tflops = step_flops(T_TOKENS, RANK) / (dt / args.steps) / 1e12
+    n, k = INTER, HIDDEN
+    gate_flops = 2.0 * T_TOKENS * n * k + 2.0 * T_TOKENS * n * RANK
+    gate_bytes = n * k * 0.5 + n * (k // 64) * 4 + T_TOKENS * k * 2 + T_TOKENS * n * 2 + T_TOKENS * RANK * 4 + n * RANK * 2
+    avg_gemm_s = sum(gemm_ms) / len(gemm_ms) / 1000.0
+    achieved = gate_flops / avg_gemm_s / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen2.5-7b-shaped layer, 7 NF4-LoRA projections, fwd+bwd, resident",
+            "tokens": T_TOKENS, "lora_rank": RANK, "lora_alpha": ALPHA, "nf4_blocksize": 64,
+            "projections_NxK": {name: [n_, k_] for name, n_, k_, _ in PROJ},
+        },
+        "tflops": round(tflops, 2),
+        "mfma_frac_step": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {
+            "kernel": "k_nf4_gemm_fwd (gate projection 18944x3584, 512 tokens, LoRA epilogue)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_gemm_s * 1e6, 2),
+            "algorithmic_flops_per_launch": gate_flops,
+            "algorithmic_bytes_per_launch": gate_bytes,
+            "hbm_gbs_algorithmic": round(gate_bytes / avg_gemm_s / 1e9, 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -145,6 +145,17 @@ int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, in
                         uint16_t* dx, float* dA, float* dB,
                         void* ws, size_t ws_bytes, nf4_stream stream);
 
+/*
+ * Instrumentation for measurement: the next nf4_lora_linear_fwd or
+ * nf4_lora_linear_bwd call made by this host thread records `start` (a
+ * hipEvent_t) on its stream immediately before launching its fused
+ * dequantise-GEMM kernel and `stop` immediately after it, so
+ * hipEventElapsedTime(start, stop) is that one kernel's device time (the
+ * small LoRA kernels and any split-K reduction fall outside). The request is
+ * consumed by that call. Passing NULL for both cancels a pending request.
+ */
+int nf4_profile_next_gemm(void* start_event, void* stop_event);
+
 /* ------------------------------------------------------------------ stream pool
  * Blockwise residency of the frozen base ([hn] main comment; [api]
  * "patch_hf_model" Behavior 5-6; [consumer] "What you need besides VRAM",

@@ -78,6 +78,20 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
+namespace {
+thread_local hipEvent_t g_prof_start = nullptr;
+thread_local hipEvent_t g_prof_stop = nullptr;
+}  // namespace
+
+void prof_gemm_begin(hipStream_t stream) {
+    if (g_prof_start) (void)hipEventRecord(g_prof_start, stream);
+}
+
+void prof_gemm_end(hipStream_t stream) {
+    if (g_prof_stop) (void)hipEventRecord(g_prof_stop, stream);
+    g_prof_start = g_prof_stop = nullptr;
+}
+
 int check_launch(const char* what) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(NF4_E_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -125,6 +139,14 @@ extern "C" {
 const char* nf4_last_error(void) { return g_error.c_str(); }
 
 int nf4_abi_version(void) { return 1; }
+
+int nf4_profile_next_gemm(void* start_event, void* stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(NF4_E_ARG, "nf4_profile_next_gemm: pass both events or neither");
+    g_prof_start = static_cast<hipEvent_t>(start_event);
+    g_prof_stop = static_cast<hipEvent_t>(stop_event);
+    return NF4_OK;
+}
 
 int nf4_codebook(float levels_out[16]) {
     if (!levels_out) return fail(NF4_E_ARG, "nf4_codebook: NULL output");
@@ -174,8 +196,8 @@ int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, in
     if (T == 0) return NF4_OK;
     if (!x || !y) return fail(NF4_E_ARG, "%s: x/y must not be NULL", fn);
     if (r > 0 && (!A || !B || !u_save)) return fail(NF4_E_ARG, "%s: r=%d needs A, B and u_save", fn, r);
-    if (!aligned(x, 16) || !aligned(y, 2) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || !aligned(u_save, 4))))
-        return fail(NF4_E_ARG, "%s: misaligned pointer (x and A need 16 bytes)", fn);
+    if (!aligned(x, 16) || !aligned(y, 16) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || !aligned(u_save, 4))))
+        return fail(NF4_E_ARG, "%s: misaligned pointer (x, y and A need 16 bytes)", fn);
     const FwdPlan p = plan_fwd(T, N, K, r);
     if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned(ws, 256)))
         return fail(NF4_E_ARG, "%s: workspace of %zu bytes (256-byte aligned) needed for T=%lld N=%lld K=%lld r=%d, got %zu",
@@ -208,10 +230,10 @@ int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, in
     if (!dy) return fail(NF4_E_ARG, "%s: dy must not be NULL", fn);
     if (r > 0 && (!x || !u_save || !A || !B || !dA || !dB))
         return fail(NF4_E_ARG, "%s: r=%d needs x, u_save, A, B, dA and dB", fn, r);
-    if (!aligned(dy, 16) || (dx && !aligned(dx, 2)) ||
-        (r > 0 && (!aligned(x, 16) || !aligned(A, 2) || !aligned(B, 2) || !aligned(u_save, 4) || !aligned(dA, 4) ||
+    if (!aligned(dy, 16) || (dx && !aligned(dx, 16)) ||
+        (r > 0 && (!aligned(x, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(u_save, 4) || !aligned(dA, 4) ||
                    !aligned(dB, 4))))
-        return fail(NF4_E_ARG, "%s: misaligned pointer (dy and x need 16 bytes)", fn);
+        return fail(NF4_E_ARG, "%s: misaligned pointer (dy, dx, x and A need 16 bytes)", fn);
     const BwdPlan p = plan_bwd(T, N, K, r);
     if (!ws || ws_bytes < p.ws_bytes || !aligned(ws, 256))
         return fail(NF4_E_ARG, "%s: workspace of %zu bytes (256-byte aligned) needed for T=%lld N=%lld K=%lld r=%d, got %zu",

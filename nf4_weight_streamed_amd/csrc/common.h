@@ -67,7 +67,23 @@ hipError_t launch_gemm_bwd_dx(const BwdPlan& p, const uint8_t* codes, const floa
 hipError_t launch_lora_da(const BwdPlan& p, const uint16_t* x, int64_t T, int64_t K, int r, float s, float* dA,
                           void* ws, hipStream_t stream);
 
+// Instrumentation events around the next fused GEMM launch (abi.cpp); no-ops unless requested.
+void prof_gemm_begin(hipStream_t stream);
+void prof_gemm_end(hipStream_t stream);
+
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split count for a GEMM with `tiles` output tiles and `steps` reduction steps: the
+// GEMM kernels run two workgroups per CU, so up to 2 * 256 workgroups run in one
+// round; a grid just above that leaves a nearly empty second round. Split only
+// shapes with fewer than 256 tiles, up to 512 workgroups, >= min_steps steps each.
+inline int64_t pick_splits(int64_t tiles, int64_t steps, int64_t min_steps) {
+    constexpr int64_t kSlots = 512;
+    if (tiles >= kSlots / 2) return 1;
+    int64_t s = kSlots / tiles;
+    s = std::min<int64_t>(s, std::max<int64_t>(1, steps / min_steps));
+    return std::max<int64_t>(1, s);
+}
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 }  // namespace nf4

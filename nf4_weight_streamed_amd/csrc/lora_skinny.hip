@@ -71,14 +71,20 @@ __global__ __launch_bounds__(kThreads) void k_lora_down_partial(const uint16_t* 
     }
 }
 
-// out[i] = sum_{z < parts} part[z * stride + i], z increasing
+// out[i] = sum over z < parts of part[z * stride + i]: 64 outputs per workgroup; thread
+// group q (of 4) adds parts z = q, q+4, ... in increasing z, then the four group sums
+// are added in group order. The order depends on `parts` only, never on timing.
 __global__ __launch_bounds__(kThreads) void k_sum_parts(const float* __restrict__ part, int parts, int64_t stride,
                                                         int64_t count, float* __restrict__ out) {
-    const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-    if (i >= count) return;
+    __shared__ float red[4][64];
+    const int o = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int64_t i = int64_t(blockIdx.x) * 64 + o;
     float v = 0.0f;
-    for (int z = 0; z < parts; ++z) v += part[size_t(z) * stride + i];
-    out[i] = v;
+    if (i < count)
+        for (int z = q; z < parts; z += 4) v += part[size_t(z) * stride + i];
+    red[q][o] = v;
+    __syncthreads();
+    if (q == 0 && i < count) out[i] = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
 }
 
 // ---------------------------------------------------------------- g and dB in one pass over dY
@@ -256,7 +262,7 @@ hipError_t launch_lora_down(const uint16_t* x, const uint16_t* A, int64_t T, int
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const int64_t count = T * r;
-    hipLaunchKernelGGL(k_sum_parts, dim3(unsigned(cdiv(count, kThreads))), dim3(kThreads), 0, stream, upart, splits,
+    hipLaunchKernelGGL(k_sum_parts, dim3(unsigned(cdiv(count, 64))), dim3(kThreads), 0, stream, upart, splits,
                        count, count, u);
     return hipGetLastError();
 }
@@ -270,7 +276,7 @@ hipError_t launch_lora_bwd_pre(const BwdPlan& p, const uint16_t* dy, const uint1
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t count = T * r;
-    hipLaunchKernelGGL(k_sum_parts, dim3(unsigned(cdiv(count, kThreads))), dim3(kThreads), 0, stream, gpart,
+    hipLaunchKernelGGL(k_sum_parts, dim3(unsigned(cdiv(count, 64))), dim3(kThreads), 0, stream, gpart,
                        p.nslab, count, count, g);
     return hipGetLastError();
 }

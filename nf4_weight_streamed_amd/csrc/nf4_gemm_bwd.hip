@@ -7,7 +7,10 @@
 // streaming the frozen base, main comment). The contraction runs over N, the
 // rows of W, while the codes are contiguous along K: each thread dequantises a
 // 4 (n) x 8 (k) patch and packs bf16 pairs across rows, so the tile lands in LDS
-// as [k][n] and the MFMA B operand is again a contiguous 16-byte read.
+// as [k][n] and the MFMA B operand is again a contiguous 16-byte read. The 16-byte
+// chunks of each LDS row are XOR-swizzled by (k / 8) % 8: the 8-byte transposed
+// stores of a wave then spread over all banks, and the fragment reads (8
+// consecutive rows share one swizzle) stay conflict-free.
 #include "common.h"
 #include "device.h"
 
@@ -91,10 +94,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[i][e] = sLut[(rc[i] >> (4 * e)) & 15] * rs[i];
+        // row k = 8*pc + e holds n = 4*pr .. 4*pr+3: chunk pr/2 (swizzled by pc), half pr&1
+        const int col = (((pr >> 1) ^ (pc & 7)) << 3) + 4 * (pr & 1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             u32x2 o = {pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e])};
-            *reinterpret_cast<u32x2*>(sWt + (8 * pc + e) * kLds + 4 * pr) = o;
+            *reinterpret_cast<u32x2*>(sWt + (8 * pc + e) * kLds + col) = o;
         }
     };
 
@@ -125,9 +130,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
                     af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
                         sA + (wm * WM + 32 * i + frag_row) * kLds + kk * 16 + frag_k));
 #pragma unroll
-                for (int j = 0; j < FK; ++j)
-                    bw[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                        sWt + (wk * WK + 32 * j + frag_row) * kLds + kk * 16 + frag_k));
+                for (int j = 0; j < FK; ++j) {
+                    const int row = wk * WK + 32 * j + frag_row;
+                    const int chunk = (2 * kk + (lane >> 5)) ^ ((row >> 3) & 7);
+                    bw[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(sWt + row * kLds + chunk * 8));
+                }
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -202,20 +209,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
             }
 }
 
-// dX = RNbf( sum_z partial[z] + s . g . A ), z in increasing order; one thread per output.
+// dX = RNbf( sum_z partial[z] + s . g . A ), z in increasing order; four consecutive
+// outputs of one row per thread (K % 64 == 0), float4 partial loads.
 __global__ __launch_bounds__(256) void k_bwd_split_reduce(const float* __restrict__ partial, int splits, int T,
                                                           int K, const float* __restrict__ g,
                                                           const uint16_t* __restrict__ A, int r, float s,
                                                           uint16_t* __restrict__ dx) {
-    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
     const int64_t total = int64_t(T) * K;
-    if (idx >= total) return;
+    if (q * 4 >= total) return;
+    const int64_t idx = q * 4;
     const int row = int(idx / K), col = int(idx % K);
-    float acc = 0.0f;
-    for (int z = 0; z < splits; ++z) acc += partial[size_t(z) * total + idx];
-    float lora = 0.0f;
-    for (int j = 0; j < r; ++j) lora += g[size_t(row) * r + j] * bf16_to_f32(A[size_t(j) * K + col]);
-    dx[idx] = bf16_bits(acc + s * lora);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(partial + size_t(z) * total + idx);
+    f32x4 lora = {0.f, 0.f, 0.f, 0.f};
+    const float* gr = g + size_t(row) * r;
+#pragma unroll 4
+    for (int j = 0; j < r; ++j) {
+        const float gj = gr[j];
+        const u32x2 a4 = *reinterpret_cast<const u32x2*>(A + size_t(j) * K + col);
+        lora[0] += gj * __uint_as_float(a4[0] << 16);
+        lora[1] += gj * __uint_as_float(a4[0] & 0xFFFF0000u);
+        lora[2] += gj * __uint_as_float(a4[1] << 16);
+        lora[3] += gj * __uint_as_float(a4[1] & 0xFFFF0000u);
+    }
+    u32x2 o = {pack_bf16x2(acc[0] + s * lora[0], acc[1] + s * lora[1]),
+               pack_bf16x2(acc[2] + s * lora[2], acc[3] + s * lora[3])};
+    *reinterpret_cast<u32x2*>(dx + idx) = o;
 }
 
 }  // namespace
@@ -226,11 +246,7 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r) {
     p.bn = 128;
     const int64_t tiles = cdiv(T, p.bm) * cdiv(K, p.bn);
     const int64_t nsteps = cdiv(N, kBN);
-    int64_t splits = 1;
-    if (tiles < 512) {
-        splits = cdiv(512, tiles);
-        splits = std::min<int64_t>(splits, std::max<int64_t>(1, nsteps / 8));
-    }
+    const int64_t splits = pick_splits(tiles, nsteps, 4);
     p.steps_per_split = int(cdiv(nsteps, splits));
     p.splits = int(cdiv(nsteps, p.steps_per_split));
     p.nslab = int(cdiv(N, 64));
@@ -251,12 +267,14 @@ hipError_t launch_gemm_bwd_dx(const BwdPlan& p, const uint8_t* codes, const floa
     const dim3 grid(unsigned(cdiv(K, p.bn)), unsigned(cdiv(T, p.bm)), unsigned(p.splits));
     const float* g = reinterpret_cast<const float*>(static_cast<char*>(ws) + p.off_g);
     float* partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_dx) : nullptr;
+    prof_gemm_begin(stream);
     hipLaunchKernelGGL((k_nf4_gemm_bwd_dx<128, 128>), grid, dim3(kThreads), 0, stream, dy, codes, absmax, g, A,
                        int(T), int(N), int(K), r, s, p.steps_per_split, dx, partial, tables());
+    prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t total = T * K;
-    hipLaunchKernelGGL(k_bwd_split_reduce, dim3(unsigned(cdiv(total, 256))), dim3(256), 0, stream, partial,
+    hipLaunchKernelGGL(k_bwd_split_reduce, dim3(unsigned(cdiv(total / 4, 256))), dim3(256), 0, stream, partial,
                        p.splits, int(T), int(K), g, A, r, s, dx);
     return hipGetLastError();
 }

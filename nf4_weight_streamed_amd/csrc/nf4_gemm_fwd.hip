@@ -217,20 +217,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_fwd(
             }
 }
 
-// y = RNbf( sum_z partial[z] + s . u . B^T ), z in increasing order; one thread per output.
+// y = RNbf( sum_z partial[z] + s . u . B^T ), z in increasing order; four consecutive
+// outputs of one row per thread (N % 16 == 0), float4 partial loads.
 __global__ __launch_bounds__(256) void k_fwd_split_reduce(const float* __restrict__ partial, int splits, int T,
                                                           int N, const float* __restrict__ u,
                                                           const uint16_t* __restrict__ B, int r, float s,
                                                           uint16_t* __restrict__ y) {
-    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
     const int64_t total = int64_t(T) * N;
-    if (idx >= total) return;
+    if (q * 4 >= total) return;
+    const int64_t idx = q * 4;
     const int row = int(idx / N), col = int(idx % N);
-    float acc = 0.0f;
-    for (int z = 0; z < splits; ++z) acc += partial[size_t(z) * total + idx];
-    float lora = 0.0f;
-    for (int j = 0; j < r; ++j) lora += u[size_t(row) * r + j] * bf16_to_f32(B[size_t(col) * r + j]);
-    y[idx] = bf16_bits(acc + s * lora);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(partial + size_t(z) * total + idx);
+    f32x4 lora = {0.f, 0.f, 0.f, 0.f};
+    const float* ur = u + size_t(row) * r;
+    const uint16_t* br = B + size_t(col) * r;
+#pragma unroll 4
+    for (int j = 0; j < r; ++j) {
+        const float uj = ur[j];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lora[c] += uj * bf16_to_f32(br[size_t(c) * r + j]);
+    }
+    u32x2 o = {pack_bf16x2(acc[0] + s * lora[0], acc[1] + s * lora[1]),
+               pack_bf16x2(acc[2] + s * lora[2], acc[3] + s * lora[3])};
+    *reinterpret_cast<u32x2*>(y + idx) = o;
 }
 
 }  // namespace
@@ -241,11 +252,7 @@ FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r) {
     p.bn = 128;
     const int64_t tiles = cdiv(T, p.bm) * cdiv(N, p.bn);
     const int64_t ksteps = K / kBK;
-    int64_t splits = 1;
-    if (tiles < 512) {
-        splits = cdiv(512, tiles);
-        splits = std::min<int64_t>(splits, std::max<int64_t>(1, ksteps / 8));
-    }
+    const int64_t splits = pick_splits(tiles, ksteps, 4);
     p.steps_per_split = int(cdiv(ksteps, splits));
     p.splits = int(cdiv(ksteps, p.steps_per_split));
     // u = x.A^T: 16-token blocks; split K until there are about 512 workgroups
@@ -267,12 +274,14 @@ hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* 
                            uint16_t* y, void* ws, hipStream_t stream) {
     const dim3 grid(unsigned(cdiv(N, p.bn)), unsigned(cdiv(T, p.bm)), unsigned(p.splits));
     float* partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ypart) : nullptr;
+    prof_gemm_begin(stream);
     hipLaunchKernelGGL((k_nf4_gemm_fwd<128, 128>), grid, dim3(kThreads), 0, stream, x, codes, absmax, u, B, int(T),
                        int(N), int(K), r, s, p.steps_per_split, y, partial, tables());
+    prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t total = T * N;
-    hipLaunchKernelGGL(k_fwd_split_reduce, dim3(unsigned(cdiv(total, 256))), dim3(256), 0, stream, partial,
+    hipLaunchKernelGGL(k_fwd_split_reduce, dim3(unsigned(cdiv(total / 4, 256))), dim3(256), 0, stream, partial,
                        p.splits, int(T), int(N), u, B, r, s, y);
     return hipGetLastError();
 }

@@ -56,6 +56,7 @@ def _load() -> C.CDLL:
         "nf4_lora_linear_fwd": (i32, [vp, vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "nf4_lora_linear_bwd_workspace": (sz, [i64, i64, i64, i32]),
         "nf4_lora_linear_bwd": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
+        "nf4_profile_next_gemm": (i32, [vp, vp]),
         "stream_pool_create": (i32, [C.POINTER(HostBlock), i32, vp, sz, i32, vp, C.POINTER(vp)]),
         "stream_pool_prefetch": (i32, [vp, i32]),
         "stream_pool_acquire": (i32, [vp, i32, vp, C.POINTER(vp)]),
@@ -113,6 +114,11 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple) -> None:
 
 def abi_version() -> int:
     return _lib.nf4_abi_version()
+
+
+def profile_next_gemm(start_event, stop_event) -> None:
+    """Record two hipEvent_t handles (ints) around the next call's fused GEMM kernel."""
+    _check(_lib.nf4_profile_next_gemm(C.c_void_p(start_event), C.c_void_p(stop_event)))
 
 
 def codebook() -> list:
