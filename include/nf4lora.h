@@ -145,6 +145,46 @@ int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, in
                         uint16_t* dx, float* dA, float* dB,
                         void* ws, size_t ws_bytes, nf4_stream stream);
 
+/* ------------------------------------------------------------------ stack glue
+ * Elementwise/row kernels of the decoder stack that the streamed base feeds
+ * (attention mixing replaced by the identity): h' = h + o(repeat_kv(v(RMSNorm(h)))),
+ * h'' = h' + down(SiLU(gate(h_m)) * up(h_m)), h_m = RMSNorm(h'). Tensors are
+ * device bf16, row-major, 2-byte aligned; math is fp32 with one bf16 rounding per
+ * output; row reductions use a fixed order. Activations are bf16 because that is
+ * the model dtype (Poros API reference, "PorosModel.from_pretrained", torch_dtype
+ * bfloat16). T == 0 / n == 0 is a no-op.
+ */
+
+/* out = RNbf(h * rstd) per row of [T][H], rstd = 1/sqrt(mean(h^2) + eps) (unit
+ * gain); rstd (fp32 [T], may be NULL) is saved for the backward. */
+int nf4_rmsnorm_fwd(const uint16_t* h, int64_t T, int64_t H, float eps, uint16_t* out, float* rstd,
+                    nf4_stream stream);
+
+/* dh = RNbf(dres + rstd*dy - rstd^3 * h * mean(dy*h)) per row; dres (the residual
+ * gradient, [T][H]) may be NULL. */
+int nf4_rmsnorm_bwd(const uint16_t* h, const float* rstd, const uint16_t* dy, const uint16_t* dres, int64_t T,
+                    int64_t H, uint16_t* dh, nf4_stream stream);
+
+/* out = RNbf(a + b + c) over n elements; c may be NULL. out may alias a or b. */
+int nf4_add_bf16(const uint16_t* a, const uint16_t* b, const uint16_t* c, int64_t n, uint16_t* out,
+                 nf4_stream stream);
+
+/* m = RNbf(SiLU(gate) * up), SiLU(z) = z / (1 + e^-z). */
+int nf4_silu_mul_fwd(const uint16_t* gate, const uint16_t* up, int64_t n, uint16_t* m, nf4_stream stream);
+
+/* dgate = RNbf(dm * up * SiLU'(gate)), dup = RNbf(dm * SiLU(gate)). */
+int nf4_silu_mul_bwd(const uint16_t* gate, const uint16_t* up, const uint16_t* dm, int64_t n, uint16_t* dgate,
+                     uint16_t* dup, nf4_stream stream);
+
+/* a [T][q] from v [T][kv]: each head_dim-wide kv head serves q/kv consecutive
+ * query heads (head_dim | kv | q). */
+int nf4_repeat_kv_fwd(const uint16_t* v, int64_t T, int64_t q, int64_t kv, int64_t head_dim, uint16_t* a,
+                      nf4_stream stream);
+
+/* dv [T][kv] = RNbf(sum over the q/kv query heads of each kv head of da), in head order. */
+int nf4_repeat_kv_bwd(const uint16_t* da, int64_t T, int64_t q, int64_t kv, int64_t head_dim, uint16_t* dv,
+                      nf4_stream stream);
+
 /*
  * Instrumentation for measurement: the next nf4_lora_linear_fwd or
  * nf4_lora_linear_bwd call made by this host thread records `start` (a

@@ -57,6 +57,13 @@ def _load() -> C.CDLL:
         "nf4_lora_linear_bwd_workspace": (sz, [i64, i64, i64, i32]),
         "nf4_lora_linear_bwd": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "nf4_profile_next_gemm": (i32, [vp, vp]),
+        "nf4_rmsnorm_fwd": (i32, [vp, i64, i64, f32, vp, vp, vp]),
+        "nf4_rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, vp, vp]),
+        "nf4_add_bf16": (i32, [vp, vp, vp, i64, vp, vp]),
+        "nf4_silu_mul_fwd": (i32, [vp, vp, i64, vp, vp]),
+        "nf4_silu_mul_bwd": (i32, [vp, vp, vp, i64, vp, vp, vp]),
+        "nf4_repeat_kv_fwd": (i32, [vp, i64, i64, i64, i64, vp, vp]),
+        "nf4_repeat_kv_bwd": (i32, [vp, i64, i64, i64, i64, vp, vp]),
         "stream_pool_create": (i32, [C.POINTER(HostBlock), i32, vp, sz, i32, vp, C.POINTER(vp)]),
         "stream_pool_prefetch": (i32, [vp, i32]),
         "stream_pool_acquire": (i32, [vp, i32, vp, C.POINTER(vp)]),
@@ -232,6 +239,82 @@ def lora_linear_bwd(codes, absmax, x, u, dy, A, B, alpha: float, dx=None, dA=Non
                                     _ptr(B), r, float(alpha), _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes,
                                     _stream(stream)))
     return dx, dA, dB
+
+
+# ---------------------------------------------------------------- stack glue (bf16 device tensors)
+
+def _bf16_like(t, shape=None):
+    return torch.empty(shape if shape is not None else t.shape, dtype=torch.bfloat16, device=t.device)
+
+
+def rmsnorm_fwd(h, eps: float = 1e-6, out=None, rstd=None, stream=None):
+    t, hd = h.shape
+    _need(h, "h", torch.bfloat16, (t, hd))
+    out = _bf16_like(h) if out is None else out
+    rstd = torch.empty(t, dtype=torch.float32, device=h.device) if rstd is None else rstd
+    _need(out, "out", torch.bfloat16, (t, hd))
+    _need(rstd, "rstd", torch.float32, (t,))
+    _check(_lib.nf4_rmsnorm_fwd(_ptr(h), t, hd, float(eps), _ptr(out), _ptr(rstd), _stream(stream)))
+    return out, rstd
+
+
+def rmsnorm_bwd(h, rstd, dy, dres=None, out=None, stream=None):
+    t, hd = h.shape
+    _need(h, "h", torch.bfloat16, (t, hd))
+    _need(rstd, "rstd", torch.float32, (t,))
+    _need(dy, "dy", torch.bfloat16, (t, hd))
+    if dres is not None:
+        _need(dres, "dres", torch.bfloat16, (t, hd))
+    out = _bf16_like(h) if out is None else out
+    _need(out, "out", torch.bfloat16, (t, hd))
+    _check(_lib.nf4_rmsnorm_bwd(_ptr(h), _ptr(rstd), _ptr(dy), _ptr(dres), t, hd, _ptr(out), _stream(stream)))
+    return out
+
+
+def add_bf16(a, b, c=None, out=None, stream=None):
+    for name, t in (("a", a), ("b", b)) + ((("c", c),) if c is not None else ()):
+        _need(t, name, torch.bfloat16, tuple(a.shape))
+    out = _bf16_like(a) if out is None else out
+    _need(out, "out", torch.bfloat16, tuple(a.shape))
+    _check(_lib.nf4_add_bf16(_ptr(a), _ptr(b), _ptr(c), a.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def silu_mul_fwd(gate, up, out=None, stream=None):
+    _need(up, "up", torch.bfloat16, tuple(gate.shape))
+    _need(gate, "gate", torch.bfloat16, tuple(gate.shape))
+    out = _bf16_like(gate) if out is None else out
+    _need(out, "out", torch.bfloat16, tuple(gate.shape))
+    _check(_lib.nf4_silu_mul_fwd(_ptr(gate), _ptr(up), gate.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def silu_mul_bwd(gate, up, dm, dgate=None, dup=None, stream=None):
+    for name, t in (("gate", gate), ("up", up), ("dm", dm)):
+        _need(t, name, torch.bfloat16, tuple(gate.shape))
+    dgate = _bf16_like(gate) if dgate is None else dgate
+    dup = _bf16_like(gate) if dup is None else dup
+    _check(_lib.nf4_silu_mul_bwd(_ptr(gate), _ptr(up), _ptr(dm), gate.numel(), _ptr(dgate), _ptr(dup),
+                                 _stream(stream)))
+    return dgate, dup
+
+
+def repeat_kv_fwd(v, q: int, head_dim: int, out=None, stream=None):
+    t, kv = v.shape
+    _need(v, "v", torch.bfloat16, (t, kv))
+    out = _bf16_like(v, (t, q)) if out is None else out
+    _need(out, "out", torch.bfloat16, (t, q))
+    _check(_lib.nf4_repeat_kv_fwd(_ptr(v), t, q, kv, head_dim, _ptr(out), _stream(stream)))
+    return out
+
+
+def repeat_kv_bwd(da, kv: int, head_dim: int, out=None, stream=None):
+    t, q = da.shape
+    _need(da, "da", torch.bfloat16, (t, q))
+    out = _bf16_like(da, (t, kv)) if out is None else out
+    _need(out, "out", torch.bfloat16, (t, kv))
+    _check(_lib.nf4_repeat_kv_bwd(_ptr(da), t, q, kv, head_dim, _ptr(out), _stream(stream)))
+    return out
 
 
 class StreamPool:

@@ -1,0 +1,327 @@
+"""Blockwise weight-streamed stack of NF4-LoRA decoder layers on one GPU.
+
+The frozen NF4 base of `block_size` layers at a time lives in one pinned host
+slab per block ("Poros on consumer GPUs", "What you need besides VRAM": the
+streamed base is pinned host memory; Poros API reference, "patch_hf_model"
+Behavior 4-6: layers regrouped into blocks of block_size, default 4, under a
+block manager). In streamed mode the slabs pass through a pool of device slots:
+block b is acquired on the compute stream while block b+1 is prefetched on a
+dedicated copy stream (HN comment thread on streaming the frozen base, main
+comment: prefetched one ahead on a dedicated stream). In resident mode every
+block has its own slot and is copied once up front. Both modes run the same
+kernels on the same bytes at the same offsets, so their results are bitwise
+equal ("Poros on consumer GPUs", "OOM playbook": block_size never affects parity).
+
+Every computation is a call into libnf4lora.so; this module only orders the
+calls, owns buffers (torch allocations) and the two streams.
+
+Layer (attention mixing replaced by the identity): h_a = RMSNorm(h);
+q, k, v = L_q/L_k/L_v(h_a); a = repeat_kv(v); h' = h + L_o(a); h_m = RMSNorm(h');
+h'' = h' + L_down(SiLU(L_gate(h_m)) * L_up(h_m)). q and k are computed and
+receive a zero gradient.
+"""
+
+from __future__ import annotations
+
+import time
+from dataclasses import dataclass
+
+import torch
+
+from . import lib
+
+PROJS = ("q", "k", "v", "o", "gate", "up", "down")
+RMS_EPS = 1e-6
+
+
+@dataclass(frozen=True)
+class StackDims:
+    hidden: int
+    q: int
+    kv: int
+    inter: int
+    head_dim: int = 128
+
+    def shapes(self) -> dict:
+        """(N, K) of each projection."""
+        h, q, kv, i = self.hidden, self.q, self.kv, self.inter
+        return {"q": (q, h), "k": (kv, h), "v": (kv, h), "o": (h, q), "gate": (i, h), "up": (i, h), "down": (h, i)}
+
+    def layer_nf4_bytes(self) -> int:
+        return sum(n * k // 2 + n * (k // 64) * 4 for n, k in self.shapes().values())
+
+
+QWEN25 = {
+    "7b": (StackDims(3584, 3584, 512, 18944), 28),
+    "32b": (StackDims(5120, 5120, 1024, 27648), 64),
+    "72b": (StackDims(8192, 8192, 1024, 29568), 80),
+}
+
+
+def _align(v: int, a: int = 256) -> int:
+    return (v + a - 1) // a * a
+
+
+def block_layout(dims: StackDims, layers: int):
+    """Offsets of every (layer-in-block, projection) piece of a block slab:
+    [{proj: (codes_off, absmax_off)}] and the slab size. Pieces are 256-byte aligned."""
+    off = 0
+    table = []
+    for _ in range(layers):
+        entry = {}
+        for name in PROJS:
+            n, k = dims.shapes()[name]
+            c_off = off
+            off = _align(off + n * k // 2)
+            a_off = off
+            off = _align(off + n * (k // 64) * 4)
+            entry[name] = (c_off, a_off)
+        table.append(entry)
+    return table, off
+
+
+class HostNF4Base:
+    """The frozen NF4 base in pinned host memory, one slab per block.
+
+    weight_fn(layer, proj, n, k) -> bf16 device tensor [n, k]; it is quantised by
+    nf4_quantize on the GPU into a staging slab that is copied into the block's
+    pinned slab (block by block, so device residency stays at one block)."""
+
+    def __init__(self, dims: StackDims, n_layers: int, block_size: int, weight_fn):
+        if block_size < 1:
+            raise ValueError("block_size must be >= 1")
+        self.dims, self.n_layers, self.block_size = dims, n_layers, block_size
+        self.n_blocks = (n_layers + block_size - 1) // block_size
+        self.layout, self.slot_bytes = block_layout(dims, block_size)
+        self.blocks = []
+        self.block_bytes = []
+        staging = torch.empty(self.slot_bytes, dtype=torch.uint8, device="cuda")
+        for b in range(self.n_blocks):
+            nl = min(block_size, n_layers - b * block_size)
+            used = block_layout(dims, nl)[1]
+            for li in range(nl):
+                layer = b * block_size + li
+                for name in PROJS:
+                    n, k = dims.shapes()[name]
+                    c_off, a_off = self.layout[li][name]
+                    w = weight_fn(layer, name, n, k)
+                    codes = staging[c_off:c_off + n * k // 2].view(n, k // 2)
+                    absmax = staging[a_off:a_off + n * (k // 64) * 4].view(torch.float32).view(n, k // 64)
+                    lib.quantize(w, codes=codes, absmax=absmax)
+                    del w
+            host = torch.empty(used, dtype=torch.uint8, pin_memory=True)
+            host.copy_(staging[:used])           # D2H into pinned memory (synchronous)
+            self.blocks.append(host)
+            self.block_bytes.append(used)
+        torch.cuda.synchronize()
+
+    def total_bytes(self) -> int:
+        return sum(self.block_bytes)
+
+
+class LoraParams:
+    """A [r, K] and B [N, r] (bf16, device) for every layer and projection, from
+    lora_fn(layer, proj, n, k) -> (A, B)."""
+
+    def __init__(self, dims: StackDims, n_layers: int, rank: int, lora_fn):
+        self.rank = rank
+        self.p = [{name: lora_fn(layer, name, *dims.shapes()[name]) for name in PROJS} for layer in range(n_layers)]
+
+
+class NF4Stack:
+    """Forward + backward over the stack, streamed through a slot pool or resident."""
+
+    def __init__(self, base: HostNF4Base, lora: LoraParams, tokens: int, alpha: float = 32.0,
+                 mode: str = "streamed", n_slots: int = 2, prefetch: bool = True):
+        if mode not in ("streamed", "resident"):
+            raise ValueError("mode must be 'streamed' or 'resident'")
+        self.base, self.lora, self.T, self.alpha = base, lora, tokens, alpha
+        self.mode, self.prefetch = mode, prefetch
+        d = base.dims
+        self.dims = d
+        nb = base.n_blocks
+        self.n_slots = nb if mode == "resident" else max(1, n_slots)
+        self.slab = torch.empty(self.n_slots * base.slot_bytes, dtype=torch.uint8, device="cuda")
+        self.copy_stream = torch.cuda.Stream()
+        self.pool = lib.StreamPool(base.blocks, self.slab, base.slot_bytes, self.n_slots, self.copy_stream)
+        self._views = [self._slot_views(s) for s in range(self.n_slots)]
+        T, r = tokens, lora.rank
+        shapes = d.shapes()
+        dev = "cuda"
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        self.ws_f = lib.workspace(max(lib.fwd_workspace_bytes(T, n, k, r) for n, k in shapes.values()))
+        self.ws_b = lib.workspace(max(lib.bwd_workspace_bytes(T, n, k, r) for n, k in shapes.values()))
+        L = base.n_layers
+        self.acts = []
+        for _ in range(L + 1):
+            self.acts.append({"h": torch.empty(T, d.hidden, **bf)})
+        for li in range(L):
+            a = self.acts[li]
+            a.update({
+                "ha": torch.empty(T, d.hidden, **bf), "v": torch.empty(T, d.kv, **bf), "a": torch.empty(T, d.q, **bf),
+                "h1": torch.empty(T, d.hidden, **bf), "hm": torch.empty(T, d.hidden, **bf),
+                "gate": torch.empty(T, d.inter, **bf), "up": torch.empty(T, d.inter, **bf),
+                "m": torch.empty(T, d.inter, **bf),
+                "rs_h": torch.empty(T, dtype=torch.float32, device=dev),
+                "rs_h1": torch.empty(T, dtype=torch.float32, device=dev),
+                "u": {name: torch.empty(T, r, dtype=torch.float32, device=dev) for name in PROJS},
+            })
+        # scratch reused by every layer (stream order makes reuse safe)
+        self.tmp = {
+            "q": torch.empty(T, d.q, **bf), "k": torch.empty(T, d.kv, **bf), "o": torch.empty(T, d.hidden, **bf),
+            "down": torch.empty(T, d.hidden, **bf),
+            "dm": torch.empty(T, d.inter, **bf), "dgate": torch.empty(T, d.inter, **bf),
+            "dup": torch.empty(T, d.inter, **bf), "dhm_g": torch.empty(T, d.hidden, **bf),
+            "dhm_u": torch.empty(T, d.hidden, **bf), "dhm": torch.empty(T, d.hidden, **bf),
+            "dh1": torch.empty(T, d.hidden, **bf), "da": torch.empty(T, d.q, **bf), "dv": torch.empty(T, d.kv, **bf),
+            "dha_v": torch.empty(T, d.hidden, **bf), "dha_q": torch.empty(T, d.hidden, **bf),
+            "dha_k": torch.empty(T, d.hidden, **bf), "dha": torch.empty(T, d.hidden, **bf),
+            "zq": torch.zeros(T, d.q, **bf), "zkv": torch.zeros(T, d.kv, **bf),
+        }
+        self.dh = [torch.empty(T, d.hidden, **bf) for _ in range(2)]
+        self.grads = [{name: (torch.empty(r, shapes[name][1], dtype=torch.float32, device=dev),
+                              torch.empty(shapes[name][0], r, dtype=torch.float32, device=dev)) for name in PROJS}
+                      for _ in range(L)]
+        if mode == "resident":
+            for b in range(nb):
+                self.pool.prefetch(b)
+            self.copy_stream.synchronize()
+
+    # ------------------------------------------------------------------ slot views
+    def _slot_views(self, slot: int):
+        sb = self.base.slot_bytes
+        out = []
+        for entry in self.base.layout:
+            v = {}
+            for name, (c_off, a_off) in entry.items():
+                n, k = self.dims.shapes()[name]
+                c = self.slab[slot * sb + c_off: slot * sb + c_off + n * k // 2].view(n, k // 2)
+                a = self.slab[slot * sb + a_off: slot * sb + a_off + n * (k // 64) * 4].view(torch.float32).view(n, k // 64)
+                v[name] = (c, a)
+            out.append(v)
+        return out
+
+    def _acquire(self, b: int):
+        ptr = self.pool.acquire(b)
+        slot = (ptr - self.slab.data_ptr()) // self.base.slot_bytes
+        return self._views[slot]
+
+    # ------------------------------------------------------------------ one layer
+    def _fwd(self, w, name, x, y, u):
+        c, a = w[name]
+        p = self.lora.p[self._layer][name]
+        lib.lora_linear_fwd(c, a, x, p[0], p[1], self.alpha, y=y, u=u, ws=self.ws_f)
+
+    def _bwd(self, w, name, x, u, dy, dx):
+        c, a = w[name]
+        p = self.lora.p[self._layer][name]
+        dA, dB = self.grads[self._layer][name]
+        lib.lora_linear_bwd(c, a, x, u, dy, p[0], p[1], self.alpha, dx=dx, dA=dA, dB=dB, ws=self.ws_b,
+                            need_dx=dx is not None)
+
+    def _layer_forward(self, li: int, w):
+        d, A, t = self.dims, self.acts[li], self.tmp
+        self._layer = li
+        lib.rmsnorm_fwd(A["h"], RMS_EPS, out=A["ha"], rstd=A["rs_h"])
+        self._fwd(w, "q", A["ha"], t["q"], A["u"]["q"])
+        self._fwd(w, "k", A["ha"], t["k"], A["u"]["k"])
+        self._fwd(w, "v", A["ha"], A["v"], A["u"]["v"])
+        lib.repeat_kv_fwd(A["v"], d.q, d.head_dim, out=A["a"])
+        self._fwd(w, "o", A["a"], t["o"], A["u"]["o"])
+        lib.add_bf16(A["h"], t["o"], out=A["h1"])
+        lib.rmsnorm_fwd(A["h1"], RMS_EPS, out=A["hm"], rstd=A["rs_h1"])
+        self._fwd(w, "gate", A["hm"], A["gate"], A["u"]["gate"])
+        self._fwd(w, "up", A["hm"], A["up"], A["u"]["up"])
+        lib.silu_mul_fwd(A["gate"], A["up"], out=A["m"])
+        self._fwd(w, "down", A["m"], t["down"], A["u"]["down"])
+        lib.add_bf16(A["h1"], t["down"], out=self.acts[li + 1]["h"])
+
+    def _layer_backward(self, li: int, w, dh_out, dh_in):
+        d, A, t = self.dims, self.acts[li], self.tmp
+        self._layer = li
+        self._bwd(w, "down", A["m"], A["u"]["down"], dh_out, t["dm"])
+        lib.silu_mul_bwd(A["gate"], A["up"], t["dm"], dgate=t["dgate"], dup=t["dup"])
+        self._bwd(w, "gate", A["hm"], A["u"]["gate"], t["dgate"], t["dhm_g"])
+        self._bwd(w, "up", A["hm"], A["u"]["up"], t["dup"], t["dhm_u"])
+        lib.add_bf16(t["dhm_g"], t["dhm_u"], out=t["dhm"])
+        lib.rmsnorm_bwd(A["h1"], A["rs_h1"], t["dhm"], dres=dh_out, out=t["dh1"])
+        self._bwd(w, "o", A["a"], A["u"]["o"], t["dh1"], t["da"])
+        lib.repeat_kv_bwd(t["da"], d.kv, d.head_dim, out=t["dv"])
+        self._bwd(w, "v", A["ha"], A["u"]["v"], t["dv"], t["dha_v"])
+        self._bwd(w, "q", A["ha"], A["u"]["q"], t["zq"], t["dha_q"])      # identity mixing: zero gradient
+        self._bwd(w, "k", A["ha"], A["u"]["k"], t["zkv"], t["dha_k"])
+        lib.add_bf16(t["dha_v"], t["dha_q"], t["dha_k"], out=t["dha"])
+        lib.rmsnorm_bwd(A["h"], A["rs_h"], t["dha"], dres=t["dh1"], out=dh_in)
+
+    # ------------------------------------------------------------------ stack passes
+    def _layers_of(self, b: int):
+        bs = self.base.block_size
+        return range(b * bs, min((b + 1) * bs, self.base.n_layers))
+
+    def forward(self, h0: torch.Tensor) -> torch.Tensor:
+        self.acts[0]["h"].copy_(h0)
+        nb = self.base.n_blocks
+        for b in range(nb):
+            w = self._acquire(b)
+            if self.prefetch and self.n_slots > 1 and b + 1 < nb:
+                self.pool.prefetch(b + 1)
+            for li in self._layers_of(b):
+                self._layer_forward(li, w[li - b * self.base.block_size])
+            self.pool.release(b)
+        return self.acts[-1]["h"]
+
+    def backward(self, dh: torch.Tensor) -> torch.Tensor:
+        nb = self.base.n_blocks
+        cur = self.dh[0]
+        cur.copy_(dh)
+        k = 1
+        for b in range(nb - 1, -1, -1):
+            w = self._acquire(b)
+            if self.prefetch and self.n_slots > 1 and b - 1 >= 0:
+                self.pool.prefetch(b - 1)
+            for li in reversed(self._layers_of(b)):
+                nxt = self.dh[k]
+                self._layer_backward(li, w[li - b * self.base.block_size], cur, nxt)
+                cur, k = nxt, 1 - k
+            self.pool.release(b)
+        return cur
+
+    def step(self, h0, dh):
+        out = self.forward(h0)
+        dh0 = self.backward(dh)
+        return out, dh0
+
+    def close(self):
+        self.pool.close()
+
+
+def qwen_weight_fn(seed: int = 42):
+    """Synthetic base weights drawn on the GPU: W ~ N(0, 0.02), bf16."""
+    def fn(layer, name, n, k):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed * 1000003 + layer * 16 + PROJS.index(name))
+        return (torch.randn(n, k, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    return fn
+
+
+def qwen_lora_fn(rank: int = 16, seed: int = 42, b_std: float = 0.01):
+    """A ~ U(+-1/sqrt(K)), B ~ N(0, b_std), bf16 on the GPU."""
+    def fn(layer, name, n, k):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed * 7919 + layer * 16 + PROJS.index(name) + 1)
+        a = ((torch.rand(rank, k, generator=g, device="cuda") * 2 - 1) / k ** 0.5).to(torch.bfloat16)
+        b = (torch.randn(n, rank, generator=g, device="cuda") * b_std).to(torch.bfloat16)
+        return a, b
+    return fn
+
+
+def timed_steps(stack: NF4Stack, h0, dh, steps: int, warmup: int = 1) -> float:
+    """Seconds per step (forward + backward over the whole stack)."""
+    for _ in range(warmup):
+        stack.step(h0, dh)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stack.step(h0, dh)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps

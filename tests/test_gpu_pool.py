@@ -1,0 +1,103 @@
+"""The stream pool on the GPU: copies land intact, reuse is ordered, states are checked."""
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _blocks(n, nbytes):
+    out = []
+    for b in range(n):
+        h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        h.copy_(torch.arange(nbytes, dtype=torch.int64).add_(977 * b).remainder_(251).to(torch.uint8))
+        out.append(h)
+    return out
+
+
+def test_pool_copies_and_states(gpu_lib):
+    L = gpu_lib
+    blocks = _blocks(4, 1 << 20)
+    slot = 1 << 20
+    slab = torch.empty(2 * slot, dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    pool = L.StreamPool(blocks, slab, slot, 2, cs)
+    try:
+        for b in range(4):
+            ptr = pool.acquire(b)
+            s = (ptr - slab.data_ptr()) // slot
+            got = slab[s * slot:(s + 1) * slot].cpu()
+            assert torch.equal(got, blocks[b]), b
+            with pytest.raises(L.Nf4Error) as e:
+                pool.acquire(b)
+            assert e.value.code == L.NF4_E_STATE
+            pool.release(b)
+            with pytest.raises(L.Nf4Error) as e:
+                pool.release(b)
+            assert e.value.code == L.NF4_E_STATE
+        st = pool.stats()
+        assert st["copies"] == 4 and st["misses"] == 4 and st["hits"] == 0 and st["evictions"] == 2
+        assert st["bytes_copied"] == 4 << 20
+        # the two most recent blocks are still resident: acquiring one is a hit
+        assert {pool.slot_block(0), pool.slot_block(1)} == {2, 3}
+        pool.acquire(3)
+        assert pool.stats()["hits"] == 1
+        pool.prefetch(1)                   # evicts block 2: the only slot not held
+        assert {pool.slot_block(0), pool.slot_block(1)} == {3, 1}
+        pool.prefetch(3)                   # already in a slot: no copy
+        assert pool.stats()["copies"] == 5
+        pool.release(3)
+    finally:
+        pool.close()
+
+
+def test_pool_busy_when_all_held(gpu_lib):
+    L = gpu_lib
+    blocks = _blocks(3, 4096)
+    slab = torch.empty(2 * 4096, dtype=torch.uint8, device="cuda")
+    pool = L.StreamPool(blocks, slab, 4096, 2, torch.cuda.Stream())
+    try:
+        pool.acquire(0)
+        pool.acquire(1)
+        with pytest.raises(L.Nf4Error) as e:
+            pool.prefetch(2)
+        assert e.value.code == L.NF4_E_BUSY
+        with pytest.raises(L.Nf4Error) as e:
+            pool.acquire(2)
+        assert e.value.code == L.NF4_E_BUSY
+        pool.release(0)
+        ptr = pool.acquire(2)          # reuses block 0's slot after its release
+        assert (ptr - slab.data_ptr()) // 4096 == 0
+        assert torch.equal(slab[:4096].cpu(), blocks[2])
+        with pytest.raises(L.Nf4Error) as e:
+            pool.prefetch(7)
+        assert e.value.code == L.NF4_E_ARG
+    finally:
+        pool.close()
+
+
+def test_pool_reuse_waits_for_compute(gpu_lib):
+    L = gpu_lib
+    """A slot is overwritten only after the kernels enqueued before its release ran:
+    a long chain of reads on the compute stream, then release + prefetch of another
+    block into the same slot; the reads must all see the old block."""
+    n = 1 << 22
+    blocks = _blocks(2, n)
+    slab = torch.empty(n, dtype=torch.uint8, device="cuda")
+    pool = L.StreamPool(blocks, slab, n, 1, torch.cuda.Stream())
+    try:
+        ptr = pool.acquire(0)
+        sums = []
+        for _ in range(50):
+            sums.append(slab.to(torch.int64).sum())          # reads on the compute stream
+        pool.release(0)
+        pool.prefetch(1)                                     # same (only) slot
+        ptr = pool.acquire(1)
+        after = slab.clone()
+        pool.release(1)
+        torch.cuda.synchronize()
+        want = int(blocks[0].to(torch.int64).sum())
+        assert all(int(s) == want for s in sums)
+        assert torch.equal(after.cpu(), blocks[1])
+    finally:
+        pool.close()
