@@ -153,12 +153,86 @@ def cpu_baseline(seconds_budget: float = 12.0) -> dict:
     }
 
 
+def pinned_h2d_gbs(torch, nbytes: int = 1 << 30) -> float:
+    """Pinned host -> device hipMemcpyAsync bandwidth on a side stream (best of 3)."""
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    best = 0.0
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s):
+            d.copy_(h, non_blocking=True)
+        s.synchronize()
+        best = max(best, nbytes / (time.perf_counter() - t0) / 1e9)
+    del h, d
+    return best
+
+
+def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2d_gbs: float) -> dict:
+    """Streamed vs resident step time of a Qwen2.5-shaped identity-mixing stack, with
+    the bitwise check, H2D traffic and copy/compute overlap."""
+    from nf4_weight_streamed_amd import stack as ST
+
+    dims, n_layers = ST.QWEN25[model]
+    t0 = time.perf_counter()
+    base = ST.HostNF4Base(dims, n_layers, block_size, ST.qwen_weight_fn())
+    lora = ST.LoraParams(dims, n_layers, RANK, ST.qwen_lora_fn())
+    build_s = time.perf_counter() - t0
+    g = torch.Generator(device="cuda")
+    g.manual_seed(42)
+    h0 = torch.randn(tokens, dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    dh = torch.randn(tokens, dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    out = {}
+    for mode in ("resident", "streamed"):
+        st = ST.NF4Stack(base, lora, tokens, ALPHA, mode=mode)
+        y, dx = st.step(h0, dh)                       # warmup (and the parity sample)
+        torch.cuda.synchronize()
+        out[mode + "_y"], out[mode + "_dx"] = y.clone(), dx.clone()
+        c0 = st.pool.stats()["bytes_copied"]
+        secs = ST.timed_steps(st, h0, dh, steps, warmup=0)
+        out[mode + "_s"] = secs
+        out[mode + "_bytes"] = (st.pool.stats()["bytes_copied"] - c0) / steps
+        st.close()
+        del st
+        torch.cuda.empty_cache()
+    flops = n_layers * sum(4 * tokens * n * k + 6 * tokens * RANK * (n + k) for n, k in dims.shapes().values())
+    r_s, s_s, nbytes = out["resident_s"], out["streamed_s"], out["streamed_bytes"]
+    copy_s = nbytes / (h2d_gbs * 1e9)
+    overlap = (r_s + copy_s - s_s) / min(r_s, copy_s) if min(r_s, copy_s) > 0 else None
+    return {
+        "workload": f"qwen2.5-{model}-shaped stack, {n_layers} layers, block_size {block_size}, {tokens} tokens, "
+                    "NF4 in pinned host, identity attention mixing, fwd+bwd",
+        "bitwise_equal_to_resident": bool(torch.equal(out["resident_y"], out["streamed_y"])
+                                          and torch.equal(out["resident_dx"], out["streamed_dx"])),
+        "resident_ms_per_step": round(r_s * 1e3, 3),
+        "streamed_ms_per_step": round(s_s * 1e3, 3),
+        "streamed_over_resident": round(s_s / r_s, 3),
+        "streamed_tokens_per_s": round(tokens / s_s, 2),
+        "streamed_tflops": round(flops / s_s / 1e12, 2),
+        "resident_tflops": round(flops / r_s / 1e12, 2),
+        "h2d_gb_per_step": round(nbytes / 1e9, 3),
+        "h2d_gbs_achieved_over_step": round(nbytes / s_s / 1e9, 2),
+        "h2d_gbs_pinned_peak_measured": round(h2d_gbs, 2),
+        "pcie_frac": round(nbytes / s_s / 1e9 / h2d_gbs, 4),
+        "pcie_floor_ratio": round(max(r_s, copy_s) / r_s, 3),
+        "copy_compute_overlap": None if overlap is None else round(overlap, 3),
+        "host_nf4_gb": round(base.total_bytes() / 1e9, 3),
+        "build_s": round(build_s, 1),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--streamed", default="7b", help="stack for the streamed measurement: 7b, 32b, 72b or none")
+    ap.add_argument("--block-size", type=int, default=4)
+    ap.add_argument("--stack-tokens", type=int, default=512)
+    ap.add_argument("--stack-steps", type=int, default=3)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "
@@ -232,6 +306,11 @@ def main() -> int:
             "hbm_gbs_algorithmic": round(gate_bytes / avg_gemm_s / 1e9, 1),
         },
     }
+    if args.streamed != "none":
+        del layer
+        torch.cuda.empty_cache()
+        h2d = pinned_h2d_gbs(torch)
+        out["streamed"] = stream_bench(torch, args.streamed, args.block_size, args.stack_tokens, args.stack_steps, h2d)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
