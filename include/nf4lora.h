@@ -115,7 +115,8 @@ size_t nf4_lora_linear_fwd_workspace(int64_t T, int64_t N, int64_t K, int r);
  *                 bytes, 256-byte aligned (NULL allowed when that size is 0);
  *                 contents on entry are ignored
  * r == 0 computes the base only (A, B, u_save may be NULL). T == 0 is a no-op.
- * Device pointers must be 16-byte aligned.
+ * Device pointers must be 16-byte aligned. Size limits (NF4_E_SHAPE beyond them,
+ * here and in nf4_lora_linear_bwd): N, K <= 2^21, N*K <= 2^31, T <= 2^30.
  */
 int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K,
                         const uint16_t* x, int64_t T,

@@ -115,9 +115,11 @@ int check_linear_common(const char* fn, const uint8_t* codes, const float* absma
     if (K % NF4_BLOCK != 0)
         return fail(NF4_E_SHAPE, "%s: K=%lld is not a multiple of %d", fn, (long long)K, NF4_BLOCK);
     if (N % 16 != 0) return fail(NF4_E_SHAPE, "%s: N=%lld is not a multiple of 16", fn, (long long)N);
-    if (N > (int64_t(1) << 30) || K > (int64_t(1) << 30) || T > (int64_t(1) << 30))
-        return fail(NF4_E_SHAPE, "%s: sizes beyond 2^30 (N=%lld K=%lld T=%lld)", fn, (long long)N, (long long)K,
-                    (long long)T);
+    // The kernels address one weight matrix, and 128-row tiles of x / dy, with 32-bit
+    // byte offsets: keep each such operand within 2^30 bytes.
+    if (N > (int64_t(1) << 21) || K > (int64_t(1) << 21) || N * K > (int64_t(1) << 31) || T > (int64_t(1) << 30))
+        return fail(NF4_E_SHAPE, "%s: sizes beyond the limits N, K <= 2^21, N*K <= 2^31, T <= 2^30 (N=%lld K=%lld T=%lld)",
+                    fn, (long long)N, (long long)K, (long long)T);
     if (r < 0 || r > NF4_MAX_RANK) return fail(NF4_E_ARG, "%s: rank r=%d outside 0..%d", fn, r, NF4_MAX_RANK);
     if (!std::isfinite(alpha)) return fail(NF4_E_ARG, "%s: alpha is not finite", fn);
     if (!codes || !absmax) return fail(NF4_E_ARG, "%s: codes/absmax must not be NULL", fn);

@@ -48,8 +48,10 @@ struct BwdPlan {
     int bm, bn;            // dX tile (tokens x in features)
     int splits;            // N (contraction) splits for dX
     int steps_per_split;
-    int nslab;             // out-feature slabs of the LoRA pre-pass (partial g)
-    size_t off_g, off_gpart, off_dx;  // workspace offsets (bytes)
+    int nslab;             // 64-feature slabs of the LoRA pre-pass (partial g per slab)
+    int pre_chunks, pre_tc;  // token chunks of the pre-pass (partial dB per chunk), tokens per chunk
+    int da_chunks, da_tc;    // token chunks of dA (partial dA per chunk), tokens per chunk
+    size_t off_g, off_gpart, off_dbpart, off_dapart, off_dx;  // workspace offsets (bytes)
     size_t ws_bytes;
 };
 BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r);
@@ -77,6 +79,15 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // GEMM kernels run two workgroups per CU, so up to 2 * 256 workgroups run in one
 // round; a grid just above that leaves a nearly empty second round. Split only
 // shapes with fewer than 256 tiles, up to 512 workgroups, >= min_steps steps each.
+// Token chunking of a skinny LoRA kernel with `slabs` 64-feature slabs: about 2048
+// small workgroups (several per CU), chunks a multiple of 32 tokens.
+inline void pick_token_chunks(int64_t slabs, int64_t T, int& chunks, int& tc) {
+    const int64_t sub = std::max<int64_t>(1, (T + 31) / 32);
+    int64_t c = std::min<int64_t>(std::max<int64_t>(1, 2048 / std::max<int64_t>(1, slabs)), sub);
+    tc = int(32 * ((sub + c - 1) / c));
+    chunks = int((T + tc - 1) / tc);
+}
+
 inline int64_t pick_splits(int64_t tiles, int64_t steps, int64_t min_steps) {
     constexpr int64_t kSlots = 512;
     if (tiles >= kSlots / 2) return 1;

@@ -48,4 +48,48 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
     lo = (__bf16)(v - (float)hi);
 }
 
+// Raw buffer resource over [base, base + bytes): loads at or beyond `bytes` return 0
+// in hardware, which replaces per-load bounds branches. Third-dword flags for the
+// gfx9 family (gfx950 included).
+// The base and size must be wave-uniform; they are passed through readfirstlane so
+// the descriptor lives in SGPRs (no per-load waterfall loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+    void* p = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, int(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000);
+}
+
+// A byte offset past every buffer the entry points accept (they cap each operand a
+// kernel wraps in one descriptor at 2^30 bytes): loads from it return zero.
+constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0));
+}
+
+__device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0));
+}
+
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0));
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 buffer_load_dwordx4 ... lds):
+// lane i of the wave writes lds_wave_base + 16 * i; out-of-range reads write zeros.
+// lds_wave_base must be wave-uniform. Completion is tracked by vmcnt of the issuing wave.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, int(off), 0, 0,
+                                             0);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained); N is a compile-time constant.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 }  // namespace nf4

@@ -5,17 +5,18 @@
 // The frozen base is only read (HN comment thread on streaming the frozen base,
 // main comment) and is NF4 with rank-r LoRA on top (Poros API reference,
 // "PorosTrainer.from_pretrained"). Design for gfx950:
-//  - workgroup tile BM tokens x BN out-features, 4 waves in a 2x2 grid, each wave
-//    (BM/2) x (BN/2) of v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators;
-//  - each K step covers one 64-element NF4 block, so a row of the W tile has one scale;
-//  - x tile: 16-byte coalesced loads -> LDS; codes: 16-byte loads (32 codes of one row
-//    per thread) -> dequantised in registers through the 16 levels held in LDS ->
-//    bf16 tile in LDS: every weight element is dequantised once per workgroup;
-//  - the next step's global loads are issued before the current step's MFMAs;
+//  - workgroup tile 128 tokens x 128 out-features, 4 waves side by side along the
+//    out-features (128 x 32 each) on v_mfma_f32_32x32x16_bf16 with fp32 accumulators;
+//  - each K step covers one 64-element NF4 block, so every weight row has one scale;
+//  - weights are dequantised by the wave that multiplies them, in registers (see the
+//    kernel comment), while the x tile goes through double-buffered LDS;
 //  - LoRA: (s.u) is split into bf16 hi + lo and contracted with B on the same
 //    accumulators (a K-extension of r per part), so y is rounded once;
 //  - split-K (for shapes with too few tiles to fill 256 CUs): fp32 partials in the
-//    caller's workspace, summed in a fixed order by k_fwd_split_reduce.
+//    caller's workspace (split 0 carries the LoRA term), summed in a fixed order
+//    and rounded once by k_split_sum_bf16.
+#include <type_traits>
+
 #include "common.h"
 #include "device.h"
 
@@ -27,221 +28,181 @@ constexpr int kBK = 64;        // K per main-loop step (= one NF4 block)
 constexpr int kLds = kBK + 8;  // LDS row pitch in bf16 (144 B: conflict-free 16 B fragment reads)
 constexpr int kThreads = 256;
 
-template <int BM, int BN>
+// ------------------------------------------------------------------------------------
+// 4 waves split the BN = 128 output features (32 each); every wave dequantises its own
+// weight fragments in registers, so no weight tile goes through LDS and each weight
+// element is dequantised once per workgroup. Within each 64-element K block the
+// contraction order is permuted identically for both operands: lane half h supplies
+// k = 32h + 8kk .. 32h + 8kk + 7 at sub-step kk, so one 16-byte code load per lane
+// covers the four sub-steps of a K step. A code byte indexes a 256-entry LDS table of
+// (level[low nibble], level[high nibble]) pairs: one 8-byte read, two fp32 multiplies
+// by the block's absmax and one bf16 pack per byte. Loads are raw buffer loads
+// (hardware zero outside the tensor); x and codes are fetched two K steps ahead; the
+// x tile is double-buffered in LDS with one barrier per K step.
 __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_fwd(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
     const float* __restrict__ u, const uint16_t* __restrict__ B, int T, int N, int K, int r, float s,
     int steps_per_split, uint16_t* __restrict__ y, float* __restrict__ partial, Tables tab) {
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int A_CHUNKS = BM * (kBK / 8) / kThreads;  // 16-byte chunks of x per thread
-    constexpr int W_PARTS = BN * 2 / kThreads;            // 32-code half rows per thread
-    static_assert(A_CHUNKS >= 1 && W_PARTS >= 1, "tile too small for 256 threads");
+    constexpr int BM = 128, BN = 128, FM = 4;
+    constexpr int A_CHUNKS = BM * (kBK / 8) / kThreads;  // 4
 
-    __shared__ __align__(16) uint16_t sA[BM * kLds];
-    __shared__ __align__(16) uint16_t sW[BN * kLds];
-    __shared__ float sLut[16];
+    __shared__ __align__(16) uint16_t sA[2][BM * kLds];
+    __shared__ __align__(16) float sLut[512];  // 256 (level[lo nibble], level[hi nibble]) pairs
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
     const int n0 = blockIdx.x * BN;
     const int m0 = blockIdx.y * BM;
     const int ksteps = K / kBK;
     const int kb_begin = blockIdx.z * steps_per_split;
     const int kb_end = min(kb_begin + steps_per_split, ksteps);
-    const size_t code_pitch = size_t(K) / 2;
-    const size_t scale_pitch = size_t(K) / 64;
+    const int frag_row = lane & 31;
+    const int half = lane >> 5;
+    sLut[2 * tid] = tab.level[tid & 15];  // entry b: the two codes of byte b
+    sLut[2 * tid + 1] = tab.level[tid >> 4];
 
-    if (tid < 16) sLut[tid] = tab.level[tid];
+    // buffer views of this workgroup's rows (offsets stay far below 2^31)
+    const uint32_t xrows = uint32_t(max(0, min(BM, T - m0)));
+    const uint32_t wrows = uint32_t(max(0, min(BN, N - n0)));
+    const auto rx = make_rsrc(x + size_t(m0) * K, xrows * uint32_t(K) * 2u);
+    const auto rcd = make_rsrc(codes + size_t(n0) * (K / 2), wrows * uint32_t(K / 2));
+    const auto rsc = make_rsrc(absmax + size_t(n0) * (K / 64), wrows * uint32_t(K / 64) * 4u);
+    const int wrow = 32 * wave + frag_row;  // this lane's weight row within the tile
+    const uint32_t c_off = uint32_t(wrow) * uint32_t(K / 2) + uint32_t(half) * 16u;
+    const uint32_t s_off = uint32_t(wrow) * uint32_t(K / 64) * 4u;
+    uint32_t x_off[A_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+        const int c = tid + kThreads * i;
+        x_off[i] = (uint32_t(c >> 3) * uint32_t(K) + uint32_t(c & 7) * 8u) * 2u;
+    }
 
-    u32x4 ra[A_CHUNKS];
-    u32x4 rc[W_PARTS];
-    float rs[W_PARTS];
-
-    auto gload = [&](int kb) {
+    u32x4 ra[2][A_CHUNKS];
+    u32x4 rc[2];
+    float rs[2];
+    auto gload = [&](int kb, u32x4 (&xa)[A_CHUNKS], u32x4& cw, float& sc) {
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) xa[i] = buf_load16(rx, x_off[i] + uint32_t(kb) * (kBK * 2));
+        cw = buf_load16(rcd, c_off + uint32_t(kb) * 32u);
+        sc = buf_load_f32(rsc, s_off + uint32_t(kb) * 4u);
+    };
+    auto store_x = [&](const u32x4 (&xa)[A_CHUNKS], int buf) {
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
             const int c = tid + kThreads * i;
-            const int row = c >> 3, col8 = c & 7;
-            const int g = m0 + row;
-            ra[i] = (g < T) ? *reinterpret_cast<const u32x4*>(x + size_t(g) * K + size_t(kb) * kBK + col8 * 8)
-                            : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(&sA[buf][(c >> 3) * kLds + (c & 7) * 8]) = xa[i];
         }
+    };
+    const char* lut = reinterpret_cast<const char*>(sLut);
+    auto dequant = [&](const u32x4& cw, float sc, bf16x8 (&wf)[4]) {
 #pragma unroll
-        for (int i = 0; i < W_PARTS; ++i) {
-            const int p = tid + kThreads * i;
-            const int row = p >> 1, half = p & 1;
-            const int g = n0 + row;
-            if (g < N) {
-                rc[i] = *reinterpret_cast<const u32x4*>(codes + size_t(g) * code_pitch + size_t(kb) * 32 + half * 16);
-                rs[i] = absmax[size_t(g) * scale_pitch + kb];
-            } else {
-                rc[i] = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-                rs[i] = 0.0f;
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = cw[q];
+            u32x4 o;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float2 lv = *reinterpret_cast<const float2*>(lut + (((w >> (8 * b)) & 0xFFu) << 3));
+                // level * absmax in fp32, then RNbf: the format's two roundings
+                o[b] = pack_bf16x2(lv.x * sc, lv.y * sc);
             }
+            wf[q] = as_bf16x8(o);
         }
     };
 
-    auto sstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            const int c = tid + kThreads * i;
-            const int row = c >> 3, col8 = c & 7;
-            *reinterpret_cast<u32x4*>(sA + row * kLds + col8 * 8) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < W_PARTS; ++i) {
-            const int p = tid + kThreads * i;
-            const int row = p >> 1, half = p & 1;
-            const float sc = rs[i];
-            uint16_t* dst = sW + row * kLds + half * 32;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t wq = rc[i][q];
-                u32x4 o;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const uint32_t byte = wq >> (8 * b);
-                    // level * absmax in fp32, then RNbf: bit-identical to the stand-alone dequantiser
-                    o[b] = pack_bf16x2(sLut[byte & 15] * sc, sLut[(byte >> 4) & 15] * sc);
-                }
-                *reinterpret_cast<u32x4*>(dst + q * 8) = o;
-            }
-        }
-    };
-
-    f32x16 acc[FM][FN];
+    f32x16 acc[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    const int frag_row = lane & 31;
-    const int frag_k = (lane >> 5) * 8;
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
 
     if (kb_begin < kb_end) {
-        gload(kb_begin);
-        __syncthreads();  // sLut visible
-        sstore();
-        __syncthreads();
-        for (int kb = kb_begin; kb < kb_end; ++kb) {
+        bf16x8 wf[4];
+        gload(kb_begin, ra[0], rc[0], rs[0]);
+        if (kb_begin + 1 < kb_end) gload(kb_begin + 1, ra[1], rc[1], rs[1]);
+        store_x(ra[0], 0);
+        __syncthreads();  // sLut and x tile 0 visible
+        dequant(rc[0], rs[0], wf);
+        // one K step; C is the compile-time register/LDS buffer of step kb (the loop is
+        // unrolled by two so that no register array is indexed at run time)
+        auto step = [&](int kb, auto c_) {
+            constexpr int C = decltype(c_)::value;
             const bool more = kb + 1 < kb_end;
-            if (more) gload(kb + 1);
+            if (kb + 2 < kb_end) gload(kb + 2, ra[C], rc[C], rs[C]);  // step kb's registers are consumed
+            const uint16_t* a_base = &sA[C][0];
 #pragma unroll
-            for (int kk = 0; kk < kBK / 16; ++kk) {
-                bf16x8 af[FM], bw[FN];
+            for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                        sA + (wm * WM + 32 * i + frag_row) * kLds + kk * 16 + frag_k));
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    bw[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                        sW + (wn * WN + 32 * j + frag_row) * kLds + kk * 16 + frag_k));
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(af[i], bw[j], acc[i][j]);
+                for (int i = 0; i < FM; ++i) {
+                    const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                        a_base + (32 * i + frag_row) * kLds + 32 * half + 8 * kk));
+                    acc[i] = mfma32x32x16(af, wf[kk], acc[i]);
+                }
+            }
+            if (more) {
+                dequant(rc[C ^ 1], rs[C ^ 1], wf);  // next step's weights, independent of the MFMAs
+                store_x(ra[C ^ 1], C ^ 1);
             }
             __syncthreads();
-            if (more) {
-                sstore();
-                __syncthreads();
-            }
+        };
+        for (int kb = kb_begin; kb < kb_end; kb += 2) {
+            step(kb, std::integral_constant<int, 0>{});
+            if (kb + 1 < kb_end) step(kb + 1, std::integral_constant<int, 1>{});
         }
     }
 
-    if (partial != nullptr) {
-        // split-K: fp32 partial tile, reduced (with the LoRA term) by k_fwd_split_reduce
-        float* dst = partial + size_t(blockIdx.z) * T * N;
+    // LoRA as a K-extension (split 0 only when split): acc += (s.u)_hi . B^T + (s.u)_lo . B^T
+    const int col = n0 + 32 * wave + frag_row;
+    for (int c0 = 0; c0 < (blockIdx.z == 0 ? r : 0); c0 += 16) {
+        bf16x8 bb;
+        const int j0 = c0 + 8 * half;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = m0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    const int col = n0 + wn * WN + 32 * j + (lane & 31);
-                    if (row < T && col < N) dst[size_t(row) * N + col] = acc[i][j][e];
-                }
-        return;
-    }
-
-    // LoRA as a K-extension: acc += (s.u)_hi . B^T + (s.u)_lo . B^T, r padded to 16.
-    for (int c0 = 0; c0 < r; c0 += 16) {
-        bf16x8 hi[FM], lo[FM], bb[FN];
-        const int j0 = c0 + frag_k;
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t bv = (col < N && j0 + e < r) ? B[size_t(col) * r + j0 + e] : uint16_t(0);
+            bb[e] = __builtin_bit_cast(__bf16, bv);
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int row = m0 + wm * WM + 32 * i + frag_row;
+            const int row = m0 + 32 * i + frag_row;
+            bf16x8 hi, lo;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float v = (row < T && j0 + e < r) ? s * u[size_t(row) * r + j0 + e] : 0.0f;
-                __bf16 h, l;
-                split_bf16(v, h, l);
-                hi[i][e] = h;
-                lo[i][e] = l;
+                __bf16 hh, ll;
+                split_bf16(v, hh, ll);
+                hi[e] = hh;
+                lo[e] = ll;
             }
+            acc[i] = mfma32x32x16(hi, bb, acc[i]);
+            acc[i] = mfma32x32x16(lo, bb, acc[i]);
         }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn * WN + 32 * j + frag_row;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint16_t bv = (col < N && j0 + e < r) ? B[size_t(col) * r + j0 + e] : uint16_t(0);
-                bb[j][e] = __builtin_bit_cast(__bf16, bv);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                acc[i][j] = mfma32x32x16(hi[i], bb[j], acc[i][j]);
-                acc[i][j] = mfma32x32x16(lo[i], bb[j], acc[i][j]);
-            }
     }
 
+    float* pdst = partial ? partial + size_t(blockIdx.z) * T * N : nullptr;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int col = n0 + wn * WN + 32 * j + (lane & 31);
-                if (row < T && col < N) y[size_t(row) * N + col] = bf16_bits(acc[i][j][e]);
+        for (int e = 0; e < 16; ++e) {
+            const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (row < T && col < N) {
+                if (pdst)
+                    pdst[size_t(row) * N + col] = acc[i][e];
+                else
+                    y[size_t(row) * N + col] = bf16_bits(acc[i][e]);
             }
+        }
 }
 
-// y = RNbf( sum_z partial[z] + s . u . B^T ), z in increasing order; four consecutive
-// outputs of one row per thread (N % 16 == 0), float4 partial loads.
-__global__ __launch_bounds__(256) void k_fwd_split_reduce(const float* __restrict__ partial, int splits, int T,
-                                                          int N, const float* __restrict__ u,
-                                                          const uint16_t* __restrict__ B, int r, float s,
-                                                          uint16_t* __restrict__ y) {
-    const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t total = int64_t(T) * N;
-    if (q * 4 >= total) return;
-    const int64_t idx = q * 4;
-    const int row = int(idx / N), col = int(idx % N);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int z = 0; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(partial + size_t(z) * total + idx);
-    f32x4 lora = {0.f, 0.f, 0.f, 0.f};
-    const float* ur = u + size_t(row) * r;
-    const uint16_t* br = B + size_t(col) * r;
-#pragma unroll 4
-    for (int j = 0; j < r; ++j) {
-        const float uj = ur[j];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) lora[c] += uj * bf16_to_f32(br[size_t(c) * r + j]);
-    }
-    u32x2 o = {pack_bf16x2(acc[0] + s * lora[0], acc[1] + s * lora[1]),
-               pack_bf16x2(acc[2] + s * lora[2], acc[3] + s * lora[3])};
-    *reinterpret_cast<u32x2*>(y + idx) = o;
+// y = RNbf( sum_z partial[z] ), z in increasing order (split 0 already holds the LoRA
+// term); four consecutive outputs per thread, float4 loads.
+__global__ __launch_bounds__(256) void k_split_sum_bf16(const float* __restrict__ partial, int splits,
+                                                        int64_t total, uint16_t* __restrict__ out) {
+    const int64_t idx = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (idx >= total) return;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(partial + idx);
+    for (int z = 1; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(partial + size_t(z) * total + idx);
+    u32x2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(out + idx) = o;
 }
 
 }  // namespace
@@ -275,14 +236,14 @@ hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* 
     const dim3 grid(unsigned(cdiv(N, p.bn)), unsigned(cdiv(T, p.bm)), unsigned(p.splits));
     float* partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ypart) : nullptr;
     prof_gemm_begin(stream);
-    hipLaunchKernelGGL((k_nf4_gemm_fwd<128, 128>), grid, dim3(kThreads), 0, stream, x, codes, absmax, u, B, int(T),
-                       int(N), int(K), r, s, p.steps_per_split, y, partial, tables());
+    hipLaunchKernelGGL(k_nf4_gemm_fwd, grid, dim3(kThreads), 0, stream, x, codes, absmax, u, B, int(T), int(N), int(K),
+                       r, s, p.steps_per_split, y, partial, tables());
     prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t total = T * N;
-    hipLaunchKernelGGL(k_fwd_split_reduce, dim3(unsigned(cdiv(total / 4, 256))), dim3(256), 0, stream, partial,
-                       p.splits, int(T), int(N), u, B, r, s, y);
+    hipLaunchKernelGGL(k_split_sum_bf16, dim3(unsigned(cdiv(total / 4, 256))), dim3(256), 0, stream, partial,
+                       p.splits, total, y);
     return hipGetLastError();
 }
 

@@ -73,6 +73,8 @@ def test_linear_fwd_validation(L):
     raw = L.raw()
     _err(L, _fwd(raw, K=100), L.NF4_E_SHAPE, "K=100")
     _err(L, _fwd(raw, N=100), L.NF4_E_SHAPE, "N=100")
+    _err(L, _fwd(raw, N=1 << 22), L.NF4_E_SHAPE, "limits")                 # 32-bit tile offsets
+    _err(L, _fwd(raw, N=1 << 21, K=1 << 11), L.NF4_E_SHAPE, "limits")      # N*K > 2^31
     _err(L, _fwd(raw, r=65), L.NF4_E_ARG, "r=65")
     _err(L, _fwd(raw, r=-1), L.NF4_E_ARG)
     _err(L, _fwd(raw, alpha=float("inf")), L.NF4_E_ARG, "alpha")
