@@ -114,6 +114,57 @@ def run_step(lib, layer, prof=None):
                             dA=p["dA"], dB=p["dB"], ws=p["wsb"])
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_nf4_gemm_fwd_gate_qwen7b_t512_traffic.md")
+# sources whose change invalidates the HBM traffic taken with the counters
+TRAFFIC_SOURCES = [os.path.join(ROOT, "nf4_weight_streamed_amd", "csrc", f)
+                   for f in ("nf4_gemm_fwd.hip", "device.h", "common.h")]
+COPY_CALIBRATION_BYTES = 1 << 30
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic() -> int | None:
+    """HBM bytes per launch of the dominant kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the copy calibration), or None when that
+    summary is missing or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_PROFILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            key, val = line[2:].split(": ", 1)
+            fields[key.strip("` ")] = val.strip("` ")
+    if fields.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch) -> None:
+    """One plain streaming kernel of known traffic for the counter calibration: an
+    elementwise negation of a 1 GiB fp32 tensor (reads 1 GiB, writes 1 GiB)."""
+    src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def cpu_baseline(seconds_budget: float = 12.0) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     the q projection (3584 x 3584) of the layer with all 512 tokens - dequantise
@@ -233,6 +284,8 @@ def main() -> int:
     ap.add_argument("--block-size", type=int, default=4)
     ap.add_argument("--stack-tokens", type=int, default=512)
     ap.add_argument("--stack-steps", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="launch one 1 GiB read + 1 GiB write elementwise kernel first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "
@@ -244,6 +297,8 @@ def main() -> int:
     from nf4_weight_streamed_amd import lib
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
     layer = build_layer(lib, torch)
     ev = HipEvents()
     for _ in range(args.warmup):
@@ -299,7 +354,7 @@ def main() -> int:
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "avg_launch_us": round(avg_gemm_s * 1e6, 2),
             "algorithmic_flops_per_launch": gate_flops,
             "algorithmic_bytes_per_launch": gate_bytes,

@@ -135,10 +135,12 @@ size_t nf4_lora_linear_bwd_workspace(int64_t T, int64_t N, int64_t K, int r);
  *     dB = s . dY^T . u                    fp32, overwritten
  *   x [T][K], u_save [T][r] (from the forward), dy [T][N]: device
  *   dx  device bf16 [T][K], or NULL to skip dX
- *   dA  device fp32 [r][K]; dB device fp32 [N][r] (may be NULL when r == 0)
+ *   dA  device fp32 [r][K], 16-byte aligned; dB device fp32 [N][r] (both may be
+ *       NULL when r == 0)
  *   ws  device workspace of at least nf4_lora_linear_bwd_workspace() bytes,
  *       256-byte aligned; its contents on entry are ignored
- * Shapes and r as in the forward.
+ * Shapes and r as in the forward. Every output is a fixed-order sum: repeated calls
+ * on the same inputs give identical bits.
  */
 int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K,
                         const uint16_t* x, const float* u_save, const uint16_t* dy, int64_t T,

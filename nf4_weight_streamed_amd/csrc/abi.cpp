@@ -208,11 +208,10 @@ int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, in
     const float scale = lora_scale(alpha, r);
     if (r > 0) {
         float* upart = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_upart);
-        st = hip_status(launch_lora_down(x, A, T, K, r, u_save, upart, p.down_splits, p.down_steps, s),
-                        "nf4_lora_linear_fwd (x.A^T)");
+        st = hip_status(launch_lora_down(p, x, A, T, K, r, upart, s), "nf4_lora_linear_fwd (x.A^T)");
         if (st != NF4_OK) return st;
     }
-    return hip_status(launch_gemm_fwd(p, codes, absmax, x, u_save, B, T, N, K, r, scale, y, ws, s),
+    return hip_status(launch_gemm_fwd(p, codes, absmax, x, B, T, N, K, r, scale, y, u_save, ws, s),
                       "nf4_lora_linear_fwd (gemm)");
 }
 
@@ -233,29 +232,26 @@ int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, in
     if (r > 0 && (!x || !u_save || !A || !B || !dA || !dB))
         return fail(NF4_E_ARG, "%s: r=%d needs x, u_save, A, B, dA and dB", fn, r);
     if (!aligned(dy, 16) || (dx && !aligned(dx, 16)) ||
-        (r > 0 && (!aligned(x, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(u_save, 4) || !aligned(dA, 4) ||
+        (r > 0 && (!aligned(x, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(u_save, 4) || !aligned(dA, 16) ||
                    !aligned(dB, 4))))
-        return fail(NF4_E_ARG, "%s: misaligned pointer (dy, dx, x and A need 16 bytes)", fn);
+        return fail(NF4_E_ARG, "%s: misaligned pointer (dy, dx, x, A and dA need 16 bytes)", fn);
     const BwdPlan p = plan_bwd(T, N, K, r);
     if (!ws || ws_bytes < p.ws_bytes || !aligned(ws, 256))
         return fail(NF4_E_ARG, "%s: workspace of %zu bytes (256-byte aligned) needed for T=%lld N=%lld K=%lld r=%d, got %zu",
                     fn, p.ws_bytes, (long long)T, (long long)N, (long long)K, r, ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float scale = lora_scale(alpha, r);
+    if (r == 0 && !dx) return NF4_OK;
+    char* w = static_cast<char*>(ws);
     if (r > 0) {
-        st = hip_status(launch_lora_bwd_pre(p, dy, B, u_save, T, N, r, scale, dB, ws, s), "nf4_lora_linear_bwd (g, dB)");
+        st = hip_status(launch_lora_bwd_pre(p, dy, B, u_save, T, N, r, scale, reinterpret_cast<float*>(w + p.off_gpart),
+                                            dB, s),
+                        "nf4_lora_linear_bwd (g, dB)");
         if (st != NF4_OK) return st;
     }
-    if (dx) {
-        st = hip_status(launch_gemm_bwd_dx(p, codes, absmax, dy, A, T, N, K, r, scale, dx, ws, s),
-                        "nf4_lora_linear_bwd (dX)");
-        if (st != NF4_OK) return st;
-    }
-    if (r > 0) {
-        st = hip_status(launch_lora_da(p, x, T, K, r, scale, dA, ws, s), "nf4_lora_linear_bwd (dA)");
-        if (st != NF4_OK) return st;
-    }
-    return NF4_OK;
+    // dX (when requested) with its LoRA term, and dA
+    return hip_status(launch_gemm_bwd(p, codes, absmax, dy, x, A, T, N, K, r, scale, dx, dA, ws, s),
+                      "nf4_lora_linear_bwd (dX, dA)");
 }
 
 }  // extern "C"

@@ -31,43 +31,49 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t 
 
 #define NF4_MAX_RANK_BLOCKS 4  // r <= 16 * NF4_MAX_RANK_BLOCKS (= NF4_MAX_RANK)
 
+// Partial counts of the skinny LoRA products, summed per tile by the GEMM kernels.
+constexpr int kMaxDownParts = 4;  // K ranges of u = x.A^T
+constexpr int kMaxGParts = 8;     // N ranges of g = dY.B
+
 // Forward plan: how the kernels are split for a shape (a pure function of the shape,
-// so repeated calls - streamed or resident - launch identical grids).
+// so repeated calls - streamed or resident - launch identical grids). Workspace:
+// [u partials | split-K partials of y].
 struct FwdPlan {
     int bm, bn;           // GEMM workgroup tile (tokens x out features)
-    int splits;           // GEMM K splits (1 = fused epilogue in the GEMM)
+    int splits;           // GEMM K splits (1: y written by the GEMM tile directly)
     int steps_per_split;  // 64-wide K steps per split
-    int down_splits;      // K splits of u = x.A^T (1 = written directly)
-    int down_steps;       // 32-wide K steps per split
+    int down_parts;       // K ranges of u = x.A^T (partials summed by the GEMM); 0 if r == 0
+    int down_steps;       // 32-wide K steps per range
     size_t off_upart, off_ypart;  // workspace offsets (bytes)
     size_t ws_bytes;
 };
 FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r);
+void plan_lora_down(FwdPlan& p, int64_t K);
 
+// Backward plan. Workspace: [g partials | dA shares per token tile | split-K
+// partials of dX].
 struct BwdPlan {
     int bm, bn;            // dX tile (tokens x in features)
     int splits;            // N (contraction) splits for dX
     int steps_per_split;
-    int nslab;             // 64-feature slabs of the LoRA pre-pass (partial g per slab)
-    int pre_chunks, pre_tc;  // token chunks of the pre-pass (partial dB per chunk), tokens per chunk
-    int da_chunks, da_tc;    // token chunks of dA (partial dA per chunk), tokens per chunk
-    size_t off_g, off_gpart, off_dbpart, off_dapart, off_dx;  // workspace offsets (bytes)
+    int mtiles, ktiles;    // dX tile grid
+    int gparts, gsteps;    // N ranges of g = dY.B (partials summed by the GEMM), 128-feature chunks each
+    size_t off_gpart, off_dapart, off_dx;  // workspace offsets (bytes)
     size_t ws_bytes;
 };
 BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r);
+void plan_lora_bwd_pre(BwdPlan& p, int64_t N);
 
-hipError_t launch_lora_down(const uint16_t* x, const uint16_t* A, int64_t T, int64_t K, int r, float* u,
-                            float* upart, int splits, int steps_per_split, hipStream_t stream);
+hipError_t launch_lora_down(const FwdPlan& p, const uint16_t* x, const uint16_t* A, int64_t T, int64_t K, int r,
+                            float* upart, hipStream_t stream);
 hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* x,
-                           const float* u, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,
-                           uint16_t* y, void* ws, hipStream_t stream);
-hipError_t launch_lora_bwd_pre(const BwdPlan& p, const uint16_t* dy, const uint16_t* B, const float* u,
-                               int64_t T, int64_t N, int r, float s, float* dB, void* ws, hipStream_t stream);
-hipError_t launch_gemm_bwd_dx(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* dy,
-                              const uint16_t* A, int64_t T, int64_t N, int64_t K, int r, float s, uint16_t* dx,
-                              void* ws, hipStream_t stream);
-hipError_t launch_lora_da(const BwdPlan& p, const uint16_t* x, int64_t T, int64_t K, int r, float s, float* dA,
-                          void* ws, hipStream_t stream);
+                           const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s, uint16_t* y,
+                           float* u_save, void* ws, hipStream_t stream);
+hipError_t launch_lora_bwd_pre(const BwdPlan& p, const uint16_t* dy, const uint16_t* B, const float* u, int64_t T,
+                               int64_t N, int r, float s, float* gpart, float* dB, hipStream_t stream);
+hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* dy,
+                           const uint16_t* x, const uint16_t* A, int64_t T, int64_t N, int64_t K, int r, float s,
+                           uint16_t* dx, float* dA, void* ws, hipStream_t stream);
 
 // Instrumentation events around the next fused GEMM launch (abi.cpp); no-ops unless requested.
 void prof_gemm_begin(hipStream_t stream);
@@ -79,15 +85,6 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // GEMM kernels run two workgroups per CU, so up to 2 * 256 workgroups run in one
 // round; a grid just above that leaves a nearly empty second round. Split only
 // shapes with fewer than 256 tiles, up to 512 workgroups, >= min_steps steps each.
-// Token chunking of a skinny LoRA kernel with `slabs` 64-feature slabs: about 2048
-// small workgroups (several per CU), chunks a multiple of 32 tokens.
-inline void pick_token_chunks(int64_t slabs, int64_t T, int& chunks, int& tc) {
-    const int64_t sub = std::max<int64_t>(1, (T + 31) / 32);
-    int64_t c = std::min<int64_t>(std::max<int64_t>(1, 2048 / std::max<int64_t>(1, slabs)), sub);
-    tc = int(32 * ((sub + c - 1) / c));
-    chunks = int((T + tc - 1) / tc);
-}
-
 inline int64_t pick_splits(int64_t tiles, int64_t steps, int64_t min_steps) {
     constexpr int64_t kSlots = 512;
     if (tiles >= kSlots / 2) return 1;

@@ -48,6 +48,20 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
     lo = (__bf16)(v - (float)hi);
 }
 
+// The dispatcher hands workgroups to the 8 XCDs (each with its own L2) round-robin
+// in linear-id order. xcd_tile_order maps linear id L of a grid of `total`
+// workgroups to a tile index such that each XCD runs one contiguous range of tile
+// indices, in order: tiles that share operands and sit next to each other in the
+// tile order then meet in the same L2 at about the same time. A bijection on
+// [0, total) for any total.
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_tile_order(uint32_t L, uint32_t total) {
+    const uint32_t q = total / kXcds, rem = total % kXcds;
+    const uint32_t xcd = L % kXcds, local = L / kXcds;
+    return xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+}
+
 // Raw buffer resource over [base, base + bytes): loads at or beyond `bytes` return 0
 // in hardware, which replaces per-load bounds branches. Third-dword flags for the
 // gfx9 family (gfx950 included).

@@ -32,10 +32,20 @@ constexpr int kThreads = 256;
 // 256-entry (level[lo], level[hi]) pair table per code byte, fp32 multiply by the
 // row's absmax, bf16 pack pairing rows - and stores the patch transposed into the
 // other LDS buffer. dY and the weight tile are double-buffered: one barrier per step.
+struct BwdLora {
+    const float* gpart;  // [parts][T][r] partials of g = dY.B
+    int parts;
+    const uint16_t* A;   // [r][K]
+    const uint16_t* x;   // [T][K]
+    float* dapart;       // [token tiles][r][K] dA share of each token tile
+    int r;
+    float s;
+};
+
 __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
-    const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
-    const float* __restrict__ g, const uint16_t* __restrict__ A, int T, int N, int K, int r, float s,
-    int steps_per_split, uint16_t* __restrict__ dx, float* __restrict__ partial, Tables tab) {
+    const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const float* __restrict__ absmax, int T,
+    int N, int K, int steps_per_split, BwdLora lora, uint16_t* __restrict__ dx, float* __restrict__ partial,
+    Tables tab) {
     constexpr int BM = 128, BK = 128;
     constexpr int WM = BM / 2, WK = BK / 2;
     constexpr int FM = WM / 32, FK = WK / 32;
@@ -49,10 +59,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wk = wave & 1;
-    const int k0 = blockIdx.x * BK;
-    const int m0 = blockIdx.y * BM;
+    // tile order: token tile fastest, then column tile, then split; per-XCD ranges,
+    // so the token tiles sharing one weight slice run together in one L2
+    const uint32_t tile = xcd_tile_order(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                                         gridDim.x * gridDim.y * gridDim.z);
+    const int tm = int(tile % gridDim.y), tc = int((tile / gridDim.y) % gridDim.x);
+    const int tz = int(tile / (gridDim.y * gridDim.x));
+    const int k0 = tc * BK;
+    const int m0 = tm * BM;
     const int nsteps = (N + kBN - 1) / kBN;
-    const int nb_begin = blockIdx.z * steps_per_split;
+    const int nb_begin = tz * steps_per_split;
     const int nb_end = min(nb_begin + steps_per_split, nsteps);
     const int frag_row = lane & 31;
     const int frag_k = (lane >> 5) * 8;
@@ -134,10 +150,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
         __syncthreads();  // sLut visible
         sstore(0);
         __syncthreads();
+        // loads are issued unconditionally (a step past the end reads data that is never
+        // used, or zeros): the compiler's wait counts then stay exact
         auto step = [&](int nb, auto c_) {
             constexpr int C = decltype(c_)::value;
             const bool more = nb + 1 < nb_end;
-            if (more) gload(nb + 1);
+            gload(nb + 1);
+            __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
 #pragma unroll
             for (int kk = 0; kk < kBN / 16; ++kk) {
                 bf16x8 af[FM], bw[FK];
@@ -159,47 +178,168 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
             if (more) sstore(C ^ 1);  // next step's tiles into the other buffers
             __syncthreads();
         };
-        for (int nb = nb_begin; nb < nb_end; nb += 2) {
+        int nb = nb_begin;
+        for (; nb + 1 < nb_end; nb += 2) {
             step(nb, std::integral_constant<int, 0>{});
-            if (nb + 1 < nb_end) step(nb + 1, std::integral_constant<int, 1>{});
+            step(nb + 1, std::integral_constant<int, 1>{});
+        }
+        if (nb < nb_end) step(nb, std::integral_constant<int, 0>{});
+    }
+
+    // LoRA (split 0 only when split). g = sum of the partials in partial order; (s.g)^T
+    // is staged as bf16 hi/lo [j][t] in the (now free) dY buffers and the x tile as
+    // [k][t] in the weight buffers. Then
+    //   dX tile += (s.g)_hi . A + (s.g)_lo . A      (K-extension on the accumulators)
+    //   dA share of this token tile = (s.g)^T . x over its tokens (k_bwd_finish adds
+    //   the shares in token-tile order: dA = ((d0 + d1) + d2) + ...)
+    const int r = lora.r;
+    if (tz == 0 && r > 0) {
+        constexpr int kTP = BM + 8;  // pitch of the [.][t] tiles
+        uint16_t* sg_hi = &sA[0][0];           // [64][kTP]
+        uint16_t* sg_lo = sg_hi + 64 * kTP;    // [64][kTP]
+        uint16_t* sxt = &sWt[0][0];            // [BK][kTP]
+        const int rp = (r + 15) & ~15;
+        // the partials region is padded to 256 bytes: 16-byte loads at 4-byte aligned
+        // offsets stay inside it; lanes j >= r are masked below
+        const auto rgp = make_rsrc(lora.gpart, (uint32_t(lora.parts) * uint32_t(T) * uint32_t(r) * 4u + 255u) & ~255u);
+        const auto rx = make_rsrc(lora.x + size_t(m0) * K, trows * uint32_t(K) * 2u);
+        // every load of the staging is issued before the first is consumed (one memory
+        // round trip at the end of the kernel, not one per loop trip)
+        constexpr int XC = BM * (BK / 8) / kThreads;  // 16-byte x chunks per thread
+        constexpr int GI = BM * 4 / kThreads;         // (t, 4-rank group) items per thread per 16 ranks
+        const auto ra = make_rsrc(lora.A, uint32_t(r) * uint32_t(K) * 2u);  // rows j >= r read zero
+        // A values of one 16-rank slice for this lane's dX fragments: B operand of the
+        // LoRA K-extension (lane: column k, ranks c0 + 8 (lane / 32) .. + 7)
+        auto load_a = [&](int c0, uint32_t (&av)[FK][8]) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int j = 0; j < FK; ++j) {
+                    const uint32_t col = uint32_t(k0 + wk * WK + 32 * j + frag_row);
+                    av[j][e] = __builtin_amdgcn_raw_buffer_load_b16(
+                        ra, int(col < uint32_t(K) ? (uint32_t(c0 + frag_k + e) * uint32_t(K) + col) * 2u : kOutOfRange),
+                        0, 0);
+                }
+        };
+        uint32_t av[FK][8];
+        load_a(0, av);
+        u32x4 xv[XC];
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            // rows past T read zero; columns past K only feed dA columns never stored
+            const int c = tid + kThreads * i, t = c / (BK / 8), k8 = 8 * (c % (BK / 8));
+            xv[i] = buf_load16(rx, (uint32_t(t) * uint32_t(K) + uint32_t(k0 + k8)) * 2u);
+        }
+        for (int jb = 0; jb < rp / 16; ++jb) {
+            f32x4 pv[GI][kMaxGParts];
+#pragma unroll
+            for (int i = 0; i < GI; ++i) {
+                const int o = tid + kThreads * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
+                const bool ok = m0 + t < T && j < r;
+                const uint32_t off = (uint32_t(m0 + t) * uint32_t(r) + uint32_t(j)) * 4u;
+#pragma unroll
+                for (int pp = 0; pp < kMaxGParts; ++pp)
+                    pv[i][pp] = __builtin_bit_cast(
+                        f32x4, buf_load16(rgp, ok && pp < lora.parts ? off + uint32_t(pp) * uint32_t(T) * uint32_t(r) * 4u
+                                                                     : kOutOfRange));
+            }
+#pragma unroll
+            for (int i = 0; i < GI; ++i) {
+                const int o = tid + kThreads * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
+                f32x4 v = pv[i][0];
+#pragma unroll
+                for (int pp = 1; pp < kMaxGParts; ++pp)
+                    if (pp < lora.parts) v += pv[i][pp];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    __bf16 hh, ll;
+                    split_bf16(j + c < r ? lora.s * v[c] : 0.0f, hh, ll);
+                    sg_hi[(j + c) * kTP + t] = __builtin_bit_cast(uint16_t, hh);
+                    sg_lo[(j + c) * kTP + t] = __builtin_bit_cast(uint16_t, ll);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int c = tid + kThreads * i, t = c / (BK / 8), k8 = 8 * (c % (BK / 8));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t w = xv[i][e >> 1];
+                sxt[(k8 + e) * kTP + t] = uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF));
+            }
+        }
+        __syncthreads();
+
+        if (dx) {
+            for (int c0 = 0; c0 < r; c0 += 16) {
+                const int j0 = c0 + frag_k;
+                if (c0 > 0) load_a(c0, av);
+                bf16x8 hi[FM], lo[FM], aa[FK];
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int t = wm * WM + 32 * i + frag_row;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        hi[i][e] = __builtin_bit_cast(__bf16, sg_hi[(j0 + e) * kTP + t]);
+                        lo[i][e] = __builtin_bit_cast(__bf16, sg_lo[(j0 + e) * kTP + t]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < FK; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) aa[j][e] = __builtin_bit_cast(__bf16, uint16_t(av[j][e]));
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FK; ++j) {
+                        acc[i][j] = mfma32x32x16(hi[i], aa[j], acc[i][j]);
+                        acc[i][j] = mfma32x32x16(lo[i], aa[j], acc[i][j]);
+                    }
+            }
+        }
+
+        // dA share of this token tile: D[k][j] over t, 16x16x32 MFMAs; wave w owns the
+        // K sub-blocks 2w, 2w+1 (16 columns each)
+        const int l16 = lane & 15, t8 = 8 * (lane >> 4);
+        float* dpart = lora.dapart + size_t(tm) * r * K;
+        for (int jb = 0; jb < rp / 16; ++jb) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                const int kb = 2 * wave + kb2;
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ts = 0; ts < BM / 32; ++ts) {
+                    const int tt = 32 * ts + t8;
+                    const bf16x8 xa = as_bf16x8(*reinterpret_cast<const u32x4*>(&sxt[(16 * kb + l16) * kTP + tt]));
+                    const bf16x8 gh = as_bf16x8(*reinterpret_cast<const u32x4*>(&sg_hi[(16 * jb + l16) * kTP + tt]));
+                    const bf16x8 gl = as_bf16x8(*reinterpret_cast<const u32x4*>(&sg_lo[(16 * jb + l16) * kTP + tt]));
+                    d = mfma16x16x32(xa, gh, d);
+                    d = mfma16x16x32(xa, gl, d);
+                }
+                // lane holds D[k = 16 kb + 4 (lane / 16) + e][j = 16 jb + lane % 16]
+                const int j = 16 * jb + l16, kq = k0 + 16 * kb + 4 * (lane >> 4);
+                if (j < r && kq < K) *reinterpret_cast<f32x4*>(&dpart[size_t(j) * K + kq]) = d;
+            }
         }
     }
 
-    // LoRA as a K-extension (split 0 only when split): acc += (s.g)_hi . A + (s.g)_lo . A
-    for (int c0 = 0; c0 < (blockIdx.z == 0 ? r : 0); c0 += 16) {
-        bf16x8 hi[FM], lo[FM], aa[FK];
-        const int j0 = c0 + frag_k;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = m0 + wm * WM + 32 * i + frag_row;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = (row < T && j0 + e < r) ? s * g[size_t(row) * r + j0 + e] : 0.0f;
-                __bf16 h, l;
-                split_bf16(v, h, l);
-                hi[i][e] = h;
-                lo[i][e] = l;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < FK; ++j) {
-            const int col = k0 + wk * WK + 32 * j + frag_row;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint16_t av = (col < K && j0 + e < r) ? A[size_t(j0 + e) * K + col] : uint16_t(0);
-                aa[j][e] = __builtin_bit_cast(__bf16, av);
-            }
-        }
+    if (!dx) return;
+    if (!partial) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FK; ++j) {
-                acc[i][j] = mfma32x32x16(hi[i], aa[j], acc[i][j]);
-                acc[i][j] = mfma32x32x16(lo[i], aa[j], acc[i][j]);
-            }
+            for (int j = 0; j < FK; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = m0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    const int col = k0 + wk * WK + 32 * j + (lane & 31);
+                    if (row < T && col < K) dx[size_t(row) * K + col] = bf16_bits(acc[i][j][e]);
+                }
+        return;
     }
 
-    float* pdst = partial ? partial + size_t(blockIdx.z) * T * K : nullptr;
+    // split N: this split's fp32 tile; k_bwd_finish adds the splits in order
+    float* pdst = partial + size_t(tz) * T * K;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -208,25 +348,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
             for (int e = 0; e < 16; ++e) {
                 const int row = m0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 const int col = k0 + wk * WK + 32 * j + (lane & 31);
-                if (row < T && col < K) {
-                    if (pdst)
-                        pdst[size_t(row) * K + col] = acc[i][j][e];
-                    else
-                        dx[size_t(row) * K + col] = bf16_bits(acc[i][j][e]);
-                }
+                if (row < T && col < K) pdst[size_t(row) * K + col] = acc[i][j][e];
             }
 }
 
-// dX = RNbf( sum_z partial[z] ), z in increasing order (split 0 already holds the
-// LoRA term); four consecutive outputs per thread, float4 loads.
-__global__ __launch_bounds__(256) void k_split_sum_bf16_dx(const float* __restrict__ partial, int splits,
-                                                           int64_t total, uint16_t* __restrict__ out) {
-    const int64_t idx = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-    if (idx >= total) return;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(partial + idx);
-    for (int z = 1; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(partial + size_t(z) * total + idx);
-    u32x2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    *reinterpret_cast<u32x2*>(out + idx) = o;
+// The backward's reductions, in one launch: blocks [0, dx_blocks) form
+// dX = RNbf(((p0 + p1) + p2) + ...) from the split partials; the rest form
+// dA = ((d0 + d1) + d2) + ... from the token tiles' shares. Four outputs per thread.
+__global__ __launch_bounds__(256) void k_bwd_finish(const float* __restrict__ dxpart, int splits, int64_t dx_total,
+                                                    uint16_t* __restrict__ dx, int64_t dx_blocks,
+                                                    const float* __restrict__ dapart, int shares, int64_t da_total,
+                                                    float* __restrict__ dA) {
+    if (int64_t(blockIdx.x) < dx_blocks) {
+        const int64_t idx = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+        if (idx >= dx_total) return;
+        f32x4 a = *reinterpret_cast<const f32x4*>(dxpart + idx);
+        for (int z = 1; z < splits; ++z) a += *reinterpret_cast<const f32x4*>(dxpart + size_t(z) * dx_total + idx);
+        const u32x2 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+        *reinterpret_cast<u32x2*>(dx + idx) = o;
+    } else {
+        const int64_t idx = ((int64_t(blockIdx.x) - dx_blocks) * 256 + threadIdx.x) * 4;
+        if (idx >= da_total) return;
+        f32x4 a = *reinterpret_cast<const f32x4*>(dapart + idx);
+        for (int z = 1; z < shares; ++z) a += *reinterpret_cast<const f32x4*>(dapart + size_t(z) * da_total + idx);
+        *reinterpret_cast<f32x4*>(dA + idx) = a;
+    }
 }
 
 }  // namespace
@@ -235,44 +381,46 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r) {
     BwdPlan p{};
     p.bm = 128;
     p.bn = 128;
-    const int64_t tiles = cdiv(T, p.bm) * cdiv(K, p.bn);
+    p.mtiles = int(cdiv(T, p.bm));
+    p.ktiles = int(cdiv(K, p.bn));
+    const int64_t tiles = int64_t(p.mtiles) * p.ktiles;
     const int64_t nsteps = cdiv(N, kBN);
     const int64_t splits = pick_splits(tiles, nsteps, 4);
     p.steps_per_split = int(cdiv(nsteps, splits));
     p.splits = int(cdiv(nsteps, p.steps_per_split));
-    p.nslab = int(cdiv(N, 64));
-    pick_token_chunks(p.nslab, T, p.pre_chunks, p.pre_tc);
-    pick_token_chunks(cdiv(K, 64), T, p.da_chunks, p.da_tc);
+    if (r > 0) plan_lora_bwd_pre(p, N);
     size_t off = 0;
-    p.off_g = off;
-    off += align256(size_t(T) * size_t(std::max(r, 1)) * 4);
     p.off_gpart = off;
-    off += r > 0 ? align256(size_t(p.nslab) * size_t(T) * size_t(r) * 4) : 0;
-    p.off_dbpart = off;
-    off += (r > 0 && p.pre_chunks > 1) ? align256(size_t(p.pre_chunks) * size_t(N) * size_t(r) * 4) : 0;
+    off += align256(size_t(p.gparts) * size_t(T) * size_t(r) * 4);
     p.off_dapart = off;
-    off += (r > 0 && p.da_chunks > 1) ? align256(size_t(p.da_chunks) * size_t(r) * size_t(K) * 4) : 0;
+    off += r > 0 ? align256(size_t(p.mtiles) * size_t(r) * size_t(K) * 4) : 0;
     p.off_dx = off;
     off += p.splits > 1 ? align256(size_t(p.splits) * size_t(T) * size_t(K) * 4) : 0;
     p.ws_bytes = off;
     return p;
 }
 
-hipError_t launch_gemm_bwd_dx(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* dy,
-                              const uint16_t* A, int64_t T, int64_t N, int64_t K, int r, float s, uint16_t* dx,
-                              void* ws, hipStream_t stream) {
-    const dim3 grid(unsigned(cdiv(K, p.bn)), unsigned(cdiv(T, p.bm)), unsigned(p.splits));
-    const float* g = reinterpret_cast<const float*>(static_cast<char*>(ws) + p.off_g);
-    float* partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_dx) : nullptr;
-    prof_gemm_begin(stream);
-    hipLaunchKernelGGL(k_nf4_gemm_bwd_dx, grid, dim3(kThreads), 0, stream, dy, codes, absmax, g, A, int(T), int(N),
-                       int(K), r, s, p.steps_per_split, dx, partial, tables());
-    prof_gemm_end(stream);
+hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* dy,
+                           const uint16_t* x, const uint16_t* A, int64_t T, int64_t N, int64_t K, int r, float s,
+                           uint16_t* dx, float* dA, void* ws, hipStream_t stream) {
+    char* w = static_cast<char*>(ws);
+    // without dx only the LoRA part runs: one workgroup per tile, no contraction steps
+    const int splits = dx ? p.splits : 1;
+    const dim3 grid(unsigned(p.ktiles), unsigned(p.mtiles), unsigned(splits));
+    float* partial = splits > 1 ? reinterpret_cast<float*>(w + p.off_dx) : nullptr;
+    float* dapart = reinterpret_cast<float*>(w + p.off_dapart);
+    const BwdLora lora{reinterpret_cast<const float*>(w + p.off_gpart), p.gparts, A, x, dapart, r, s};
+    if (dx) prof_gemm_begin(stream);
+    hipLaunchKernelGGL(k_nf4_gemm_bwd_dx, grid, dim3(kThreads), 0, stream, dy, codes, absmax, int(T), int(N), int(K),
+                       dx ? p.steps_per_split : 0, lora, dx, partial, tables());
+    if (dx) prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splits == 1) return e;
-    const int64_t total = T * K;
-    hipLaunchKernelGGL(k_split_sum_bf16_dx, dim3(unsigned(cdiv(total / 4, 256))), dim3(256), 0, stream, partial,
-                       p.splits, total, dx);
+    if (e != hipSuccess) return e;
+    const int64_t dx_total = splits > 1 ? T * K : 0, da_total = r > 0 ? int64_t(r) * K : 0;
+    const int64_t dx_blocks = cdiv(dx_total / 4, 256), da_blocks = cdiv(da_total / 4, 256);
+    if (dx_blocks + da_blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_bwd_finish, dim3(unsigned(dx_blocks + da_blocks)), dim3(256), 0, stream, partial, splits,
+                       dx_total, dx, dx_blocks, dapart, p.mtiles, da_total, dA);
     return hipGetLastError();
 }
 

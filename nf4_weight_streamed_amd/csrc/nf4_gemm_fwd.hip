@@ -13,8 +13,9 @@
 //  - LoRA: (s.u) is split into bf16 hi + lo and contracted with B on the same
 //    accumulators (a K-extension of r per part), so y is rounded once;
 //  - split-K (for shapes with too few tiles to fill 256 CUs): fp32 partials in the
-//    caller's workspace (split 0 carries the LoRA term), summed in a fixed order
-//    and rounded once by k_split_sum_bf16.
+//    caller's workspace (split 0 carries the LoRA term), added in split order and
+//    rounded once by k_split_sum_bf16 (a kernel boundary, not in-kernel signalling:
+//    the per-XCD L2 caches are only made coherent by whole-cache maintenance).
 #include <type_traits>
 
 #include "common.h"
@@ -26,25 +27,38 @@ namespace {
 
 constexpr int kBK = 64;        // K per main-loop step (= one NF4 block)
 constexpr int kLds = kBK + 8;  // LDS row pitch in bf16 (144 B: conflict-free 16 B fragment reads)
-constexpr int kThreads = 256;
+constexpr int kFwdWaves = 4;   // waves per workgroup (each 128 tokens x 128 / kFwdWaves features)
 
 // ------------------------------------------------------------------------------------
-// 4 waves split the BN = 128 output features (32 each); every wave dequantises its own
-// weight fragments in registers, so no weight tile goes through LDS and each weight
-// element is dequantised once per workgroup. Within each 64-element K block the
-// contraction order is permuted identically for both operands: lane half h supplies
-// k = 32h + 8kk .. 32h + 8kk + 7 at sub-step kk, so one 16-byte code load per lane
-// covers the four sub-steps of a K step. A code byte indexes a 256-entry LDS table of
-// (level[low nibble], level[high nibble]) pairs: one 8-byte read, two fp32 multiplies
-// by the block's absmax and one bf16 pack per byte. Loads are raw buffer loads
-// (hardware zero outside the tensor); x and codes are fetched two K steps ahead; the
-// x tile is double-buffered in LDS with one barrier per K step.
-__global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_fwd(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
-    const float* __restrict__ u, const uint16_t* __restrict__ B, int T, int N, int K, int r, float s,
-    int steps_per_split, uint16_t* __restrict__ y, float* __restrict__ partial, Tables tab) {
-    constexpr int BM = 128, BN = 128, FM = 4;
-    constexpr int A_CHUNKS = BM * (kBK / 8) / kThreads;  // 4
+// NW waves split the BN = 128 output features (128 / NW each, FN = 4 / NW fragments of
+// 32); every wave dequantises its own weight fragments in registers, so no weight tile
+// goes through LDS and each weight element is dequantised once per workgroup. Each x
+// fragment read from LDS feeds FN MFMAs, so fewer, wider waves read less LDS per MAC.
+// Within each 64-element K block the contraction order is permuted identically for
+// both operands: lane half h supplies k = 32h + 8kk .. 32h + 8kk + 7 at sub-step kk, so
+// one 16-byte code load per lane and fragment covers the four sub-steps of a K step.
+// A code byte indexes a 256-entry LDS table of (level[low nibble], level[high nibble])
+// pairs: one 8-byte read, two fp32 multiplies by the block's absmax and one bf16 pack
+// per byte. Loads are raw buffer loads (hardware zero outside the tensor); codes are
+// fetched two K steps ahead, x one step ahead; the x tile is double-buffered in LDS
+// with one barrier per K step.
+struct FwdLora {
+    const float* upart;  // [parts][T][r] partials of u = x.A^T
+    int parts;
+    float* u_save;       // [T][r] the summed u, written by the column-0 tiles
+    const uint16_t* B;   // [N][r]
+    int r;
+    float s;
+};
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const float* __restrict__ absmax, int T,
+    int N, int K, int steps_per_split, FwdLora lora, uint16_t* __restrict__ y, float* __restrict__ partial,
+    Tables tab) {
+    constexpr int NT = 64 * NW;
+    constexpr int BM = 128, BN = 128, FM = 4, FN = 4 / NW;
+    constexpr int A_CHUNKS = BM * (kBK / 8) / NT;
 
     __shared__ __align__(16) uint16_t sA[2][BM * kLds];
     __shared__ __align__(16) float sLut[512];  // 256 (level[lo nibble], level[hi nibble]) pairs
@@ -52,15 +66,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_fwd(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int n0 = blockIdx.x * BN;
-    const int m0 = blockIdx.y * BM;
+    // tile order: token tile fastest, then column tile, then split; per-XCD ranges,
+    // so the token tiles sharing one weight slice run together in one L2
+    const uint32_t tile = xcd_tile_order(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                                         gridDim.x * gridDim.y * gridDim.z);
+    const int tm = int(tile % gridDim.y), tc = int((tile / gridDim.y) % gridDim.x);
+    const int tz = int(tile / (gridDim.y * gridDim.x));
+    const int n0 = tc * BN;
+    const int m0 = tm * BM;
     const int ksteps = K / kBK;
-    const int kb_begin = blockIdx.z * steps_per_split;
+    const int kb_begin = tz * steps_per_split;
     const int kb_end = min(kb_begin + steps_per_split, ksteps);
     const int frag_row = lane & 31;
     const int half = lane >> 5;
-    sLut[2 * tid] = tab.level[tid & 15];  // entry b: the two codes of byte b
-    sLut[2 * tid + 1] = tab.level[tid >> 4];
+    for (int i = tid; i < 256; i += NT) {  // entry b: the two codes of byte b
+        sLut[2 * i] = tab.level[i & 15];
+        sLut[2 * i + 1] = tab.level[i >> 4];
+    }
 
     // buffer views of this workgroup's rows (offsets stay far below 2^31)
     const uint32_t xrows = uint32_t(max(0, min(BM, T - m0)));
@@ -68,67 +90,88 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_fwd(
     const auto rx = make_rsrc(x + size_t(m0) * K, xrows * uint32_t(K) * 2u);
     const auto rcd = make_rsrc(codes + size_t(n0) * (K / 2), wrows * uint32_t(K / 2));
     const auto rsc = make_rsrc(absmax + size_t(n0) * (K / 64), wrows * uint32_t(K / 64) * 4u);
-    const int wrow = 32 * wave + frag_row;  // this lane's weight row within the tile
-    const uint32_t c_off = uint32_t(wrow) * uint32_t(K / 2) + uint32_t(half) * 16u;
-    const uint32_t s_off = uint32_t(wrow) * uint32_t(K / 64) * 4u;
+    uint32_t c_off[FN], s_off[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int wrow = 32 * (FN * wave + j) + frag_row;  // this lane's weight row of fragment j
+        c_off[j] = uint32_t(wrow) * uint32_t(K / 2) + uint32_t(half) * 16u;
+        s_off[j] = uint32_t(wrow) * uint32_t(K / 64) * 4u;
+    }
     uint32_t x_off[A_CHUNKS];
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
-        const int c = tid + kThreads * i;
+        const int c = tid + NT * i;
         x_off[i] = (uint32_t(c >> 3) * uint32_t(K) + uint32_t(c & 7) * 8u) * 2u;
     }
 
-    u32x4 ra[2][A_CHUNKS];
-    u32x4 rc[2];
-    float rs[2];
-    auto gload = [&](int kb, u32x4 (&xa)[A_CHUNKS], u32x4& cw, float& sc) {
+    u32x4 ra[A_CHUNKS];
+    u32x4 rc[2][FN];
+    float rs[2][FN];
+    auto gload_x = [&](int kb) {
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) xa[i] = buf_load16(rx, x_off[i] + uint32_t(kb) * (kBK * 2));
-        cw = buf_load16(rcd, c_off + uint32_t(kb) * 32u);
-        sc = buf_load_f32(rsc, s_off + uint32_t(kb) * 4u);
+        for (int i = 0; i < A_CHUNKS; ++i) ra[i] = buf_load16(rx, x_off[i] + uint32_t(kb) * (kBK * 2));
     };
-    auto store_x = [&](const u32x4 (&xa)[A_CHUNKS], int buf) {
+    auto gload_w = [&](int kb, u32x4 (&cw)[FN], float (&sc)[FN]) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            cw[j] = buf_load16(rcd, c_off[j] + uint32_t(kb) * 32u);
+            sc[j] = buf_load_f32(rsc, s_off[j] + uint32_t(kb) * 4u);
+        }
+    };
+    auto store_x = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
-            const int c = tid + kThreads * i;
-            *reinterpret_cast<u32x4*>(&sA[buf][(c >> 3) * kLds + (c & 7) * 8]) = xa[i];
+            const int c = tid + NT * i;
+            *reinterpret_cast<u32x4*>(&sA[buf][(c >> 3) * kLds + (c & 7) * 8]) = ra[i];
         }
     };
     const char* lut = reinterpret_cast<const char*>(sLut);
-    auto dequant = [&](const u32x4& cw, float sc, bf16x8 (&wf)[4]) {
+    bf16x8 wf[FN][4];
+    auto dequant = [&](const u32x4 (&cw)[FN], const float (&sc)[FN]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t w = cw[q];
-            u32x4 o;
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float2 lv = *reinterpret_cast<const float2*>(lut + (((w >> (8 * b)) & 0xFFu) << 3));
-                // level * absmax in fp32, then RNbf: the format's two roundings
-                o[b] = pack_bf16x2(lv.x * sc, lv.y * sc);
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w = cw[j][q];
+                u32x4 o;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const float2 lv = *reinterpret_cast<const float2*>(lut + (((w >> (8 * b)) & 0xFFu) << 3));
+                    // level * absmax in fp32, then RNbf: the format's two roundings
+                    o[b] = pack_bf16x2(lv.x * sc[j], lv.y * sc[j]);
+                }
+                wf[j][q] = as_bf16x8(o);
             }
-            wf[q] = as_bf16x8(o);
-        }
     };
 
-    f32x16 acc[FM];
+    f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     if (kb_begin < kb_end) {
-        bf16x8 wf[4];
-        gload(kb_begin, ra[0], rc[0], rs[0]);
-        if (kb_begin + 1 < kb_end) gload(kb_begin + 1, ra[1], rc[1], rs[1]);
-        store_x(ra[0], 0);
+        gload_x(kb_begin);
+        gload_w(kb_begin, rc[0], rs[0]);
+        gload_w(kb_begin + 1, rc[1], rs[1]);
+        store_x(0);
         __syncthreads();  // sLut and x tile 0 visible
-        dequant(rc[0], rs[0], wf);
+        dequant(rc[0], rs[0]);
         // one K step; C is the compile-time register/LDS buffer of step kb (the loop is
         // unrolled by two so that no register array is indexed at run time)
+        // Loads are issued unconditionally (a step past the end reads data that is never
+        // used, or zeros beyond the buffer): with a fixed issue pattern the compiler's
+        // wait counts stay exact and never drain the next step's loads.
         auto step = [&](int kb, auto c_) {
             constexpr int C = decltype(c_)::value;
             const bool more = kb + 1 < kb_end;
-            if (kb + 2 < kb_end) gload(kb + 2, ra[C], rc[C], rs[C]);  // step kb's registers are consumed
+            gload_x(kb + 1);                // ra was stored last step
+            gload_w(kb + 2, rc[C], rs[C]);  // step kb's codes are already in wf
+            // keep the loads here, ahead of the MFMAs: sinking them next to their use
+            // would expose their full latency
+            __builtin_amdgcn_sched_barrier(0);
             const uint16_t* a_base = &sA[C][0];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -136,72 +179,156 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_fwd(
                 for (int i = 0; i < FM; ++i) {
                     const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(
                         a_base + (32 * i + frag_row) * kLds + 32 * half + 8 * kk));
-                    acc[i] = mfma32x32x16(af, wf[kk], acc[i]);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(af, wf[j][kk], acc[i][j]);
                 }
             }
             if (more) {
-                dequant(rc[C ^ 1], rs[C ^ 1], wf);  // next step's weights, independent of the MFMAs
-                store_x(ra[C ^ 1], C ^ 1);
+                dequant(rc[C ^ 1], rs[C ^ 1]);  // next step's weights, independent of the MFMAs
+                store_x(C ^ 1);
             }
             __syncthreads();
         };
-        for (int kb = kb_begin; kb < kb_end; kb += 2) {
+        int kb = kb_begin;
+        for (; kb + 1 < kb_end; kb += 2) {
             step(kb, std::integral_constant<int, 0>{});
-            if (kb + 1 < kb_end) step(kb + 1, std::integral_constant<int, 1>{});
+            step(kb + 1, std::integral_constant<int, 1>{});
+        }
+        if (kb < kb_end) step(kb, std::integral_constant<int, 0>{});
+    }
+
+    // LoRA as a K-extension (split 0 only when split): acc += (s.u)_hi . B^T + (s.u)_lo . B^T.
+    // u = sum of the partials in partial order, staged as bf16 hi/lo [t][j] in the (now
+    // free) x buffers; the column-0 tiles also store it as u_save. B rows past N and
+    // entries j >= r load from beyond the buffers (zero).
+    const int r = lora.r;
+    if (tz == 0 && r > 0) {
+        uint16_t* su_hi = &sA[0][0];
+        uint16_t* su_lo = &sA[1][0];
+        const int rp = (r + 15) & ~15;
+        // the partials region is padded to 256 bytes: 16-byte loads at 4-byte aligned
+        // offsets stay inside it; lanes j >= r are masked below
+        const uint32_t ubytes = (uint32_t(lora.parts) * uint32_t(T) * uint32_t(r) * 4u + 255u) & ~255u;
+        const auto rup = make_rsrc(lora.upart, ubytes);
+        const auto rb = make_rsrc(lora.B, uint32_t(N) * uint32_t(r) * 2u);
+        const bool write_u = tc == 0;
+        // B values of one 16-rank slice for this lane's fragments (lane: column n, ranks
+        // c0 + 8 (lane / 32) .. + 7): one 16-byte load when rows are 16-byte multiples
+        auto load_b = [&](int c0, u32x4 (&bv)[FN]) {
+            const int jr = c0 + 8 * half;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const uint32_t col = uint32_t(n0 + 32 * (FN * wave + j) + frag_row);
+                if (r % 8 == 0) {
+                    bv[j] = buf_load16(rb, jr < r ? (col * uint32_t(r) + uint32_t(jr)) * 2u : kOutOfRange);
+                } else {
+                    uint32_t h[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        h[e] = __builtin_amdgcn_raw_buffer_load_b16(
+                            rb, int(jr + e < r ? (col * uint32_t(r) + uint32_t(jr + e)) * 2u : kOutOfRange), 0, 0);
+                    bv[j] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+                }
+            }
+        };
+        u32x4 bv[FN];
+        load_b(0, bv);
+        // s.u staged as bf16 hi/lo [t][j]: items of 4 ranks, every load issued first
+        constexpr int UI = BM * 4 / NT;  // (t, 4-rank group) items per thread per 16 ranks
+        for (int jb = 0; jb < rp / 16; ++jb) {
+            f32x4 pv[UI][kMaxDownParts];
+#pragma unroll
+            for (int i = 0; i < UI; ++i) {
+                const int o = tid + NT * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
+                const bool ok = m0 + t < T && j < r;
+                const uint32_t off = (uint32_t(m0 + t) * uint32_t(r) + uint32_t(j)) * 4u;
+#pragma unroll
+                for (int pp = 0; pp < kMaxDownParts; ++pp)
+                    pv[i][pp] = __builtin_bit_cast(
+                        f32x4, buf_load16(rup, ok && pp < lora.parts ? off + uint32_t(pp) * uint32_t(T) * uint32_t(r) * 4u
+                                                                     : kOutOfRange));
+            }
+#pragma unroll
+            for (int i = 0; i < UI; ++i) {
+                const int o = tid + NT * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
+                f32x4 v = pv[i][0];
+#pragma unroll
+                for (int pp = 1; pp < kMaxDownParts; ++pp)
+                    if (pp < lora.parts) v += pv[i][pp];
+                uint16_t hb[4], lb[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float vc = j + c < r ? v[c] : 0.0f;
+                    if (write_u && m0 + t < T && j + c < r) lora.u_save[size_t(m0 + t) * r + j + c] = vc;
+                    __bf16 hh, ll;
+                    split_bf16(lora.s * vc, hh, ll);
+                    hb[c] = __builtin_bit_cast(uint16_t, hh);
+                    lb[c] = __builtin_bit_cast(uint16_t, ll);
+                }
+                *reinterpret_cast<u32x2*>(&su_hi[t * kLds + j]) = u32x2{hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16)};
+                *reinterpret_cast<u32x2*>(&su_lo[t * kLds + j]) = u32x2{lb[0] | (uint32_t(lb[1]) << 16), lb[2] | (uint32_t(lb[3]) << 16)};
+            }
+        }
+        __syncthreads();
+        for (int c0 = 0; c0 < r; c0 += 16) {
+            const int j0 = c0 + 8 * half;
+            if (c0 > 0) load_b(c0, bv);
+            bf16x8 bb[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bb[j] = as_bf16x8(bv[j]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int t = 32 * i + frag_row;
+                const bf16x8 hi = as_bf16x8(*reinterpret_cast<const u32x4*>(&su_hi[t * kLds + j0]));
+                const bf16x8 lo = as_bf16x8(*reinterpret_cast<const u32x4*>(&su_lo[t * kLds + j0]));
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    acc[i][j] = mfma32x32x16(hi, bb[j], acc[i][j]);
+                    acc[i][j] = mfma32x32x16(lo, bb[j], acc[i][j]);
+                }
+            }
         }
     }
 
-    // LoRA as a K-extension (split 0 only when split): acc += (s.u)_hi . B^T + (s.u)_lo . B^T
-    const int col = n0 + 32 * wave + frag_row;
-    for (int c0 = 0; c0 < (blockIdx.z == 0 ? r : 0); c0 += 16) {
-        bf16x8 bb;
-        const int j0 = c0 + 8 * half;
+    if (!partial) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint16_t bv = (col < N && j0 + e < r) ? B[size_t(col) * r + j0 + e] : uint16_t(0);
-            bb[e] = __builtin_bit_cast(__bf16, bv);
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + 32 * (FN * wave + j) + frag_row;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
+                    if (row < T && col < N) y[size_t(row) * N + col] = bf16_bits(acc[i][j][e]);
+                }
         }
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = m0 + 32 * i + frag_row;
-            bf16x8 hi, lo;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = (row < T && j0 + e < r) ? s * u[size_t(row) * r + j0 + e] : 0.0f;
-                __bf16 hh, ll;
-                split_bf16(v, hh, ll);
-                hi[e] = hh;
-                lo[e] = ll;
-            }
-            acc[i] = mfma32x32x16(hi, bb, acc[i]);
-            acc[i] = mfma32x32x16(lo, bb, acc[i]);
-        }
+        return;
     }
 
-    float* pdst = partial ? partial + size_t(blockIdx.z) * T * N : nullptr;
+    // split K: this split's fp32 tile; k_split_sum_bf16 adds the splits in order
+    float* pdst = partial + size_t(tz) * T * N;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) {
+        const int col = n0 + 32 * (FN * wave + j) + frag_row;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (row < T && col < N) {
-                if (pdst)
-                    pdst[size_t(row) * N + col] = acc[i][e];
-                else
-                    y[size_t(row) * N + col] = bf16_bits(acc[i][e]);
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
+                if (row < T && col < N) pdst[size_t(row) * N + col] = acc[i][j][e];
             }
-        }
+    }
 }
 
-// y = RNbf( sum_z partial[z] ), z in increasing order (split 0 already holds the LoRA
-// term); four consecutive outputs per thread, float4 loads.
+// y = RNbf(((p0 + p1) + p2) + ...): the split partials added in split order (split 0
+// holds the LoRA term), rounded once; four consecutive outputs per thread.
 __global__ __launch_bounds__(256) void k_split_sum_bf16(const float* __restrict__ partial, int splits,
                                                         int64_t total, uint16_t* __restrict__ out) {
     const int64_t idx = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
     if (idx >= total) return;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(partial + idx);
-    for (int z = 1; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(partial + size_t(z) * total + idx);
-    u32x2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    f32x4 a = *reinterpret_cast<const f32x4*>(partial + idx);
+    for (int z = 1; z < splits; ++z) a += *reinterpret_cast<const f32x4*>(partial + size_t(z) * total + idx);
+    const u32x2 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
     *reinterpret_cast<u32x2*>(out + idx) = o;
 }
 
@@ -216,28 +343,27 @@ FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r) {
     const int64_t splits = pick_splits(tiles, ksteps, 4);
     p.steps_per_split = int(cdiv(ksteps, splits));
     p.splits = int(cdiv(ksteps, p.steps_per_split));
-    // u = x.A^T: 16-token blocks; split K until there are about 512 workgroups
-    const int64_t tb = cdiv(T, 16), ks32 = K / 32;
-    int64_t ds = std::min<int64_t>(cdiv(512, tb), std::max<int64_t>(1, ks32 / 8));
-    ds = std::max<int64_t>(ds, 1);
-    p.down_steps = int(cdiv(ks32, ds));
-    p.down_splits = r > 0 ? int(cdiv(ks32, p.down_steps)) : 0;
-    p.off_upart = 0;
-    const size_t upart = p.down_splits > 1 ? align256(size_t(p.down_splits) * size_t(T) * size_t(r) * 4) : 0;
-    p.off_ypart = upart;
-    const size_t ypart = p.splits > 1 ? align256(size_t(p.splits) * size_t(T) * size_t(N) * 4) : 0;
-    p.ws_bytes = upart + ypart;
+    if (r > 0) plan_lora_down(p, K);
+    size_t off = 0;
+    p.off_upart = off;
+    off += align256(size_t(p.down_parts) * size_t(T) * size_t(r) * 4);
+    p.off_ypart = off;
+    off += p.splits > 1 ? align256(size_t(p.splits) * size_t(T) * size_t(N) * 4) : 0;
+    p.ws_bytes = off;
     return p;
 }
 
 hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* x,
-                           const float* u, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,
-                           uint16_t* y, void* ws, hipStream_t stream) {
+                           const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s, uint16_t* y,
+                           float* u_save, void* ws, hipStream_t stream) {
+    char* w = static_cast<char*>(ws);
     const dim3 grid(unsigned(cdiv(N, p.bn)), unsigned(cdiv(T, p.bm)), unsigned(p.splits));
-    float* partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ypart) : nullptr;
+    float* partial = p.splits > 1 ? reinterpret_cast<float*>(w + p.off_ypart) : nullptr;
+    const FwdLora lora{r > 0 ? reinterpret_cast<const float*>(w + p.off_upart) : nullptr, p.down_parts, u_save, B,
+                       r, s};
     prof_gemm_begin(stream);
-    hipLaunchKernelGGL(k_nf4_gemm_fwd, grid, dim3(kThreads), 0, stream, x, codes, absmax, u, B, int(T), int(N), int(K),
-                       r, s, p.steps_per_split, y, partial, tables());
+    hipLaunchKernelGGL(k_nf4_gemm_fwd<kFwdWaves>, grid, dim3(64 * kFwdWaves), 0, stream, x, codes, absmax, int(T),
+                       int(N), int(K), p.steps_per_split, lora, y, partial, tables());
     prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;

@@ -64,6 +64,8 @@ def test_single_linear_workload(gpu_lib):
     (200, 512, 3584, 16),    # skinny N with split-K (k/v-like)
     (96, 3584, 512, 16),     # long N, short K
     (513, 160, 192, 16),     # T one past a tile boundary
+    (150, 208, 384, 5),      # odd rank: partial 4-rank groups, unaligned rows of u, g, B
+    (129, 3584, 640, 12),    # rank 12: B rows not a 16-byte multiple; dX split over N
 ])
 def test_shapes(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
