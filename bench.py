@@ -50,6 +50,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
         self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
 
     def create(self) -> int:
         e = C.c_void_p()
@@ -61,6 +62,9 @@ class HipEvents:
         ms = C.c_float()
         assert self.hip.hipEventElapsedTime(C.byref(ms), C.c_void_p(a), C.c_void_p(b)) == 0
         return float(ms.value)
+
+    def record(self, e: int, stream: int) -> None:
+        assert self.hip.hipEventRecord(C.c_void_p(e), C.c_void_p(stream)) == 0
 
     def destroy(self, e: int) -> None:
         self.hip.hipEventDestroy(C.c_void_p(e))
@@ -274,6 +278,73 @@ def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2
     }
 
 
+SMALL_T = (1, 8, 16, 32, 64)
+SMALL_T_SHAPES = [  # (model, projection, N, K)
+    ("7b", "q", 3584, 3584), ("7b", "k", 512, 3584), ("7b", "gate", 18944, 3584), ("7b", "down", 3584, 18944),
+    ("72b", "q", 8192, 8192), ("72b", "k", 1024, 8192), ("72b", "gate", 29568, 8192), ("72b", "down", 8192, 29568),
+]
+
+
+def small_t_sweep(lib, torch, ev: "HipEvents", reps: int = 8) -> dict:
+    """Device time of one projection's forward and backward at T in {1, 8, 16, 32, 64}
+    against HBM bytes = 1.125NK + T(6K + 4N + 8r) + 8r(N + K) (the base is read once in
+    the forward and once in the backward). Four weight sets (>= 512 MB for the large
+    shapes) are cycled so that the 256 MB last-level cache cannot serve repeated reads."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(42)
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for model, proj, n, k in SMALL_T_SHAPES:
+        nsets = 4 if n * k * 0.5625 * 4 >= 512e6 else max(4, int(512e6 // (n * k * 0.5625)) + 1)
+        sets = []
+        for _ in range(nsets):
+            w = (torch.randn(n, k, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+            sets.append(lib.quantize(w))
+            del w
+        a = ((torch.rand(RANK, k, generator=g, device="cuda") * 2 - 1) / k ** 0.5).to(torch.bfloat16)
+        b = (torch.randn(n, RANK, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+        for t in SMALL_T:
+            x = torch.randn(t, k, generator=g, device="cuda").to(torch.bfloat16)
+            dy = torch.randn(t, n, generator=g, device="cuda").to(torch.bfloat16)
+            y = torch.empty(t, n, dtype=torch.bfloat16, device="cuda")
+            u = torch.empty(t, RANK, dtype=torch.float32, device="cuda")
+            dx = torch.empty(t, k, dtype=torch.bfloat16, device="cuda")
+            da = torch.empty(RANK, k, dtype=torch.float32, device="cuda")
+            db = torch.empty(n, RANK, dtype=torch.float32, device="cuda")
+            wsf = lib.workspace(lib.fwd_workspace_bytes(t, n, k, RANK))
+            wsb = lib.workspace(lib.bwd_workspace_bytes(t, n, k, RANK))
+
+            def fwd(i):
+                c, s_ = sets[i % nsets]
+                lib.lora_linear_fwd(c, s_, x, a, b, ALPHA, y=y, u=u, ws=wsf)
+
+            def bwd(i):
+                c, s_ = sets[i % nsets]
+                lib.lora_linear_bwd(c, s_, x, u, dy, a, b, ALPHA, dx=dx, dA=da, dB=db, ws=wsb)
+
+            res = {}
+            for name, fn in (("fwd", fwd), ("bwd", bwd)):
+                for i in range(nsets):
+                    fn(i)
+                e0, e1 = ev.create(), ev.create()
+                ev.record(e0, stream)
+                for i in range(reps * nsets):
+                    fn(i)
+                ev.record(e1, stream)
+                res[name] = ev.elapsed_ms(e0, e1) * 1e3 / (reps * nsets)
+                ev.destroy(e0)
+                ev.destroy(e1)
+            nbytes = 1.125 * n * k + t * (6 * k + 4 * n + 8 * RANK) + 8 * RANK * (n + k)
+            us = res["fwd"] + res["bwd"]
+            rows.append({"model": model, "proj": proj, "N": n, "K": k, "T": t, "fwd_us": round(res["fwd"], 2),
+                         "bwd_us": round(res["bwd"], 2), "hbm_gbs": round(nbytes / us / 1e3, 1),
+                         "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del sets
+        torch.cuda.empty_cache()
+    return {"rows": rows, "bytes_formula": "1.125NK + T(6K + 4N + 8r) + 8r(N + K)", "peak_gbs": HBM_PEAK_GBS,
+            "weight_sets_cycled": ">= 4, >= 512 MB", "r": RANK}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +355,8 @@ def main() -> int:
     ap.add_argument("--block-size", type=int, default=4)
     ap.add_argument("--stack-tokens", type=int, default=512)
     ap.add_argument("--stack-steps", type=int, default=3)
+    ap.add_argument("--small-t-sweep", action="store_true",
+                    help="instead of the layer step: per-projection fwd/bwd device time at T = 1..64 vs HBM bytes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="launch one 1 GiB read + 1 GiB write elementwise kernel first (counter calibration)")
     args = ap.parse_args()
@@ -297,6 +370,11 @@ def main() -> int:
     from nf4_weight_streamed_amd import lib
 
     torch.cuda.set_device(0)
+    if args.small_t_sweep:
+        out = {"metric": "NF4-LoRA linear fwd+bwd device time at small T; % of HBM roofline", "n_gpus": 1,
+               "dtype": "bf16", "data": "synthetic", "small_t": small_t_sweep(lib, torch, HipEvents())}
+        print(json.dumps(out), flush=True)
+        return 0
     if args.copy_calibration:
         copy_calibration(torch)
     layer = build_layer(lib, torch)

@@ -206,6 +206,9 @@ int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, in
                     fn, p.ws_bytes, (long long)T, (long long)N, (long long)K, r, ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float scale = lora_scale(alpha, r);
+    if (p.skinny)
+        return hip_status(launch_skinny_fwd(p.sk, codes, absmax, x, A, B, T, N, K, r, scale, y, u_save, ws, s),
+                          "nf4_lora_linear_fwd (few-token path)");
     if (r > 0) {
         float* upart = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_upart);
         st = hip_status(launch_lora_down(p, x, A, T, K, r, upart, s), "nf4_lora_linear_fwd (x.A^T)");
@@ -249,6 +252,9 @@ int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, in
                         "nf4_lora_linear_bwd (g, dB)");
         if (st != NF4_OK) return st;
     }
+    if (p.skinny)
+        return hip_status(launch_skinny_bwd(p.sk, p, codes, absmax, dy, x, A, T, N, K, r, scale, dx, dA, ws, s),
+                          "nf4_lora_linear_bwd (few-token path)");
     // dX (when requested) with its LoRA term, and dA
     return hip_status(launch_gemm_bwd(p, codes, absmax, dy, x, A, T, N, K, r, scale, dx, dA, ws, s),
                       "nf4_lora_linear_bwd (dX, dA)");

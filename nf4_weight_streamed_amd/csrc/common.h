@@ -33,7 +33,25 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t 
 
 // Partial counts of the skinny LoRA products, summed per tile by the GEMM kernels.
 constexpr int kMaxDownParts = 4;  // K ranges of u = x.A^T
-constexpr int kMaxGParts = 8;     // N ranges of g = dY.B
+constexpr int kMaxGParts = 8;     // N ranges of g = dY.B (128-token path)
+constexpr int kMaxGPartsFew = 64; // N ranges of g = dY.B (few-token path: summed once per token)
+
+// Few-token path (T <= kSkinnyT; measured faster than the 128-token kernels up to T = 16,
+// slower from T = 32): streaming kernels with 16-token MFMA blocks and fp32
+// partials over a split contraction, finished (split sum + LoRA + rounding) by a
+// second kernel. Workspace: [partials | u partials] (forward) / [g partials | dX
+// partials] (backward).
+constexpr int64_t kSkinnyT = 16;
+struct SkinnyPlan {
+    int row_blocks;       // forward: 128-row workgroups
+    int col_blocks;       // backward: 128-column workgroups
+    int splits;           // contraction splits (grid y)
+    int steps_per_split;
+    size_t off_part, off_upart;  // workspace offsets (bytes)
+    size_t ws_bytes;
+};
+SkinnyPlan plan_skinny_fwd(int64_t T, int64_t N, int64_t K, int r);
+SkinnyPlan plan_skinny_bwd(int64_t T, int64_t N, int64_t K);
 
 // Forward plan: how the kernels are split for a shape (a pure function of the shape,
 // so repeated calls - streamed or resident - launch identical grids). Workspace:
@@ -46,6 +64,8 @@ struct FwdPlan {
     int down_steps;       // 32-wide K steps per range
     size_t off_upart, off_ypart;  // workspace offsets (bytes)
     size_t ws_bytes;
+    bool skinny;          // few-token path (then only sk and ws_bytes apply)
+    SkinnyPlan sk;
 };
 FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r);
 void plan_lora_down(FwdPlan& p, int64_t K);
@@ -60,9 +80,11 @@ struct BwdPlan {
     int gparts, gsteps;    // N ranges of g = dY.B (partials summed by the GEMM), 128-feature chunks each
     size_t off_gpart, off_dapart, off_dx;  // workspace offsets (bytes)
     size_t ws_bytes;
+    bool skinny;           // few-token path: g partials and dX partials (sk) at off_gpart / off_dx
+    SkinnyPlan sk;
 };
 BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r);
-void plan_lora_bwd_pre(BwdPlan& p, int64_t N);
+void plan_lora_bwd_pre(BwdPlan& p, int64_t N, int max_parts);  // g partials over N ranges
 
 hipError_t launch_lora_down(const FwdPlan& p, const uint16_t* x, const uint16_t* A, int64_t T, int64_t K, int r,
                             float* upart, hipStream_t stream);
@@ -74,6 +96,13 @@ hipError_t launch_lora_bwd_pre(const BwdPlan& p, const uint16_t* dy, const uint1
 hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* dy,
                            const uint16_t* x, const uint16_t* A, int64_t T, int64_t N, int64_t K, int r, float s,
                            uint16_t* dx, float* dA, void* ws, hipStream_t stream);
+
+hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* x,
+                             const uint16_t* A, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,
+                             uint16_t* y, float* u_save, void* ws, hipStream_t stream);
+hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8_t* codes, const float* absmax,
+                             const uint16_t* dy, const uint16_t* x, const uint16_t* A, int64_t T, int64_t N,
+                             int64_t K, int r, float s, uint16_t* dx, float* dA, void* ws, hipStream_t stream);
 
 // Instrumentation events around the next fused GEMM launch (abi.cpp); no-ops unless requested.
 void prof_gemm_begin(hipStream_t stream);

@@ -284,9 +284,9 @@ void plan_lora_down(FwdPlan& p, int64_t K) {
     p.down_parts = int(cdiv(ks32, p.down_steps));
 }
 
-void plan_lora_bwd_pre(BwdPlan& p, int64_t N) {
+void plan_lora_bwd_pre(BwdPlan& p, int64_t N, int max_parts) {
     const int64_t chunks = cdiv(N, kGChunk);
-    const int64_t parts = std::max<int64_t>(1, std::min<int64_t>(kMaxGParts, chunks / 2));
+    const int64_t parts = std::max<int64_t>(1, std::min<int64_t>(max_parts, chunks / 2));
     p.gsteps = int(cdiv(chunks, parts));
     p.gparts = int(cdiv(chunks, p.gsteps));
 }

@@ -379,6 +379,15 @@ __global__ __launch_bounds__(256) void k_bwd_finish(const float* __restrict__ dx
 
 BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r) {
     BwdPlan p{};
+    if (T <= kSkinnyT) {
+        p.skinny = true;
+        p.sk = plan_skinny_bwd(T, N, K);
+        if (r > 0) plan_lora_bwd_pre(p, N, kMaxGPartsFew);
+        p.off_gpart = 0;
+        p.off_dx = align256(size_t(p.gparts) * size_t(T) * size_t(r) * 4);
+        p.ws_bytes = p.off_dx + p.sk.ws_bytes;
+        return p;
+    }
     p.bm = 128;
     p.bn = 128;
     p.mtiles = int(cdiv(T, p.bm));
@@ -388,7 +397,7 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r) {
     const int64_t splits = pick_splits(tiles, nsteps, 4);
     p.steps_per_split = int(cdiv(nsteps, splits));
     p.splits = int(cdiv(nsteps, p.steps_per_split));
-    if (r > 0) plan_lora_bwd_pre(p, N);
+    if (r > 0) plan_lora_bwd_pre(p, N, kMaxGParts);
     size_t off = 0;
     p.off_gpart = off;
     off += align256(size_t(p.gparts) * size_t(T) * size_t(r) * 4);

@@ -336,6 +336,12 @@ __global__ __launch_bounds__(256) void k_split_sum_bf16(const float* __restrict_
 
 FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r) {
     FwdPlan p{};
+    if (T <= kSkinnyT) {
+        p.skinny = true;
+        p.sk = plan_skinny_fwd(T, N, K, r);
+        p.ws_bytes = p.sk.ws_bytes;
+        return p;
+    }
     p.bm = 128;
     p.bn = 128;
     const int64_t tiles = cdiv(T, p.bm) * cdiv(N, p.bn);

@@ -71,6 +71,40 @@ def test_shapes(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
 
 
+@pytest.mark.parametrize("t,n,k,r", [
+    (1, 3584, 3584, 16),     # one token, q-shaped: forward split over K, backward over N
+    (7, 208, 384, 5),        # odd rank, ragged rows (208 = 128 + 80)
+    (16, 512, 3584, 64),     # the largest few-token batch at the maximum rank
+    (3, 144, 128, 0),        # base only
+    (12, 4096, 256, 16),     # long N, short K (one K step)
+])
+def test_few_token_path(gpu_lib, t, n, k, r):
+    """T <= 16 runs the streaming kernels (16-token MFMA blocks, split contraction)."""
+    _check_case(gpu_lib, t, n, k, r)
+
+
+def test_few_token_dx_skipped(gpu_lib):
+    case = S.linear_case(4, 256, 512)
+    wq, dev = _prepare(gpu_lib, case, 16)
+    y, u = gpu_lib.lora_linear_fwd(dev["codes"], dev["absmax"], dev["x"], dev["A"], dev["B"], 32.0)
+    dx, da, db = gpu_lib.lora_linear_bwd(dev["codes"], dev["absmax"], dev["x"], u, dev["dY"], dev["A"], dev["B"],
+                                         32.0, need_dx=False)
+    torch.cuda.synchronize()
+    assert dx is None
+    _, da_ref, db_ref = O.lora_linear_bwd(case["x"], wq, case["A"], case["B"], 32.0, case["dY"])
+    check_f32_output(f32_of(da), da_ref, "dA")
+    check_f32_output(f32_of(db), db_ref, "dB")
+
+
+def test_few_token_repeat_is_bitwise_identical(gpu_lib):
+    case = S.linear_case(9, 3584, 3584, proj="q")
+    _, dev = _prepare(gpu_lib, case, 16)
+    a = _run(gpu_lib, dev, 32.0)
+    b = _run(gpu_lib, dev, 32.0)
+    for p, q in zip(a, b):
+        assert torch.equal(p, q)
+
+
 def test_base_only_rank0(gpu_lib):
     _check_case(gpu_lib, 100, 256, 512, 0)
 
