@@ -208,6 +208,42 @@ def cpu_baseline(seconds_budget: float = 12.0) -> dict:
     }
 
 
+def measured_mfma_tflops(lib, torch, ev: "HipEvents") -> float:
+    """bf16 MFMA issue rate with the GEMMs' instruction (v_mfma_f32_32x32x16_bf16): 512
+    workgroups x 4 waves, each 8 independent MFMAs per round on registers."""
+    wg, iters = 512, 4000
+    out = torch.empty(4 * wg, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    lib.probe_mfma(out, wg, 100)
+    e0, e1 = ev.create(), ev.create()
+    ev.record(e0, stream)
+    lib.probe_mfma(out, wg, iters)
+    ev.record(e1, stream)
+    ms = ev.elapsed_ms(e0, e1)
+    ev.destroy(e0)
+    ev.destroy(e1)
+    return wg * 4 * iters * 8 * 32768 / (ms * 1e-3) / 1e12  # 32x32x16 MACs x 2 per MFMA
+
+
+def measured_copy_gbs(torch, ev: "HipEvents", nbytes: int = 1 << 30) -> float:
+    """Device-to-device copy of 1 GiB (read + write counted): the measured HBM ceiling."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = ev.create(), ev.create()
+    ev.record(e0, stream)
+    for _ in range(5):
+        dst.copy_(src)
+    ev.record(e1, stream)
+    ms = ev.elapsed_ms(e0, e1) / 5
+    ev.destroy(e0)
+    ev.destroy(e1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def pinned_h2d_gbs(torch, nbytes: int = 1 << 30) -> float:
     """Pinned host -> device hipMemcpyAsync bandwidth on a side stream (best of 3)."""
     h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
@@ -371,8 +407,14 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     if args.small_t_sweep:
+        ev = HipEvents()
+        sweep = small_t_sweep(lib, torch, ev)
+        copy_meas = measured_copy_gbs(torch, ev)
+        for row in sweep["rows"]:
+            row["hbm_frac_vs_measured_copy"] = round(row["hbm_gbs"] / copy_meas, 4)
+        sweep["hbm_copy_gbs_measured"] = round(copy_meas, 1)
         out = {"metric": "NF4-LoRA linear fwd+bwd device time at small T; % of HBM roofline", "n_gpus": 1,
-               "dtype": "bf16", "data": "synthetic", "small_t": small_t_sweep(lib, torch, HipEvents())}
+               "dtype": "bf16", "data": "synthetic", "small_t": sweep}
         print(json.dumps(out), flush=True)
         return 0
     if args.copy_calibration:
@@ -397,6 +439,8 @@ def main() -> int:
     for e in starts + stops:
         ev.destroy(e)
 
+    mfma_meas = measured_mfma_tflops(lib, torch, ev)
+    copy_meas = measured_copy_gbs(torch, ev)
     ms = dt * 1000.0 / args.steps
     tokens_per_s = T_TOKENS / (dt / args.steps)
     tflops = step_flops(T_TOKENS, RANK) / (dt / args.steps) / 1e12
@@ -432,11 +476,19 @@ def main() -> int:
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "peak_measured": round(mfma_meas, 1),
+            "frac_vs_measured": round(achieved / mfma_meas, 4),
             "traffic": measured_traffic(),
             "avg_launch_us": round(avg_gemm_s * 1e6, 2),
             "algorithmic_flops_per_launch": gate_flops,
             "algorithmic_bytes_per_launch": gate_bytes,
             "hbm_gbs_algorithmic": round(gate_bytes / avg_gemm_s / 1e9, 1),
+        },
+        "denominators": {
+            "mfma_bf16_tflops_published": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_bf16_tflops_measured": round(mfma_meas, 1),
+            "hbm_gbs_published": HBM_PEAK_GBS,
+            "hbm_copy_gbs_measured": round(copy_meas, 1),
         },
     }
     if args.streamed != "none":

@@ -199,6 +199,17 @@ int nf4_repeat_kv_bwd(const uint16_t* da, int64_t T, int64_t q, int64_t kv, int6
  */
 int nf4_profile_next_gemm(void* start_event, void* stop_event);
 
+/*
+ * Instrumentation: the bf16 MFMA issue rate, for reporting achieved TFLOP/s against a
+ * measured ceiling beside the published one. Launches `workgroups` workgroups of 4
+ * waves on `stream`; each wave runs `iters` rounds of 8 independent
+ * v_mfma_f32_32x32x16_bf16 on register operands (32768 * 8 * iters FLOP per wave) and
+ * writes one float to out[4 * workgroup + wave] (device fp32, 4 * workgroups
+ * entries, caller-owned). Time it with events on the same stream. NF4_E_ARG for
+ * workgroups or iters < 1 or a NULL out.
+ */
+int nf4_probe_mfma(float* out, int workgroups, int iters, nf4_stream stream);
+
 /* ------------------------------------------------------------------ stream pool
  * Blockwise residency of the frozen base ([hn] main comment; [api]
  * "patch_hf_model" Behavior 5-6; [consumer] "What you need besides VRAM",

@@ -142,6 +142,12 @@ const char* nf4_last_error(void) { return g_error.c_str(); }
 
 int nf4_abi_version(void) { return 1; }
 
+int nf4_probe_mfma(float* out, int workgroups, int iters, nf4_stream stream) {
+    if (!out || workgroups < 1 || iters < 1)
+        return fail(NF4_E_ARG, "nf4_probe_mfma: need out != NULL, workgroups >= 1, iters >= 1");
+    return hip_status(launch_probe_mfma(out, workgroups, iters, static_cast<hipStream_t>(stream)), "nf4_probe_mfma");
+}
+
 int nf4_profile_next_gemm(void* start_event, void* stop_event) {
     if ((start_event == nullptr) != (stop_event == nullptr))
         return fail(NF4_E_ARG, "nf4_profile_next_gemm: pass both events or neither");

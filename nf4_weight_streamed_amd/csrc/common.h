@@ -104,6 +104,8 @@ hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8
                              const uint16_t* dy, const uint16_t* x, const uint16_t* A, int64_t T, int64_t N,
                              int64_t K, int r, float s, uint16_t* dx, float* dA, void* ws, hipStream_t stream);
 
+hipError_t launch_probe_mfma(float* out, int workgroups, int iters, hipStream_t stream);
+
 // Instrumentation events around the next fused GEMM launch (abi.cpp); no-ops unless requested.
 void prof_gemm_begin(hipStream_t stream);
 void prof_gemm_end(hipStream_t stream);

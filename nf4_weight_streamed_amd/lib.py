@@ -57,6 +57,7 @@ def _load() -> C.CDLL:
         "nf4_lora_linear_bwd_workspace": (sz, [i64, i64, i64, i32]),
         "nf4_lora_linear_bwd": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "nf4_profile_next_gemm": (i32, [vp, vp]),
+        "nf4_probe_mfma": (i32, [vp, i32, i32, vp]),
         "nf4_rmsnorm_fwd": (i32, [vp, i64, i64, f32, vp, vp, vp]),
         "nf4_rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, vp, vp]),
         "nf4_add_bf16": (i32, [vp, vp, vp, i64, vp, vp]),
@@ -126,6 +127,14 @@ def abi_version() -> int:
 def profile_next_gemm(start_event, stop_event) -> None:
     """Record two hipEvent_t handles (ints) around the next call's fused GEMM kernel."""
     _check(_lib.nf4_profile_next_gemm(C.c_void_p(start_event), C.c_void_p(stop_event)))
+
+
+def probe_mfma(out, workgroups: int, iters: int, stream=None) -> None:
+    """Launch the bf16 MFMA-rate probe (32768 * 8 * iters FLOP per wave, 4 waves per
+    workgroup); out: device fp32 tensor of >= 4 * workgroups entries."""
+    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < 4 * workgroups:
+        raise ValueError("probe_mfma: out must be a device fp32 tensor of >= 4 * workgroups entries")
+    _check(_lib.nf4_probe_mfma(_ptr(out), int(workgroups), int(iters), _stream(stream)))
 
 
 def codebook() -> list:
