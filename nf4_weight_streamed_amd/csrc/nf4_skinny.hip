@@ -13,6 +13,8 @@
 // v_mfma_f32_16x16x32_bf16; both GEMM kernels split their contraction over the grid's
 // y dimension and write fp32 partials, which the finish kernels add in split order,
 // together with the LoRA terms, and round once.
+#include <type_traits>
+
 #include "common.h"
 #include "device.h"
 
@@ -28,46 +30,39 @@ constexpr int kDK = 256;      // forward: K per main-loop step (four NF4 blocks)
 constexpr int kXP = kDK + 8;  // LDS pitch of the x tile (bf16)
 
 // ------------------------------------------------------------------ forward
-// Workgroup = 128 weight rows (wave w: rows 32w .. 32w+31, two 16-row blocks) x one K
-// range of 256-wide steps; blockIdx.x == row_blocks is the u workgroup, which runs the
-// same loop on the rows of A (bf16, no dequantisation; wave w: ranks 16w .. 16w+15) for
-// u = x.A^T. Within a step the contraction order is permuted identically for both
-// operands: lane quarter q (lane / 16) supplies k = 64q + 8c .. 64q + 8c + 7 at MFMA
-// chunk c (0..7), so a lane's 32 bytes of codes are one whole NF4 block of its row (one
-// scale). The x tile of the step is staged in double-buffered LDS; codes, scales and x
-// are loaded one step ahead (16 KB of codes in flight per workgroup). Output: fp32
-// partials ypart[split][T][N] and upart[split][T][r].
-// The body of both roles; U (the u role) is a template parameter so that each main
-// loop is one branch-free block the scheduler can interleave across chunks.
-template <int TB, bool U>
-__device__ __forceinline__ void skinny_fwd_body(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
-                                                const float* __restrict__ absmax, const uint16_t* __restrict__ A,
-                                                int T, int N, int K, int r, int steps_per_split,
-                                                float* __restrict__ ypart, float* __restrict__ upart,
-                                                const Tables& tab, uint16_t* sXflat, float* sLut) {
-    constexpr int TP = 16 * TB;                    // padded tokens
-    constexpr int XCH = TP * (kDK / 8) / kThreads;  // 16-byte x chunks per thread per step (2 TB)
-    typedef uint16_t XTile[TP * kXP];
-    XTile* sX = reinterpret_cast<XTile*>(sXflat);
-    constexpr bool u_role = U;
+// Weight workgroups: 128 weight rows (wave w: rows 32w .. 32w+31, two 16-row blocks) x
+// one K range of 256-wide steps. Within a step the contraction order is permuted
+// identically for both operands: lane quarter q (lane / 16) supplies k = 64q + 8c ..
+// 64q + 8c + 7 at MFMA chunk c (0..7), so a lane's 32 bytes of codes per row block are
+// one whole NF4 block (one scale). Codes, scales and x are loaded two steps ahead into a
+// ring of three register sets (about 32 KB of codes in flight per workgroup: the kernel
+// is bound by memory latency x bytes in flight); the x tile of the current step is in
+// double-buffered LDS. Output: fp32 partials ypart[split][T][N].
+//
+// u workgroups (blockIdx.x >= row_blocks, kUParts per split): the rows of A (bf16, wave
+// w: ranks 16w .. 16w+15) against the same x for u = x.A^T, each over a quarter of the
+// split's steps with plain loads (few registers, so the weight workgroups keep their
+// occupancy) -> upart[split * kUParts + part][T][r].
+constexpr int kUParts = 4;
 
+template <int TB>
+__device__ __forceinline__ void skinny_fwd_weights(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
+                                                   const float* __restrict__ absmax, int T, int N, int K,
+                                                   int steps_per_split, float* __restrict__ ypart,
+                                                   uint16_t* sXflat, const float* sLut) {
+    constexpr int TP = 16 * TB;
+    constexpr int XCH = TP * (kDK / 8) / kThreads;  // 16-byte x chunks per thread per step (2 TB)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q = lane >> 4;
     const int nsteps = (K + kDK - 1) / kDK;
     const int kb_begin = int(blockIdx.y) * steps_per_split;
     const int kb_end = min(kb_begin + steps_per_split, nsteps);
-    for (int i = tid; i < 256; i += kThreads) {
-        sLut[2 * i] = tab.level[i & 15];
-        sLut[2 * i + 1] = tab.level[i >> 4];
-    }
-
     const auto rx = make_rsrc(x, uint32_t(T) * uint32_t(K) * 2u);
     const auto rcd = make_rsrc(codes, uint32_t(N) * uint32_t(K / 2));
     const auto rsc = make_rsrc(absmax, uint32_t(N) * uint32_t(K / 64) * 4u);
-    const auto ra = make_rsrc(A, uint32_t(r) * uint32_t(K) * 2u);
-    // rows past N (ranks past r) lie beyond the buffers and read as zero codes, scale
-    // and A values; columns past K read other rows' data against zero x columns
-    const int n0 = int(blockIdx.x) * kRows + 32 * wave;  // this wave's first row
+    // rows past N lie beyond the buffers (zero codes and scale); columns past K read
+    // other rows' data against zero x columns
+    const int n0 = int(blockIdx.x) * kRows + 32 * wave;
     uint32_t c_off[2], s_off[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -75,43 +70,51 @@ __device__ __forceinline__ void skinny_fwd_body(const uint16_t* __restrict__ x, 
         c_off[nb] = n * uint32_t(K / 2) + uint32_t(q) * 32u;
         s_off[nb] = (n * uint32_t(K / 64) + uint32_t(q)) * 4u;
     }
-    const uint32_t a_off = uint32_t(16 * wave + l16) * uint32_t(K) * 2u + uint32_t(q) * 128u;
-
-    u32x4 cw[2][2];  // codes [row block][16-byte piece]
-    float sc[2];
-    u32x4 av[8];     // u role: A values, 8 k per piece
-    u32x4 xv[XCH];
-    auto gload = [&](int kb) {
+    struct Set {
+        u32x4 cw[2][2];  // codes [row block][16-byte piece]
+        float sc[2];
+        u32x4 xv[XCH];
+    };
+    Set ring[3];
+    auto gload = [&](int kb, Set& st) {
         const uint32_t k0 = uint32_t(kb) * kDK;
-        if constexpr (u_role) {
 #pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const bool ok = kb < nsteps && int(k0) + 64 * q + 8 * p < K;
-                av[p] = buf_load16(ra, ok ? a_off + k0 * 2u + uint32_t(p) * 16u : kOutOfRange);
-            }
-        } else {
+        for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-                for (int p = 0; p < 2; ++p) cw[nb][p] = buf_load16(rcd, c_off[nb] + k0 / 2u + uint32_t(p) * 16u);
-                sc[nb] = buf_load_f32(rsc, s_off[nb] + (k0 / 64u) * 4u);
-            }
+            for (int p = 0; p < 2; ++p) st.cw[nb][p] = buf_load16(rcd, c_off[nb] + k0 / 2u + uint32_t(p) * 16u);
+            st.sc[nb] = buf_load_f32(rsc, s_off[nb] + (k0 / 64u) * 4u);
         }
+        // only the threads of real tokens load (the padded rows stay zero in LDS):
+        // vector-memory instructions, not bytes, limit this kernel
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
             const int c = tid + kThreads * i;  // token c / 32, columns 8 (c % 32)
             const int t = c / (kDK / 8), k8 = 8 * (c % (kDK / 8));
-            const bool ok = t < T && int(k0) + k8 < K;
-            xv[i] = buf_load16(rx, ok ? (uint32_t(t) * uint32_t(K) + k0 + uint32_t(k8)) * 2u : kOutOfRange);
+            if (t < T) {
+                const bool ok = int(k0) + k8 < K;
+                st.xv[i] = buf_load16(rx, ok ? (uint32_t(t) * uint32_t(K) + k0 + uint32_t(k8)) * 2u : kOutOfRange);
+            }
         }
     };
-    auto store_x = [&](int buf) {
+    typedef uint16_t XTile[TP * kXP];
+    XTile* sX = reinterpret_cast<XTile*>(sXflat);
+    auto store_x = [&](const Set& st, int buf) {
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
             const int c = tid + kThreads * i;
-            *reinterpret_cast<u32x4*>(&sX[buf][(c / (kDK / 8)) * kXP + 8 * (c % (kDK / 8))]) = xv[i];
+            if (c / (kDK / 8) < T)
+                *reinterpret_cast<u32x4*>(&sX[buf][(c / (kDK / 8)) * kXP + 8 * (c % (kDK / 8))]) = st.xv[i];
         }
     };
+    // rows of the padded token block past T are zero in both buffers for the whole loop
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int c = tid + kThreads * i;
+        if (c / (kDK / 8) >= T) {
+            *reinterpret_cast<u32x4*>(&sX[0][(c / (kDK / 8)) * kXP + 8 * (c % (kDK / 8))]) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(&sX[1][(c / (kDK / 8)) * kXP + 8 * (c % (kDK / 8))]) = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
     const char* lut = reinterpret_cast<const char*>(sLut);
 
     f32x4 acc[TB][2];
@@ -121,55 +124,51 @@ __device__ __forceinline__ void skinny_fwd_body(const uint16_t* __restrict__ x, 
         for (int nb = 0; nb < 2; ++nb) acc[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (kb_begin < kb_end) {
-        gload(kb_begin);
-        store_x(0);
+        gload(kb_begin, ring[0]);
+        gload(kb_begin + 1, ring[1]);
+        store_x(ring[0], 0);
         __syncthreads();  // sLut and x tile 0
-        for (int kb = kb_begin; kb < kb_end; ++kb) {
+        // one step on ring slot C (compile-time: the loop is unrolled by three)
+        auto step = [&](int kb, auto c_) {
+            constexpr int C = decltype(c_)::value;
             const int buf = (kb - kb_begin) & 1;
-            u32x4 ccw[2][2], cav[8];
-            float csc[2];
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                csc[nb] = sc[nb];
-                ccw[nb][0] = cw[nb][0];
-                ccw[nb][1] = cw[nb][1];
-            }
-#pragma unroll
-            for (int p = 0; p < 8; ++p) cav[p] = av[p];
-            gload(kb + 1);  // one step ahead; past the range: unused data or zeros
+            gload(kb + 2, ring[(C + 2) % 3]);  // two steps ahead; past the range: unused or zeros
             __builtin_amdgcn_sched_barrier(0);
-            bf16x8 bw[8][2];
-            if constexpr (u_role) {
+            const Set& cur = ring[C];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) bw[c][0] = as_bf16x8(cav[c]);
-            } else {
+            for (int c = 0; c < 8; ++c) {
+                bf16x8 bw[2];
 #pragma unroll
-                for (int c = 0; c < 8; ++c)
+                for (int nb = 0; nb < 2; ++nb) {
+                    const uint32_t w = cur.cw[nb][c >> 2][c & 3];
+                    u32x4 o;
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) {
-                        const uint32_t w = ccw[nb][c >> 2][c & 3];
-                        u32x4 o;
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) {
-                            const float2 lv = *reinterpret_cast<const float2*>(lut + (((w >> (8 * b)) & 0xFFu) << 3));
-                            // level * absmax in fp32, then RNbf: the format's two roundings
-                            o[b] = pack_bf16x2(lv.x * csc[nb], lv.y * csc[nb]);
-                        }
-                        bw[c][nb] = as_bf16x8(o);
+                    for (int b = 0; b < 4; ++b) {
+                        const float2 lv = *reinterpret_cast<const float2*>(lut + (((w >> (8 * b)) & 0xFFu) << 3));
+                        // level * absmax in fp32, then RNbf: the format's two roundings
+                        o[b] = pack_bf16x2(lv.x * cur.sc[nb], lv.y * cur.sc[nb]);
                     }
-            }
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
+                    bw[nb] = as_bf16x8(o);
+                }
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
                     const bf16x8 xa = as_bf16x8(
                         *reinterpret_cast<const u32x4*>(&sX[buf][(16 * tb + l16) * kXP + 64 * q + 8 * c]));
-                    acc[tb][0] = mfma16x16x32(xa, bw[c][0], acc[tb][0]);
-                    if constexpr (!u_role) acc[tb][1] = mfma16x16x32(xa, bw[c][1], acc[tb][1]);
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) acc[tb][nb] = mfma16x16x32(xa, bw[nb], acc[tb][nb]);
                 }
-            store_x(buf ^ 1);
+            }
+            store_x(ring[(C + 1) % 3], buf ^ 1);  // the next step's x (loaded a step ago)
             __syncthreads();
+        };
+        int kb = kb_begin;
+        for (; kb + 2 < kb_end; kb += 3) {
+            step(kb, std::integral_constant<int, 0>{});
+            step(kb + 1, std::integral_constant<int, 1>{});
+            step(kb + 2, std::integral_constant<int, 2>{});
         }
+        if (kb < kb_end) step(kb, std::integral_constant<int, 0>{});
+        if (kb + 1 < kb_end) step(kb + 1, std::integral_constant<int, 1>{});
     }
 
     // lane holds D[t = 16 tb + 4 q + e][row = 16 nb + l16]
@@ -179,16 +178,83 @@ __device__ __forceinline__ void skinny_fwd_body(const uint16_t* __restrict__ x, 
         for (int e = 0; e < 4; ++e) {
             const int t = 16 * tb + 4 * q + e;
             if (t >= T) continue;
-            if constexpr (u_role) {
-                const int j = 16 * wave + l16;
-                if (j < r) upart[(size_t(blockIdx.y) * T + t) * r + j] = acc[tb][0][e];
-            } else {
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const int n = n0 + 16 * nb + l16;
-                    if (n < N) ypart[(size_t(blockIdx.y) * T + t) * N + n] = acc[tb][nb][e];
-                }
+            for (int nb = 0; nb < 2; ++nb) {
+                const int n = n0 + 16 * nb + l16;
+                if (n < N) ypart[(size_t(blockIdx.y) * T + t) * N + n] = acc[tb][nb][e];
             }
+        }
+}
+
+template <int TB>
+__device__ __forceinline__ void skinny_fwd_u(const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, int T,
+                                             int K, int r, int steps_per_split, int part, float* __restrict__ upart,
+                                             uint16_t* sX) {
+    constexpr int TP = 16 * TB;
+    constexpr int XCH = TP * (kDK / 8) / kThreads;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, q = lane >> 4;
+    const int nsteps = (K + kDK - 1) / kDK;
+    const int split_begin = int(blockIdx.y) * steps_per_split;
+    const int split_end = min(split_begin + steps_per_split, nsteps);
+    const int per = (split_end - split_begin + kUParts - 1) / kUParts;
+    const int kb_begin = split_begin + part * per;
+    const int kb_end = min(kb_begin + per, split_end);
+    const auto rx = make_rsrc(x, uint32_t(T) * uint32_t(K) * 2u);
+    const auto ra = make_rsrc(A, uint32_t(r) * uint32_t(K) * 2u);  // ranks past r read zero
+    const uint32_t a_off = uint32_t(16 * wave + l16) * uint32_t(K) * 2u + uint32_t(q) * 128u;
+    f32x4 acc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // rows of the padded token block past T stay zero; only real tokens' x is loaded
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int c = tid + kThreads * i;
+        if (c / (kDK / 8) >= T)
+            *reinterpret_cast<u32x4*>(&sX[(c / (kDK / 8)) * kXP + 8 * (c % (kDK / 8))]) = u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
+        const uint32_t k0 = uint32_t(kb) * kDK;
+        u32x4 av[8], xv[XCH];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const bool ok = int(k0) + 64 * q + 8 * p < K;
+            av[p] = buf_load16(ra, ok ? a_off + k0 * 2u + uint32_t(p) * 16u : kOutOfRange);
+        }
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+            const int c = tid + kThreads * i;
+            const int t = c / (kDK / 8), k8 = 8 * (c % (kDK / 8));
+            if (t < T) {
+                const bool ok = int(k0) + k8 < K;
+                xv[i] = buf_load16(rx, ok ? (uint32_t(t) * uint32_t(K) + k0 + uint32_t(k8)) * 2u : kOutOfRange);
+            }
+        }
+        __syncthreads();  // the previous step's x reads are done
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+            const int c = tid + kThreads * i;
+            if (c / (kDK / 8) < T)
+                *reinterpret_cast<u32x4*>(&sX[(c / (kDK / 8)) * kXP + 8 * (c % (kDK / 8))]) = xv[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const bf16x8 xa =
+                    as_bf16x8(*reinterpret_cast<const u32x4*>(&sX[(16 * tb + l16) * kXP + 64 * q + 8 * c]));
+                acc[tb] = mfma16x16x32(xa, as_bf16x8(av[c]), acc[tb]);
+            }
+    }
+    const int j = 16 * wave + l16;
+    float* dst = upart + size_t(int(blockIdx.y) * kUParts + part) * T * r;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * tb + 4 * q + e;
+            if (t < T && j < r) dst[size_t(t) * r + j] = acc[tb][e];
         }
 }
 
@@ -199,19 +265,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_skinny_fwd(
     float* __restrict__ ypart, float* __restrict__ upart, Tables tab) {
     __shared__ __align__(16) uint16_t sX[2 * 16 * TB * kXP];
     __shared__ __align__(16) float sLut[512];
-    if (int(blockIdx.x) == row_blocks)
-        skinny_fwd_body<TB, true>(x, codes, absmax, A, T, N, K, r, steps_per_split, ypart, upart, tab, sX, sLut);
-    else
-        skinny_fwd_body<TB, false>(x, codes, absmax, A, T, N, K, r, steps_per_split, ypart, upart, tab, sX, sLut);
+    if (int(blockIdx.x) >= row_blocks) {
+        skinny_fwd_u<TB>(x, A, T, K, r, steps_per_split, int(blockIdx.x) - row_blocks, upart, sX);
+        return;
+    }
+    for (int i = threadIdx.x; i < 256; i += kThreads) {
+        sLut[2 * i] = tab.level[i & 15];
+        sLut[2 * i + 1] = tab.level[i >> 4];
+    }
+    skinny_fwd_weights<TB>(x, codes, absmax, T, N, K, steps_per_split, ypart, sX, sLut);
 }
 
-// y[t][n] = RNbf( sum_z ypart[z][t][n] + s . sum_j u[t][j] B[n][j] ), u = sum_z
-// upart[z], partials added in split order. Grid (features / 512, tokens / 8):
-// 2 features per thread, their B rows in registers, u of the 8 tokens staged in LDS;
-// the column-0 workgroups store u_save. All split partials of a thread's 8 tokens
-// are loaded before the first is added.
-constexpr int kFinCols = 512;
-constexpr int kFinT = 8;
+constexpr int kFinCols = 512;  // finish kernels: features per workgroup
+constexpr int kFinT = 8;       // finish kernels: tokens per workgroup (dX / y)
 
 // Stage rows [t0, t0 + rows) of an fp32 [T][r] tensor given as `parts` partials
 // (src[p * T * r + t * r + j]) into dst[t - t0][j] with row pitch `pitch` (>= r):
@@ -248,16 +314,21 @@ __device__ __forceinline__ void stage_partial_sums(float* dst, const float* src,
     }
 }
 
+// y[t][n] = RNbf( sum_z ypart[z][t][n] + s . sum_j u[t][j] B[n][j] ), u = the sum of
+// its partials in partial order, the split partials added in split order. Grid
+// (features / 512, tokens / 8): 2 features per thread, their B rows in registers, u of
+// the 8 tokens staged in LDS; the column-0 workgroups store u_save. All split partials
+// of a thread's 8 tokens are loaded before the first is added.
 template <int RB>
 __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __restrict__ ypart,
-                                                                 const float* __restrict__ upart, int splits,
-                                                                 const uint16_t* __restrict__ B, int T, int N,
-                                                                 int r, float s, uint16_t* __restrict__ y,
+                                                                 const float* __restrict__ upart, int uparts,
+                                                                 int splits, const uint16_t* __restrict__ B, int T,
+                                                                 int N, int r, float s, uint16_t* __restrict__ y,
                                                                  float* __restrict__ u_save) {
     __shared__ float su[kFinT * kMaxRank];  // u [t - t0][j]
     const int tid = threadIdx.x;
     const int t0 = int(blockIdx.y) * kFinT, nt = min(kFinT, T - t0);
-    stage_partial_sums(su, upart, splits, T, r, t0, nt, r);
+    stage_partial_sums(su, upart, uparts, T, r, t0, nt, r);
     const int n = int(blockIdx.x) * kFinCols + 2 * tid;
     // B rows n, n + 1 (ranks j >= r and rows past N read zero)
     const auto rb = make_rsrc(B, uint32_t(N) * uint32_t(r) * 2u);
@@ -556,7 +627,7 @@ template <int TB>
 void launch_fwd_tb(const SkinnyPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* x,
                    const uint16_t* A, int64_t T, int64_t N, int64_t K, int r, float* ypart, float* upart,
                    hipStream_t stream) {
-    const dim3 grid(unsigned(p.row_blocks + (r > 0 ? 1 : 0)), unsigned(p.splits));
+    const dim3 grid(unsigned(p.row_blocks + (r > 0 ? kUParts : 0)), unsigned(p.splits));
     hipLaunchKernelGGL(k_skinny_fwd<TB>, grid, dim3(kThreads), 0, stream, x, codes, absmax, A, int(T), int(N), int(K),
                        r, p.steps_per_split, p.row_blocks, ypart, upart, tables());
 }
@@ -622,7 +693,7 @@ SkinnyPlan plan_skinny_fwd(int64_t T, int64_t N, int64_t K, int r) {
     p.off_part = 0;
     size_t off = align256(size_t(p.splits) * size_t(T) * size_t(N) * 4);
     p.off_upart = off;
-    off += align256(size_t(p.splits) * size_t(T) * size_t(std::max(r, 1)) * 4);
+    off += align256(size_t(p.splits) * kUParts * size_t(T) * size_t(std::max(r, 1)) * 4);
     p.ws_bytes = off;
     return p;
 }
@@ -658,14 +729,15 @@ hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const fl
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 fgrid(unsigned(cdiv(N, kFinCols)), unsigned(cdiv(T, kFinT)));
+    const int uparts = p.splits * kUParts;
     switch (std::max(1, (r + 15) / 16)) {
-        case 1: hipLaunchKernelGGL(k_skinny_fwd_finish<1>, fgrid, dim3(kThreads), 0, stream, ypart, upart, p.splits, B,
+        case 1: hipLaunchKernelGGL(k_skinny_fwd_finish<1>, fgrid, dim3(kThreads), 0, stream, ypart, upart, uparts, p.splits, B,
                                    int(T), int(N), r, s, y, u_save); break;
-        case 2: hipLaunchKernelGGL(k_skinny_fwd_finish<2>, fgrid, dim3(kThreads), 0, stream, ypart, upart, p.splits, B,
+        case 2: hipLaunchKernelGGL(k_skinny_fwd_finish<2>, fgrid, dim3(kThreads), 0, stream, ypart, upart, uparts, p.splits, B,
                                    int(T), int(N), r, s, y, u_save); break;
-        case 3: hipLaunchKernelGGL(k_skinny_fwd_finish<3>, fgrid, dim3(kThreads), 0, stream, ypart, upart, p.splits, B,
+        case 3: hipLaunchKernelGGL(k_skinny_fwd_finish<3>, fgrid, dim3(kThreads), 0, stream, ypart, upart, uparts, p.splits, B,
                                    int(T), int(N), r, s, y, u_save); break;
-        default: hipLaunchKernelGGL(k_skinny_fwd_finish<4>, fgrid, dim3(kThreads), 0, stream, ypart, upart, p.splits, B,
+        default: hipLaunchKernelGGL(k_skinny_fwd_finish<4>, fgrid, dim3(kThreads), 0, stream, ypart, upart, uparts, p.splits, B,
                                     int(T), int(N), r, s, y, u_save); break;
     }
     return hipGetLastError();
