@@ -325,7 +325,9 @@ def small_t_sweep(lib, torch, ev: "HipEvents", reps: int = 8) -> dict:
     """Device time of one projection's forward and backward at T in {1, 8, 16, 32, 64}
     against HBM bytes = 1.125NK + T(6K + 4N + 8r) + 8r(N + K) (the base is read once in
     the forward and once in the backward). Four weight sets (>= 512 MB for the large
-    shapes) are cycled so that the 256 MB last-level cache cannot serve repeated reads."""
+    shapes) are cycled so that the 256 MB last-level cache cannot serve repeated reads.
+    Device time comes from replaying the calls captured in one graph; the eager loop's
+    time (host launches included) is reported beside it."""
     g = torch.Generator(device="cuda")
     g.manual_seed(42)
     stream = torch.cuda.current_stream().cuda_stream
@@ -358,22 +360,39 @@ def small_t_sweep(lib, torch, ev: "HipEvents", reps: int = 8) -> dict:
                 c, s_ = sets[i % nsets]
                 lib.lora_linear_bwd(c, s_, x, u, dy, a, b, ALPHA, dx=dx, dA=da, dB=db, ws=wsb)
 
-            res = {}
+            res, eager = {}, {}
+            calls = reps * nsets
             for name, fn in (("fwd", fwd), ("bwd", bwd)):
                 for i in range(nsets):
                     fn(i)
+                # eager: host launches included (the small shapes are launch-bound)
                 e0, e1 = ev.create(), ev.create()
                 ev.record(e0, stream)
-                for i in range(reps * nsets):
+                for i in range(calls):
                     fn(i)
                 ev.record(e1, stream)
-                res[name] = ev.elapsed_ms(e0, e1) * 1e3 / (reps * nsets)
+                eager[name] = ev.elapsed_ms(e0, e1) * 1e3 / calls
+                # device time: the same calls captured once in a graph (the library
+                # allocates nothing and issues no memset), replayed back to back
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    for i in range(calls):
+                        fn(i)
+                graph.replay()
+                torch.cuda.synchronize()
+                ev.record(e0, stream)
+                graph.replay()
+                ev.record(e1, stream)
+                res[name] = ev.elapsed_ms(e0, e1) * 1e3 / calls
                 ev.destroy(e0)
                 ev.destroy(e1)
+                del graph
             nbytes = 1.125 * n * k + t * (6 * k + 4 * n + 8 * RANK) + 8 * RANK * (n + k)
             us = res["fwd"] + res["bwd"]
             rows.append({"model": model, "proj": proj, "N": n, "K": k, "T": t, "fwd_us": round(res["fwd"], 2),
-                         "bwd_us": round(res["bwd"], 2), "hbm_gbs": round(nbytes / us / 1e3, 1),
+                         "bwd_us": round(res["bwd"], 2), "fwd_us_eager": round(eager["fwd"], 2),
+                         "bwd_us_eager": round(eager["bwd"], 2), "hbm_gbs": round(nbytes / us / 1e3, 1),
                          "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
         del sets
         torch.cuda.empty_cache()

@@ -1,5 +1,5 @@
-// NF4-LoRA linear for few tokens (the plans route T <= 16 here; the kernels accept
-// T <= 64): the same operations as the 128-token GEMMs, organised for the HBM-bound
+// NF4-LoRA linear for few tokens (the plans route T <= 16 here; the forward kernels
+// accept T <= 64, the backward ones T <= 16): the same operations as the 128-token GEMMs, organised for the HBM-bound
 // regime, where every weight byte should be read once and streamed at full rate while
 // MFMA work is cheap.
 //
@@ -277,48 +277,76 @@ __global__ __launch_bounds__(kThreads, 2) void k_skinny_fwd(
 }
 
 constexpr int kFinCols = 512;  // finish kernels: features per workgroup
-constexpr int kFinT = 8;       // finish kernels: tokens per workgroup (dX / y)
+constexpr int kFinT = 8;       // forward finish: tokens per workgroup
 
-// Stage rows [t0, t0 + rows) of an fp32 [T][r] tensor given as `parts` partials
-// (src[p * T * r + t * r + j]) into dst[t - t0][j] with row pitch `pitch` (>= r):
-// the sum over p in increasing order; entries with t >= T or j >= r are 0. Every load
-// of a thread's items is issued before the first is added (8 parts at a time).
-__device__ __forceinline__ void stage_partial_sums(float* dst, const float* src, int parts, int T, int r, int t0,
-                                                   int rows, int pitch) {
+// Stage rows [t0, t0 + rows) and columns [j0, j0 + pitch) of an fp32 [T][r] tensor
+// given as `parts` partials (src[p * T * r + t * r + j]) into dst[t - t0][j - j0];
+// entries with t >= T or j >= r are 0. With few items the parts are split into G
+// interleaved groups (G threads per item, G = 2 .. 16): each thread issues all of its
+// loads (8 at a time) before adding, and the group sums are added in group order
+// through `tmp` (kThreads floats of LDS). With many items (G = 1) each thread adds the
+// parts of its items in part order, 32 loads at a time. Ends with a barrier.
+__device__ __forceinline__ void stage_partial_sums(float* dst, float* tmp, const float* src, int parts, int T, int r,
+                                                   int t0, int rows, int j0, int pitch) {
     const uint32_t stride = uint32_t(T) * uint32_t(r);
     const auto rs = make_rsrc(src, uint32_t(parts) * stride * 4u);
+    const int tid = int(threadIdx.x);
     const int count = rows * pitch;
-    for (int o0 = int(threadIdx.x); o0 < count; o0 += 4 * kThreads) {
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int p0 = 0; p0 < parts; p0 += 8) {
-            float pv[4][8];
+    int G = 1;
+    while (G < 16 && 2 * G * count <= kThreads) G *= 2;
+    if (G == 1) {
+        for (int o = tid; o < count; o += kThreads) {
+            const int t = t0 + o / pitch, j = j0 + o % pitch;
+            const bool ok = t < T && j < r;
+            float v = 0.0f;
+            for (int p0 = 0; p0 < parts; p0 += 32) {
+                float pv[32];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int o = o0 + i * kThreads, t = t0 + o / pitch, j = o % pitch;
-                const bool ok = o < count && t < T && j < r;
+                for (int pp = 0; pp < 32; ++pp)
+                    pv[pp] = buf_load_f32(rs, ok && p0 + pp < parts
+                                                  ? (uint32_t(p0 + pp) * stride + uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u
+                                                  : kOutOfRange);
 #pragma unroll
-                for (int pp = 0; pp < 8; ++pp)
-                    pv[i][pp] = buf_load_f32(rs, ok && p0 + pp < parts
-                                                     ? (uint32_t(p0 + pp) * stride + uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u
-                                                     : kOutOfRange);
+                for (int pp = 0; pp < 32; ++pp)
+                    if (p0 + pp < parts) v += pv[pp];
             }
+            dst[o] = v;
+        }
+        __syncthreads();
+        return;
+    }
+    const int o = tid / G, g = tid % G;
+    const int t = t0 + o / pitch, j = j0 + o % pitch;
+    const bool ok = o < count && t < T && j < r;
+    float v = 0.0f;
+    for (int p0 = g; p0 < parts; p0 += 8 * G) {
+        float pv[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int pp = 0; pp < 8; ++pp)
-                    if (p0 + pp < parts) v[i] += pv[i][pp];
+        for (int pp = 0; pp < 8; ++pp) {
+            const int p = p0 + pp * G;
+            pv[pp] = buf_load_f32(rs, ok && p < parts ? (uint32_t(p) * stride + uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u
+                                                      : kOutOfRange);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (o0 + i * kThreads < count) dst[o0 + i * kThreads] = v[i];
+        for (int pp = 0; pp < 8; ++pp)
+            if (p0 + pp * G < parts) v += pv[pp];
     }
+    tmp[tid] = v;  // tid = o * G + g
+    __syncthreads();
+    if (tid < count) {
+        float sum = 0.0f;
+        for (int gg = 0; gg < G; ++gg) sum += tmp[tid * G + gg];
+        dst[tid] = sum;
+    }
+    __syncthreads();
 }
 
 // y[t][n] = RNbf( sum_z ypart[z][t][n] + s . sum_j u[t][j] B[n][j] ), u = the sum of
-// its partials in partial order, the split partials added in split order. Grid
-// (features / 512, tokens / 8): 2 features per thread, their B rows in registers, u of
-// the 8 tokens staged in LDS; the column-0 workgroups store u_save. All split partials
-// of a thread's 8 tokens are loaded before the first is added.
+// its partials, the split partials added in split order. Grid (features / 512,
+// tokens / 8): 2 features per thread, their B rows in registers, u of the 8 tokens
+// staged in LDS; the column-0 workgroups store u_save. The B rows and the first round
+// of split partials are loaded before u is staged; each later round is loaded while the
+// one before it is added.
 template <int RB>
 __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __restrict__ ypart,
                                                                  const float* __restrict__ upart, int uparts,
@@ -326,46 +354,58 @@ __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __r
                                                                  int N, int r, float s, uint16_t* __restrict__ y,
                                                                  float* __restrict__ u_save) {
     __shared__ float su[kFinT * kMaxRank];  // u [t - t0][j]
+    __shared__ float stmp[kThreads];
     const int tid = threadIdx.x;
     const int t0 = int(blockIdx.y) * kFinT, nt = min(kFinT, T - t0);
-    stage_partial_sums(su, upart, uparts, T, r, t0, nt, r);
     const int n = int(blockIdx.x) * kFinCols + 2 * tid;
     // B rows n, n + 1 (ranks j >= r and rows past N read zero)
     const auto rb = make_rsrc(B, uint32_t(N) * uint32_t(r) * 2u);
     constexpr int R = 16 * RB;  // ranks held per thread (>= r)
-    float b0[R], b1[R];
+    uint32_t bw[R];  // B[n][j] (low half), B[n + 1][j] (high half)
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        const bool ok = j < r;
-        b0[j] = bf16_to_f32(uint16_t(__builtin_amdgcn_raw_buffer_load_b16(
-            rb, int(ok ? (uint32_t(n) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0)));
-        b1[j] = bf16_to_f32(uint16_t(__builtin_amdgcn_raw_buffer_load_b16(
-            rb, int(ok ? (uint32_t(n + 1) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0)));
+        const bool ok = j < r && n < N;
+        const uint32_t lo = uint16_t(__builtin_amdgcn_raw_buffer_load_b16(
+            rb, int(ok ? (uint32_t(n) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0));
+        const uint32_t hi = uint16_t(__builtin_amdgcn_raw_buffer_load_b16(
+            rb, int(ok ? (uint32_t(n + 1) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0));
+        bw[j] = lo | (hi << 16);
     }
-    __syncthreads();
-    if (blockIdx.x == 0)
-        for (int o = tid; o < nt * r; o += kThreads) u_save[size_t(t0) * r + o] = su[o];
-    if (n >= N) return;  // N % 16 == 0: both features are in or out
+    constexpr int ZR = 4;  // splits per round
     const auto rp = make_rsrc(ypart, uint32_t(splits) * uint32_t(T) * uint32_t(N) * 4u);
+    auto load_round = [&](int z0, u32x2 (&pv)[ZR][kFinT]) {
+#pragma unroll
+        for (int zz = 0; zz < ZR; ++zz)
+#pragma unroll
+            for (int i = 0; i < kFinT; ++i) {
+                const bool ok = z0 + zz < splits && i < nt && n < N;
+                pv[zz][i] = buf_load8(
+                    rp, ok ? ((uint32_t(z0 + zz) * uint32_t(T) + uint32_t(t0 + i)) * uint32_t(N) + uint32_t(n)) * 4u
+                           : kOutOfRange);
+            }
+    };
     f32x2 acc[kFinT];
 #pragma unroll
     for (int i = 0; i < kFinT; ++i) acc[i] = f32x2{0.f, 0.f};
-    for (int z0 = 0; z0 < splits; z0 += 4) {
-        u32x2 pv[4][kFinT];
+    auto add_round = [&](int z0, const u32x2 (&pv)[ZR][kFinT]) {
 #pragma unroll
-        for (int zz = 0; zz < 4; ++zz)
-#pragma unroll
-            for (int i = 0; i < kFinT; ++i) {
-                const bool ok = z0 + zz < splits && i < nt;
-                pv[zz][i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                    rp, int(ok ? ((uint32_t(z0 + zz) * uint32_t(T) + uint32_t(t0 + i)) * uint32_t(N) + uint32_t(n)) * 4u
-                               : kOutOfRange), 0, 0));
-            }
-#pragma unroll
-        for (int zz = 0; zz < 4; ++zz)
+        for (int zz = 0; zz < ZR; ++zz)
             if (z0 + zz < splits)
 #pragma unroll
                 for (int i = 0; i < kFinT; ++i) acc[i] += __builtin_bit_cast(f32x2, pv[zz][i]);
+    };
+    u32x2 pa[ZR][kFinT], pb[ZR][kFinT];
+    load_round(0, pa);
+    stage_partial_sums(su, stmp, upart, uparts, T, r, t0, nt, 0, r);
+    if (blockIdx.x == 0)
+        for (int o = tid; o < nt * r; o += kThreads) u_save[size_t(t0) * r + o] = su[o];
+    if (n >= N) return;  // N % 16 == 0: both features are in or out
+    for (int z0 = 0; z0 < splits; z0 += 2 * ZR) {
+        load_round(z0 + ZR, pb);
+        add_round(z0, pa);
+        if (z0 + ZR >= splits) break;
+        load_round(z0 + 2 * ZR, pa);
+        add_round(z0 + ZR, pb);
     }
 #pragma unroll
     for (int i = 0; i < kFinT; ++i) {
@@ -375,252 +415,232 @@ __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __r
         for (int j = 0; j < R; ++j)
             if (j < r) {
                 const float uj = su[i * r + j];
-                l0 += uj * b0[j];
-                l1 += uj * b1[j];
+                l0 += uj * __uint_as_float(bw[j] << 16);
+                l1 += uj * __uint_as_float(bw[j] & 0xFFFF0000u);
             }
         *reinterpret_cast<uint32_t*>(&y[size_t(t0 + i) * N + n]) = pack_bf16x2(acc[i][0] + s * l0, acc[i][1] + s * l1);
     }
 }
 
 // ------------------------------------------------------------------ backward dX
-// Workgroup = 128 input features (wave w: columns 32w .. 32w+31, two 16-column blocks)
-// x one N range of 64-wide steps. Per step each thread dequantises a 4 (n) x 8 (k)
-// patch (pair table, as in the large backward kernel) and stores it transposed into
-// LDS as [k][n] (16-byte chunks XOR-swizzled by (k/8)%8); dY of the step is staged as
-// [t][n]. Both double-buffered, loads one step ahead, one barrier per step.
+// dX = dY . W contracts over the weight rows n, so a lane that dequantises 8
+// consecutive rows of one weight column already holds a B operand of
+// v_mfma_f32_16x16x32_bf16 (8 contraction elements of one output column): no
+// transpose through LDS. Workgroup = 256 features x one range of 32-row steps; lane
+// (l16, q) reads 8 bytes of codes (16 features, inside one NF4 block) of rows
+// 8q .. 8q+7 of a step, and MFMA j (0..15) takes feature 16 l16 + j from every lane,
+// so its output column l16 is feature 16 l16 + j. The four waves take interleaved
+// steps of the workgroup's range and add their sums through LDS in a fixed order.
+// Scales: two dwords per lane and step ([row][block] in memory), exchanged through the
+// wave's own LDS slice as [block][row]. Codes, scales and dY are loaded two steps ahead
+// into a ring of three register sets. T <= 16 (one 16-token MFMA block).
 // Output: fp32 partials dxpart[split][T][K].
-constexpr int kBN = 64;       // N per step
-constexpr int kCols = 128;    // K per workgroup
-constexpr int kWP = kBN + 8;  // LDS pitch (bf16)
+constexpr int kBCols = 256;  // features per workgroup
+constexpr int kBRows = 32;   // weight rows per wave step
 
-template <int TB>
-__global__ __launch_bounds__(kThreads, 2) void k_skinny_bwd(
-    const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const float* __restrict__ absmax, int T,
-    int N, int K, int steps_per_split, float* __restrict__ dxpart, Tables tab) {
-    constexpr int TP = 16 * TB;
-    constexpr int DCH = TP * (kBN / 8);  // 16-byte dY chunks per step (<= 512)
-
-    __shared__ __align__(16) uint16_t sW[2][kCols * kWP];
-    __shared__ __align__(16) uint16_t sD[2][TP * kWP];
+__global__ __launch_bounds__(kThreads, 2) void k_skinny_bwd(const uint16_t* __restrict__ dy,
+                                                            const uint8_t* __restrict__ codes,
+                                                            const float* __restrict__ absmax, int T, int N, int K,
+                                                            int steps_per_split, float* __restrict__ dxpart,
+                                                            Tables tab) {
     __shared__ __align__(16) float sLut[512];
+    __shared__ __align__(16) float sSc[4][4 * kBRows];  // per wave: scales [block][row]
+    __shared__ __align__(16) float sRed[2][16][kBCols];  // cross-wave sums [token][feature]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q = lane >> 4;
-    const int k0 = int(blockIdx.x) * kCols;
-    const int nsteps = (N + kBN - 1) / kBN;
-    const int nb_begin = int(blockIdx.y) * steps_per_split;
-    const int nb_end = min(nb_begin + steps_per_split, nsteps);
+    const int k0 = int(blockIdx.x) * kBCols;
+    const int nsteps = (N + kBRows - 1) / kBRows;
+    const int s_begin = int(blockIdx.y) * steps_per_split;
+    const int s_end = min(s_begin + steps_per_split, nsteps);
+    const int nw = max(0, (s_end - s_begin - wave + 3) / 4);  // this wave's steps
     sLut[2 * tid] = tab.level[tid & 15];
     sLut[2 * tid + 1] = tab.level[tid >> 4];
 
-    const int pr = tid >> 4, pc = tid & 15;  // patch: rows 4 pr .. 4 pr + 3, columns 8 pc .. 8 pc + 7
     const auto rdy = make_rsrc(dy, uint32_t(T) * uint32_t(N) * 2u);
     const auto rcd = make_rsrc(codes, uint32_t(N) * uint32_t(K / 2));
     const auto rsc = make_rsrc(absmax, uint32_t(N) * uint32_t(K / 64) * 4u);
-    const uint32_t kc = uint32_t(k0 + 8 * pc);
-
-    uint32_t rc[4];
-    float rs[4];
-    u32x4 dv[(DCH + kThreads - 1) / kThreads];
-    auto gload = [&](int nb) {
-        // rows past N are beyond both buffers (zero); columns past K only reach dX
-        // columns that are never stored
+    // rows past N lie beyond the code and scale buffers (zero weights) and their dY is
+    // not loaded; features past K read other rows' data and only reach dX columns that
+    // are never stored
+    const uint32_t c_lane = uint32_t(8 * q) * uint32_t(K / 2) + uint32_t(k0 + 16 * l16) / 2u;
+    const uint32_t s_lane = (uint32_t(lane >> 2) * uint32_t(K / 64) + uint32_t(k0 / 64 + (lane & 3))) * 4u;
+    struct Set {
+        u32x2 cw[8];  // codes of rows 8q + i, 16 features
+        float sc[2];  // scales: row 16h + lane / 4, block lane % 4
+        u32x4 dv;     // dY[t = l16][8q .. 8q + 7]
+    };
+    Set ring[3];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t n = uint32_t(nb * kBN + 4 * pr + i);
-            rc[i] = buf_load_u32(rcd, n * uint32_t(K / 2) + kc / 2);
-            rs[i] = buf_load_f32(rsc, n * uint32_t(K / 64) * 4u + (kc / 64) * 4u);
-        }
+    for (int c = 0; c < 3; ++c) ring[c].dv = u32x4{0u, 0u, 0u, 0u};
+    auto gload = [&](int i, Set& st) {
+        const uint32_t n0 = uint32_t(s_begin + wave + 4 * i) * kBRows;
 #pragma unroll
-        for (int i = 0; i < (DCH + kThreads - 1) / kThreads; ++i) {
-            const int c = tid + kThreads * i, t = c / (kBN / 8), n8 = 8 * (c % (kBN / 8));
-            const bool ok = c < DCH && t < T && nb * kBN + n8 < N;
-            dv[i] = buf_load16(rdy, ok ? (uint32_t(t) * uint32_t(N) + uint32_t(nb * kBN + n8)) * 2u : kOutOfRange);
-        }
+        for (int r8 = 0; r8 < 8; ++r8) st.cw[r8] = buf_load8(rcd, (n0 + uint32_t(r8)) * uint32_t(K / 2) + c_lane);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) st.sc[h] = buf_load_f32(rsc, (n0 + 16u * h) * uint32_t(K / 64) * 4u + s_lane);
+        const bool ok = l16 < T && int(n0) + 8 * q < N;
+        st.dv = buf_load16(rdy, ok ? (uint32_t(l16) * uint32_t(N) + n0 + uint32_t(8 * q)) * 2u : kOutOfRange);
     };
     const char* lut = reinterpret_cast<const char*>(sLut);
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < (DCH + kThreads - 1) / kThreads; ++i) {
-            const int c = tid + kThreads * i;
-            if (c < DCH) *reinterpret_cast<u32x4*>(&sD[buf][(c / (kBN / 8)) * kWP + 8 * (c % (kBN / 8))]) = dv[i];
-        }
-        float v[4][8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float2 lv = *reinterpret_cast<const float2*>(lut + (((rc[i] >> (8 * b)) & 0xFFu) << 3));
-                v[i][2 * b] = lv.x * rs[i];  // level * absmax in fp32, RNbf below
-                v[i][2 * b + 1] = lv.y * rs[i];
-            }
-        const int col = (((pr >> 1) ^ (pc & 7)) << 3) + 4 * (pr & 1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const u32x2 o = {pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e])};
-            *reinterpret_cast<u32x2*>(&sW[buf][(8 * pc + e) * kWP + col]) = o;
-        }
-    };
+    float* ssc = sSc[wave];
 
-    f32x4 acc[TB][2];
+    f32x4 acc[16];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) acc[tb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // sLut
 
-    if (nb_begin < nb_end) {
-        gload(nb_begin);
-        __syncthreads();  // sLut
-        sstore(0);
-        __syncthreads();
-        for (int nb = nb_begin; nb < nb_end; ++nb) {
-            const int buf = (nb - nb_begin) & 1;
-            gload(nb + 1);  // one step ahead; past the range: unused data or zeros
+    if (nw > 0) {
+        gload(0, ring[0]);
+        gload(1, ring[1]);
+        // one step on ring slot C (compile-time: the loop is unrolled by three)
+        auto step = [&](int i, auto c_) {
+            constexpr int C = decltype(c_)::value;
+            gload(i + 2, ring[(C + 2) % 3]);  // two steps ahead; past the range: unused or zeros
             __builtin_amdgcn_sched_barrier(0);
+            const Set& cur = ring[C];
+            // the wave's LDS slice: written and read by this wave only, in program order
+            ssc[(lane & 3) * kBRows + (lane >> 2)] = cur.sc[0];
+            ssc[(lane & 3) * kBRows + 16 + (lane >> 2)] = cur.sc[1];
+            __builtin_amdgcn_wave_barrier();
+            const f32x4 sa = *reinterpret_cast<const f32x4*>(&ssc[(l16 >> 2) * kBRows + 8 * q]);
+            const f32x4 sb = *reinterpret_cast<const f32x4*>(&ssc[(l16 >> 2) * kBRows + 8 * q + 4]);
+            __builtin_amdgcn_wave_barrier();
+            const float sc[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+            const bf16x8 da = as_bf16x8(cur.dv);
 #pragma unroll
-            for (int c = 0; c < kBN / 32; ++c) {
-                bf16x8 bw[2];
+            for (int p = 0; p < 8; ++p) {  // features 2p, 2p + 1 of the lane's 16
+                float v0[8], v1[8];
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    const int kr = 32 * wave + 16 * cb + l16;  // tile row k
-                    const int chunk = (4 * c + q) ^ ((kr >> 3) & 7);
-                    bw[cb] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sW[buf][kr * kWP + 8 * chunk]));
+                for (int r8 = 0; r8 < 8; ++r8) {
+                    const uint32_t byte = (cur.cw[r8][p >> 2] >> (8 * (p & 3))) & 0xFFu;
+                    const float2 lv = *reinterpret_cast<const float2*>(lut + (byte << 3));
+                    v0[r8] = lv.x * sc[r8];  // level * absmax in fp32, RNbf below
+                    v1[r8] = lv.y * sc[r8];
                 }
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    const bf16x8 da = as_bf16x8(
-                        *reinterpret_cast<const u32x4*>(&sD[buf][(16 * tb + l16) * kWP + 32 * c + 8 * q]));
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) acc[tb][cb] = mfma16x16x32(da, bw[cb], acc[tb][cb]);
-                }
+                const u32x4 f0 = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v0[4], v0[5]),
+                                  pack_bf16x2(v0[6], v0[7])};
+                const u32x4 f1 = {pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]), pack_bf16x2(v1[4], v1[5]),
+                                  pack_bf16x2(v1[6], v1[7])};
+                acc[2 * p] = mfma16x16x32(da, as_bf16x8(f0), acc[2 * p]);
+                acc[2 * p + 1] = mfma16x16x32(da, as_bf16x8(f1), acc[2 * p + 1]);
             }
-            sstore(buf ^ 1);
-            __syncthreads();
+        };
+        int i = 0;
+        for (; i + 2 < nw; i += 3) {
+            step(i, std::integral_constant<int, 0>{});
+            step(i + 1, std::integral_constant<int, 1>{});
+            step(i + 2, std::integral_constant<int, 2>{});
         }
+        if (i < nw) step(i, std::integral_constant<int, 0>{});
+        if (i + 1 < nw) step(i + 1, std::integral_constant<int, 1>{});
     }
 
-    float* dst = dxpart + size_t(blockIdx.y) * T * K;
+    // lane holds D[t = 4q + e][feature 16 l16 + j] in acc[j][e]; sum (w0 + w2) + (w1 + w3)
+    if (wave >= 2)
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            const int k = k0 + 32 * wave + 16 * cb + l16;
+            for (int m = 0; m < 4; ++m)
+                *reinterpret_cast<f32x4*>(&sRed[wave - 2][4 * q + e][16 * l16 + 4 * m]) =
+                    f32x4{acc[4 * m][e], acc[4 * m + 1][e], acc[4 * m + 2][e], acc[4 * m + 3][e]};
+    __syncthreads();
+    if (wave < 2)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tb + 4 * q + e;
-                if (t < T && k < K) dst[size_t(t) * K + k] = acc[tb][cb][e];
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4* o = reinterpret_cast<f32x4*>(&sRed[wave][4 * q + e][16 * l16 + 4 * m]);
+                *o = *o + f32x4{acc[4 * m][e], acc[4 * m + 1][e], acc[4 * m + 2][e], acc[4 * m + 3][e]};
             }
-        }
+    __syncthreads();
+    const int k = k0 + tid;
+    if (k < K) {
+        float* dst = dxpart + size_t(blockIdx.y) * T * K + k;
+        for (int t = 0; t < T; ++t) dst[size_t(t) * K] = sRed[0][t][tid] + sRed[1][t][tid];
+    }
 }
 
-// Backward finish, two kinds of workgroups in one launch; g = sum of the pre-pass's
-// partials in partial order, staged in LDS:
-//  - blocks [0, dx_blocks): grid (features / 512, tokens / 8), 2 features per thread
-//    with their A columns in registers: dX[t][k] = RNbf( sum_z dxpart[z][t][k] +
-//    s . sum_j g[t][j] A[j][k] ), all split partials of the 8 tokens loaded first;
-//  - the rest: 512 features (2 per thread) x all ranks: dA[j][k] = s . sum_t g[t][j]
+// Backward finish, two kinds of workgroups in one launch; g = the sum of the pre-pass's
+// partials, staged in LDS after each thread has issued its other loads:
+//  - blocks [0, dx_blocks): one token x 512 features (2 per thread, their A columns in
+//    registers): dX[t][k] = RNbf( sum_z dxpart[z][t][k] + s . sum_j g[t][j] A[j][k] ),
+//    the split partials (at most kMaxBwdSplits) all loaded at once, added in split order;
+//  - the rest: 512 features (2 per thread) x 16 ranks: dA[j][k] = s . sum_t g[t][j]
 //    x[t][k], every token's x loaded first, tokens added in increasing order.
-template <int RB, int TB>
+constexpr int kMaxBwdSplits = 32;
+
+template <int RB>
 __global__ __launch_bounds__(kThreads) void k_skinny_bwd_finish(
     const float* __restrict__ dxpart, int splits, const float* __restrict__ gpart, int gparts,
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ x, int T, int K, int r, float s, int dx_col_blocks,
     int dx_blocks, uint16_t* __restrict__ dx, float* __restrict__ dA) {
-    __shared__ float sg[kSkinnyMaxT * kMaxRank];  // g [t][j] (dX role: the 8 tokens only)
+    constexpr int R = 16 * RB;  // ranks held per thread (>= r)
+    __shared__ __align__(16) float sg[kSkinnyMaxT * 16];  // g [t][j - j0] (dA role) or g [t][j] (dX role)
+    __shared__ float stmp[kThreads];
     const int tid = threadIdx.x;
-    const bool dx_role = int(blockIdx.x) < dx_blocks;
-    const int t0 = dx_role ? (int(blockIdx.x) / dx_col_blocks) * kFinT : 0;
-    const int nt = dx_role ? min(kFinT, T - t0) : T;
-    // dX role: [8 tokens][r]; dA role: [16 TB][16 RB], zero-padded
-    if (dx_role)
-        stage_partial_sums(sg, gpart, gparts, T, r, t0, nt, r);
-    else
-        stage_partial_sums(sg, gpart, gparts, T, r, 0, 16 * TB, 16 * RB);
-    if (dx_role) {
+    if (int(blockIdx.x) < dx_blocks) {
+        const int t = int(blockIdx.x) / dx_col_blocks;
         const int k = (int(blockIdx.x) % dx_col_blocks) * kFinCols + 2 * tid;
         // A[j][k], A[j][k+1] (ranks j >= r and columns past K read zero)
         const auto ra = make_rsrc(A, uint32_t(r) * uint32_t(K) * 2u);
-        constexpr int R = 16 * RB;  // ranks held per thread (>= r)
-        float a0[R], a1[R];
+        uint32_t aw[R];
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-            const uint32_t w = buf_load_u32(ra, j < r && k < K ? (uint32_t(j) * uint32_t(K) + uint32_t(k)) * 2u : kOutOfRange);
-            a0[j] = __uint_as_float(w << 16);
-            a1[j] = __uint_as_float(w & 0xFFFF0000u);
-        }
-        __syncthreads();
-        if (k >= K) return;  // K % 64 == 0: both features are in or out
+        for (int j = 0; j < R; ++j)
+            aw[j] = buf_load_u32(ra, j < r && k < K ? (uint32_t(j) * uint32_t(K) + uint32_t(k)) * 2u : kOutOfRange);
         const auto rp = make_rsrc(dxpart, uint32_t(splits) * uint32_t(T) * uint32_t(K) * 4u);
-        f32x2 acc[kFinT];
+        u32x2 pv[kMaxBwdSplits];
 #pragma unroll
-        for (int i = 0; i < kFinT; ++i) acc[i] = f32x2{0.f, 0.f};
-        for (int z0 = 0; z0 < splits; z0 += 4) {
-            u32x2 pv[4][kFinT];
+        for (int z = 0; z < kMaxBwdSplits; ++z)
+            pv[z] = buf_load8(rp, z < splits && k < K ? ((uint32_t(z) * uint32_t(T) + uint32_t(t)) * uint32_t(K) + uint32_t(k)) * 4u
+                                                      : kOutOfRange);
+        stage_partial_sums(sg, stmp, gpart, gparts, T, r, t, 1, 0, r);
+        if (k >= K) return;  // K % 64 == 0: both features are in or out
+        f32x2 acc = {0.f, 0.f};
 #pragma unroll
-            for (int zz = 0; zz < 4; ++zz)
+        for (int z = 0; z < kMaxBwdSplits; ++z)
+            if (z < splits) acc += __builtin_bit_cast(f32x2, pv[z]);
+        float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
-                for (int i = 0; i < kFinT; ++i) {
-                    const bool ok = z0 + zz < splits && i < nt;
-                    pv[zz][i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                        rp, int(ok ? ((uint32_t(z0 + zz) * uint32_t(T) + uint32_t(t0 + i)) * uint32_t(K) + uint32_t(k)) * 4u
-                                   : kOutOfRange), 0, 0));
-                }
-#pragma unroll
-            for (int zz = 0; zz < 4; ++zz)
-                if (z0 + zz < splits)
-#pragma unroll
-                    for (int i = 0; i < kFinT; ++i) acc[i] += __builtin_bit_cast(f32x2, pv[zz][i]);
-        }
-#pragma unroll
-        for (int i = 0; i < kFinT; ++i) {
-            if (i >= nt) break;
-            float l0 = 0.0f, l1 = 0.0f;
-#pragma unroll
-            for (int j = 0; j < R; ++j)
-                if (j < r) {
-                    const float gj = sg[i * r + j];
-                    l0 += gj * a0[j];
-                    l1 += gj * a1[j];
-                }
-            *reinterpret_cast<uint32_t*>(&dx[size_t(t0 + i) * K + k]) =
-                pack_bf16x2(acc[i][0] + s * l0, acc[i][1] + s * l1);
-        }
+        for (int j = 0; j < R; ++j)
+            if (j < r) {
+                const float gj = sg[j];
+                l0 += gj * __uint_as_float(aw[j] << 16);
+                l1 += gj * __uint_as_float(aw[j] & 0xFFFF0000u);
+            }
+        *reinterpret_cast<uint32_t*>(&dx[size_t(t) * K + k]) = pack_bf16x2(acc[0] + s * l0, acc[1] + s * l1);
         return;
     }
-    const int k = (int(blockIdx.x) - dx_blocks) * kFinCols + 2 * tid;
+    // dA role: block (column block, rank block of 16)
+    const int da = int(blockIdx.x) - dx_blocks;
+    const int k = (da % dx_col_blocks) * kFinCols + 2 * tid;
+    const int j0 = 16 * (da / dx_col_blocks);
     const auto rx = make_rsrc(x, uint32_t(T) * uint32_t(K) * 2u);
-    constexpr int R = 16 * RB;  // ranks held per thread (>= r)
-    float c0[R], c1[R];
+    uint32_t xv[kSkinnyMaxT];  // tokens past T read zero (and their staged g is zero)
 #pragma unroll
-    for (int j = 0; j < R; ++j) c0[j] = c1[j] = 0.0f;
-    // tokens in groups of 8, the next group's x loaded while the current one is added;
-    // tokens past T have x = 0 and g = 0 (staged zero)
-    auto load8 = [&](int t0, uint32_t (&xv)[8]) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            xv[i] = buf_load_u32(rx, t0 + i < T ? (uint32_t(t0 + i) * uint32_t(K) + uint32_t(k)) * 2u : kOutOfRange);
-    };
-    uint32_t xa[8], xb[8];
-    load8(0, xa);
-    __syncthreads();
+    for (int t = 0; t < kSkinnyMaxT; ++t)
+        xv[t] = buf_load_u32(rx, t < T && k < K ? (uint32_t(t) * uint32_t(K) + uint32_t(k)) * 2u : kOutOfRange);
+    stage_partial_sums(sg, stmp, gpart, gparts, T, r, 0, kSkinnyMaxT, j0, 16);
     if (k >= K) return;
-    for (int t0 = 0; t0 < 16 * TB; t0 += 8) {
-        load8(t0 + 8, xb);
+    float c0[16], c1[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float x0 = __uint_as_float(xa[i] << 16), x1 = __uint_as_float(xa[i] & 0xFFFF0000u);
+    for (int j = 0; j < 16; ++j) c0[j] = c1[j] = 0.0f;
 #pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const float gj = sg[(t0 + i) * R + j];
-                c0[j] += gj * x0;
-                c1[j] += gj * x1;
+    for (int t = 0; t < kSkinnyMaxT; ++t) {
+        const float x0 = __uint_as_float(xv[t] << 16), x1 = __uint_as_float(xv[t] & 0xFFFF0000u);
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sg[t * 16 + 4 * j4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                c0[4 * j4 + e] += g4[e] * x0;
+                c1[4 * j4 + e] += g4[e] * x1;
             }
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xa[i] = xb[i];
     }
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-        if (j < r) *reinterpret_cast<f32x2*>(&dA[size_t(j) * K + k]) = f32x2{s * c0[j], s * c1[j]};
+    for (int j = 0; j < 16; ++j)
+        if (j0 + j < r) *reinterpret_cast<f32x2*>(&dA[size_t(j0 + j) * K + k]) = f32x2{s * c0[j], s * c1[j]};
 }
 
 template <int TB>
@@ -632,43 +652,12 @@ void launch_fwd_tb(const SkinnyPlan& p, const uint8_t* codes, const float* absma
                        r, p.steps_per_split, p.row_blocks, ypart, upart, tables());
 }
 
-template <int TB>
-void launch_bwd_tb(const SkinnyPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* dy, int64_t T,
-                   int64_t N, int64_t K, float* dxpart, hipStream_t stream) {
-    const dim3 grid(unsigned(p.col_blocks), unsigned(p.splits));
-    hipLaunchKernelGGL(k_skinny_bwd<TB>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, int(T), int(N), int(K),
-                       p.steps_per_split, dxpart, tables());
-}
-
-template <int RB, int TB>
-void launch_bwd_finish_rt(dim3 grid, hipStream_t stream, const float* dxpart, int splits, const float* gpart,
-                          int gparts, const uint16_t* A, const uint16_t* x, int T, int K, int r, float s,
-                          int col_blocks, int dx_blocks, uint16_t* dx, float* dA) {
-    hipLaunchKernelGGL((k_skinny_bwd_finish<RB, TB>), grid, dim3(kThreads), 0, stream, dxpart, splits, gpart, gparts,
-                       A, x, T, K, r, s, col_blocks, dx_blocks, dx, dA);
-}
-
 template <int RB>
-void launch_bwd_finish_r(int tb, dim3 grid, hipStream_t stream, const float* dxpart, int splits, const float* gpart,
-                         int gparts, const uint16_t* A, const uint16_t* x, int T, int K, int r, float s,
-                         int col_blocks, int dx_blocks, uint16_t* dx, float* dA) {
-    switch (tb) {
-        case 1: launch_bwd_finish_rt<RB, 1>(grid, stream, dxpart, splits, gpart, gparts, A, x, T, K, r, s, col_blocks, dx_blocks, dx, dA); break;
-        case 2: launch_bwd_finish_rt<RB, 2>(grid, stream, dxpart, splits, gpart, gparts, A, x, T, K, r, s, col_blocks, dx_blocks, dx, dA); break;
-        case 3: launch_bwd_finish_rt<RB, 3>(grid, stream, dxpart, splits, gpart, gparts, A, x, T, K, r, s, col_blocks, dx_blocks, dx, dA); break;
-        default: launch_bwd_finish_rt<RB, 4>(grid, stream, dxpart, splits, gpart, gparts, A, x, T, K, r, s, col_blocks, dx_blocks, dx, dA); break;
-    }
-}
-
-void launch_bwd_finish(int rb, int tb, dim3 grid, hipStream_t stream, const float* dxpart, int splits,
-                       const float* gpart, int gparts, const uint16_t* A, const uint16_t* x, int T, int K, int r,
-                       float s, int col_blocks, int dx_blocks, uint16_t* dx, float* dA) {
-    switch (rb) {
-        case 1: launch_bwd_finish_r<1>(tb, grid, stream, dxpart, splits, gpart, gparts, A, x, T, K, r, s, col_blocks, dx_blocks, dx, dA); break;
-        case 2: launch_bwd_finish_r<2>(tb, grid, stream, dxpart, splits, gpart, gparts, A, x, T, K, r, s, col_blocks, dx_blocks, dx, dA); break;
-        case 3: launch_bwd_finish_r<3>(tb, grid, stream, dxpart, splits, gpart, gparts, A, x, T, K, r, s, col_blocks, dx_blocks, dx, dA); break;
-        default: launch_bwd_finish_r<4>(tb, grid, stream, dxpart, splits, gpart, gparts, A, x, T, K, r, s, col_blocks, dx_blocks, dx, dA); break;
-    }
+void launch_bwd_finish_r(dim3 grid, hipStream_t stream, const float* dxpart, int splits, const float* gpart, int gparts,
+                         const uint16_t* A, const uint16_t* x, int T, int K, int r, float s, int col_blocks,
+                         int dx_blocks, uint16_t* dx, float* dA) {
+    hipLaunchKernelGGL(k_skinny_bwd_finish<RB>, grid, dim3(kThreads), 0, stream, dxpart, splits, gpart, gparts, A, x, T,
+                       K, r, s, col_blocks, dx_blocks, dx, dA);
 }
 
 // Workgroups of a streaming kernel: 2 per CU, each running several steps so that its
@@ -700,11 +689,15 @@ SkinnyPlan plan_skinny_fwd(int64_t T, int64_t N, int64_t K, int r) {
 
 SkinnyPlan plan_skinny_bwd(int64_t T, int64_t N, int64_t K) {
     SkinnyPlan p{};
-    p.col_blocks = int(cdiv(K, kCols));
-    const int64_t steps = cdiv(N, kBN);
+    p.col_blocks = int(cdiv(K, kBCols));
+    const int64_t steps = cdiv(N, kBRows);
+    // split N until about kStreamWGs workgroups with >= 2 steps per wave; the fp32
+    // partials (8 x splits x T x K bytes written and read back) stay within half of the
+    // codes (N x K / 2 bytes); at most kMaxBwdSplits (the finish kernel loads them at once)
     int64_t s = std::max<int64_t>(1, kStreamWGs / p.col_blocks);
-    s = std::min<int64_t>(s, std::max<int64_t>(1, steps / kMinSteps));
-    s = std::min<int64_t>(s, std::max<int64_t>(1, N / (64 * T)));
+    s = std::min<int64_t>(s, std::max<int64_t>(1, steps / 8));
+    s = std::min<int64_t>(s, std::max<int64_t>(1, N / (32 * T)));
+    s = std::min<int64_t>(s, kMaxBwdSplits);
     p.steps_per_split = int(cdiv(steps, s));
     p.splits = int(cdiv(steps, p.steps_per_split));
     p.off_part = 0;
@@ -748,25 +741,27 @@ hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8
                              int64_t K, int r, float s, uint16_t* dx, float* dA, void* ws, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
     float* dxpart = reinterpret_cast<float*>(w + bp.off_dx);
+    if (T > kSkinnyMaxT) return hipErrorInvalidValue;  // one 16-token MFMA block
     if (dx) {
         prof_gemm_begin(stream);
-        switch ((T + 15) / 16) {
-            case 1: launch_bwd_tb<1>(p, codes, absmax, dy, T, N, K, dxpart, stream); break;
-            case 2: launch_bwd_tb<2>(p, codes, absmax, dy, T, N, K, dxpart, stream); break;
-            case 3: launch_bwd_tb<3>(p, codes, absmax, dy, T, N, K, dxpart, stream); break;
-            default: launch_bwd_tb<4>(p, codes, absmax, dy, T, N, K, dxpart, stream); break;
-        }
+        hipLaunchKernelGGL(k_skinny_bwd, dim3(unsigned(p.col_blocks), unsigned(p.splits)), dim3(kThreads), 0, stream, dy,
+                           codes, absmax, int(T), int(N), int(K), p.steps_per_split, dxpart, tables());
         prof_gemm_end(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int col_blocks = int(cdiv(K, kFinCols));
-    const int dx_blocks = dx ? col_blocks * int(cdiv(T, kFinT)) : 0;
-    const int da_blocks = r > 0 ? col_blocks : 0;
+    const int dx_blocks = dx ? col_blocks * int(T) : 0;
+    const int da_blocks = col_blocks * ((r + 15) / 16);
     if (dx_blocks + da_blocks == 0) return hipSuccess;
-    launch_bwd_finish(std::max(1, (r + 15) / 16), int((T + 15) / 16), dim3(unsigned(dx_blocks + da_blocks)), stream,
-                      dxpart, p.splits, reinterpret_cast<const float*>(w + bp.off_gpart), bp.gparts, A, x, int(T),
-                      int(K), r, s, col_blocks, dx_blocks, dx, dA);
+    const dim3 grid(unsigned(dx_blocks + da_blocks));
+    const float* gpart = reinterpret_cast<const float*>(w + bp.off_gpart);
+    switch (std::max(1, (r + 15) / 16)) {
+        case 1: launch_bwd_finish_r<1>(grid, stream, dxpart, p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA); break;
+        case 2: launch_bwd_finish_r<2>(grid, stream, dxpart, p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA); break;
+        case 3: launch_bwd_finish_r<3>(grid, stream, dxpart, p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA); break;
+        default: launch_bwd_finish_r<4>(grid, stream, dxpart, p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA); break;
+    }
     return hipGetLastError();
 }
 
