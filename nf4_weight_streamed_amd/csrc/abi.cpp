@@ -252,15 +252,17 @@ int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, in
     const float scale = lora_scale(alpha, r);
     if (r == 0 && !dx) return NF4_OK;
     char* w = static_cast<char*>(ws);
+    // few-token path: the g / dB pre-pass runs inside the dX launch
+    if (p.skinny)
+        return hip_status(launch_skinny_bwd(p.sk, p, codes, absmax, dy, x, A, B, u_save, T, N, K, r, scale, dx, dA, dB,
+                                            ws, s),
+                          "nf4_lora_linear_bwd (few-token path)");
     if (r > 0) {
         st = hip_status(launch_lora_bwd_pre(p, dy, B, u_save, T, N, r, scale, reinterpret_cast<float*>(w + p.off_gpart),
                                             dB, s),
                         "nf4_lora_linear_bwd (g, dB)");
         if (st != NF4_OK) return st;
     }
-    if (p.skinny)
-        return hip_status(launch_skinny_bwd(p.sk, p, codes, absmax, dy, x, A, T, N, K, r, scale, dx, dA, ws, s),
-                          "nf4_lora_linear_bwd (few-token path)");
     // dX (when requested) with its LoRA term, and dA
     return hip_status(launch_gemm_bwd(p, codes, absmax, dy, x, A, T, N, K, r, scale, dx, dA, ws, s),
                       "nf4_lora_linear_bwd (dX, dA)");

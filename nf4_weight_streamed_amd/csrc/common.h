@@ -100,9 +100,11 @@ hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* 
 hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* x,
                              const uint16_t* A, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,
                              uint16_t* y, float* u_save, void* ws, hipStream_t stream);
+// dX partials and the g / dB pre-pass in one launch, then the finish kernel (dX, dA)
 hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8_t* codes, const float* absmax,
-                             const uint16_t* dy, const uint16_t* x, const uint16_t* A, int64_t T, int64_t N,
-                             int64_t K, int r, float s, uint16_t* dx, float* dA, void* ws, hipStream_t stream);
+                             const uint16_t* dy, const uint16_t* x, const uint16_t* A, const uint16_t* B,
+                             const float* u, int64_t T, int64_t N, int64_t K, int r, float s, uint16_t* dx, float* dA,
+                             float* dB, void* ws, hipStream_t stream);
 
 hipError_t launch_probe_mfma(float* out, int workgroups, int iters, hipStream_t stream);
 

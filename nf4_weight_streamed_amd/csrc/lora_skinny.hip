@@ -13,6 +13,7 @@
 // reduction has a fixed order: results do not depend on scheduling.
 #include "common.h"
 #include "device.h"
+#include "lora_pre.h"
 
 namespace nf4 {
 
@@ -73,176 +74,13 @@ __global__ __launch_bounds__(kThreads) void k_lora_down(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------- backward pre-pass
-// One launch, two kinds of workgroups:
-//  - g role, blocks [0, gblocks): 32 tokens x one N range (part p); per 128-feature
-//    chunk the B rows are staged transposed in LDS ([j][n], double-buffered, loads
-//    one chunk ahead) and each wave contracts 16 tokens x 64 features straight from
-//    dY in registers; the two waves of a token half add up in fixed order -> gpart[p].
-//  - dB role, the rest: 64 features x all tokens in 32-token sub-chunks (dY
-//    transposed and (s.u) hi/lo staged in LDS, loads one sub-chunk ahead) -> dB.
-constexpr int kTC = 32;       // tokens per dB sub-chunk / per g workgroup
-constexpr int kGChunk = 128;  // features per g chunk
-
-template <int RB>
-struct GSmem {
-    uint16_t bt[2][16 * RB][kGChunk + 8];
-    float red[4][RB][64][4];
-};
-template <int RB>
-struct DbSmem {
-    uint16_t dyt[64][kTC + 8];       // [n][t]
-    uint16_t uh[16 * RB][kTC + 8];   // (s.u)^T hi [j][t]
-    uint16_t ul[16 * RB][kTC + 8];   // lo
-};
-
-template <int RB>
-__device__ void g_role(const uint16_t* __restrict__ dy, const uint16_t* __restrict__ B, int T, int N, int r,
-                       int steps_per_part, int blk, float* __restrict__ gpart, GSmem<RB>& sm) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int tblocks = (T + kTC - 1) / kTC;
-    const int t0 = (blk % tblocks) * kTC, part = blk / tblocks;
-    const int c_begin = part * steps_per_part;
-    const int c_end = min(c_begin + steps_per_part, (N + kGChunk - 1) / kGChunk);
-    const int th = wave & 1, nh = wave >> 1;  // token half, feature half of a chunk
-    const auto rdy = make_rsrc(dy + size_t(t0) * N, uint32_t(max(0, min(kTC, T - t0))) * uint32_t(N) * 2u);
-    const auto rb = make_rsrc(B, uint32_t(N) * uint32_t(r) * 2u);  // rows n >= N read as zero
-    const uint32_t dyrow = uint32_t(16 * th + (lane & 15)) * uint32_t(N) * 2u;
-    const int kof = 8 * (lane >> 4);
-    constexpr int BV = kGChunk * 16 * RB / kThreads;  // B values per thread per chunk
-
-    uint32_t bv[BV];
-    u32x4 dv[2];
-    auto gload = [&](int c) {
-        const int n0 = c * kGChunk;
-#pragma unroll
-        for (int i = 0; i < BV; ++i) {
-            const int o = tid + kThreads * i;  // o = n * 16 RB + j
-            const int n = o / (16 * RB), j = o % (16 * RB);
-            bv[i] = __builtin_amdgcn_raw_buffer_load_b16(
-                rb, int(j < r ? (uint32_t(n0 + n) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0);
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int n = n0 + 64 * nh + 32 * kk + kof;
-            dv[kk] = buf_load16(rdy, n < N ? dyrow + uint32_t(n) * 2u : kOutOfRange);
-        }
-    };
-    auto bstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < BV; ++i) {
-            const int o = tid + kThreads * i;
-            sm.bt[buf][o % (16 * RB)][o / (16 * RB)] = uint16_t(bv[i]);
-        }
-    };
-
-    f32x4 acc[RB];
-#pragma unroll
-    for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (c_begin < c_end) {
-        gload(c_begin);
-        bstore(0);
-        __syncthreads();
-        for (int c = c_begin; c < c_end; ++c) {
-            const int buf = (c - c_begin) & 1;
-            const u32x4 d0 = dv[0], d1 = dv[1];
-            gload(c + 1);  // one chunk ahead; past the range: unused data or zeros
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                const uint16_t* row = &sm.bt[buf][16 * b + (lane & 15)][64 * nh + kof];
-                acc[b] = mfma16x16x32(as_bf16x8(d0), as_bf16x8(*reinterpret_cast<const u32x4*>(row)), acc[b]);
-                acc[b] = mfma16x16x32(as_bf16x8(d1), as_bf16x8(*reinterpret_cast<const u32x4*>(row + 32)), acc[b]);
-            }
-            bstore(buf ^ 1);
-            __syncthreads();
-        }
-    }
-#pragma unroll
-    for (int b = 0; b < RB; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.red[wave][b][lane][e] = acc[b][e];
-    __syncthreads();
-    float* dst = gpart + size_t(part) * T * r;
-    for (int o = tid; o < kTC * r; o += kThreads) {
-        const int t = o / r, j = o % r;
-        const int h = t >> 4, tt = t & 15;
-        const int b = j >> 4, l = 16 * (tt >> 2) + (j & 15), e = tt & 3;
-        // waves h (features 0-63 of each chunk) and h + 2 (64-127), in that order
-        const float v = sm.red[h][b][l][e] + sm.red[h + 2][b][l][e];
-        if (t0 + t < T) dst[size_t(t0 + t) * r + j] = v;
-    }
-}
-
-template <int RB>
-__device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict__ u, int T, int N, int r, float s,
-                        int blk, float* __restrict__ dB, DbSmem<RB>& sm) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blk * 64;
-    const int lt = tid >> 3, ln8 = (tid & 7) * 8;  // this thread's 16-byte piece of a sub-chunk
-    constexpr int UV = kTC * 16 * RB / kThreads;   // u values per thread per sub-chunk
-    const auto rdy = make_rsrc(dy, uint32_t(T) * uint32_t(N) * 2u);
-    const auto ru = make_rsrc(u, uint32_t(T) * uint32_t(r) * 4u);
-    u32x4 vdy;
-    float uv[UV];
-    auto gload = [&](int t0) {
-        const bool ok = t0 + lt < T && n0 + ln8 < N;
-        vdy = buf_load16(rdy, ok ? (uint32_t(t0 + lt) * uint32_t(N) + uint32_t(n0 + ln8)) * 2u : kOutOfRange);
-#pragma unroll
-        for (int i = 0; i < UV; ++i) {
-            const int o = tid + kThreads * i;  // o = t * 16 RB + j
-            const int t = o / (16 * RB), j = o % (16 * RB);
-            uv[i] = buf_load_f32(ru, (t0 + t < T && j < r) ? (uint32_t(t0 + t) * uint32_t(r) + uint32_t(j)) * 4u
-                                                           : kOutOfRange);
-        }
-    };
-    auto sstore = [&]() {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t w = vdy[e >> 1];
-            sm.dyt[ln8 + e][lt] = uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF));
-        }
-#pragma unroll
-        for (int i = 0; i < UV; ++i) {
-            const int o = tid + kThreads * i;
-            const int t = o / (16 * RB), j = o % (16 * RB);
-            __bf16 h, l;
-            split_bf16(s * uv[i], h, l);
-            sm.uh[j][t] = __builtin_bit_cast(uint16_t, h);
-            sm.ul[j][t] = __builtin_bit_cast(uint16_t, l);
-        }
-    };
-    f32x4 acc[RB];
-#pragma unroll
-    for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int kof = 8 * (lane >> 4);
-    gload(0);
-    for (int t0 = 0; t0 < T; t0 += kTC) {
-        __syncthreads();  // the previous sub-chunk's reads are done
-        sstore();
-        __syncthreads();
-        gload(t0 + kTC);  // past the end: zeros
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.dyt[16 * wave + (lane & 15)][kof]));
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            const bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.uh[16 * b + (lane & 15)][kof]));
-            const bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.ul[16 * b + (lane & 15)][kof]));
-            acc[b] = mfma16x16x32(a, bh, acc[b]);
-            acc[b] = mfma16x16x32(a, bl, acc[b]);
-        }
-    }
-#pragma unroll
-    for (int b = 0; b < RB; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int n = n0 + 16 * wave + 4 * (lane >> 4) + e, j = 16 * b + (lane & 15);
-            if (n < N && j < r) dB[size_t(n) * r + j] = acc[b][e];
-        }
-}
-
-template <int RB>
-union PreSmem {
-    GSmem<RB> g;
-    DbSmem<RB> d;
-};
+// One launch, the two roles of lora_pre.h: g workgroups [0, gblocks), dB workgroups
+// the rest.
+using pre::db_role;
+using pre::g_role;
+using pre::kGChunk;
+using pre::kTC;
+using pre::PreSmem;
 
 template <int RB>
 __global__ __launch_bounds__(kThreads) void k_lora_bwd_pre(const uint16_t* __restrict__ dy,

@@ -17,6 +17,7 @@
 
 #include "common.h"
 #include "device.h"
+#include "lora_pre.h"
 
 namespace nf4 {
 
@@ -438,14 +439,19 @@ __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __r
 constexpr int kBCols = 256;  // features per workgroup
 constexpr int kBRows = 32;   // weight rows per wave step
 
-__global__ __launch_bounds__(kThreads, 2) void k_skinny_bwd(const uint16_t* __restrict__ dy,
-                                                            const uint8_t* __restrict__ codes,
-                                                            const float* __restrict__ absmax, int T, int N, int K,
-                                                            int steps_per_split, float* __restrict__ dxpart,
-                                                            Tables tab) {
-    __shared__ __align__(16) float sLut[512];
-    __shared__ __align__(16) float sSc[4][4 * kBRows];  // per wave: scales [block][row]
-    __shared__ __align__(16) float sRed[2][16][kBCols];  // cross-wave sums [token][feature]
+struct BwdSmem {
+    float lut[512];
+    float sc[4][4 * kBRows];    // per wave: scales [block][row]
+    float red[2][16][kBCols];   // cross-wave sums [token][feature]
+};
+
+__device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes,
+                                              const float* __restrict__ absmax, int T, int N, int K,
+                                              int steps_per_split, float* __restrict__ dxpart, const Tables& tab,
+                                              BwdSmem& sm) {
+    float* sLut = sm.lut;
+    auto& sSc = sm.sc;
+    auto& sRed = sm.red;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q = lane >> 4;
@@ -559,6 +565,32 @@ __global__ __launch_bounds__(kThreads, 2) void k_skinny_bwd(const uint16_t* __re
         float* dst = dxpart + size_t(blockIdx.y) * T * K + k;
         for (int t = 0; t < T; ++t) dst[size_t(t) * K] = sRed[0][t][tid] + sRed[1][t][tid];
     }
+}
+
+// The backward launch: grid (dx_cols + pre_cols, splits). Columns below dx_cols are dX
+// workgroups (column block x split); the rest run the LoRA pre-pass roles, numbered
+// (x - dx_cols) + pre_cols . y: g workgroups [0, gblocks), dB workgroups
+// [gblocks, gblocks + dblocks), the remainder exit. The roles share no data inside the
+// launch (g is summed by the finish kernel, dB is final).
+template <int RB>
+__global__ __launch_bounds__(kThreads, 2) void k_skinny_bwd(
+    const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
+    const uint16_t* __restrict__ B, const float* __restrict__ u, int T, int N, int K, int r, float s,
+    int steps_per_split, int dx_cols, int pre_cols, int gsteps, int gblocks, int dblocks, float* __restrict__ dxpart,
+    float* __restrict__ gpart, float* __restrict__ dB, Tables tab) {
+    __shared__ __align__(16) union {
+        BwdSmem dx;
+        pre::PreSmem<RB> pre;
+    } sm;
+    if (int(blockIdx.x) < dx_cols) {
+        skinny_bwd_dx(dy, codes, absmax, T, N, K, steps_per_split, dxpart, tab, sm.dx);
+        return;
+    }
+    const int blk = int(blockIdx.x) - dx_cols + pre_cols * int(blockIdx.y);
+    if (blk < gblocks)
+        pre::g_role<RB>(dy, B, T, N, r, gsteps, blk, gpart, sm.pre.g);
+    else if (blk < gblocks + dblocks)
+        pre::db_role<RB>(dy, u, T, N, r, s, blk - gblocks, dB, sm.pre.d);
 }
 
 // Backward finish, two kinds of workgroups in one launch; g = the sum of the pre-pass's
@@ -737,16 +769,32 @@ hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const fl
 }
 
 hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8_t* codes, const float* absmax,
-                             const uint16_t* dy, const uint16_t* x, const uint16_t* A, int64_t T, int64_t N,
-                             int64_t K, int r, float s, uint16_t* dx, float* dA, void* ws, hipStream_t stream) {
+                             const uint16_t* dy, const uint16_t* x, const uint16_t* A, const uint16_t* B,
+                             const float* u, int64_t T, int64_t N, int64_t K, int r, float s, uint16_t* dx, float* dA,
+                             float* dB, void* ws, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
     float* dxpart = reinterpret_cast<float*>(w + bp.off_dx);
+    float* gpart = reinterpret_cast<float*>(w + bp.off_gpart);
     if (T > kSkinnyMaxT) return hipErrorInvalidValue;  // one 16-token MFMA block
-    if (dx) {
-        prof_gemm_begin(stream);
-        hipLaunchKernelGGL(k_skinny_bwd, dim3(unsigned(p.col_blocks), unsigned(p.splits)), dim3(kThreads), 0, stream, dy,
-                           codes, absmax, int(T), int(N), int(K), p.steps_per_split, dxpart, tables());
-        prof_gemm_end(stream);
+    const int dx_cols = dx ? p.col_blocks : 0;
+    const int splits = dx ? p.splits : 1;
+    const int gblocks = r > 0 ? int(cdiv(T, pre::kTC)) * bp.gparts : 0;
+    const int dblocks = r > 0 ? int(cdiv(N, 64)) : 0;
+    const int pre_cols = int(cdiv(gblocks + dblocks, splits));
+    if (dx_cols + pre_cols > 0) {
+        const dim3 grid(unsigned(dx_cols + pre_cols), unsigned(splits));
+        if (dx) prof_gemm_begin(stream);
+        switch (std::max(1, (r + 15) / 16)) {
+            case 1: hipLaunchKernelGGL(k_skinny_bwd<1>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
+                                       p.steps_per_split, dx_cols, pre_cols, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
+            case 2: hipLaunchKernelGGL(k_skinny_bwd<2>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
+                                       p.steps_per_split, dx_cols, pre_cols, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
+            case 3: hipLaunchKernelGGL(k_skinny_bwd<3>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
+                                       p.steps_per_split, dx_cols, pre_cols, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
+            default: hipLaunchKernelGGL(k_skinny_bwd<4>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
+                                        p.steps_per_split, dx_cols, pre_cols, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
+        }
+        if (dx) prof_gemm_end(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -755,7 +803,6 @@ hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8
     const int da_blocks = col_blocks * ((r + 15) / 16);
     if (dx_blocks + da_blocks == 0) return hipSuccess;
     const dim3 grid(unsigned(dx_blocks + da_blocks));
-    const float* gpart = reinterpret_cast<const float*>(w + bp.off_gpart);
     switch (std::max(1, (r + 15) / 16)) {
         case 1: launch_bwd_finish_r<1>(grid, stream, dxpart, p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA); break;
         case 2: launch_bwd_finish_r<2>(grid, stream, dxpart, p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA); break;
