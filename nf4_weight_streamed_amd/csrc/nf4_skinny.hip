@@ -277,8 +277,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_skinny_fwd(
     skinny_fwd_weights<TB>(x, codes, absmax, T, N, K, steps_per_split, ypart, sX, sLut);
 }
 
-constexpr int kFinCols = 512;  // finish kernels: features per workgroup
-constexpr int kFinT = 8;       // forward finish: tokens per workgroup
+// Finish kernels: 64 features (one per lane) x 4 tokens (one per wave) per workgroup,
+// with short loops and few unrolled bodies - they run once per call, so their code is
+// fetched cold - and every independent load issued before the first wait.
+constexpr int kFinF = 64;
+constexpr int kFinTk = 4;
+constexpr int kMaxSplits = 32;  // split partials a finish thread loads at once
+
+// Split partials of one output element: v[z] = src[base + z * zstride] for z < splits,
+// 0 (out-of-range read) for the rest; sum_splits adds all kMaxSplits in split order
+// (the zeros past `splits` leave the sum unchanged).
+__device__ __forceinline__ void load_splits(float (&v)[kMaxSplits], __amdgpu_buffer_rsrc_t rp, int splits,
+                                            uint32_t base, uint32_t zstride, bool live) {
+#pragma unroll
+    for (int z = 0; z < kMaxSplits; ++z)
+        v[z] = buf_load_f32(rp, live && z < splits ? base + uint32_t(z) * zstride : kOutOfRange);
+}
+
+__device__ __forceinline__ float sum_splits(const float (&v)[kMaxSplits]) {
+    float acc = v[0];
+#pragma unroll
+    for (int z = 1; z < kMaxSplits; ++z) acc += v[z];
+    return acc;
+}
 
 // Stage rows [t0, t0 + rows) and columns [j0, j0 + pitch) of an fp32 [T][r] tensor
 // given as `parts` partials (src[p * T * r + t * r + j]) into dst[t - t0][j - j0];
@@ -342,85 +363,45 @@ __device__ __forceinline__ void stage_partial_sums(float* dst, float* tmp, const
     __syncthreads();
 }
 
-// y[t][n] = RNbf( sum_z ypart[z][t][n] + s . sum_j u[t][j] B[n][j] ), u = the sum of
-// its partials, the split partials added in split order. Grid (features / 512,
-// tokens / 8): 2 features per thread, their B rows in registers, u of the 8 tokens
-// staged in LDS; the column-0 workgroups store u_save. The B rows and the first round
-// of split partials are loaded before u is staged; each later round is loaded while the
-// one before it is added.
-template <int RB>
+// y[t][n] = RNbf( sum_z ypart[z][t][n] + s . sum_j u[t][j] B[n][j] ): lane = feature n,
+// wave = token t; u = the sum of its partials and the B rows of the 64 features are
+// staged in LDS; the column-0 workgroups store u_save.
 __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __restrict__ ypart,
                                                                  const float* __restrict__ upart, int uparts,
                                                                  int splits, const uint16_t* __restrict__ B, int T,
                                                                  int N, int r, float s, uint16_t* __restrict__ y,
                                                                  float* __restrict__ u_save) {
-    __shared__ float su[kFinT * kMaxRank];  // u [t - t0][j]
+    __shared__ float su[kFinTk * kMaxRank];  // u [t - t0][j]
+    __shared__ float sB[kMaxRank * kFinF];   // B^T [j][n - n0]
     __shared__ float stmp[kThreads];
-    const int tid = threadIdx.x;
-    const int t0 = int(blockIdx.y) * kFinT, nt = min(kFinT, T - t0);
-    const int n = int(blockIdx.x) * kFinCols + 2 * tid;
-    // B rows n, n + 1 (ranks j >= r and rows past N read zero)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = int(blockIdx.x) * kFinF, t0 = int(blockIdx.y) * kFinTk;
+    const int n = n0 + lane, t = t0 + wave;
+    const bool live = n < N && t < T;
+    float pv[kMaxSplits];
+    load_splits(pv, make_rsrc(ypart, uint32_t(splits) * uint32_t(T) * uint32_t(N) * 4u), splits,
+                (uint32_t(t) * uint32_t(N) + uint32_t(n)) * 4u, uint32_t(T) * uint32_t(N) * 4u, live);
+    // B[n][j] for j = wave + 4i, all loads first (rows past N and ranks past r read 0)
     const auto rb = make_rsrc(B, uint32_t(N) * uint32_t(r) * 2u);
-    constexpr int R = 16 * RB;  // ranks held per thread (>= r)
-    uint32_t bw[R];  // B[n][j] (low half), B[n + 1][j] (high half)
+    constexpr int BV = kMaxRank / kFinTk;
+    uint32_t bv[BV];
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-        const bool ok = j < r && n < N;
-        const uint32_t lo = uint16_t(__builtin_amdgcn_raw_buffer_load_b16(
-            rb, int(ok ? (uint32_t(n) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0));
-        const uint32_t hi = uint16_t(__builtin_amdgcn_raw_buffer_load_b16(
-            rb, int(ok ? (uint32_t(n + 1) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0));
-        bw[j] = lo | (hi << 16);
+    for (int i = 0; i < BV; ++i) {
+        const int j = wave + kFinTk * i;
+        bv[i] = __builtin_amdgcn_raw_buffer_load_b16(
+            rb, int(j < r ? (uint32_t(n) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0);
     }
-    constexpr int ZR = 4;  // splits per round
-    const auto rp = make_rsrc(ypart, uint32_t(splits) * uint32_t(T) * uint32_t(N) * 4u);
-    auto load_round = [&](int z0, u32x2 (&pv)[ZR][kFinT]) {
 #pragma unroll
-        for (int zz = 0; zz < ZR; ++zz)
-#pragma unroll
-            for (int i = 0; i < kFinT; ++i) {
-                const bool ok = z0 + zz < splits && i < nt && n < N;
-                pv[zz][i] = buf_load8(
-                    rp, ok ? ((uint32_t(z0 + zz) * uint32_t(T) + uint32_t(t0 + i)) * uint32_t(N) + uint32_t(n)) * 4u
-                           : kOutOfRange);
-            }
-    };
-    f32x2 acc[kFinT];
-#pragma unroll
-    for (int i = 0; i < kFinT; ++i) acc[i] = f32x2{0.f, 0.f};
-    auto add_round = [&](int z0, const u32x2 (&pv)[ZR][kFinT]) {
-#pragma unroll
-        for (int zz = 0; zz < ZR; ++zz)
-            if (z0 + zz < splits)
-#pragma unroll
-                for (int i = 0; i < kFinT; ++i) acc[i] += __builtin_bit_cast(f32x2, pv[zz][i]);
-    };
-    u32x2 pa[ZR][kFinT], pb[ZR][kFinT];
-    load_round(0, pa);
-    stage_partial_sums(su, stmp, upart, uparts, T, r, t0, nt, 0, r);
+    for (int i = 0; i < BV; ++i) sB[(wave + kFinTk * i) * kFinF + lane] = bf16_to_f32(uint16_t(bv[i]));
+    stage_partial_sums(su, stmp, upart, uparts, T, r, t0, kFinTk, 0, r);  // ends with a barrier
     if (blockIdx.x == 0)
-        for (int o = tid; o < nt * r; o += kThreads) u_save[size_t(t0) * r + o] = su[o];
-    if (n >= N) return;  // N % 16 == 0: both features are in or out
-    for (int z0 = 0; z0 < splits; z0 += 2 * ZR) {
-        load_round(z0 + ZR, pb);
-        add_round(z0, pa);
-        if (z0 + ZR >= splits) break;
-        load_round(z0 + 2 * ZR, pa);
-        add_round(z0 + ZR, pb);
-    }
-#pragma unroll
-    for (int i = 0; i < kFinT; ++i) {
-        if (i >= nt) break;
-        float l0 = 0.0f, l1 = 0.0f;
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            if (j < r) {
-                const float uj = su[i * r + j];
-                l0 += uj * __uint_as_float(bw[j] << 16);
-                l1 += uj * __uint_as_float(bw[j] & 0xFFFF0000u);
-            }
-        *reinterpret_cast<uint32_t*>(&y[size_t(t0 + i) * N + n]) = pack_bf16x2(acc[i][0] + s * l0, acc[i][1] + s * l1);
-    }
+        for (int o = tid; o < min(kFinTk, T - t0) * r; o += kThreads) u_save[size_t(t0) * r + o] = su[o];
+    if (!live) return;
+    const float acc = sum_splits(pv);
+    float l = 0.0f;
+#pragma unroll 8
+    for (int j = 0; j < r; ++j) l += su[wave * r + j] * sB[j * kFinF + lane];
+    y[size_t(t) * N + n] = bf16_bits(acc + s * l);
 }
 
 // ------------------------------------------------------------------ backward dX
@@ -593,86 +574,63 @@ __global__ __launch_bounds__(kThreads, 2) void k_skinny_bwd(
         pre::db_role<RB>(dy, u, T, N, r, s, blk - gblocks, dB, sm.pre.d);
 }
 
-// Backward finish, two kinds of workgroups in one launch; g = the sum of the pre-pass's
-// partials, staged in LDS after each thread has issued its other loads:
-//  - blocks [0, dx_blocks): one token x 512 features (2 per thread, their A columns in
-//    registers): dX[t][k] = RNbf( sum_z dxpart[z][t][k] + s . sum_j g[t][j] A[j][k] ),
-//    the split partials (at most kMaxBwdSplits) all loaded at once, added in split order;
-//  - the rest: 512 features (2 per thread) x 16 ranks: dA[j][k] = s . sum_t g[t][j]
-//    x[t][k], every token's x loaded first, tokens added in increasing order.
-constexpr int kMaxBwdSplits = 32;
-
-template <int RB>
+// Backward finish, two kinds of workgroups in one launch (64 features each, lane =
+// feature k); g = the sum of the pre-pass's partials, staged in LDS:
+//  - blocks [0, dx_blocks): wave = token t: dX[t][k] = RNbf( sum_z dxpart[z][t][k] +
+//    s . sum_j g[t][j] A[j][k] ), A[:, k0 .. k0 + 63] staged in LDS;
+//  - the rest: wave w takes ranks j = w, w + 4, ...: dA[j][k] = s . sum_t g[t][j] x[t][k],
+//    x[:, k0 .. k0 + 63] staged in LDS, tokens added in increasing order.
 __global__ __launch_bounds__(kThreads) void k_skinny_bwd_finish(
     const float* __restrict__ dxpart, int splits, const float* __restrict__ gpart, int gparts,
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ x, int T, int K, int r, float s, int dx_col_blocks,
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ x, int T, int K, int r, float s, int col_blocks,
     int dx_blocks, uint16_t* __restrict__ dx, float* __restrict__ dA) {
-    constexpr int R = 16 * RB;  // ranks held per thread (>= r)
-    __shared__ __align__(16) float sg[kSkinnyMaxT * 16];  // g [t][j - j0] (dA role) or g [t][j] (dX role)
+    __shared__ float sg[kSkinnyMaxT * kMaxRank];   // g [t - t0][j]
+    __shared__ float sw[kMaxRank * kFinF];  // A [j][k - k0] or x [t][k - k0]
     __shared__ float stmp[kThreads];
-    const int tid = threadIdx.x;
-    if (int(blockIdx.x) < dx_blocks) {
-        const int t = int(blockIdx.x) / dx_col_blocks;
-        const int k = (int(blockIdx.x) % dx_col_blocks) * kFinCols + 2 * tid;
-        // A[j][k], A[j][k+1] (ranks j >= r and columns past K read zero)
-        const auto ra = make_rsrc(A, uint32_t(r) * uint32_t(K) * 2u);
-        uint32_t aw[R];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool dx_role = int(blockIdx.x) < dx_blocks;
+    const int b = dx_role ? int(blockIdx.x) : int(blockIdx.x) - dx_blocks;
+    const int k0 = (b % col_blocks) * kFinF, k = k0 + lane;
+    // A rows (dX role) or x rows (dA role), columns k0 .. k0 + 63: all loads first
+    const int wrows = dx_role ? r : T;
+    const auto rw = dx_role ? make_rsrc(A, uint32_t(r) * uint32_t(K) * 2u) : make_rsrc(x, uint32_t(T) * uint32_t(K) * 2u);
+    constexpr int WV = kMaxRank / kFinTk;  // rows wave + 4i
+    uint32_t wv[WV];
 #pragma unroll
-        for (int j = 0; j < R; ++j)
-            aw[j] = buf_load_u32(ra, j < r && k < K ? (uint32_t(j) * uint32_t(K) + uint32_t(k)) * 2u : kOutOfRange);
-        const auto rp = make_rsrc(dxpart, uint32_t(splits) * uint32_t(T) * uint32_t(K) * 4u);
-        u32x2 pv[kMaxBwdSplits];
+    for (int i = 0; i < WV; ++i) {
+        const int row = wave + kFinTk * i;
+        wv[i] = __builtin_amdgcn_raw_buffer_load_b16(
+            rw, int(row < wrows && k < K ? (uint32_t(row) * uint32_t(K) + uint32_t(k)) * 2u : kOutOfRange), 0, 0);
+    }
+    if (dx_role) {
+        const int t = (b / col_blocks) * kFinTk + wave;
+        const bool live = t < T && k < K;
+        float pv[kMaxSplits];
+        load_splits(pv, make_rsrc(dxpart, uint32_t(splits) * uint32_t(T) * uint32_t(K) * 4u), splits,
+                    (uint32_t(t) * uint32_t(K) + uint32_t(k)) * 4u, uint32_t(T) * uint32_t(K) * 4u, live);
 #pragma unroll
-        for (int z = 0; z < kMaxBwdSplits; ++z)
-            pv[z] = buf_load8(rp, z < splits && k < K ? ((uint32_t(z) * uint32_t(T) + uint32_t(t)) * uint32_t(K) + uint32_t(k)) * 4u
-                                                      : kOutOfRange);
-        stage_partial_sums(sg, stmp, gpart, gparts, T, r, t, 1, 0, r);
-        if (k >= K) return;  // K % 64 == 0: both features are in or out
-        f32x2 acc = {0.f, 0.f};
-#pragma unroll
-        for (int z = 0; z < kMaxBwdSplits; ++z)
-            if (z < splits) acc += __builtin_bit_cast(f32x2, pv[z]);
-        float l0 = 0.0f, l1 = 0.0f;
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            if (j < r) {
-                const float gj = sg[j];
-                l0 += gj * __uint_as_float(aw[j] << 16);
-                l1 += gj * __uint_as_float(aw[j] & 0xFFFF0000u);
-            }
-        *reinterpret_cast<uint32_t*>(&dx[size_t(t) * K + k]) = pack_bf16x2(acc[0] + s * l0, acc[1] + s * l1);
+        for (int i = 0; i < WV; ++i) sw[(wave + kFinTk * i) * kFinF + lane] = bf16_to_f32(uint16_t(wv[i]));
+        const int tb0 = (b / col_blocks) * kFinTk;
+        stage_partial_sums(sg, stmp, gpart, gparts, T, r, tb0, kFinTk, 0, r);  // ends with a barrier
+        if (!live) return;
+        const float acc = sum_splits(pv);
+        float l = 0.0f;
+#pragma unroll 8
+        for (int j = 0; j < r; ++j) l += sg[wave * r + j] * sw[j * kFinF + lane];
+        dx[size_t(t) * K + k] = bf16_bits(acc + s * l);
         return;
     }
-    // dA role: block (column block, rank block of 16)
-    const int da = int(blockIdx.x) - dx_blocks;
-    const int k = (da % dx_col_blocks) * kFinCols + 2 * tid;
-    const int j0 = 16 * (da / dx_col_blocks);
-    const auto rx = make_rsrc(x, uint32_t(T) * uint32_t(K) * 2u);
-    uint32_t xv[kSkinnyMaxT];  // tokens past T read zero (and their staged g is zero)
 #pragma unroll
-    for (int t = 0; t < kSkinnyMaxT; ++t)
-        xv[t] = buf_load_u32(rx, t < T && k < K ? (uint32_t(t) * uint32_t(K) + uint32_t(k)) * 2u : kOutOfRange);
-    stage_partial_sums(sg, stmp, gpart, gparts, T, r, 0, kSkinnyMaxT, j0, 16);
+    for (int i = 0; i < WV; ++i) sw[(wave + kFinTk * i) * kFinF + lane] = bf16_to_f32(uint16_t(wv[i]));
+    stage_partial_sums(sg, stmp, gpart, gparts, T, r, 0, T, 0, r);  // ends with a barrier
     if (k >= K) return;
-    float c0[16], c1[16];
+    for (int j = wave; j < r; j += 4) {
+        float c = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) c0[j] = c1[j] = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kSkinnyMaxT; ++t) {
-        const float x0 = __uint_as_float(xv[t] << 16), x1 = __uint_as_float(xv[t] & 0xFFFF0000u);
-#pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sg[t * 16 + 4 * j4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                c0[4 * j4 + e] += g4[e] * x0;
-                c1[4 * j4 + e] += g4[e] * x1;
-            }
-        }
+        for (int t = 0; t < kSkinnyMaxT; ++t)
+            if (t < T) c += sg[t * r + j] * sw[t * kFinF + lane];
+        dA[size_t(j) * K + k] = s * c;
     }
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-        if (j0 + j < r) *reinterpret_cast<f32x2*>(&dA[size_t(j0 + j) * K + k]) = f32x2{s * c0[j], s * c1[j]};
 }
 
 template <int TB>
@@ -684,18 +642,29 @@ void launch_fwd_tb(const SkinnyPlan& p, const uint8_t* codes, const float* absma
                        r, p.steps_per_split, p.row_blocks, ypart, upart, tables());
 }
 
-template <int RB>
-void launch_bwd_finish_r(dim3 grid, hipStream_t stream, const float* dxpart, int splits, const float* gpart, int gparts,
-                         const uint16_t* A, const uint16_t* x, int T, int K, int r, float s, int col_blocks,
-                         int dx_blocks, uint16_t* dx, float* dA) {
-    hipLaunchKernelGGL(k_skinny_bwd_finish<RB>, grid, dim3(kThreads), 0, stream, dxpart, splits, gpart, gparts, A, x, T,
-                       K, r, s, col_blocks, dx_blocks, dx, dA);
-}
+// Split policy of the streaming kernels (measured on the 7B and 72B projection shapes
+// at T = 1..16): about kWGs workgroups of at least kMinSteps main-loop steps each -
+// longer-running workgroups stream better than more of them - unless that leaves
+// fewer than kFillWGs workgroups, then down to one step each; the fp32 partials
+// (written once and read back once, mostly in the last-level cache) at most
+// 1/kPartialDiv of the code bytes; at most kMaxSplits splits (the finish kernels load
+// them all at once).
+constexpr int64_t kFillWGs = 256;
+constexpr int64_t kFwdWGs = 512;
+constexpr int64_t kFwdMinSteps = 4;
+constexpr int64_t kFwdPartialDiv = 2;
+constexpr int64_t kBwdWGs = 512;
+constexpr int64_t kBwdMinSteps = 4;  // one per wave
+constexpr int64_t kBwdPartialDiv = 1;
 
-// Workgroups of a streaming kernel: 2 per CU, each running several steps so that its
-// loads stay in steady state.
-constexpr int64_t kStreamWGs = 512;
-constexpr int64_t kMinSteps = 4;
+int64_t pick_skinny_splits(int64_t blocks, int64_t steps, int64_t wgs, int64_t min_steps, int64_t partial_cap) {
+    int64_t by_steps = std::max<int64_t>(1, steps / min_steps);
+    if (blocks * by_steps < kFillWGs) by_steps = std::min<int64_t>(steps, cdiv(kFillWGs, blocks));
+    int64_t s = std::max<int64_t>(1, wgs / blocks);
+    s = std::min<int64_t>(s, by_steps);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, partial_cap));
+    return std::min<int64_t>(s, kMaxSplits);
+}
 
 }  // namespace
 
@@ -703,12 +672,8 @@ SkinnyPlan plan_skinny_fwd(int64_t T, int64_t N, int64_t K, int r) {
     SkinnyPlan p{};
     p.row_blocks = int(cdiv(N, kRows));
     const int64_t steps = cdiv(K, kDK);
-    // split K until about kStreamWGs workgroups, >= 2 steps each; the fp32 partials,
-    // written and read back (8 x splits x T x N bytes), stay within about a quarter of
-    // the codes (N x K / 2 bytes)
-    int64_t s = std::max<int64_t>(1, kStreamWGs / (p.row_blocks + 1));
-    s = std::min<int64_t>(s, std::max<int64_t>(1, steps / kMinSteps));
-    s = std::min<int64_t>(s, std::max<int64_t>(1, K / (64 * T)));
+    // partial bytes 8 s T N <= N K / (2 kPartialDiv); one u workgroup set per split
+    const int64_t s = pick_skinny_splits(p.row_blocks + 1, steps, kFwdWGs, kFwdMinSteps, K / (16 * kFwdPartialDiv * T));
     p.steps_per_split = int(cdiv(steps, s));
     p.splits = int(cdiv(steps, p.steps_per_split));
     p.off_part = 0;
@@ -723,13 +688,8 @@ SkinnyPlan plan_skinny_bwd(int64_t T, int64_t N, int64_t K) {
     SkinnyPlan p{};
     p.col_blocks = int(cdiv(K, kBCols));
     const int64_t steps = cdiv(N, kBRows);
-    // split N until about kStreamWGs workgroups with >= 2 steps per wave; the fp32
-    // partials (8 x splits x T x K bytes written and read back) stay within half of the
-    // codes (N x K / 2 bytes); at most kMaxBwdSplits (the finish kernel loads them at once)
-    int64_t s = std::max<int64_t>(1, kStreamWGs / p.col_blocks);
-    s = std::min<int64_t>(s, std::max<int64_t>(1, steps / 8));
-    s = std::min<int64_t>(s, std::max<int64_t>(1, N / (32 * T)));
-    s = std::min<int64_t>(s, kMaxBwdSplits);
+    // partial bytes 8 s T K <= N K / (2 kPartialDiv)
+    const int64_t s = pick_skinny_splits(p.col_blocks, steps, kBwdWGs, kBwdMinSteps, N / (16 * kBwdPartialDiv * T));
     p.steps_per_split = int(cdiv(steps, s));
     p.splits = int(cdiv(steps, p.steps_per_split));
     p.off_part = 0;
@@ -753,18 +713,9 @@ hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const fl
     prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 fgrid(unsigned(cdiv(N, kFinCols)), unsigned(cdiv(T, kFinT)));
-    const int uparts = p.splits * kUParts;
-    switch (std::max(1, (r + 15) / 16)) {
-        case 1: hipLaunchKernelGGL(k_skinny_fwd_finish<1>, fgrid, dim3(kThreads), 0, stream, ypart, upart, uparts, p.splits, B,
-                                   int(T), int(N), r, s, y, u_save); break;
-        case 2: hipLaunchKernelGGL(k_skinny_fwd_finish<2>, fgrid, dim3(kThreads), 0, stream, ypart, upart, uparts, p.splits, B,
-                                   int(T), int(N), r, s, y, u_save); break;
-        case 3: hipLaunchKernelGGL(k_skinny_fwd_finish<3>, fgrid, dim3(kThreads), 0, stream, ypart, upart, uparts, p.splits, B,
-                                   int(T), int(N), r, s, y, u_save); break;
-        default: hipLaunchKernelGGL(k_skinny_fwd_finish<4>, fgrid, dim3(kThreads), 0, stream, ypart, upart, uparts, p.splits, B,
-                                    int(T), int(N), r, s, y, u_save); break;
-    }
+    const dim3 fgrid(unsigned(cdiv(N, kFinF)), unsigned(cdiv(T, kFinTk)));
+    hipLaunchKernelGGL(k_skinny_fwd_finish, fgrid, dim3(kThreads), 0, stream, ypart, upart, p.splits * kUParts,
+                       p.splits, B, int(T), int(N), r, s, y, u_save);
     return hipGetLastError();
 }
 
@@ -798,17 +749,12 @@ hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int col_blocks = int(cdiv(K, kFinCols));
-    const int dx_blocks = dx ? col_blocks * int(T) : 0;
-    const int da_blocks = col_blocks * ((r + 15) / 16);
+    const int col_blocks = int(cdiv(K, kFinF));
+    const int dx_blocks = dx ? col_blocks * int(cdiv(T, kFinTk)) : 0;
+    const int da_blocks = r > 0 ? col_blocks : 0;
     if (dx_blocks + da_blocks == 0) return hipSuccess;
-    const dim3 grid(unsigned(dx_blocks + da_blocks));
-    switch (std::max(1, (r + 15) / 16)) {
-        case 1: launch_bwd_finish_r<1>(grid, stream, dxpart, p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA); break;
-        case 2: launch_bwd_finish_r<2>(grid, stream, dxpart, p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA); break;
-        case 3: launch_bwd_finish_r<3>(grid, stream, dxpart, p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA); break;
-        default: launch_bwd_finish_r<4>(grid, stream, dxpart, p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA); break;
-    }
+    hipLaunchKernelGGL(k_skinny_bwd_finish, dim3(unsigned(dx_blocks + da_blocks)), dim3(kThreads), 0, stream, dxpart,
+                       p.splits, gpart, bp.gparts, A, x, int(T), int(K), r, s, col_blocks, dx_blocks, dx, dA);
     return hipGetLastError();
 }
 
