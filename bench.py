@@ -400,6 +400,45 @@ def small_t_sweep(lib, torch, ev: "HipEvents", reps: int = 8) -> dict:
             "weight_sets_cycled": ">= 4, >= 512 MB", "r": RANK}
 
 
+MERGE_SHAPES = [("7b", "gate", 18944, 3584), ("72b", "gate", 29568, 8192)]
+
+
+def merge_measure(lib, torch, ev: "HipEvents", reps: int = 4) -> dict:
+    """Device time of nf4_merge_lora (merge_and_unload: the dense bf16 W + s.B.A) on the
+    gate shapes, r = 16, against HBM bytes = 0.5625 NK (codes + scales read) + 2 NK
+    (merged weight written); weight sets cycled past the last-level cache."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for model, proj, n, k in MERGE_SHAPES:
+        nsets = max(2, int(768e6 // (n * k * 2.5625)) + 1)
+        sets = []
+        for _ in range(nsets):
+            w = (torch.randn(n, k, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+            sets.append(lib.quantize(w))
+            del w
+        a = ((torch.rand(RANK, k, generator=g, device="cuda") * 2 - 1) / k ** 0.5).to(torch.bfloat16)
+        b = (torch.randn(n, RANK, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+        outs = [torch.empty(n, k, dtype=torch.bfloat16, device="cuda") for _ in range(nsets)]
+        for i in range(nsets):
+            lib.merge_lora(sets[i][0], sets[i][1], a, b, ALPHA, out=outs[i])
+        e0, e1 = ev.create(), ev.create()
+        ev.record(e0, stream)
+        for i in range(reps * nsets):
+            lib.merge_lora(sets[i % nsets][0], sets[i % nsets][1], a, b, ALPHA, out=outs[i % nsets])
+        ev.record(e1, stream)
+        us = ev.elapsed_ms(e0, e1) * 1e3 / (reps * nsets)
+        ev.destroy(e0)
+        ev.destroy(e1)
+        nbytes = 2.5625 * n * k
+        rows.append({"model": model, "proj": proj, "N": n, "K": k, "r": RANK, "us": round(us, 2),
+                     "hbm_gbs": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del sets, outs
+        torch.cuda.empty_cache()
+    return {"rows": rows, "bytes_formula": "0.5625NK + 2NK", "peak_gbs": HBM_PEAK_GBS}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,12 +451,14 @@ def main() -> int:
     ap.add_argument("--stack-steps", type=int, default=3)
     ap.add_argument("--small-t-sweep", action="store_true",
                     help="instead of the layer step: per-projection fwd/bwd device time at T = 1..64 vs HBM bytes")
+    ap.add_argument("--merge", action="store_true",
+                    help="instead of the layer step: merge_and_unload (dense W + s.B.A) device time vs HBM bytes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="launch one 1 GiB read + 1 GiB write elementwise kernel first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "
-              "how it would shard is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
+              "GPU; sharding across GPUs is not built)", file=sys.stderr)
         return 2
 
     import torch
@@ -435,6 +476,16 @@ def main() -> int:
         out = {"metric": "NF4-LoRA linear fwd+bwd device time at small T; % of HBM roofline", "n_gpus": 1,
                "dtype": "bf16", "data": "synthetic", "small_t": sweep}
         print(json.dumps(out), flush=True)
+        return 0
+    if args.merge:
+        ev = HipEvents()
+        res = merge_measure(lib, torch, ev)
+        copy_meas = measured_copy_gbs(torch, ev)
+        for row in res["rows"]:
+            row["hbm_frac_vs_measured_copy"] = round(row["hbm_gbs"] / copy_meas, 4)
+        res["hbm_copy_gbs_measured"] = round(copy_meas, 1)
+        print(json.dumps({"metric": "merge_and_unload device time; % of HBM roofline", "n_gpus": 1, "dtype": "bf16",
+                          "data": "synthetic", "merge": res}), flush=True)
         return 0
     if args.copy_calibration:
         copy_calibration(torch)

@@ -96,6 +96,23 @@ int nf4_quantize(const void* w, int in_dtype, int64_t rows, int64_t cols,
 int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int64_t cols,
                    uint16_t* w_bf16, nf4_stream stream);
 
+/*
+ * Merged dense weight of a LoRA-adapted NF4 linear ([api] "PorosModel.merge_and_unload":
+ * the adapters are merged into the base and the module unloaded; the merged weight is
+ * kept dense in the model dtype, bf16, not re-quantised):
+ *     W_m[n][k] = RNbf( RN32( W[n][k] + RN32(s . l[n][k]) ) ),  l = sum_j B[n][j] A[j][k]
+ * with W the dequantised base, s = RN32(alpha / r), l an fp32 sum in rank order
+ * (fused multiply-adds). Not on the training path: a one-time export.
+ *   codes/absmax  device, the NF4 base W [N][K] (K % 64 == 0)
+ *   A             device bf16 [r][K];  B device bf16 [N][r]   (r in 0..NF4_MAX_RANK)
+ *   w_out         device bf16 [N][K]  (written; 16-byte aligned)
+ * r == 0 writes the dequantised base (A, B may be NULL). Size limits as
+ * nf4_lora_linear_fwd (N, K <= 2^21, N*K <= 2^31).
+ */
+int nf4_merge_lora(const uint8_t* codes, const float* absmax, int64_t N, int64_t K,
+                   const uint16_t* A, const uint16_t* B, int r, float alpha,
+                   uint16_t* w_out, nf4_stream stream);
+
 /* Bytes of device workspace nf4_lora_linear_fwd needs for these sizes (may be 0). */
 size_t nf4_lora_linear_fwd_workspace(int64_t T, int64_t N, int64_t K, int r);
 

@@ -190,6 +190,26 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int6
                       "nf4_dequantize");
 }
 
+int nf4_merge_lora(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, const uint16_t* A,
+                   const uint16_t* B, int r, float alpha, uint16_t* w_out, nf4_stream stream) {
+    const char* fn = "nf4_merge_lora";
+    if (N <= 0 || K <= 0 || K % NF4_BLOCK != 0)
+        return fail(NF4_E_SHAPE, "%s: need N > 0 and K a positive multiple of %d (got N=%lld K=%lld)", fn, NF4_BLOCK,
+                    (long long)N, (long long)K);
+    if (N > (int64_t(1) << 21) || K > (int64_t(1) << 21) || N * K > (int64_t(1) << 31))
+        return fail(NF4_E_SHAPE, "%s: sizes beyond the limits N, K <= 2^21, N*K <= 2^31 (N=%lld K=%lld)", fn,
+                    (long long)N, (long long)K);
+    if (r < 0 || r > NF4_MAX_RANK) return fail(NF4_E_ARG, "%s: rank r=%d outside 0..%d", fn, r, NF4_MAX_RANK);
+    if (!std::isfinite(alpha)) return fail(NF4_E_ARG, "%s: alpha is not finite", fn);
+    if (!codes || !absmax || !w_out || (r > 0 && (!A || !B)))
+        return fail(NF4_E_ARG, "%s: NULL pointer (codes, absmax, w_out; A and B when r > 0)", fn);
+    if (!aligned(codes, 4) || !aligned(absmax, 4) || !aligned(w_out, 16) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2))))
+        return fail(NF4_E_ARG, "%s: misaligned pointer (w_out and A need 16 bytes, codes and absmax 4)", fn);
+    return hip_status(launch_merge_lora(codes, absmax, N, K, A, B, r, lora_scale(alpha, r), w_out,
+                                        static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
 size_t nf4_lora_linear_fwd_workspace(int64_t T, int64_t N, int64_t K, int r) {
     if (T <= 0 || N <= 0 || K <= 0 || K % NF4_BLOCK != 0 || r < 0 || r > NF4_MAX_RANK) return 0;
     return plan_fwd(T, N, K, r).ws_bytes;

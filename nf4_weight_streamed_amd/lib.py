@@ -52,6 +52,7 @@ def _load() -> C.CDLL:
         "nf4_codebook": (i32, [C.POINTER(C.c_float)]),
         "nf4_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "nf4_dequantize": (i32, [vp, vp, i64, i64, vp, vp]),
+        "nf4_merge_lora": (i32, [vp, vp, i64, i64, vp, vp, i32, f32, vp, vp]),
         "nf4_lora_linear_fwd_workspace": (sz, [i64, i64, i64, i32]),
         "nf4_lora_linear_fwd": (i32, [vp, vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "nf4_lora_linear_bwd_workspace": (sz, [i64, i64, i64, i32]),
@@ -171,6 +172,25 @@ def dequantize(codes: torch.Tensor, absmax: torch.Tensor, out: torch.Tensor | No
         out = torch.empty((n, k), dtype=torch.bfloat16, device=codes.device)
     _need(out, "out", torch.bfloat16, (n, k))
     _check(_lib.nf4_dequantize(_ptr(codes), _ptr(absmax), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def merge_lora(codes: torch.Tensor, absmax: torch.Tensor, A, B, alpha: float, out: torch.Tensor | None = None,
+               stream=None):
+    """Dense merged weight RNbf(W + RN32((alpha/r) . B.A)) [N, K] bf16 (merge_and_unload)."""
+    n, kh = codes.shape
+    k = kh * 2
+    r = 0 if A is None else A.shape[0]
+    _need(codes, "codes", torch.uint8, (n, kh))
+    _need(absmax, "absmax", torch.float32, (n, k // NF4_BLOCK))
+    if r > 0:
+        _need(A, "A", torch.bfloat16, (r, k))
+        _need(B, "B", torch.bfloat16, (n, r))
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=codes.device)
+    _need(out, "out", torch.bfloat16, (n, k))
+    _check(_lib.nf4_merge_lora(_ptr(codes), _ptr(absmax), n, k, _ptr(A) if r else None, _ptr(B) if r else None, r,
+                               float(alpha), _ptr(out), _stream(stream)))
     return out
 
 

@@ -16,7 +16,7 @@ Pages cited (by title and section):
               main comment: the base is read, never written; it streams into a
               pool of pre-allocated device buffers one layer/block at a time.
 
-Readings where the pages are silent (each is restated with its reason in the design doc):
+Readings where the pages are silent:
   R1  NF4 levels are QLoRA's 4-bit NormalFloat: 8 positive and 7 negative N(0,1)
       quantiles normalised to +-1 plus an exact zero, built in fp64 with the
       conventional offset delta = ((1-1/30)+(1-1/32))/2 and rounded once to fp32.
@@ -38,6 +38,10 @@ Readings where the pages are silent (each is restated with its reason in DESIGN.
       [api] PorosModel.from_pretrained torch_dtype) at the outputs listed in
       ``stack_forward``; the oracle rounds at the same points (``round_storage``)
       and computes everything between them in fp64.
+  R12 merge_and_unload ([api] "PorosModel.merge_and_unload": the adapters are merged
+      into the base and the module unloaded): the merged weight is W + s.B.A, kept
+      dense in the model dtype (bf16); the pages do not re-quantise it, and a dense
+      weight keeps the merged module's output equal to the adapted one's.
 
 Pins (tests/test_oracle_*.py), one line per function:
   nf4_codebook     pinned: two independent inverse-normal routines agree bitwise;
@@ -51,6 +55,8 @@ Pins (tests/test_oracle_*.py), one line per function:
   lora_linear_fwd  pinned: integer closed form; B = 0 equals the base-only GEMM;
                    central finite differences of <dY, y>.
   lora_linear_bwd  pinned: central finite differences; dot-product adjoint identity.
+  merge_lora       pinned: x.W_m^T equals the (separately pinned) LoRA forward y; B = 0
+                   gives the dequantised base bit for bit; integer brute force.
   stack_forward/backward  pinned: central finite differences (storage rounding
                    off); zero-weight layers are the identity; RMSNorm and SiLU
                    against textbook closed forms; storage rounding = f32_to_bf16_bits.
@@ -72,7 +78,7 @@ __all__ = [
     "nf4_codebook", "f32_to_bf16_bits", "bf16_bits_to_f64", "round_bf16",
     "quantize", "unpack_codes", "dequantize",
     "lora_scale", "lora_linear_fwd", "lora_linear_bwd", "lora_linear_fwd_f64",
-    "lora_linear_bwd_f64", "rel_l2",
+    "lora_linear_bwd_f64", "rel_l2", "merge_lora",
     "rmsnorm_fwd", "rmsnorm_bwd", "silu", "silu_grad",
     "StackLayerDims", "stack_forward", "stack_backward",
 ]
@@ -221,6 +227,16 @@ def lora_linear_bwd(x, w, a, b, alpha, dy):
     a = _as_f64(a)
     return lora_linear_bwd_f64(_as_f64(x), _as_f64(w), a, _as_f64(b),
                                lora_scale(alpha, a.shape[0]), _as_f64(dy))
+
+
+def merge_lora(w, a, b, alpha):
+    """Merged dense weight W + s.B.A (R12) in float64, unrounded.
+
+    W [N, K] is the dequantised base (bf16 bits or floats), A [r, K], B [N, r];
+    s = lora_scale(alpha, r). The exported weight is this value rounded to bf16.
+    """
+    a = _as_f64(a)
+    return _as_f64(w) + lora_scale(alpha, a.shape[0]) * (_as_f64(b) @ a)
 
 
 def rel_l2(a, ref) -> float:

@@ -20,7 +20,7 @@ RANK = 16
 ALPHA = 32.0
 
 PROJ_IDS = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "single": 7}
-TENSOR_IDS = {"W": 0, "x": 1, "A": 2, "B": 3, "dY": 4, "h0": 5, "dH": 6}
+TENSOR_IDS = {"W": 0, "x": 1, "A": 2, "B": 3, "dY": 4, "h0": 5, "dH": 6, "codes": 7, "absmax": 8}
 
 # (hidden, q, kv, intermediate, layers) of the Qwen2.5-shaped stacks
 QWEN_SHAPES = {
@@ -90,3 +90,13 @@ def proj_shapes(hidden: int, q: int, kv: int, inter: int) -> dict:
     """(N, K) of the seven projections of one layer, in layer order."""
     return {"q": (q, hidden), "k": (kv, hidden), "v": (kv, hidden), "o": (hidden, q),
             "gate": (inter, hidden), "up": (inter, hidden), "down": (hidden, inter)}
+
+
+def nf4_storage(n: int, k: int, proj: str = "single", layer: int = 0, seed: int = SEED):
+    """Random NF4 storage (codes uint8 [N, K/2], absmax float32 [N, K/64]) for the
+    full-size checks, where quantising a large weight on the CPU would be slow:
+    uniform code bytes, and block scales spread like the largest |value| of 64 draws
+    of N(0, 0.02) (0.02 x U(2.0, 2.9))."""
+    codes = rng("codes", proj, layer, seed).integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    absmax = (0.02 * rng("absmax", proj, layer, seed).uniform(2.0, 2.9, size=(n, k // 64))).astype(np.float32)
+    return codes, absmax

@@ -86,6 +86,22 @@ def test_linear_fwd_validation(L):
     _err(L, _fwd(raw, N=3584, K=3584, T=512, ws_bytes=need - 1), L.NF4_E_ARG, str(need))
 
 
+def test_merge_validation(L):
+    raw = L.raw()
+
+    def merge(N=128, K=128, r=16, alpha=32.0, codes=FAKE, A=FAKE, out=FAKE):
+        return raw.nf4_merge_lora(codes, FAKE, N, K, A, FAKE, r, alpha, out, None)
+
+    _err(L, merge(K=100), L.NF4_E_SHAPE, "K=100")
+    _err(L, merge(N=0), L.NF4_E_SHAPE)
+    _err(L, merge(N=1 << 21, K=1 << 11), L.NF4_E_SHAPE, "limits")
+    _err(L, merge(r=65), L.NF4_E_ARG, "r=65")
+    _err(L, merge(alpha=float("nan")), L.NF4_E_ARG, "alpha")
+    _err(L, merge(codes=None), L.NF4_E_ARG, "NULL")
+    _err(L, merge(A=None), L.NF4_E_ARG, "NULL")
+    _err(L, merge(out=C.c_void_p(0x10008)), L.NF4_E_ARG, "aligned")
+
+
 def test_linear_bwd_validation(L):
     raw = L.raw()
     need = L.bwd_workspace_bytes(256, 1024, 1024, 16)

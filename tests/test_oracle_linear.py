@@ -128,3 +128,42 @@ def test_bits_inputs_equal_float_inputs():
 def test_rel_l2():
     assert O.rel_l2([1.0, 0.0], [1.0, 0.0]) == 0.0
     assert np.isclose(O.rel_l2([3.0, 4.0], [0.0, 5.0]), np.sqrt(10.0) / 5.0)
+
+
+# ----------------------------------------------------------------- merge_and_unload (R12)
+
+def test_merge_reproduces_the_adapted_forward():
+    """x.(W + s.B.A)^T is the LoRA forward's y (an identity of the two definitions)."""
+    rng = np.random.default_rng(21)
+    x = rng.normal(size=(6, 128))
+    w = rng.normal(size=(10, 128))
+    a = rng.normal(size=(5, 128))
+    b = rng.normal(size=(10, 5))
+    wm = O.merge_lora(w, a, b, 32.0)
+    y, _ = O.lora_linear_fwd(x, w, a, b, 32.0)
+    assert wm.shape == w.shape
+    assert np.allclose(x @ wm.T, y, rtol=1e-12, atol=1e-12)
+
+
+def test_merge_with_zero_b_is_the_dequantised_base():
+    rng = np.random.default_rng(22)
+    w = rng.normal(size=(16, 128)).astype(np.float32)
+    codes, absmax = O.quantize(w)
+    wq = O.dequantize(codes, absmax)
+    a = O.f32_to_bf16_bits(rng.normal(size=(4, 128)).astype(np.float32))
+    b = np.zeros((16, 4), np.uint16)
+    assert np.array_equal(O.f32_to_bf16_bits(O.merge_lora(wq, a, b, 32.0).astype(np.float32)), wq)
+
+
+def test_merge_integer_bruteforce():
+    """Small integers: every merged entry by Python integer loops."""
+    rng = np.random.default_rng(23)
+    n, k, r = 3, 8, 2
+    w = _ints(rng, (n, k), -4, 4)
+    a = _ints(rng, (r, k), -3, 3)
+    b = _ints(rng, (n, r), -3, 3)
+    wm = O.merge_lora(w, a, b, 4.0)          # s = 4 / 2 = 2
+    wi, ai, bi = w.astype(int).tolist(), a.astype(int).tolist(), b.astype(int).tolist()
+    for i in range(n):
+        for kk in range(k):
+            assert wm[i, kk] == wi[i][kk] + 2 * sum(bi[i][j] * ai[j][kk] for j in range(r))
