@@ -276,15 +276,19 @@ def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2
     h0 = torch.randn(tokens, dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
     dh = torch.randn(tokens, dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
     out = {}
-    for mode in ("resident", "streamed"):
-        st = ST.NF4Stack(base, lora, tokens, ALPHA, mode=mode)
+    # resident, streamed, and streamed with rematerialisation (block-boundary states kept,
+    # each block's forward recomputed in its backward visit)
+    for mode, remat, key in (("resident", False, "resident"), ("streamed", False, "streamed"),
+                             ("streamed", True, "remat")):
+        st = ST.NF4Stack(base, lora, tokens, ALPHA, mode=mode, remat=remat)
         y, dx = st.step(h0, dh)                       # warmup (and the parity sample)
         torch.cuda.synchronize()
-        out[mode + "_y"], out[mode + "_dx"] = y.clone(), dx.clone()
+        out[key + "_y"], out[key + "_dx"] = y.clone(), dx.clone()
+        out[key + "_act"] = st.activation_bytes()
         c0 = st.pool.stats()["bytes_copied"]
         secs = ST.timed_steps(st, h0, dh, steps, warmup=0)
-        out[mode + "_s"] = secs
-        out[mode + "_bytes"] = (st.pool.stats()["bytes_copied"] - c0) / steps
+        out[key + "_s"] = secs
+        out[key + "_bytes"] = (st.pool.stats()["bytes_copied"] - c0) / steps
         st.close()
         del st
         torch.cuda.empty_cache()
@@ -311,6 +315,15 @@ def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2
         "copy_compute_overlap": None if overlap is None else round(overlap, 3),
         "host_nf4_gb": round(base.total_bytes() / 1e9, 3),
         "build_s": round(build_s, 1),
+        "remat": {
+            "bitwise_equal_to_resident": bool(torch.equal(out["resident_y"], out["remat_y"])
+                                              and torch.equal(out["resident_dx"], out["remat_dx"])),
+            "streamed_ms_per_step": round(out["remat_s"] * 1e3, 3),
+            "over_streamed": round(out["remat_s"] / s_s, 3),
+            "activation_gb": round(out["remat_act"] / 1e9, 3),
+            "activation_gb_stored": round(out["streamed_act"] / 1e9, 3),
+            "h2d_gb_per_step": round(out["remat_bytes"] / 1e9, 3),
+        },
     }
 
 

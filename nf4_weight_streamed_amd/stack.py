@@ -12,6 +12,14 @@ block has its own slot and is copied once up front. Both modes run the same
 kernels on the same bytes at the same offsets, so their results are bitwise
 equal ("Poros on consumer GPUs", "OOM playbook": block_size never affects parity).
 
+With remat=True only the block-boundary hidden states are kept through the
+forward pass; the backward visit of block b (its base is resident for that visit
+anyway) first recomputes the block's forward from its boundary into one block's
+worth of activation buffers ("Poros on consumer GPUs", "OOM playbook": the
+activation memory held is that at the rematerialisation boundary). Every
+kernel is deterministic, so the recomputed activations - and every gradient - are
+bitwise those of the stored-activation run.
+
 Every computation is a call into libnf4lora.so; this module only orders the
 calls, owns buffers (torch allocations) and the two streams.
 
@@ -132,11 +140,11 @@ class NF4Stack:
     """Forward + backward over the stack, streamed through a slot pool or resident."""
 
     def __init__(self, base: HostNF4Base, lora: LoraParams, tokens: int, alpha: float = 32.0,
-                 mode: str = "streamed", n_slots: int = 2, prefetch: bool = True):
+                 mode: str = "streamed", n_slots: int = 2, prefetch: bool = True, remat: bool = False):
         if mode not in ("streamed", "resident"):
             raise ValueError("mode must be 'streamed' or 'resident'")
         self.base, self.lora, self.T, self.alpha = base, lora, tokens, alpha
-        self.mode, self.prefetch = mode, prefetch
+        self.mode, self.prefetch, self.remat = mode, prefetch, remat
         d = base.dims
         self.dims = d
         nb = base.n_blocks
@@ -152,10 +160,14 @@ class NF4Stack:
         self.ws_f = lib.workspace(max(lib.fwd_workspace_bytes(T, n, k, r) for n, k in shapes.values()))
         self.ws_b = lib.workspace(max(lib.bwd_workspace_bytes(T, n, k, r) for n, k in shapes.values()))
         L = base.n_layers
+        # activation sets: one per layer, or (remat) one per layer of a block, plus the
+        # block-boundary hidden states
+        n_sets = base.block_size if remat else L
         self.acts = []
-        for _ in range(L + 1):
+        for _ in range(n_sets + 1):
             self.acts.append({"h": torch.empty(T, d.hidden, **bf)})
-        for li in range(L):
+        self.boundary = [torch.empty(T, d.hidden, **bf) for _ in range(base.n_blocks + 1)] if remat else None
+        for li in range(n_sets):
             a = self.acts[li]
             a.update({
                 "ha": torch.empty(T, d.hidden, **bf), "v": torch.empty(T, d.kv, **bf), "a": torch.empty(T, d.q, **bf),
@@ -206,6 +218,28 @@ class NF4Stack:
         slot = (ptr - self.slab.data_ptr()) // self.base.slot_bytes
         return self._views[slot]
 
+    # ------------------------------------------------------------------ activation sets
+    def _act(self, li: int) -> dict:
+        """Activations of layer li (its input "h" and everything the backward reads)."""
+        return self.acts[li % self.base.block_size] if self.remat else self.acts[li]
+
+    def _h_out(self, li: int) -> torch.Tensor:
+        """Where layer li writes its output hidden state."""
+        if not self.remat:
+            return self.acts[li + 1]["h"]
+        bs = self.base.block_size
+        if (li + 1) % bs == 0 or li + 1 == self.base.n_layers:
+            return self.boundary[li // bs + 1]
+        return self.acts[(li + 1) % bs]["h"]
+
+    def activation_bytes(self) -> int:
+        """Device bytes held for activations between the forward and the backward pass."""
+        n = sum(t.numel() * t.element_size() for a in self.acts for t in a.values() if isinstance(t, torch.Tensor))
+        n += sum(t.numel() * t.element_size() for a in self.acts if "u" in a for t in a["u"].values())
+        if self.boundary is not None:
+            n += sum(t.numel() * t.element_size() for t in self.boundary)
+        return n
+
     # ------------------------------------------------------------------ one layer
     def _fwd(self, w, name, x, y, u):
         c, a = w[name]
@@ -220,7 +254,7 @@ class NF4Stack:
                             need_dx=dx is not None)
 
     def _layer_forward(self, li: int, w):
-        d, A, t = self.dims, self.acts[li], self.tmp
+        d, A, t = self.dims, self._act(li), self.tmp
         self._layer = li
         lib.rmsnorm_fwd(A["h"], RMS_EPS, out=A["ha"], rstd=A["rs_h"])
         self._fwd(w, "q", A["ha"], t["q"], A["u"]["q"])
@@ -234,10 +268,10 @@ class NF4Stack:
         self._fwd(w, "up", A["hm"], A["up"], A["u"]["up"])
         lib.silu_mul_fwd(A["gate"], A["up"], out=A["m"])
         self._fwd(w, "down", A["m"], t["down"], A["u"]["down"])
-        lib.add_bf16(A["h1"], t["down"], out=self.acts[li + 1]["h"])
+        lib.add_bf16(A["h1"], t["down"], out=self._h_out(li))
 
     def _layer_backward(self, li: int, w, dh_out, dh_in):
-        d, A, t = self.dims, self.acts[li], self.tmp
+        d, A, t = self.dims, self._act(li), self.tmp
         self._layer = li
         self._bwd(w, "down", A["m"], A["u"]["down"], dh_out, t["dm"])
         lib.silu_mul_bwd(A["gate"], A["up"], t["dm"], dgate=t["dgate"], dup=t["dup"])
@@ -258,17 +292,22 @@ class NF4Stack:
         bs = self.base.block_size
         return range(b * bs, min((b + 1) * bs, self.base.n_layers))
 
+    def _block_forward(self, b: int, w):
+        if self.remat:
+            self.acts[0]["h"].copy_(self.boundary[b])
+        for li in self._layers_of(b):
+            self._layer_forward(li, w[li - b * self.base.block_size])
+
     def forward(self, h0: torch.Tensor) -> torch.Tensor:
-        self.acts[0]["h"].copy_(h0)
+        (self.boundary[0] if self.remat else self.acts[0]["h"]).copy_(h0)
         nb = self.base.n_blocks
         for b in range(nb):
             w = self._acquire(b)
             if self.prefetch and self.n_slots > 1 and b + 1 < nb:
                 self.pool.prefetch(b + 1)
-            for li in self._layers_of(b):
-                self._layer_forward(li, w[li - b * self.base.block_size])
+            self._block_forward(b, w)
             self.pool.release(b)
-        return self.acts[-1]["h"]
+        return self.boundary[nb] if self.remat else self.acts[-1]["h"]
 
     def backward(self, dh: torch.Tensor) -> torch.Tensor:
         nb = self.base.n_blocks
@@ -279,6 +318,10 @@ class NF4Stack:
             w = self._acquire(b)
             if self.prefetch and self.n_slots > 1 and b - 1 >= 0:
                 self.pool.prefetch(b - 1)
+            if self.remat:
+                # recompute the block's activations from its boundary (the block's last
+                # layer rewrites boundary[b + 1] with the same bits)
+                self._block_forward(b, w)
             for li in reversed(self._layers_of(b)):
                 nxt = self.dh[k]
                 self._layer_backward(li, w[li - b * self.base.block_size], cur, nxt)

@@ -119,6 +119,24 @@ def test_streamed_equals_resident_tiny(ST, block_size):
             assert got["stats"]["misses"] == 1       # only block 0 of the first forward
 
 
+@pytest.mark.parametrize("block_size", [1, 2, 3])
+def test_remat_equals_stored_activations_tiny(ST, block_size):
+    """Rematerialisation (block-boundary states kept, each block's forward recomputed in
+    its backward visit) gives bitwise the results of the stored-activation run, in both
+    modes, with fewer activation bytes."""
+    L, T = 7, 48
+    _, _, base, lora = _tiny_stack(ST, L, block_size)
+    ref = _run(ST, base, lora, T, "resident")
+    for mode, kw in (("resident", {}), ("streamed", {"prefetch": True}), ("streamed", {"prefetch": False})):
+        got = _run(ST, base, lora, T, mode, remat=True, **kw)
+        _same(got, ref)
+    full = ST.NF4Stack(base, lora, T, 32.0, mode="resident")
+    rem = ST.NF4Stack(base, lora, T, 32.0, mode="resident", remat=True)
+    assert rem.activation_bytes() < full.activation_bytes()
+    full.close()
+    rem.close()
+
+
 def test_block_size_never_changes_results(ST):
     L, T = 6, 32
     runs = []
@@ -131,12 +149,15 @@ def test_block_size_never_changes_results(ST):
 
 def test_qwen7b_stack_streamed_equals_resident(ST):
     """28 Qwen2.5-7B-shaped layers, block_size 4, 512 tokens: streamed (2 slots,
-    prefetch one ahead) vs fully resident, bitwise."""
+    prefetch one ahead), with stored and with recomputed activations, vs fully
+    resident, bitwise."""
     dims, L = ST.QWEN25["7b"]
     base = ST.HostNF4Base(dims, L, 4, ST.qwen_weight_fn())
     lora = ST.LoraParams(dims, L, 16, ST.qwen_lora_fn())
     ref = _run(ST, base, lora, 512, "resident")
     got = _run(ST, base, lora, 512, "streamed")
+    _same(got, ref)
+    got = _run(ST, base, lora, 512, "streamed", remat=True)
     _same(got, ref)
     assert torch.isfinite(ref["out"].float()).all() and torch.isfinite(ref["dh0"].float()).all()
     assert got["stats"]["bytes_copied"] > 2 * base.total_bytes()
