@@ -261,14 +261,17 @@ def pinned_h2d_gbs(torch, nbytes: int = 1 << 30) -> float:
     return best
 
 
-def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2d_gbs: float) -> dict:
+def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2d_gbs: float,
+                 base_kind: str = "nf4") -> dict:
     """Streamed vs resident step time of a Qwen2.5-shaped identity-mixing stack, with
-    the bitwise check, H2D traffic and copy/compute overlap."""
+    the bitwise check, H2D traffic and copy/compute overlap. base_kind "bf16" streams a
+    dense bf16 base (the experimental bf16_bitwise mode) instead of NF4."""
     from nf4_weight_streamed_amd import stack as ST
 
     dims, n_layers = ST.QWEN25[model]
     t0 = time.perf_counter()
-    base = ST.HostNF4Base(dims, n_layers, block_size, ST.qwen_weight_fn())
+    host_cls = ST.HostBF16Base if base_kind == "bf16" else ST.HostNF4Base
+    base = host_cls(dims, n_layers, block_size, ST.qwen_weight_fn())
     lora = ST.LoraParams(dims, n_layers, RANK, ST.qwen_lora_fn())
     build_s = time.perf_counter() - t0
     g = torch.Generator(device="cuda")
@@ -298,7 +301,7 @@ def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2
     overlap = (r_s + copy_s - s_s) / min(r_s, copy_s) if min(r_s, copy_s) > 0 else None
     return {
         "workload": f"qwen2.5-{model}-shaped stack, {n_layers} layers, block_size {block_size}, {tokens} tokens, "
-                    "NF4 in pinned host, identity attention mixing, fwd+bwd",
+                    f"{'dense bf16' if base_kind == 'bf16' else 'NF4'} in pinned host, identity attention mixing, fwd+bwd",
         "bitwise_equal_to_resident": bool(torch.equal(out["resident_y"], out["streamed_y"])
                                           and torch.equal(out["resident_dx"], out["streamed_dx"])),
         "resident_ms_per_step": round(r_s * 1e3, 3),
@@ -313,7 +316,7 @@ def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2
         "pcie_frac": round(nbytes / s_s / 1e9 / h2d_gbs, 4),
         "pcie_floor_ratio": round(max(r_s, copy_s) / r_s, 3),
         "copy_compute_overlap": None if overlap is None else round(overlap, 3),
-        "host_nf4_gb": round(base.total_bytes() / 1e9, 3),
+        "host_base_gb": round(base.total_bytes() / 1e9, 3),
         "build_s": round(build_s, 1),
         "remat": {
             "bitwise_equal_to_resident": bool(torch.equal(out["resident_y"], out["remat_y"])
@@ -460,6 +463,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--streamed", default="7b", help="stack for the streamed measurement: 7b, 32b, 72b or none")
     ap.add_argument("--block-size", type=int, default=4)
+    ap.add_argument("--stream-base", default="nf4", choices=("nf4", "bf16"),
+                    help="format of the streamed base: nf4, or dense bf16 (the bf16_bitwise mode)")
     ap.add_argument("--stack-tokens", type=int, default=512)
     ap.add_argument("--stack-steps", type=int, default=3)
     ap.add_argument("--small-t-sweep", action="store_true",
@@ -578,7 +583,8 @@ def main() -> int:
         del layer
         torch.cuda.empty_cache()
         h2d = pinned_h2d_gbs(torch)
-        out["streamed"] = stream_bench(torch, args.streamed, args.block_size, args.stack_tokens, args.stack_steps, h2d)
+        out["streamed"] = stream_bench(torch, args.streamed, args.block_size, args.stack_tokens, args.stack_steps, h2d,
+                                       args.stream_base)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -165,6 +165,26 @@ int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, in
                         uint16_t* dx, float* dA, float* dB,
                         void* ws, size_t ws_bytes, nf4_stream stream);
 
+/*
+ * Dense-bf16 base variant of the linear ([api] "PorosTrainer.from_pretrained", quantization
+ * "bf16_bitwise": an experimental dense-BF16 base streamed blockwise with bitwise resident
+ * parity). Same computation, arguments, workspace rules, limits and errors as
+ * nf4_lora_linear_fwd / nf4_lora_linear_bwd, with the frozen base given directly as
+ *   w   device bf16 [N][K], 16-byte aligned, N*K <= 2^30
+ * in place of codes + absmax. Every T runs the 128-token kernels (no few-token path).
+ */
+size_t nf4_lora_linear_fwd_bf16_workspace(int64_t T, int64_t N, int64_t K, int r);
+int nf4_lora_linear_fwd_bf16(const uint16_t* w, int64_t N, int64_t K,
+                             const uint16_t* x, int64_t T,
+                             const uint16_t* A, const uint16_t* B, int r, float alpha,
+                             uint16_t* y, float* u_save, void* ws, size_t ws_bytes, nf4_stream stream);
+size_t nf4_lora_linear_bwd_bf16_workspace(int64_t T, int64_t N, int64_t K, int r);
+int nf4_lora_linear_bwd_bf16(const uint16_t* w, int64_t N, int64_t K,
+                             const uint16_t* x, const float* u_save, const uint16_t* dy, int64_t T,
+                             const uint16_t* A, const uint16_t* B, int r, float alpha,
+                             uint16_t* dx, float* dA, float* dB,
+                             void* ws, size_t ws_bytes, nf4_stream stream);
+
 /* ------------------------------------------------------------------ stack glue
  * Elementwise/row kernels of the decoder stack that the streamed base feeds
  * (attention mixing replaced by the identity): h' = h + o(repeat_kv(v(RMSNorm(h)))),

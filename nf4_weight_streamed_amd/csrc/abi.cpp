@@ -128,6 +128,20 @@ int check_linear_common(const char* fn, const uint8_t* codes, const float* absma
     return NF4_OK;
 }
 
+// The dense-bf16 base [N][K]: the NF4 limits, and N*K <= 2^30 (2 bytes a weight within
+// 32-bit offsets).
+int check_linear_dense(const char* fn, const uint16_t* w, int64_t N, int64_t K, int64_t T, int r, float alpha) {
+    // the shape / rank / alpha checks of the NF4 entry points, with stand-ins for codes and absmax
+    static const uint8_t kStandIn[16] __attribute__((aligned(16))) = {};
+    int st = check_linear_common(fn, kStandIn, reinterpret_cast<const float*>(kStandIn), N, K, T, r, alpha);
+    if (st != NF4_OK) return st;
+    if (!w) return fail(NF4_E_ARG, "%s: the bf16 base must not be NULL", fn);
+    if (N * K > (int64_t(1) << 30))
+        return fail(NF4_E_SHAPE, "%s: dense base beyond N*K <= 2^30 (N=%lld K=%lld)", fn, (long long)N, (long long)K);
+    if (!aligned(w, 16)) return fail(NF4_E_ARG, "%s: the bf16 base must be 16-byte aligned", fn);
+    return NF4_OK;
+}
+
 float lora_scale(float alpha, int r) { return r > 0 ? alpha / float(r) : 0.0f; }
 
 }  // namespace
@@ -215,18 +229,37 @@ size_t nf4_lora_linear_fwd_workspace(int64_t T, int64_t N, int64_t K, int r) {
     return plan_fwd(T, N, K, r).ws_bytes;
 }
 
-int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, const uint16_t* x,
-                        int64_t T, const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* y,
-                        float* u_save, void* ws, size_t ws_bytes, nf4_stream stream) {
-    const char* fn = "nf4_lora_linear_fwd";
-    int st = check_linear_common(fn, codes, absmax, N, K, T, r, alpha);
-    if (st != NF4_OK) return st;
+size_t nf4_lora_linear_fwd_bf16_workspace(int64_t T, int64_t N, int64_t K, int r) {
+    if (T <= 0 || N <= 0 || K <= 0 || K % NF4_BLOCK != 0 || r < 0 || r > NF4_MAX_RANK) return 0;
+    return plan_fwd(T, N, K, r, true).ws_bytes;
+}
+
+size_t nf4_lora_linear_bwd_workspace(int64_t T, int64_t N, int64_t K, int r) {
+    if (T <= 0 || N <= 0 || K <= 0 || K % NF4_BLOCK != 0 || r < 0 || r > NF4_MAX_RANK) return 0;
+    return plan_bwd(T, N, K, r).ws_bytes;
+}
+
+size_t nf4_lora_linear_bwd_bf16_workspace(int64_t T, int64_t N, int64_t K, int r) {
+    if (T <= 0 || N <= 0 || K <= 0 || K % NF4_BLOCK != 0 || r < 0 || r > NF4_MAX_RANK) return 0;
+    return plan_bwd(T, N, K, r, true).ws_bytes;
+}
+
+}  // extern "C"
+
+namespace nf4 {
+namespace {
+
+// The forward after the base-specific checks; the base is NF4 (codes, absmax) or dense
+// bf16 (wdense not NULL).
+int linear_fwd(const char* fn, const uint8_t* codes, const float* absmax, const uint16_t* wdense, int64_t N, int64_t K,
+               const uint16_t* x, int64_t T, const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* y,
+               float* u_save, void* ws, size_t ws_bytes, nf4_stream stream) {
     if (T == 0) return NF4_OK;
     if (!x || !y) return fail(NF4_E_ARG, "%s: x/y must not be NULL", fn);
     if (r > 0 && (!A || !B || !u_save)) return fail(NF4_E_ARG, "%s: r=%d needs A, B and u_save", fn, r);
     if (!aligned(x, 16) || !aligned(y, 16) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || !aligned(u_save, 4))))
         return fail(NF4_E_ARG, "%s: misaligned pointer (x, y and A need 16 bytes)", fn);
-    const FwdPlan p = plan_fwd(T, N, K, r);
+    const FwdPlan p = plan_fwd(T, N, K, r, wdense != nullptr);
     if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes || !aligned(ws, 256)))
         return fail(NF4_E_ARG, "%s: workspace of %zu bytes (256-byte aligned) needed for T=%lld N=%lld K=%lld r=%d, got %zu",
                     fn, p.ws_bytes, (long long)T, (long long)N, (long long)K, r, ws_bytes);
@@ -237,25 +270,17 @@ int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, in
                           "nf4_lora_linear_fwd (few-token path)");
     if (r > 0) {
         float* upart = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_upart);
-        st = hip_status(launch_lora_down(p, x, A, T, K, r, upart, s), "nf4_lora_linear_fwd (x.A^T)");
+        int st = hip_status(launch_lora_down(p, x, A, T, K, r, upart, s), "nf4_lora_linear_fwd (x.A^T)");
         if (st != NF4_OK) return st;
     }
-    return hip_status(launch_gemm_fwd(p, codes, absmax, x, B, T, N, K, r, scale, y, u_save, ws, s),
+    return hip_status(launch_gemm_fwd(p, codes, absmax, wdense, x, B, T, N, K, r, scale, y, u_save, ws, s),
                       "nf4_lora_linear_fwd (gemm)");
 }
 
-size_t nf4_lora_linear_bwd_workspace(int64_t T, int64_t N, int64_t K, int r) {
-    if (T <= 0 || N <= 0 || K <= 0 || K % NF4_BLOCK != 0 || r < 0 || r > NF4_MAX_RANK) return 0;
-    return plan_bwd(T, N, K, r).ws_bytes;
-}
-
-int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, const uint16_t* x,
-                        const float* u_save, const uint16_t* dy, int64_t T, const uint16_t* A, const uint16_t* B,
-                        int r, float alpha, uint16_t* dx, float* dA, float* dB, void* ws, size_t ws_bytes,
-                        nf4_stream stream) {
-    const char* fn = "nf4_lora_linear_bwd";
-    int st = check_linear_common(fn, codes, absmax, N, K, T, r, alpha);
-    if (st != NF4_OK) return st;
+int linear_bwd(const char* fn, const uint8_t* codes, const float* absmax, const uint16_t* wdense, int64_t N, int64_t K,
+               const uint16_t* x, const float* u_save, const uint16_t* dy, int64_t T, const uint16_t* A,
+               const uint16_t* B, int r, float alpha, uint16_t* dx, float* dA, float* dB, void* ws, size_t ws_bytes,
+               nf4_stream stream) {
     if (T == 0) return NF4_OK;
     if (!dy) return fail(NF4_E_ARG, "%s: dy must not be NULL", fn);
     if (r > 0 && (!x || !u_save || !A || !B || !dA || !dB))
@@ -264,7 +289,7 @@ int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, in
         (r > 0 && (!aligned(x, 16) || !aligned(A, 16) || !aligned(B, 2) || !aligned(u_save, 4) || !aligned(dA, 16) ||
                    !aligned(dB, 4))))
         return fail(NF4_E_ARG, "%s: misaligned pointer (dy, dx, x, A and dA need 16 bytes)", fn);
-    const BwdPlan p = plan_bwd(T, N, K, r);
+    const BwdPlan p = plan_bwd(T, N, K, r, wdense != nullptr);
     if (!ws || ws_bytes < p.ws_bytes || !aligned(ws, 256))
         return fail(NF4_E_ARG, "%s: workspace of %zu bytes (256-byte aligned) needed for T=%lld N=%lld K=%lld r=%d, got %zu",
                     fn, p.ws_bytes, (long long)T, (long long)N, (long long)K, r, ws_bytes);
@@ -278,14 +303,58 @@ int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, in
                                             ws, s),
                           "nf4_lora_linear_bwd (few-token path)");
     if (r > 0) {
-        st = hip_status(launch_lora_bwd_pre(p, dy, B, u_save, T, N, r, scale, reinterpret_cast<float*>(w + p.off_gpart),
-                                            dB, s),
-                        "nf4_lora_linear_bwd (g, dB)");
+        int st = hip_status(launch_lora_bwd_pre(p, dy, B, u_save, T, N, r, scale,
+                                                reinterpret_cast<float*>(w + p.off_gpart), dB, s),
+                            "nf4_lora_linear_bwd (g, dB)");
         if (st != NF4_OK) return st;
     }
     // dX (when requested) with its LoRA term, and dA
-    return hip_status(launch_gemm_bwd(p, codes, absmax, dy, x, A, T, N, K, r, scale, dx, dA, ws, s),
+    return hip_status(launch_gemm_bwd(p, codes, absmax, wdense, dy, x, A, T, N, K, r, scale, dx, dA, ws, s),
                       "nf4_lora_linear_bwd (dX, dA)");
+}
+
+}  // namespace
+}  // namespace nf4
+
+extern "C" {
+
+int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, const uint16_t* x,
+                        int64_t T, const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* y,
+                        float* u_save, void* ws, size_t ws_bytes, nf4_stream stream) {
+    const char* fn = "nf4_lora_linear_fwd";
+    const int st = nf4::check_linear_common(fn, codes, absmax, N, K, T, r, alpha);
+    if (st != NF4_OK) return st;
+    return nf4::linear_fwd(fn, codes, absmax, nullptr, N, K, x, T, A, B, r, alpha, y, u_save, ws, ws_bytes, stream);
+}
+
+int nf4_lora_linear_fwd_bf16(const uint16_t* w, int64_t N, int64_t K, const uint16_t* x, int64_t T,
+                             const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* y, float* u_save,
+                             void* ws, size_t ws_bytes, nf4_stream stream) {
+    const char* fn = "nf4_lora_linear_fwd_bf16";
+    const int st = nf4::check_linear_dense(fn, w, N, K, T, r, alpha);
+    if (st != NF4_OK) return st;
+    return nf4::linear_fwd(fn, nullptr, nullptr, w, N, K, x, T, A, B, r, alpha, y, u_save, ws, ws_bytes, stream);
+}
+
+int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, const uint16_t* x,
+                        const float* u_save, const uint16_t* dy, int64_t T, const uint16_t* A, const uint16_t* B,
+                        int r, float alpha, uint16_t* dx, float* dA, float* dB, void* ws, size_t ws_bytes,
+                        nf4_stream stream) {
+    const char* fn = "nf4_lora_linear_bwd";
+    const int st = nf4::check_linear_common(fn, codes, absmax, N, K, T, r, alpha);
+    if (st != NF4_OK) return st;
+    return nf4::linear_bwd(fn, codes, absmax, nullptr, N, K, x, u_save, dy, T, A, B, r, alpha, dx, dA, dB, ws,
+                           ws_bytes, stream);
+}
+
+int nf4_lora_linear_bwd_bf16(const uint16_t* w, int64_t N, int64_t K, const uint16_t* x, const float* u_save,
+                             const uint16_t* dy, int64_t T, const uint16_t* A, const uint16_t* B, int r, float alpha,
+                             uint16_t* dx, float* dA, float* dB, void* ws, size_t ws_bytes, nf4_stream stream) {
+    const char* fn = "nf4_lora_linear_bwd_bf16";
+    const int st = nf4::check_linear_dense(fn, w, N, K, T, r, alpha);
+    if (st != NF4_OK) return st;
+    return nf4::linear_bwd(fn, nullptr, nullptr, w, N, K, x, u_save, dy, T, A, B, r, alpha, dx, dA, dB, ws, ws_bytes,
+                           stream);
 }
 
 }  // extern "C"

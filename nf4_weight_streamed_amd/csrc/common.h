@@ -67,7 +67,7 @@ struct FwdPlan {
     bool skinny;          // few-token path (then only sk and ws_bytes apply)
     SkinnyPlan sk;
 };
-FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r);
+FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r, bool dense = false);  // dense: bf16 base, 128-token kernels only
 void plan_lora_down(FwdPlan& p, int64_t K);
 
 // Backward plan. Workspace: [g partials | dA shares per token tile | split-K
@@ -83,19 +83,20 @@ struct BwdPlan {
     bool skinny;           // few-token path: g partials and dX partials (sk) at off_gpart / off_dx
     SkinnyPlan sk;
 };
-BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r);
+BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense = false);
 void plan_lora_bwd_pre(BwdPlan& p, int64_t N, int max_parts);  // g partials over N ranges
 
 hipError_t launch_lora_down(const FwdPlan& p, const uint16_t* x, const uint16_t* A, int64_t T, int64_t K, int r,
                             float* upart, hipStream_t stream);
-hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* x,
-                           const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s, uint16_t* y,
-                           float* u_save, void* ws, hipStream_t stream);
+// the base is NF4 (codes, absmax) or, when wdense is not NULL, dense bf16 [N][K]
+hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* wdense,
+                           const uint16_t* x, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,
+                           uint16_t* y, float* u_save, void* ws, hipStream_t stream);
 hipError_t launch_lora_bwd_pre(const BwdPlan& p, const uint16_t* dy, const uint16_t* B, const float* u, int64_t T,
                                int64_t N, int r, float s, float* gpart, float* dB, hipStream_t stream);
-hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* dy,
-                           const uint16_t* x, const uint16_t* A, int64_t T, int64_t N, int64_t K, int r, float s,
-                           uint16_t* dx, float* dA, void* ws, hipStream_t stream);
+hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* wdense,
+                           const uint16_t* dy, const uint16_t* x, const uint16_t* A, int64_t T, int64_t N, int64_t K,
+                           int r, float s, uint16_t* dx, float* dA, void* ws, hipStream_t stream);
 
 hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* x,
                              const uint16_t* A, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,

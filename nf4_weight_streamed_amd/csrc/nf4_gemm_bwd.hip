@@ -10,7 +10,10 @@
 // as [k][n] and the MFMA B operand is again a contiguous 16-byte read. The 16-byte
 // chunks of each LDS row are XOR-swizzled by (k / 8) % 8: the 8-byte transposed
 // stores of a wave then spread over all banks, and the fragment reads (8
-// consecutive rows share one swizzle) stay conflict-free.
+// consecutive rows share one swizzle) stay conflict-free. With kDense the base is
+// dense bf16 (the experimental "bf16_bitwise" streaming mode of the Poros API
+// reference, "PorosTrainer.from_pretrained"): the patch is four 16-byte row pieces,
+// paired across rows the same way, with nothing to dequantise.
 #include <type_traits>
 
 #include "common.h"
@@ -42,8 +45,9 @@ struct BwdLora {
     float s;
 };
 
+template <bool kDense>
 __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
-    const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const float* __restrict__ absmax, int T,
+    const uint16_t* __restrict__ dy, const void* __restrict__ weights, const float* __restrict__ absmax, int T,
     int N, int K, int steps_per_split, BwdLora lora, uint16_t* __restrict__ dx, float* __restrict__ partial,
     Tables tab) {
     constexpr int BM = 128, BK = 128;
@@ -81,8 +85,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     const auto rdy = make_rsrc(dy + size_t(m0) * N, trows * uint32_t(N) * 2u);
     // codes/absmax of the whole matrix (the entry points keep N*K/2 below 2^30 bytes);
     // patches beyond N or K load from kOutOfRange and read as zero
-    const auto rcd = make_rsrc(codes, uint32_t(N) * uint32_t(K / 2));
-    const auto rsc = make_rsrc(absmax, uint32_t(N) * uint32_t(K / 64) * 4u);
+    // dense bf16: N*K*2 bytes (the entry points keep N*K <= 2^30)
+    const auto rcd = make_rsrc(weights, uint32_t(N) * uint32_t(K) * (kDense ? 2u : 1u) / (kDense ? 1u : 2u));
+    const auto rsc = make_rsrc(kDense ? nullptr : absmax, kDense ? 0u : uint32_t(N) * uint32_t(K / 64) * 4u);
     const uint32_t kc = uint32_t(k0 + 8 * pc);
     uint32_t a_off[A_CHUNKS];
 #pragma unroll
@@ -92,8 +97,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     }
 
     u32x4 ra[A_CHUNKS];
-    uint32_t rc[4];
+    uint32_t rc[4];  // NF4: 8 codes of each patch row
     float rs[4];
+    u32x4 rw[4];     // dense: 8 bf16 of each patch row
     auto gload = [&](int nb) {
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
@@ -107,8 +113,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t n = uint32_t(nb * kBN + 4 * pr + i);
-            rc[i] = buf_load_u32(rcd, n * uint32_t(K / 2) + kc / 2);
-            rs[i] = buf_load_f32(rsc, n * uint32_t(K / 64) * 4u + (kc / 64) * 4u);
+            if constexpr (kDense) {
+                rw[i] = buf_load16(rcd, (n * uint32_t(K) + kc) * 2u);
+            } else {
+                rc[i] = buf_load_u32(rcd, n * uint32_t(K / 2) + kc / 2);
+                rs[i] = buf_load_f32(rsc, n * uint32_t(K / 64) * 4u + (kc / 64) * 4u);
+            }
         }
     };
     const char* lut = reinterpret_cast<const char*>(sLut);
@@ -117,6 +127,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
         for (int i = 0; i < A_CHUNKS; ++i) {
             const int c = tid + kThreads * i;
             *reinterpret_cast<u32x4*>(&sA[buf][(c >> 3) * kLds + (c & 7) * 8]) = ra[i];
+        }
+        // row k = 8*pc + e holds n = 4*pr .. 4*pr+3: chunk pr/2 (swizzled by pc), half pr&1
+        const int col = (((pr >> 1) ^ (pc & 7)) << 3) + 4 * (pr & 1);
+        if constexpr (kDense) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sh = 16 * (e & 1);
+                auto bits = [&](int i) { return (rw[i][e >> 1] >> sh) & 0xFFFFu; };
+                const u32x2 o = {bits(0) | (bits(1) << 16), bits(2) | (bits(3) << 16)};
+                *reinterpret_cast<u32x2*>(&sWt[buf][(8 * pc + e) * kLds + col]) = o;
+            }
+            return;
         }
         float v[4][8];
 #pragma unroll
@@ -128,8 +150,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
                 v[i][2 * b] = lv.x * rs[i];
                 v[i][2 * b + 1] = lv.y * rs[i];
             }
-        // row k = 8*pc + e holds n = 4*pr .. 4*pr+3: chunk pr/2 (swizzled by pc), half pr&1
-        const int col = (((pr >> 1) ^ (pc & 7)) << 3) + 4 * (pr & 1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             u32x2 o = {pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e])};
@@ -377,9 +397,9 @@ __global__ __launch_bounds__(256) void k_bwd_finish(const float* __restrict__ dx
 
 }  // namespace
 
-BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r) {
+BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     BwdPlan p{};
-    if (T <= kSkinnyT) {
+    if (T <= kSkinnyT && !dense) {
         p.skinny = true;
         p.sk = plan_skinny_bwd(T, N, K);
         if (r > 0) plan_lora_bwd_pre(p, N, kMaxGPartsFew);
@@ -409,9 +429,9 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r) {
     return p;
 }
 
-hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* dy,
-                           const uint16_t* x, const uint16_t* A, int64_t T, int64_t N, int64_t K, int r, float s,
-                           uint16_t* dx, float* dA, void* ws, hipStream_t stream) {
+hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* wdense,
+                           const uint16_t* dy, const uint16_t* x, const uint16_t* A, int64_t T, int64_t N, int64_t K,
+                           int r, float s, uint16_t* dx, float* dA, void* ws, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
     // without dx only the LoRA part runs: one workgroup per tile, no contraction steps
     const int splits = dx ? p.splits : 1;
@@ -420,8 +440,14 @@ hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* 
     float* dapart = reinterpret_cast<float*>(w + p.off_dapart);
     const BwdLora lora{reinterpret_cast<const float*>(w + p.off_gpart), p.gparts, A, x, dapart, r, s};
     if (dx) prof_gemm_begin(stream);
-    hipLaunchKernelGGL(k_nf4_gemm_bwd_dx, grid, dim3(kThreads), 0, stream, dy, codes, absmax, int(T), int(N), int(K),
-                       dx ? p.steps_per_split : 0, lora, dx, partial, tables());
+    if (wdense)
+        hipLaunchKernelGGL(k_nf4_gemm_bwd_dx<true>, grid, dim3(kThreads), 0, stream, dy,
+                           static_cast<const void*>(wdense), nullptr, int(T), int(N), int(K),
+                           dx ? p.steps_per_split : 0, lora, dx, partial, tables());
+    else
+        hipLaunchKernelGGL(k_nf4_gemm_bwd_dx<false>, grid, dim3(kThreads), 0, stream, dy,
+                           static_cast<const void*>(codes), absmax, int(T), int(N), int(K),
+                           dx ? p.steps_per_split : 0, lora, dx, partial, tables());
     if (dx) prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -16,6 +16,10 @@
 //    caller's workspace (split 0 carries the LoRA term), added in split order and
 //    rounded once by k_split_sum_bf16 (a kernel boundary, not in-kernel signalling:
 //    the per-XCD L2 caches are only made coherent by whole-cache maintenance).
+// The same kernel, with kDense, takes a dense bf16 base instead (the experimental
+// dense-bf16 streaming mode of the Poros API reference, "PorosTrainer.from_pretrained"
+// quantization "bf16_bitwise"): each lane then loads its 32 weights of a K step as four
+// 16-byte pieces, already in MFMA fragment order, and nothing is dequantised.
 #include <type_traits>
 
 #include "common.h"
@@ -51,9 +55,9 @@ struct FwdLora {
     float s;
 };
 
-template <int NW>
+template <int NW, bool kDense>
 __global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const float* __restrict__ absmax, int T,
+    const uint16_t* __restrict__ x, const void* __restrict__ weights, const float* __restrict__ absmax, int T,
     int N, int K, int steps_per_split, FwdLora lora, uint16_t* __restrict__ y, float* __restrict__ partial,
     Tables tab) {
     constexpr int NT = 64 * NW;
@@ -88,13 +92,16 @@ __global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
     const uint32_t xrows = uint32_t(max(0, min(BM, T - m0)));
     const uint32_t wrows = uint32_t(max(0, min(BN, N - n0)));
     const auto rx = make_rsrc(x + size_t(m0) * K, xrows * uint32_t(K) * 2u);
-    const auto rcd = make_rsrc(codes + size_t(n0) * (K / 2), wrows * uint32_t(K / 2));
-    const auto rsc = make_rsrc(absmax + size_t(n0) * (K / 64), wrows * uint32_t(K / 64) * 4u);
+    // weight operand: NF4 codes (0.5 B / weight) + scales, or dense bf16 (2 B / weight)
+    constexpr uint32_t kWBytesPerStep = kDense ? kBK * 2 : kBK / 2;  // per row and K step
+    const auto rcd = make_rsrc(static_cast<const uint8_t*>(weights) + size_t(n0) * kWBytesPerStep * (K / kBK),
+                               wrows * uint32_t(K / kBK) * kWBytesPerStep);
+    const auto rsc = make_rsrc(kDense ? nullptr : absmax + size_t(n0) * (K / 64), kDense ? 0u : wrows * uint32_t(K / 64) * 4u);
     uint32_t c_off[FN], s_off[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int wrow = 32 * (FN * wave + j) + frag_row;  // this lane's weight row of fragment j
-        c_off[j] = uint32_t(wrow) * uint32_t(K / 2) + uint32_t(half) * 16u;
+        c_off[j] = uint32_t(wrow) * uint32_t(K / kBK) * kWBytesPerStep + uint32_t(half) * (kWBytesPerStep / 2);
         s_off[j] = uint32_t(wrow) * uint32_t(K / 64) * 4u;
     }
     uint32_t x_off[A_CHUNKS];
@@ -104,18 +111,20 @@ __global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
         x_off[i] = (uint32_t(c >> 3) * uint32_t(K) + uint32_t(c & 7) * 8u) * 2u;
     }
 
+    constexpr int WP = kDense ? 4 : 1;  // 16-byte weight pieces per lane, fragment and K step
     u32x4 ra[A_CHUNKS];
-    u32x4 rc[2][FN];
+    u32x4 rc[2][FN][WP];
     float rs[2][FN];
     auto gload_x = [&](int kb) {
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) ra[i] = buf_load16(rx, x_off[i] + uint32_t(kb) * (kBK * 2));
     };
-    auto gload_w = [&](int kb, u32x4 (&cw)[FN], float (&sc)[FN]) {
+    auto gload_w = [&](int kb, u32x4 (&cw)[FN][WP], float (&sc)[FN]) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            cw[j] = buf_load16(rcd, c_off[j] + uint32_t(kb) * 32u);
-            sc[j] = buf_load_f32(rsc, s_off[j] + uint32_t(kb) * 4u);
+#pragma unroll
+            for (int q = 0; q < WP; ++q) cw[j][q] = buf_load16(rcd, c_off[j] + uint32_t(kb) * kWBytesPerStep + 16u * q);
+            if constexpr (!kDense) sc[j] = buf_load_f32(rsc, s_off[j] + uint32_t(kb) * 4u);
         }
     };
     auto store_x = [&](int buf) {
@@ -127,12 +136,16 @@ __global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
     };
     const char* lut = reinterpret_cast<const char*>(sLut);
     bf16x8 wf[FN][4];
-    auto dequant = [&](const u32x4 (&cw)[FN], const float (&sc)[FN]) {
+    auto dequant = [&](const u32x4 (&cw)[FN][WP], const float (&sc)[FN]) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t w = cw[j][q];
+                if constexpr (kDense) {
+                    wf[j][q] = as_bf16x8(cw[j][q]);
+                    continue;
+                }
+                const uint32_t w = cw[j][0][q];
                 u32x4 o;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
@@ -334,9 +347,9 @@ __global__ __launch_bounds__(256) void k_split_sum_bf16(const float* __restrict_
 
 }  // namespace
 
-FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r) {
+FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     FwdPlan p{};
-    if (T <= kSkinnyT) {
+    if (T <= kSkinnyT && !dense) {
         p.skinny = true;
         p.sk = plan_skinny_fwd(T, N, K, r);
         p.ws_bytes = p.sk.ws_bytes;
@@ -359,17 +372,23 @@ FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r) {
     return p;
 }
 
-hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* x,
-                           const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s, uint16_t* y,
-                           float* u_save, void* ws, hipStream_t stream) {
+hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* wdense,
+                           const uint16_t* x, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,
+                           uint16_t* y, float* u_save, void* ws, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
     const dim3 grid(unsigned(cdiv(N, p.bn)), unsigned(cdiv(T, p.bm)), unsigned(p.splits));
     float* partial = p.splits > 1 ? reinterpret_cast<float*>(w + p.off_ypart) : nullptr;
     const FwdLora lora{r > 0 ? reinterpret_cast<const float*>(w + p.off_upart) : nullptr, p.down_parts, u_save, B,
                        r, s};
     prof_gemm_begin(stream);
-    hipLaunchKernelGGL(k_nf4_gemm_fwd<kFwdWaves>, grid, dim3(64 * kFwdWaves), 0, stream, x, codes, absmax, int(T),
-                       int(N), int(K), p.steps_per_split, lora, y, partial, tables());
+    if (wdense)
+        hipLaunchKernelGGL((k_nf4_gemm_fwd<kFwdWaves, true>), grid, dim3(64 * kFwdWaves), 0, stream, x,
+                           static_cast<const void*>(wdense), nullptr, int(T), int(N), int(K), p.steps_per_split, lora, y,
+                           partial, tables());
+    else
+        hipLaunchKernelGGL((k_nf4_gemm_fwd<kFwdWaves, false>), grid, dim3(64 * kFwdWaves), 0, stream, x,
+                           static_cast<const void*>(codes), absmax, int(T), int(N), int(K), p.steps_per_split, lora, y,
+                           partial, tables());
     prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;

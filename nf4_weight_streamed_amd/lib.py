@@ -56,6 +56,10 @@ def _load() -> C.CDLL:
         "nf4_lora_linear_fwd_workspace": (sz, [i64, i64, i64, i32]),
         "nf4_lora_linear_fwd": (i32, [vp, vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "nf4_lora_linear_bwd_workspace": (sz, [i64, i64, i64, i32]),
+        "nf4_lora_linear_fwd_bf16_workspace": (sz, [i64, i64, i64, i32]),
+        "nf4_lora_linear_fwd_bf16": (i32, [vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "nf4_lora_linear_bwd_bf16_workspace": (sz, [i64, i64, i64, i32]),
+        "nf4_lora_linear_bwd_bf16": (i32, [vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "nf4_lora_linear_bwd": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "nf4_profile_next_gemm": (i32, [vp, vp]),
         "nf4_probe_mfma": (i32, [vp, i32, i32, vp]),
@@ -268,6 +272,72 @@ def lora_linear_bwd(codes, absmax, x, u, dy, A, B, alpha: float, dx=None, dA=Non
                                     _ptr(B), r, float(alpha), _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes,
                                     _stream(stream)))
     return dx, dA, dB
+
+
+def lora_linear_fwd_bf16(w, x, A, B, alpha: float, y=None, u=None, ws=None, stream=None):
+    """The linear forward with a dense bf16 base w [N, K] (the "bf16_bitwise" mode). Returns (y, u)."""
+    n, k = w.shape
+    t = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(w, "w", torch.bfloat16, (n, k))
+    _need(x, "x", torch.bfloat16, (t, k))
+    if r:
+        _need(A, "A", torch.bfloat16, (r, k))
+        _need(B, "B", torch.bfloat16, (n, r))
+    if y is None:
+        y = torch.empty((t, n), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, (t, n))
+    if r and u is None:
+        u = torch.empty((t, r), dtype=torch.float32, device=x.device)
+    if r:
+        _need(u, "u", torch.float32, (t, r))
+    need = int(_lib.nf4_lora_linear_fwd_bf16_workspace(t, n, k, r))
+    if ws is None and need:
+        ws = workspace(need, x.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.nf4_lora_linear_fwd_bf16(_ptr(w), n, k, _ptr(x), t, _ptr(A), _ptr(B), r, float(alpha), _ptr(y),
+                                         _ptr(u), _ptr(ws), ws_bytes, _stream(stream)))
+    return y, u
+
+
+def lora_linear_bwd_bf16(w, x, u, dy, A, B, alpha: float, dx=None, dA=None, dB=None, ws=None, need_dx: bool = True,
+                         stream=None):
+    """The linear backward with a dense bf16 base w [N, K]: returns (dx or None, dA, dB)."""
+    n, k = w.shape
+    t = dy.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(w, "w", torch.bfloat16, (n, k))
+    _need(dy, "dy", torch.bfloat16, (t, n))
+    if r:
+        _need(x, "x", torch.bfloat16, (t, k))
+        _need(u, "u", torch.float32, (t, r))
+        _need(A, "A", torch.bfloat16, (r, k))
+        _need(B, "B", torch.bfloat16, (n, r))
+        if dA is None:
+            dA = torch.empty((r, k), dtype=torch.float32, device=dy.device)
+        if dB is None:
+            dB = torch.empty((n, r), dtype=torch.float32, device=dy.device)
+        _need(dA, "dA", torch.float32, (r, k))
+        _need(dB, "dB", torch.float32, (n, r))
+    if need_dx and dx is None:
+        dx = torch.empty((t, k), dtype=torch.bfloat16, device=dy.device)
+    if dx is not None:
+        _need(dx, "dx", torch.bfloat16, (t, k))
+    if ws is None:
+        ws = workspace(int(_lib.nf4_lora_linear_bwd_bf16_workspace(t, n, k, r)), dy.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.nf4_lora_linear_bwd_bf16(_ptr(w), n, k, _ptr(x), _ptr(u), _ptr(dy), t, _ptr(A), _ptr(B), r,
+                                         float(alpha), _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes,
+                                         _stream(stream)))
+    return dx, dA, dB
+
+
+def fwd_bf16_workspace_bytes(T: int, N: int, K: int, r: int) -> int:
+    return int(_lib.nf4_lora_linear_fwd_bf16_workspace(T, N, K, r))
+
+
+def bwd_bf16_workspace_bytes(T: int, N: int, K: int, r: int) -> int:
+    return int(_lib.nf4_lora_linear_bwd_bf16_workspace(T, N, K, r))
 
 
 # ---------------------------------------------------------------- stack glue (bf16 device tensors)

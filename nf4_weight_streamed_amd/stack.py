@@ -12,6 +12,10 @@ block has its own slot and is copied once up front. Both modes run the same
 kernels on the same bytes at the same offsets, so their results are bitwise
 equal ("Poros on consumer GPUs", "OOM playbook": block_size never affects parity).
 
+HostBF16Base holds a dense bf16 base instead (the experimental "bf16_bitwise"
+mode of the Poros API reference, "PorosTrainer.from_pretrained"); the stack then
+calls the dense entry points, with the same pool, modes and parity.
+
 With remat=True only the block-boundary hidden states are kept through the
 forward pass; the backward visit of block b (its base is resident for that visit
 anyway) first recomputes the block's forward from its boundary into one block's
@@ -95,6 +99,8 @@ class HostNF4Base:
     nf4_quantize on the GPU into a staging slab that is copied into the block's
     pinned slab (block by block, so device residency stays at one block)."""
 
+    dense = False
+
     def __init__(self, dims: StackDims, n_layers: int, block_size: int, weight_fn):
         if block_size < 1:
             raise ValueError("block_size must be >= 1")
@@ -117,6 +123,59 @@ class HostNF4Base:
                     absmax = staging[a_off:a_off + n * (k // 64) * 4].view(torch.float32).view(n, k // 64)
                     lib.quantize(w, codes=codes, absmax=absmax)
                     del w
+            host = torch.empty(used, dtype=torch.uint8, pin_memory=True)
+            host.copy_(staging[:used])           # D2H into pinned memory (synchronous)
+            self.blocks.append(host)
+            self.block_bytes.append(used)
+        torch.cuda.synchronize()
+
+    def total_bytes(self) -> int:
+        return sum(self.block_bytes)
+
+
+def block_layout_bf16(dims: StackDims, layers: int):
+    """Dense-bf16 slabs: [{proj: (w_off,)}] and the slab size, pieces 256-byte aligned."""
+    off = 0
+    table = []
+    for _ in range(layers):
+        entry = {}
+        for name in PROJS:
+            n, k = dims.shapes()[name]
+            entry[name] = (off,)
+            off = _align(off + n * k * 2)
+        table.append(entry)
+    return table, off
+
+
+class HostBF16Base:
+    """The frozen base as dense bf16 in pinned host memory, one slab per block (the
+    experimental "bf16_bitwise" mode of the Poros API reference,
+    "PorosTrainer.from_pretrained": a dense-BF16 base streamed blockwise, bitwise equal
+    to a resident run; 2 bytes a weight against NF4's 0.5625).
+
+    weight_fn(layer, proj, n, k) -> bf16 device tensor [n, k], staged on the device
+    and copied into the block's pinned slab block by block."""
+
+    dense = True
+
+    def __init__(self, dims: StackDims, n_layers: int, block_size: int, weight_fn):
+        if block_size < 1:
+            raise ValueError("block_size must be >= 1")
+        self.dims, self.n_layers, self.block_size = dims, n_layers, block_size
+        self.n_blocks = (n_layers + block_size - 1) // block_size
+        self.layout, self.slot_bytes = block_layout_bf16(dims, block_size)
+        self.blocks = []
+        self.block_bytes = []
+        staging = torch.empty(self.slot_bytes, dtype=torch.uint8, device="cuda")
+        for b in range(self.n_blocks):
+            nl = min(block_size, n_layers - b * block_size)
+            used = block_layout_bf16(dims, nl)[1]
+            for li in range(nl):
+                layer = b * block_size + li
+                for name in PROJS:
+                    n, k = dims.shapes()[name]
+                    (w_off,) = self.layout[li][name]
+                    staging[w_off:w_off + n * k * 2].view(torch.bfloat16).view(n, k).copy_(weight_fn(layer, name, n, k))
             host = torch.empty(used, dtype=torch.uint8, pin_memory=True)
             host.copy_(staging[:used])           # D2H into pinned memory (synchronous)
             self.blocks.append(host)
@@ -157,8 +216,10 @@ class NF4Stack:
         shapes = d.shapes()
         dev = "cuda"
         bf = dict(dtype=torch.bfloat16, device=dev)
-        self.ws_f = lib.workspace(max(lib.fwd_workspace_bytes(T, n, k, r) for n, k in shapes.values()))
-        self.ws_b = lib.workspace(max(lib.bwd_workspace_bytes(T, n, k, r) for n, k in shapes.values()))
+        fws = lib.fwd_bf16_workspace_bytes if base.dense else lib.fwd_workspace_bytes
+        bws = lib.bwd_bf16_workspace_bytes if base.dense else lib.bwd_workspace_bytes
+        self.ws_f = lib.workspace(max(fws(T, n, k, r) for n, k in shapes.values()))
+        self.ws_b = lib.workspace(max(bws(T, n, k, r) for n, k in shapes.values()))
         L = base.n_layers
         # activation sets: one per layer, or (remat) one per layer of a block, plus the
         # block-boundary hidden states
@@ -205,8 +266,13 @@ class NF4Stack:
         out = []
         for entry in self.base.layout:
             v = {}
-            for name, (c_off, a_off) in entry.items():
+            for name, offs in entry.items():
                 n, k = self.dims.shapes()[name]
+                if self.base.dense:
+                    (w_off,) = offs
+                    v[name] = (self.slab[slot * sb + w_off: slot * sb + w_off + n * k * 2].view(torch.bfloat16).view(n, k),)
+                    continue
+                c_off, a_off = offs
                 c = self.slab[slot * sb + c_off: slot * sb + c_off + n * k // 2].view(n, k // 2)
                 a = self.slab[slot * sb + a_off: slot * sb + a_off + n * (k // 64) * 4].view(torch.float32).view(n, k // 64)
                 v[name] = (c, a)
@@ -242,14 +308,21 @@ class NF4Stack:
 
     # ------------------------------------------------------------------ one layer
     def _fwd(self, w, name, x, y, u):
-        c, a = w[name]
         p = self.lora.p[self._layer][name]
+        if self.base.dense:
+            lib.lora_linear_fwd_bf16(w[name][0], x, p[0], p[1], self.alpha, y=y, u=u, ws=self.ws_f)
+            return
+        c, a = w[name]
         lib.lora_linear_fwd(c, a, x, p[0], p[1], self.alpha, y=y, u=u, ws=self.ws_f)
 
     def _bwd(self, w, name, x, u, dy, dx):
-        c, a = w[name]
         p = self.lora.p[self._layer][name]
         dA, dB = self.grads[self._layer][name]
+        if self.base.dense:
+            lib.lora_linear_bwd_bf16(w[name][0], x, u, dy, p[0], p[1], self.alpha, dx=dx, dA=dA, dB=dB, ws=self.ws_b,
+                                     need_dx=dx is not None)
+            return
+        c, a = w[name]
         lib.lora_linear_bwd(c, a, x, u, dy, p[0], p[1], self.alpha, dx=dx, dA=dA, dB=dB, ws=self.ws_b,
                             need_dx=dx is not None)
 

@@ -102,6 +102,25 @@ def test_merge_validation(L):
     _err(L, merge(out=C.c_void_p(0x10008)), L.NF4_E_ARG, "aligned")
 
 
+def test_dense_linear_validation(L):
+    raw = L.raw()
+
+    def fwd(w=FAKE, N=128, K=128, T=4, r=16):
+        return raw.nf4_lora_linear_fwd_bf16(w, N, K, FAKE, T, FAKE, FAKE, r, 32.0, FAKE, FAKE, FAKE, 1 << 30, None)
+
+    _err(L, fwd(w=None), L.NF4_E_ARG, "bf16 base")
+    _err(L, fwd(w=C.c_void_p(0x10008)), L.NF4_E_ARG, "16-byte")
+    _err(L, fwd(K=100), L.NF4_E_SHAPE, "K=100")
+    _err(L, fwd(N=1 << 20, K=1 << 11), L.NF4_E_SHAPE, "2^30")      # N*K = 2^31: beyond the dense limit
+    _err(L, fwd(r=65), L.NF4_E_ARG, "r=65")
+    assert fwd(T=0) == 0
+    rc = raw.nf4_lora_linear_bwd_bf16(None, 128, 128, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 16, 32.0, FAKE, FAKE, FAKE,
+                                      FAKE, 1 << 30, None)
+    _err(L, rc, L.NF4_E_ARG, "bf16 base")
+    # the dense variant never takes the few-token path: its plans differ from the NF4 ones at small T
+    assert L.bwd_bf16_workspace_bytes(4, 1024, 1024, 16) != L.bwd_workspace_bytes(4, 1024, 1024, 16)
+
+
 def test_linear_bwd_validation(L):
     raw = L.raw()
     need = L.bwd_workspace_bytes(256, 1024, 1024, 16)

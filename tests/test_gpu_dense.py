@@ -1,0 +1,130 @@
+"""The dense-bf16 base variant (the experimental "bf16_bitwise" mode of the Poros API
+reference, "PorosTrainer.from_pretrained"): the linear vs the fp64 oracle with W the
+bf16 weights themselves, and the streamed dense stack vs resident, bitwise."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic_inputs as S
+from helpers import bits_of, check_bf16_output, check_f32_output, f32_of, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+PROJS = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+@pytest.mark.parametrize("t,n,k,r", [
+    (256, 1024, 1024, 16),   # the single-linear workload
+    (300, 400, 640, 16),     # ragged in every dimension
+    (1, 128, 256, 16),       # one token (128-token kernels for every T)
+    (17, 3584, 512, 5),      # odd rank
+    (129, 512, 3584, 64),    # maximum rank, split contraction
+    (64, 256, 512, 0),       # base only
+])
+def test_dense_linear_matches_oracle(gpu_lib, t, n, k, r):
+    case = S.linear_case(t, n, k, r=max(r, 1))
+    if r == 0:
+        case["A"], case["B"] = np.zeros((0, k), np.uint16), np.zeros((n, 0), np.uint16)
+    w = to_dev_bf16(case["W"])
+    A = to_dev_bf16(case["A"]) if r else None
+    B = to_dev_bf16(case["B"]) if r else None
+    y, u = gpu_lib.lora_linear_fwd_bf16(w, to_dev_bf16(case["x"]), A, B, 32.0)
+    dx, da, db = gpu_lib.lora_linear_bwd_bf16(w, to_dev_bf16(case["x"]), u, to_dev_bf16(case["dY"]), A, B, 32.0)
+    torch.cuda.synchronize()
+    y_ref, u_ref = O.lora_linear_fwd(case["x"], case["W"], case["A"], case["B"], 32.0)
+    dx_ref, da_ref, db_ref = O.lora_linear_bwd(case["x"], case["W"], case["A"], case["B"], 32.0, case["dY"])
+    check_bf16_output(bits_of(y), y_ref, f"dense y {t}x{n}x{k} r{r}")
+    check_bf16_output(bits_of(dx), dx_ref, f"dense dX {t}x{n}x{k} r{r}")
+    if r:
+        check_f32_output(f32_of(u), u_ref, "u")
+        check_f32_output(f32_of(da), da_ref, "dA")
+        check_f32_output(f32_of(db), db_ref, "dB")
+
+
+def test_dense_equals_nf4_on_the_dequantised_base(gpu_lib):
+    """Fed the dequantised NF4 base as dense weights, the dense kernels compute the
+    NF4 kernels' results bit for bit (same tiles, same contraction order)."""
+    t, n, k = 200, 768, 1024
+    case = S.linear_case(t, n, k)
+    codes, absmax = O.quantize(O.bf16_bits_to_f64(case["W"]).astype(np.float32))
+    wq = to_dev_bf16(O.dequantize(codes, absmax))
+    c, s = torch.from_numpy(codes).cuda(), torch.from_numpy(absmax).cuda()
+    x, dy, A, B = (to_dev_bf16(case[key]) for key in ("x", "dY", "A", "B"))
+    y1, u1 = gpu_lib.lora_linear_fwd(c, s, x, A, B, 32.0)
+    y2, u2 = gpu_lib.lora_linear_fwd_bf16(wq, x, A, B, 32.0)
+    d1 = gpu_lib.lora_linear_bwd(c, s, x, u1, dy, A, B, 32.0)
+    d2 = gpu_lib.lora_linear_bwd_bf16(wq, x, u2, dy, A, B, 32.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(u1, u2)
+    for a, b in zip(d1, d2):
+        assert torch.equal(a, b)
+
+
+@pytest.fixture(scope="module")
+def ST(gpu_lib):
+    from nf4_weight_streamed_amd import stack
+
+    return stack
+
+
+def _dense_stack(ST, n_layers, block_size):
+    dims = ST.StackDims(hidden=128, q=128, kv=32, inter=256, head_dim=32)
+    w = {(l, p): S.weight(*dims.shapes()[p], proj=p, layer=l) for l in range(n_layers) for p in PROJS}
+    lo = {}
+    for l in range(n_layers):
+        for p in PROJS:
+            n, k = dims.shapes()[p]
+            lo[(l, p)] = (S.lora_a(16, k, proj=p, layer=l), S.lora_b(n, 16, proj=p, layer=l, std=0.05))
+    base = ST.HostBF16Base(dims, n_layers, block_size, lambda l, p, n, k: to_dev_bf16(w[(l, p)]))
+    lora = ST.LoraParams(dims, n_layers, 16, lambda l, p, n, k: tuple(to_dev_bf16(t) for t in lo[(l, p)]))
+    return dims, w, lo, base, lora
+
+
+def _step(ST, base, lora, T, mode, **kw):
+    st = ST.NF4Stack(base, lora, T, 32.0, mode=mode, **kw)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    h0 = torch.randn(T, base.dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    dh = torch.randn(T, base.dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    out, dh0 = st.step(h0, dh)
+    out2, _ = st.step(h0, dh)
+    torch.cuda.synchronize()
+    res = (out.clone(), dh0.clone(), out2.clone(), [{p: (a.clone(), b.clone()) for p, (a, b) in gl.items()}
+                                                   for gl in st.grads])
+    st.close()
+    return res
+
+
+@pytest.mark.parametrize("block_size", [1, 2, 3])
+def test_dense_stack_streamed_equals_resident(ST, block_size):
+    _, _, _, base, lora = _dense_stack(ST, 5, block_size)
+    ref = _step(ST, base, lora, 40, "resident")
+    for kw in ({"prefetch": True}, {"prefetch": False}, {"prefetch": True, "remat": True}):
+        got = _step(ST, base, lora, 40, "streamed", **kw)
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]) and torch.equal(got[2], ref[0])
+        for ga, gb in zip(got[3], ref[3]):
+            for p in PROJS:
+                assert torch.equal(ga[p][0], gb[p][0]) and torch.equal(ga[p][1], gb[p][1])
+
+
+def test_dense_stack_matches_oracle(ST):
+    L, T, alpha = 3, 40, 32.0
+    dims, w, lo, base, lora = _dense_stack(ST, L, 2)
+    h0 = S.activations(T, dims.hidden, tensor="h0")
+    dh = S.activations(T, dims.hidden, tensor="dH")
+    st = ST.NF4Stack(base, lora, T, alpha, mode="streamed")
+    out, dh0 = st.step(to_dev_bf16(h0), to_dev_bf16(dh))
+    torch.cuda.synchronize()
+    od = O.StackLayerDims(dims.hidden, dims.q, dims.kv, dims.inter, dims.head_dim)
+    layers = [{p: (w[(l, p)], lo[(l, p)][0], lo[(l, p)][1]) for p in PROJS} for l in range(L)]
+    out_ref, saved = O.stack_forward(h0, layers, od, alpha)
+    dh0_ref, grads = O.stack_backward(dh, layers, od, alpha, saved)
+    assert O.rel_l2(O.bf16_bits_to_f64(bits_of(out)), out_ref) <= 2e-3
+    assert O.rel_l2(O.bf16_bits_to_f64(bits_of(dh0)), dh0_ref) <= 2e-3
+    for l in range(L):
+        for p in ("v", "o", "gate", "up", "down"):
+            dA, dB = st.grads[l][p]
+            assert O.rel_l2(f32_of(dA), grads[l][p + "_dA"]) <= 2e-3, (l, p)
+            assert O.rel_l2(f32_of(dB), grads[l][p + "_dB"]) <= 2e-3, (l, p)
+    st.close()
