@@ -32,8 +32,8 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t 
 #define NF4_MAX_RANK_BLOCKS 4  // r <= 16 * NF4_MAX_RANK_BLOCKS (= NF4_MAX_RANK)
 
 // Partial counts of the skinny LoRA products, summed per tile by the GEMM kernels.
-constexpr int kMaxDownParts = 4;  // K ranges of u = x.A^T
-constexpr int kMaxGParts = 8;     // N ranges of g = dY.B (128-token path)
+constexpr int kMaxDownParts = 16; // K ranges of u = x.A^T
+constexpr int kMaxGParts = 16;    // N ranges of g = dY.B (128-token path)
 constexpr int kMaxGPartsFew = 64; // N ranges of g = dY.B (few-token path: summed by the finish kernel)
 
 // Few-token path (T <= kSkinnyT; measured faster than the 128-token kernels up to T = 16,

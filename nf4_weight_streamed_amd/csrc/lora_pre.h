@@ -19,21 +19,24 @@ constexpr int kThreads = 256;
 //    chunk the B rows are staged transposed in LDS ([j][n], double-buffered, loads
 //    one chunk ahead) and each wave contracts 16 tokens x 64 features straight from
 //    dY in registers; the two waves of a token half add up in fixed order -> gpart[p].
-//  - dB role: 64 features x all tokens in 32-token sub-chunks (dY
-//    transposed and (s.u) hi/lo staged in LDS, loads one sub-chunk ahead) -> dB.
-constexpr int kTC = 32;       // tokens per dB sub-chunk / per g workgroup
-constexpr int kGChunk = 128;  // features per g chunk
+//  - dB role: 64 features x all tokens in DBT-token sub-chunks (dY
+//    transposed and (s.u) hi/lo staged in LDS, loads one sub-chunk ahead) -> dB;
+//    with many tokens the sub-chunks are long (kDbTLong) so that few of them (one
+//    memory round trip each) run in sequence.
+constexpr int kTC = 32;         // tokens per g workgroup; dB sub-chunk for few tokens
+constexpr int kDbTLong = 128;   // dB sub-chunk for many tokens
+constexpr int kGChunk = 128;    // features per g chunk
 
 template <int RB>
 struct GSmem {
     uint16_t bt[2][16 * RB][kGChunk + 8];
     float red[4][RB][64][4];
 };
-template <int RB>
+template <int RB, int DBT>
 struct DbSmem {
-    uint16_t dyt[64][kTC + 8];       // [n][t]
-    uint16_t uh[16 * RB][kTC + 8];   // (s.u)^T hi [j][t]
-    uint16_t ul[16 * RB][kTC + 8];   // lo
+    uint16_t dyt[64][DBT + 8];       // [n][t]
+    uint16_t uh[16 * RB][DBT + 8];   // (s.u)^T hi [j][t]
+    uint16_t ul[16 * RB][DBT + 8];   // lo
 };
 
 template <int RB>
@@ -113,20 +116,25 @@ __device__ void g_role(const uint16_t* __restrict__ dy, const uint16_t* __restri
     }
 }
 
-template <int RB>
+template <int RB, int DBT>
 __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict__ u, int T, int N, int r, float s,
-                        int blk, float* __restrict__ dB, DbSmem<RB>& sm) {
+                        int blk, float* __restrict__ dB, DbSmem<RB, DBT>& sm) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blk * 64;
-    const int lt = tid >> 3, ln8 = (tid & 7) * 8;  // this thread's 16-byte piece of a sub-chunk
-    constexpr int UV = kTC * 16 * RB / kThreads;   // u values per thread per sub-chunk
+    const int lt = tid >> 3, ln8 = (tid & 7) * 8;  // 16-byte pieces: tokens lt + 32 i, features ln8 .. ln8 + 7
+    constexpr int DV = DBT / 32;                   // dY pieces per thread per sub-chunk
+    constexpr int UV = DBT * 16 * RB / kThreads;   // u values per thread per sub-chunk
     const auto rdy = make_rsrc(dy, uint32_t(T) * uint32_t(N) * 2u);
     const auto ru = make_rsrc(u, uint32_t(T) * uint32_t(r) * 4u);
-    u32x4 vdy;
+    u32x4 vdy[DV];
     float uv[UV];
     auto gload = [&](int t0) {
-        const bool ok = t0 + lt < T && n0 + ln8 < N;
-        vdy = buf_load16(rdy, ok ? (uint32_t(t0 + lt) * uint32_t(N) + uint32_t(n0 + ln8)) * 2u : kOutOfRange);
+#pragma unroll
+        for (int i = 0; i < DV; ++i) {
+            const int t = t0 + lt + 32 * i;
+            const bool ok = t < T && n0 + ln8 < N;
+            vdy[i] = buf_load16(rdy, ok ? (uint32_t(t) * uint32_t(N) + uint32_t(n0 + ln8)) * 2u : kOutOfRange);
+        }
 #pragma unroll
         for (int i = 0; i < UV; ++i) {
             const int o = tid + kThreads * i;  // o = t * 16 RB + j
@@ -137,10 +145,12 @@ __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict
     };
     auto sstore = [&]() {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t w = vdy[e >> 1];
-            sm.dyt[ln8 + e][lt] = uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF));
-        }
+        for (int i = 0; i < DV; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t w = vdy[i][e >> 1];
+                sm.dyt[ln8 + e][lt + 32 * i] = uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF));
+            }
 #pragma unroll
         for (int i = 0; i < UV; ++i) {
             const int o = tid + kThreads * i;
@@ -156,18 +166,22 @@ __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict
     for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int kof = 8 * (lane >> 4);
     gload(0);
-    for (int t0 = 0; t0 < T; t0 += kTC) {
+    for (int t0 = 0; t0 < T; t0 += DBT) {
         __syncthreads();  // the previous sub-chunk's reads are done
         sstore();
         __syncthreads();
-        gload(t0 + kTC);  // past the end: zeros
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.dyt[16 * wave + (lane & 15)][kof]));
+        gload(t0 + DBT);  // past the end: zeros
 #pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            const bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.uh[16 * b + (lane & 15)][kof]));
-            const bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.ul[16 * b + (lane & 15)][kof]));
-            acc[b] = mfma16x16x32(a, bh, acc[b]);
-            acc[b] = mfma16x16x32(a, bl, acc[b]);
+        for (int kk = 0; kk < DBT / 32; ++kk) {  // tokens in increasing order
+            const bf16x8 a =
+                as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.dyt[16 * wave + (lane & 15)][32 * kk + kof]));
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.uh[16 * b + (lane & 15)][32 * kk + kof]));
+                const bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.ul[16 * b + (lane & 15)][32 * kk + kof]));
+                acc[b] = mfma16x16x32(a, bh, acc[b]);
+                acc[b] = mfma16x16x32(a, bl, acc[b]);
+            }
         }
     }
 #pragma unroll
@@ -179,10 +193,10 @@ __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict
         }
 }
 
-template <int RB>
+template <int RB, int DBT>
 union PreSmem {
     GSmem<RB> g;
-    DbSmem<RB> d;
+    DbSmem<RB, DBT> d;
 };
 
 }  // namespace pre

@@ -88,11 +88,11 @@ __global__ __launch_bounds__(kThreads) void k_lora_bwd_pre(const uint16_t* __res
                                                            const float* __restrict__ u, int T, int N, int r, float s,
                                                            int gsteps, int gblocks, float* __restrict__ gpart,
                                                            float* __restrict__ dB) {
-    __shared__ __align__(16) PreSmem<RB> sm;
+    __shared__ __align__(16) PreSmem<RB, pre::kDbTLong> sm;
     if (int(blockIdx.x) < gblocks)
         g_role<RB>(dy, B, T, N, r, gsteps, blockIdx.x, gpart, sm.g);
     else
-        db_role<RB>(dy, u, T, N, r, s, int(blockIdx.x) - gblocks, dB, sm.d);
+        db_role<RB, pre::kDbTLong>(dy, u, T, N, r, s, int(blockIdx.x) - gblocks, dB, sm.d);
 }
 
 template <int RB>

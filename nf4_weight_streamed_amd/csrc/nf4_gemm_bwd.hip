@@ -250,26 +250,35 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
             const int c = tid + kThreads * i, t = c / (BK / 8), k8 = 8 * (c % (BK / 8));
             xv[i] = buf_load16(rx, (uint32_t(t) * uint32_t(K) + uint32_t(k0 + k8)) * 2u);
         }
+        constexpr int GR = 8;  // partials loaded per round
         for (int jb = 0; jb < rp / 16; ++jb) {
-            f32x4 pv[GI][kMaxGParts];
+            f32x4 gsum[GI];
 #pragma unroll
-            for (int i = 0; i < GI; ++i) {
-                const int o = tid + kThreads * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
-                const bool ok = m0 + t < T && j < r;
-                const uint32_t off = (uint32_t(m0 + t) * uint32_t(r) + uint32_t(j)) * 4u;
+            for (int i = 0; i < GI; ++i) gsum[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int p0 = 0; p0 < lora.parts; p0 += GR) {  // partials in partial order
+                f32x4 pv[GI][GR];
 #pragma unroll
-                for (int pp = 0; pp < kMaxGParts; ++pp)
-                    pv[i][pp] = __builtin_bit_cast(
-                        f32x4, buf_load16(rgp, ok && pp < lora.parts ? off + uint32_t(pp) * uint32_t(T) * uint32_t(r) * 4u
-                                                                     : kOutOfRange));
+                for (int i = 0; i < GI; ++i) {
+                    const int o = tid + kThreads * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
+                    const bool ok = m0 + t < T && j < r;
+                    const uint32_t off = (uint32_t(m0 + t) * uint32_t(r) + uint32_t(j)) * 4u;
+#pragma unroll
+                    for (int pp = 0; pp < GR; ++pp)
+                        pv[i][pp] = __builtin_bit_cast(
+                            f32x4, buf_load16(rgp, ok && p0 + pp < lora.parts
+                                                       ? off + uint32_t(p0 + pp) * uint32_t(T) * uint32_t(r) * 4u
+                                                       : kOutOfRange));
+                }
+#pragma unroll
+                for (int i = 0; i < GI; ++i)
+#pragma unroll
+                    for (int pp = 0; pp < GR; ++pp)
+                        if (p0 + pp < lora.parts) gsum[i] += pv[i][pp];
             }
 #pragma unroll
             for (int i = 0; i < GI; ++i) {
                 const int o = tid + kThreads * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
-                f32x4 v = pv[i][0];
-#pragma unroll
-                for (int pp = 1; pp < kMaxGParts; ++pp)
-                    if (pp < lora.parts) v += pv[i][pp];
+                const f32x4 v = gsum[i];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     __bf16 hh, ll;

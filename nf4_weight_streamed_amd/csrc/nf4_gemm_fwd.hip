@@ -32,6 +32,9 @@ namespace {
 constexpr int kBK = 64;        // K per main-loop step (= one NF4 block)
 constexpr int kLds = kBK + 8;  // LDS row pitch in bf16 (144 B: conflict-free 16 B fragment reads)
 constexpr int kFwdWaves = 4;   // waves per workgroup (each 128 tokens x 128 / kFwdWaves features)
+constexpr int kFwdXAhead = 1;  // K steps x is loaded ahead of its use (register sets)
+constexpr int kFwdWAhead = 2;  // K steps the weights are loaded ahead of their dequantisation
+constexpr int kFwdOccupancy = 3;  // waves per SIMD the register budget must allow (3 tiles per CU)
 
 // ------------------------------------------------------------------------------------
 // NW waves split the BN = 128 output features (128 / NW each, FN = 4 / NW fragments of
@@ -56,7 +59,7 @@ struct FwdLora {
 };
 
 template <int NW, bool kDense>
-__global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
+__global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
     const uint16_t* __restrict__ x, const void* __restrict__ weights, const float* __restrict__ absmax, int T,
     int N, int K, int steps_per_split, FwdLora lora, uint16_t* __restrict__ y, float* __restrict__ partial,
     Tables tab) {
@@ -112,12 +115,17 @@ __global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
     }
 
     constexpr int WP = kDense ? 4 : 1;  // 16-byte weight pieces per lane, fragment and K step
-    u32x4 ra[A_CHUNKS];
-    u32x4 rc[2][FN][WP];
-    float rs[2][FN];
-    auto gload_x = [&](int kb) {
+    // register rings: x of a step is loaded PX steps ahead (PX sets), the weights PW steps
+    // ahead (PW sets); one tile alone on a CU is bound by these loads' latency
+    constexpr int PX = kDense ? 1 : kFwdXAhead, PW = kDense ? 2 : kFwdWAhead;  // dense: 4x the weight registers
+    constexpr int U = (PX > PW ? PX : PW) > 2 ? 4 : 2;  // loop unroll: a multiple of 2, PX and PW
+    static_assert(U % PX == 0 && U % PW == 0, "ring sizes must divide the unroll");
+    u32x4 ra[PX][A_CHUNKS];
+    u32x4 rc[PW][FN][WP];
+    float rs[PW][FN];
+    auto gload_x = [&](int kb, u32x4 (&xa)[A_CHUNKS]) {
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) ra[i] = buf_load16(rx, x_off[i] + uint32_t(kb) * (kBK * 2));
+        for (int i = 0; i < A_CHUNKS; ++i) xa[i] = buf_load16(rx, x_off[i] + uint32_t(kb) * (kBK * 2));
     };
     auto gload_w = [&](int kb, u32x4 (&cw)[FN][WP], float (&sc)[FN]) {
 #pragma unroll
@@ -127,34 +135,37 @@ __global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
             if constexpr (!kDense) sc[j] = buf_load_f32(rsc, s_off[j] + uint32_t(kb) * 4u);
         }
     };
-    auto store_x = [&](int buf) {
+    auto store_x = [&](const u32x4 (&xa)[A_CHUNKS], int buf) {
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
             const int c = tid + NT * i;
-            *reinterpret_cast<u32x4*>(&sA[buf][(c >> 3) * kLds + (c & 7) * 8]) = ra[i];
+            *reinterpret_cast<u32x4*>(&sA[buf][(c >> 3) * kLds + (c & 7) * 8]) = xa[i];
         }
     };
     const char* lut = reinterpret_cast<const char*>(sLut);
     bf16x8 wf[FN][4];
+    // weight fragments of sub-step q (all FN fragments) from a register set
+    auto dequant_q = [&](const u32x4 (&cw)[FN][WP], const float (&sc)[FN], int q) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            if constexpr (kDense) {
+                wf[j][q] = as_bf16x8(cw[j][q]);
+                continue;
+            }
+            const uint32_t w = cw[j][0][q];
+            u32x4 o;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float2 lv = *reinterpret_cast<const float2*>(lut + (((w >> (8 * b)) & 0xFFu) << 3));
+                // level * absmax in fp32, then RNbf: the format's two roundings
+                o[b] = pack_bf16x2(lv.x * sc[j], lv.y * sc[j]);
+            }
+            wf[j][q] = as_bf16x8(o);
+        }
+    };
     auto dequant = [&](const u32x4 (&cw)[FN][WP], const float (&sc)[FN]) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if constexpr (kDense) {
-                    wf[j][q] = as_bf16x8(cw[j][q]);
-                    continue;
-                }
-                const uint32_t w = cw[j][0][q];
-                u32x4 o;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const float2 lv = *reinterpret_cast<const float2*>(lut + (((w >> (8 * b)) & 0xFFu) << 3));
-                    // level * absmax in fp32, then RNbf: the format's two roundings
-                    o[b] = pack_bf16x2(lv.x * sc[j], lv.y * sc[j]);
-                }
-                wf[j][q] = as_bf16x8(o);
-            }
+        for (int q = 0; q < 4; ++q) dequant_q(cw, sc, q);
     };
 
     f32x16 acc[FM][FN];
@@ -166,26 +177,27 @@ __global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     if (kb_begin < kb_end) {
-        gload_x(kb_begin);
-        gload_w(kb_begin, rc[0], rs[0]);
-        gload_w(kb_begin + 1, rc[1], rs[1]);
-        store_x(0);
+#pragma unroll
+        for (int i = 0; i < PX; ++i) gload_x(kb_begin + i, ra[i]);
+#pragma unroll
+        for (int i = 0; i < PW; ++i) gload_w(kb_begin + i, rc[i], rs[i]);
+        store_x(ra[0], 0);
         __syncthreads();  // sLut and x tile 0 visible
         dequant(rc[0], rs[0]);
-        // one K step; C is the compile-time register/LDS buffer of step kb (the loop is
-        // unrolled by two so that no register array is indexed at run time)
-        // Loads are issued unconditionally (a step past the end reads data that is never
-        // used, or zeros beyond the buffer): with a fixed issue pattern the compiler's
-        // wait counts stay exact and never drain the next step's loads.
+        // one K step; C = (kb - kb_begin) mod U at compile time (the loop is unrolled by U
+        // so that no register array is indexed at run time): LDS buffer C mod 2, x set
+        // C mod PX, weight set C mod PW. Loads are issued unconditionally (a step past the
+        // end reads data that is never used, or zeros beyond the buffer): with a fixed
+        // issue pattern the compiler's wait counts stay exact and never drain later loads.
         auto step = [&](int kb, auto c_) {
             constexpr int C = decltype(c_)::value;
             const bool more = kb + 1 < kb_end;
-            gload_x(kb + 1);                // ra was stored last step
-            gload_w(kb + 2, rc[C], rs[C]);  // step kb's codes are already in wf
+            gload_x(kb + PX, ra[C % PX]);               // that set was stored into LDS last step
+            gload_w(kb + PW, rc[C % PW], rs[C % PW]);   // that set is this step's, already dequantised
             // keep the loads here, ahead of the MFMAs: sinking them next to their use
             // would expose their full latency
             __builtin_amdgcn_sched_barrier(0);
-            const uint16_t* a_base = &sA[C][0];
+            const uint16_t* a_base = &sA[C & 1][0];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -197,17 +209,29 @@ __global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
                 }
             }
             if (more) {
-                dequant(rc[C ^ 1], rs[C ^ 1]);  // next step's weights, independent of the MFMAs
-                store_x(C ^ 1);
+                dequant(rc[(C + 1) % PW], rs[(C + 1) % PW]);  // next step's weights, independent of the MFMAs
+                store_x(ra[(C + 1) % PX], (C + 1) & 1);
             }
             __syncthreads();
         };
         int kb = kb_begin;
-        for (; kb + 1 < kb_end; kb += 2) {
-            step(kb, std::integral_constant<int, 0>{});
-            step(kb + 1, std::integral_constant<int, 1>{});
+        if constexpr (U == 4) {
+            for (; kb + 3 < kb_end; kb += 4) {
+                step(kb, std::integral_constant<int, 0>{});
+                step(kb + 1, std::integral_constant<int, 1>{});
+                step(kb + 2, std::integral_constant<int, 2>{});
+                step(kb + 3, std::integral_constant<int, 3>{});
+            }
+            if (kb < kb_end) step(kb, std::integral_constant<int, 0>{});
+            if (kb + 1 < kb_end) step(kb + 1, std::integral_constant<int, 1>{});
+            if (kb + 2 < kb_end) step(kb + 2, std::integral_constant<int, 2>{});
+        } else {
+            for (; kb + 1 < kb_end; kb += 2) {
+                step(kb, std::integral_constant<int, 0>{});
+                step(kb + 1, std::integral_constant<int, 1>{});
+            }
+            if (kb < kb_end) step(kb, std::integral_constant<int, 0>{});
         }
-        if (kb < kb_end) step(kb, std::integral_constant<int, 0>{});
     }
 
     // LoRA as a K-extension (split 0 only when split): acc += (s.u)_hi . B^T + (s.u)_lo . B^T.
@@ -248,26 +272,35 @@ __global__ __launch_bounds__(64 * NW, 2) void k_nf4_gemm_fwd(
         load_b(0, bv);
         // s.u staged as bf16 hi/lo [t][j]: items of 4 ranks, every load issued first
         constexpr int UI = BM * 4 / NT;  // (t, 4-rank group) items per thread per 16 ranks
+        constexpr int UR = 4;  // partials loaded per round
         for (int jb = 0; jb < rp / 16; ++jb) {
-            f32x4 pv[UI][kMaxDownParts];
+            f32x4 usum[UI];
 #pragma unroll
-            for (int i = 0; i < UI; ++i) {
-                const int o = tid + NT * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
-                const bool ok = m0 + t < T && j < r;
-                const uint32_t off = (uint32_t(m0 + t) * uint32_t(r) + uint32_t(j)) * 4u;
+            for (int i = 0; i < UI; ++i) usum[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int p0 = 0; p0 < lora.parts; p0 += UR) {  // partials in partial order
+                f32x4 pv[UI][UR];
 #pragma unroll
-                for (int pp = 0; pp < kMaxDownParts; ++pp)
-                    pv[i][pp] = __builtin_bit_cast(
-                        f32x4, buf_load16(rup, ok && pp < lora.parts ? off + uint32_t(pp) * uint32_t(T) * uint32_t(r) * 4u
-                                                                     : kOutOfRange));
+                for (int i = 0; i < UI; ++i) {
+                    const int o = tid + NT * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
+                    const bool ok = m0 + t < T && j < r;
+                    const uint32_t off = (uint32_t(m0 + t) * uint32_t(r) + uint32_t(j)) * 4u;
+#pragma unroll
+                    for (int pp = 0; pp < UR; ++pp)
+                        pv[i][pp] = __builtin_bit_cast(
+                            f32x4, buf_load16(rup, ok && p0 + pp < lora.parts
+                                                       ? off + uint32_t(p0 + pp) * uint32_t(T) * uint32_t(r) * 4u
+                                                       : kOutOfRange));
+                }
+#pragma unroll
+                for (int i = 0; i < UI; ++i)
+#pragma unroll
+                    for (int pp = 0; pp < UR; ++pp)
+                        if (p0 + pp < lora.parts) usum[i] += pv[i][pp];
             }
 #pragma unroll
             for (int i = 0; i < UI; ++i) {
                 const int o = tid + NT * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
-                f32x4 v = pv[i][0];
-#pragma unroll
-                for (int pp = 1; pp < kMaxDownParts; ++pp)
-                    if (pp < lora.parts) v += pv[i][pp];
+                const f32x4 v = usum[i];
                 uint16_t hb[4], lb[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {

@@ -561,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_skinny_bwd(
     float* __restrict__ gpart, float* __restrict__ dB, Tables tab) {
     __shared__ __align__(16) union {
         BwdSmem dx;
-        pre::PreSmem<RB> pre;
+        pre::PreSmem<RB, pre::kTC> pre;
     } sm;
     if (int(blockIdx.x) < dx_cols) {
         skinny_bwd_dx(dy, codes, absmax, T, N, K, steps_per_split, dxpart, tab, sm.dx);
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_skinny_bwd(
     if (blk < gblocks)
         pre::g_role<RB>(dy, B, T, N, r, gsteps, blk, gpart, sm.pre.g);
     else if (blk < gblocks + dblocks)
-        pre::db_role<RB>(dy, u, T, N, r, s, blk - gblocks, dB, sm.pre.d);
+        pre::db_role<RB, pre::kTC>(dy, u, T, N, r, s, blk - gblocks, dB, sm.pre.d);
 }
 
 // Backward finish, two kinds of workgroups in one launch (64 features each, lane =
