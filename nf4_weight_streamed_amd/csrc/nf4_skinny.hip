@@ -35,16 +35,19 @@ constexpr int kXP = kDK + 8;  // LDS pitch of the x tile (bf16)
 // one K range of 256-wide steps. Within a step the contraction order is permuted
 // identically for both operands: lane quarter q (lane / 16) supplies k = 64q + 8c ..
 // 64q + 8c + 7 at MFMA chunk c (0..7), so a lane's 32 bytes of codes per row block are
-// one whole NF4 block (one scale). Codes, scales and x are loaded two steps ahead into a
-// ring of three register sets (about 32 KB of codes in flight per workgroup: the kernel
-// is bound by memory latency x bytes in flight); the x tile of the current step is in
-// double-buffered LDS. Output: fp32 partials ypart[split][T][N].
+// one whole NF4 block (one scale). Codes, scales and x are loaded kFRing - 1 steps ahead
+// into a ring of kFRing register sets (two, measured: the fewer registers let four
+// workgroups share a CU, which keeps more bytes in flight than a deeper ring would); the
+// x tile of the current step is in double-buffered LDS. Output: fp32 partials
+// ypart[split][T][N].
 //
 // u workgroups (blockIdx.x >= row_blocks, kUParts per split): the rows of A (bf16, wave
 // w: ranks 16w .. 16w+15) against the same x for u = x.A^T, each over a quarter of the
 // split's steps with plain loads (few registers, so the weight workgroups keep their
 // occupancy) -> upart[split * kUParts + part][T][r].
 constexpr int kUParts = 4;
+constexpr int kFRing = 2;       // forward weight workgroups: register sets (loads kFRing - 1 steps ahead)
+static_assert(kFRing == 2 || kFRing == 3, "ring of two or three register sets");
 
 template <int TB>
 __device__ __forceinline__ void skinny_fwd_weights(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
@@ -76,7 +79,8 @@ __device__ __forceinline__ void skinny_fwd_weights(const uint16_t* __restrict__ 
         float sc[2];
         u32x4 xv[XCH];
     };
-    Set ring[3];
+    constexpr int R = kFRing;
+    Set ring[R];
     auto gload = [&](int kb, Set& st) {
         const uint32_t k0 = uint32_t(kb) * kDK;
 #pragma unroll
@@ -125,15 +129,15 @@ __device__ __forceinline__ void skinny_fwd_weights(const uint16_t* __restrict__ 
         for (int nb = 0; nb < 2; ++nb) acc[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (kb_begin < kb_end) {
-        gload(kb_begin, ring[0]);
-        gload(kb_begin + 1, ring[1]);
+#pragma unroll
+        for (int c = 0; c < R - 1; ++c) gload(kb_begin + c, ring[c]);
         store_x(ring[0], 0);
         __syncthreads();  // sLut and x tile 0
-        // one step on ring slot C (compile-time: the loop is unrolled by three)
+        // one step on ring slot C (compile-time: the loop is unrolled by R)
         auto step = [&](int kb, auto c_) {
             constexpr int C = decltype(c_)::value;
             const int buf = (kb - kb_begin) & 1;
-            gload(kb + 2, ring[(C + 2) % 3]);  // two steps ahead; past the range: unused or zeros
+            gload(kb + R - 1, ring[(C + R - 1) % R]);  // R - 1 steps ahead; past the range: unused or zeros
             __builtin_amdgcn_sched_barrier(0);
             const Set& cur = ring[C];
 #pragma unroll
@@ -159,17 +163,25 @@ __device__ __forceinline__ void skinny_fwd_weights(const uint16_t* __restrict__ 
                     for (int nb = 0; nb < 2; ++nb) acc[tb][nb] = mfma16x16x32(xa, bw[nb], acc[tb][nb]);
                 }
             }
-            store_x(ring[(C + 1) % 3], buf ^ 1);  // the next step's x (loaded a step ago)
+            store_x(ring[(C + 1) % R], buf ^ 1);  // the next step's x (loaded earlier)
             __syncthreads();
         };
         int kb = kb_begin;
-        for (; kb + 2 < kb_end; kb += 3) {
-            step(kb, std::integral_constant<int, 0>{});
-            step(kb + 1, std::integral_constant<int, 1>{});
-            step(kb + 2, std::integral_constant<int, 2>{});
+        if constexpr (R == 3) {
+            for (; kb + 2 < kb_end; kb += 3) {
+                step(kb, std::integral_constant<int, 0>{});
+                step(kb + 1, std::integral_constant<int, 1>{});
+                step(kb + 2, std::integral_constant<int, 2>{});
+            }
+            if (kb < kb_end) step(kb, std::integral_constant<int, 0>{});
+            if (kb + 1 < kb_end) step(kb + 1, std::integral_constant<int, 1>{});
+        } else {
+            for (; kb + 1 < kb_end; kb += 2) {
+                step(kb, std::integral_constant<int, 0>{});
+                step(kb + 1, std::integral_constant<int, 1>{});
+            }
+            if (kb < kb_end) step(kb, std::integral_constant<int, 0>{});
         }
-        if (kb < kb_end) step(kb, std::integral_constant<int, 0>{});
-        if (kb + 1 < kb_end) step(kb + 1, std::integral_constant<int, 1>{});
     }
 
     // lane holds D[t = 16 tb + 4 q + e][row = 16 nb + l16]
@@ -414,11 +426,15 @@ __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __r
 // so its output column l16 is feature 16 l16 + j. The four waves take interleaved
 // steps of the workgroup's range and add their sums through LDS in a fixed order.
 // Scales: two dwords per lane and step ([row][block] in memory), exchanged through the
-// wave's own LDS slice as [block][row]. Codes, scales and dY are loaded two steps ahead
-// into a ring of three register sets. T <= 16 (one 16-token MFMA block).
+// wave's own LDS slice as [block][row]. Codes, scales and dY are loaded kBRing - 1 steps
+// ahead into a ring of kBRing register sets (two, measured: three workgroups per CU then
+// fit in the registers). T <= 16 (one 16-token MFMA block).
 // Output: fp32 partials dxpart[split][T][K].
 constexpr int kBCols = 256;  // features per workgroup
 constexpr int kBRows = 32;   // weight rows per wave step
+constexpr int kBRing = 2;    // register sets: loads run kBRing - 1 steps ahead
+constexpr int kBOccupancy = 3;  // waves per SIMD the register budget must allow
+static_assert(kBRing == 2 || kBRing == 3, "ring of two or three register sets");
 
 struct BwdSmem {
     float lut[512];
@@ -457,9 +473,10 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
         float sc[2];  // scales: row 16h + lane / 4, block lane % 4
         u32x4 dv;     // dY[t = l16][8q .. 8q + 7]
     };
-    Set ring[3];
+    constexpr int R = kBRing;
+    Set ring[R];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) ring[c].dv = u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < R; ++c) ring[c].dv = u32x4{0u, 0u, 0u, 0u};
     auto gload = [&](int i, Set& st) {
         const uint32_t n0 = uint32_t(s_begin + wave + 4 * i) * kBRows;
 #pragma unroll
@@ -478,12 +495,12 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
     __syncthreads();  // sLut
 
     if (nw > 0) {
-        gload(0, ring[0]);
-        gload(1, ring[1]);
-        // one step on ring slot C (compile-time: the loop is unrolled by three)
+#pragma unroll
+        for (int c = 0; c < R - 1; ++c) gload(c, ring[c]);
+        // one step on ring slot C (compile-time: the loop is unrolled by R)
         auto step = [&](int i, auto c_) {
             constexpr int C = decltype(c_)::value;
-            gload(i + 2, ring[(C + 2) % 3]);  // two steps ahead; past the range: unused or zeros
+            gload(i + R - 1, ring[(C + R - 1) % R]);  // R - 1 steps ahead; past the range: unused or zeros
             __builtin_amdgcn_sched_barrier(0);
             const Set& cur = ring[C];
             // the wave's LDS slice: written and read by this wave only, in program order
@@ -514,13 +531,21 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
             }
         };
         int i = 0;
-        for (; i + 2 < nw; i += 3) {
-            step(i, std::integral_constant<int, 0>{});
-            step(i + 1, std::integral_constant<int, 1>{});
-            step(i + 2, std::integral_constant<int, 2>{});
+        if constexpr (R == 3) {
+            for (; i + 2 < nw; i += 3) {
+                step(i, std::integral_constant<int, 0>{});
+                step(i + 1, std::integral_constant<int, 1>{});
+                step(i + 2, std::integral_constant<int, 2>{});
+            }
+            if (i < nw) step(i, std::integral_constant<int, 0>{});
+            if (i + 1 < nw) step(i + 1, std::integral_constant<int, 1>{});
+        } else {
+            for (; i + 1 < nw; i += 2) {
+                step(i, std::integral_constant<int, 0>{});
+                step(i + 1, std::integral_constant<int, 1>{});
+            }
+            if (i < nw) step(i, std::integral_constant<int, 0>{});
         }
-        if (i < nw) step(i, std::integral_constant<int, 0>{});
-        if (i + 1 < nw) step(i + 1, std::integral_constant<int, 1>{});
     }
 
     // lane holds D[t = 4q + e][feature 16 l16 + j] in acc[j][e]; sum (w0 + w2) + (w1 + w3)
@@ -554,7 +579,7 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
 // [gblocks, gblocks + dblocks), the remainder exit. The roles share no data inside the
 // launch (g is summed by the finish kernel, dB is final).
 template <int RB>
-__global__ __launch_bounds__(kThreads, 2) void k_skinny_bwd(
+__global__ __launch_bounds__(kThreads, kBOccupancy) void k_skinny_bwd(
     const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
     const uint16_t* __restrict__ B, const float* __restrict__ u, int T, int N, int K, int r, float s,
     int steps_per_split, int dx_cols, int pre_cols, int gsteps, int gblocks, int dblocks, float* __restrict__ dxpart,
@@ -653,7 +678,7 @@ constexpr int64_t kFillWGs = 256;
 constexpr int64_t kFwdWGs = 512;
 constexpr int64_t kFwdMinSteps = 4;
 constexpr int64_t kFwdPartialDiv = 2;
-constexpr int64_t kBwdWGs = 512;
+constexpr int64_t kBwdWGs = 768;
 constexpr int64_t kBwdMinSteps = 4;  // one per wave
 constexpr int64_t kBwdPartialDiv = 1;
 
