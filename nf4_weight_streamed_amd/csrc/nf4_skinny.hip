@@ -1,18 +1,19 @@
-// NF4-LoRA linear for few tokens (the plans route T <= 16 here; the forward kernels
-// accept T <= 64, the backward ones T <= 16): the same operations as the 128-token GEMMs, organised for the HBM-bound
-// regime, where every weight byte should be read once and streamed at full rate while
-// MFMA work is cheap.
+// NF4-LoRA linear for few tokens (T <= 16, one 16-token MFMA block): the same operations
+// as the 128-token GEMMs, organised for the HBM-bound regime, where every weight byte
+// should be read once and streamed at full rate while MFMA work is cheap.
 //
 //   forward:  y  = RNbf( x . W^T + s . u . B^T ),  u = x . A^T (saved)
 //   backward: dX = RNbf( dY . W + s . g . A ),     dA = s . g^T . x
-//             (g and dB from k_lora_bwd_pre)
+//             (g and dB from the pre-pass roles of lora_pre.h, run as extra
+//             workgroups of the backward launch)
 //
 // The frozen NF4 base is only read (HN comment thread on streaming the frozen base,
 // main comment); LoRA rank r and alpha as in the Poros API reference
-// ("PorosTrainer.from_pretrained"). Tokens are padded to TB blocks of 16 for
-// v_mfma_f32_16x16x32_bf16; both GEMM kernels split their contraction over the grid's
-// y dimension and write fp32 partials, which the finish kernels add in split order,
-// together with the LoRA terms, and round once.
+// ("PorosTrainer.from_pretrained"). Tokens are padded to one block of 16 for
+// v_mfma_f32_16x16x32_bf16 (the forward's TB template counts such blocks; only TB = 1
+// is launched); both GEMM kernels split their contraction over the grid's y dimension
+// and write fp32 partials, which the finish kernels add in split order, together with
+// the LoRA terms, and round once.
 #include <type_traits>
 
 #include "common.h"
@@ -728,13 +729,9 @@ hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const fl
     char* w = static_cast<char*>(ws);
     float* ypart = reinterpret_cast<float*>(w + p.off_part);
     float* upart = reinterpret_cast<float*>(w + p.off_upart);
+    if (T > kSkinnyMaxT) return hipErrorInvalidValue;  // one 16-token MFMA block
     prof_gemm_begin(stream);
-    switch ((T + 15) / 16) {
-        case 1: launch_fwd_tb<1>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream); break;
-        case 2: launch_fwd_tb<2>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream); break;
-        case 3: launch_fwd_tb<3>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream); break;
-        default: launch_fwd_tb<4>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream); break;
-    }
+    launch_fwd_tb<1>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream);
     prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
