@@ -70,12 +70,16 @@ struct FwdPlan {
 FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r, bool dense = false);  // dense: bf16 base, 128-token kernels only
 void plan_lora_down(FwdPlan& p, int64_t K);
 
-// Backward plan. Workspace: [g partials | dA shares per token tile | split-K
-// partials of dX].
+// Backward plan. Workspace: [g partials | dA shares per token tile | fp32 partial
+// tiles of the split dX tiles].
+// dX tiles (token tile fastest) 0 .. full-1 run whole; the last `tail` tiles are
+// split over the contraction (N) into `pieces` ranges of steps_per_piece steps, one
+// workgroup each, so that the workgroups of the last round fill the chip; with few
+// tiles every tile is split (full = 0).
 struct BwdPlan {
     int bm, bn;            // dX tile (tokens x in features)
-    int splits;            // N (contraction) splits for dX
-    int steps_per_split;
+    int full, tail;        // whole tiles, split tiles
+    int pieces, steps_per_piece;
     int mtiles, ktiles;    // dX tile grid
     int gparts, gsteps;    // N ranges of g = dY.B (partials summed by the GEMM), 128-feature chunks each
     size_t off_gpart, off_dapart, off_dx;  // workspace offsets (bytes)

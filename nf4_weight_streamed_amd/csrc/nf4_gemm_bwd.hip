@@ -26,6 +26,7 @@ namespace {
 constexpr int kBN = 64;        // contraction (N) per main-loop step
 constexpr int kLds = kBN + 8;  // LDS pitch in bf16
 constexpr int kThreads = 256;
+constexpr int64_t kBwdSlots = 512;  // resident workgroups: two per CU (LDS), 256 CUs
 
 // Workgroup tile: 128 tokens x 128 input features, 4 waves in a 2x2 grid (64 x 64
 // each, 32x32x16 MFMA), contraction steps of 64 over N. Per step each thread loads
@@ -35,6 +36,16 @@ constexpr int kThreads = 256;
 // 256-entry (level[lo], level[hi]) pair table per code byte, fp32 multiply by the
 // row's absmax, bf16 pack pairing rows - and stores the patch transposed into the
 // other LDS buffer. dY and the weight tile are double-buffered: one barrier per step.
+// Which tile (and contraction range) each workgroup of the 1-D grid takes: ids
+// 0 .. full-1 are whole tiles, the rest pieces of the last `tail` tiles, piece z of
+// tile full + q at id full + z * tail + q. Both ranges are laid over the XCDs
+// separately (full is a multiple of the XCD count), so every XCD gets the same share
+// of whole tiles and of pieces.
+struct BwdTiles {
+    int full, tail, pieces, steps_per_piece;
+    int mtiles;  // token tiles (tile index = token tile + mtiles * column tile)
+};
+
 struct BwdLora {
     const float* gpart;  // [parts][T][r] partials of g = dY.B
     int parts;
@@ -48,8 +59,7 @@ struct BwdLora {
 template <bool kDense>
 __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     const uint16_t* __restrict__ dy, const void* __restrict__ weights, const float* __restrict__ absmax, int T,
-    int N, int K, int steps_per_split, BwdLora lora, uint16_t* __restrict__ dx, float* __restrict__ partial,
-    Tables tab) {
+    int N, int K, BwdTiles tl, BwdLora lora, uint16_t* __restrict__ dx, float* __restrict__ partial, Tables tab) {
     constexpr int BM = 128, BK = 128;
     constexpr int WM = BM / 2, WK = BK / 2;
     constexpr int FM = WM / 32, FK = WK / 32;
@@ -63,17 +73,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wk = wave & 1;
-    // tile order: token tile fastest, then column tile, then split; per-XCD ranges,
-    // so the token tiles sharing one weight slice run together in one L2
-    const uint32_t tile = xcd_tile_order(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
-                                         gridDim.x * gridDim.y * gridDim.z);
-    const int tm = int(tile % gridDim.y), tc = int((tile / gridDim.y) % gridDim.x);
-    const int tz = int(tile / (gridDim.y * gridDim.x));
+    // tile order: token tile fastest, then column tile (then piece); per-XCD ranges, so
+    // the token tiles sharing one weight slice run together in one L2. Without dX
+    // (dx == NULL) only the LoRA part runs: no contraction steps.
+    const int nsteps = dx ? (N + kBN - 1) / kBN : 0;
+    int tile, tz = 0, nb_begin = 0, nb_end = nsteps;
+    float* ptile = nullptr;  // fp32 partial tile of a split tile
+    if (int(blockIdx.x) < tl.full) {
+        tile = int(xcd_tile_order(blockIdx.x, uint32_t(tl.full)));
+    } else {
+        const int u = int(xcd_tile_order(blockIdx.x - uint32_t(tl.full), uint32_t(tl.tail * tl.pieces)));
+        const int q = u % tl.tail;
+        tz = u / tl.tail;
+        tile = tl.full + q;
+        nb_begin = tz * tl.steps_per_piece;
+        nb_end = min(nb_begin + tl.steps_per_piece, nsteps);
+        ptile = partial + (size_t(tz) * tl.tail + q) * (BM * BK);
+    }
+    const int tm = tile % tl.mtiles, tc = tile / tl.mtiles;
     const int k0 = tc * BK;
     const int m0 = tm * BM;
-    const int nsteps = (N + kBN - 1) / kBN;
-    const int nb_begin = tz * steps_per_split;
-    const int nb_end = min(nb_begin + steps_per_split, nsteps);
     const int frag_row = lane & 31;
     const int frag_k = (lane >> 5) * 8;
     sLut[2 * tid] = tab.level[tid & 15];  // entry b: the two codes of byte b
@@ -353,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     }
 
     if (!dx) return;
-    if (!partial) {
+    if (!ptile) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -367,34 +386,45 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
         return;
     }
 
-    // split N: this split's fp32 tile; k_bwd_finish adds the splits in order
-    float* pdst = partial + size_t(tz) * T * K;
+    // a piece of a split tile: the whole fp32 tile [BM][BK] (rows past T and columns
+    // past K included; never read back); k_bwd_finish adds the pieces in order
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FK; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int col = k0 + wk * WK + 32 * j + (lane & 31);
-                if (row < T && col < K) pdst[size_t(row) * K + col] = acc[i][j][e];
+                const int row = wm * WM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int col = wk * WK + 32 * j + (lane & 31);
+                ptile[row * BK + col] = acc[i][j][e];
             }
 }
 
 // The backward's reductions, in one launch: blocks [0, dx_blocks) form
-// dX = RNbf(((p0 + p1) + p2) + ...) from the split partials; the rest form
-// dA = ((d0 + d1) + d2) + ... from the token tiles' shares. Four outputs per thread.
-__global__ __launch_bounds__(256) void k_bwd_finish(const float* __restrict__ dxpart, int splits, int64_t dx_total,
-                                                    uint16_t* __restrict__ dx, int64_t dx_blocks,
+// dX = RNbf(((p0 + p1) + p2) + ...) of the split tiles from their pieces' fp32 tiles;
+// the rest form dA = ((d0 + d1) + d2) + ... from the token tiles' shares. Four
+// outputs per thread.
+struct BwdFinishDx {
+    const float* part;  // [pieces][tail][BM * BK]
+    int full, tail, pieces, mtiles, bm, bk;
+    int T, K;
+};
+
+__global__ __launch_bounds__(256) void k_bwd_finish(BwdFinishDx f, uint16_t* __restrict__ dx, int64_t dx_blocks,
                                                     const float* __restrict__ dapart, int shares, int64_t da_total,
                                                     float* __restrict__ dA) {
     if (int64_t(blockIdx.x) < dx_blocks) {
+        const int64_t tile_elems = int64_t(f.bm) * f.bk, total = int64_t(f.tail) * tile_elems;
         const int64_t idx = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-        if (idx >= dx_total) return;
-        f32x4 a = *reinterpret_cast<const f32x4*>(dxpart + idx);
-        for (int z = 1; z < splits; ++z) a += *reinterpret_cast<const f32x4*>(dxpart + size_t(z) * dx_total + idx);
+        if (idx >= total) return;
+        const int q = int(idx / tile_elems), loc = int(idx % tile_elems);
+        const int tile = f.full + q;
+        const int row = (tile % f.mtiles) * f.bm + loc / f.bk, col = (tile / f.mtiles) * f.bk + loc % f.bk;
+        if (row >= f.T || col >= f.K) return;  // K % 64 == 0: the four columns are all in or all out
+        f32x4 a = *reinterpret_cast<const f32x4*>(f.part + idx);
+        for (int z = 1; z < f.pieces; ++z) a += *reinterpret_cast<const f32x4*>(f.part + z * total + idx);
         const u32x2 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-        *reinterpret_cast<u32x2*>(dx + idx) = o;
+        *reinterpret_cast<u32x2*>(dx + size_t(row) * f.K + col) = o;
     } else {
         const int64_t idx = ((int64_t(blockIdx.x) - dx_blocks) * 256 + threadIdx.x) * 4;
         if (idx >= da_total) return;
@@ -423,9 +453,26 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     p.ktiles = int(cdiv(K, p.bn));
     const int64_t tiles = int64_t(p.mtiles) * p.ktiles;
     const int64_t nsteps = cdiv(N, kBN);
+    // Under 256 tiles: every tile split (about 512 workgroups in all). Many: whole
+    // rounds of kSlots tiles (two workgroups per CU, set by LDS) run whole and a last,
+    // partial round of at most half the slots is split to fill them.
+    int64_t tail = 0, pieces = 1;
     const int64_t splits = pick_splits(tiles, nsteps, 4);
-    p.steps_per_split = int(cdiv(nsteps, splits));
-    p.splits = int(cdiv(nsteps, p.steps_per_split));
+    if (splits > 1) {
+        tail = tiles;
+        pieces = splits;
+    } else if (tiles > kBwdSlots) {
+        const int64_t last = tiles % kBwdSlots;
+        const int64_t pc = last > 0 ? std::min<int64_t>(kBwdSlots / last, nsteps / 4) : 1;
+        if (last > 0 && last <= kBwdSlots / 2 && pc >= 2) {
+            tail = last;
+            pieces = pc;
+        }
+    }
+    p.steps_per_piece = int(cdiv(nsteps, pieces));
+    p.pieces = tail > 0 ? int(cdiv(nsteps, p.steps_per_piece)) : 1;
+    p.tail = int(tail);
+    p.full = int(tiles - tail);  // 0 or a multiple of kBwdSlots (a multiple of the XCD count)
     if (r > 0) plan_lora_bwd_pre(p, N, kMaxGParts);
     size_t off = 0;
     p.off_gpart = off;
@@ -433,7 +480,7 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     p.off_dapart = off;
     off += r > 0 ? align256(size_t(p.mtiles) * size_t(r) * size_t(K) * 4) : 0;
     p.off_dx = off;
-    off += p.splits > 1 ? align256(size_t(p.splits) * size_t(T) * size_t(K) * 4) : 0;
+    off += p.tail > 0 ? align256(size_t(p.pieces) * size_t(p.tail) * size_t(p.bm) * size_t(p.bn) * 4) : 0;
     p.ws_bytes = off;
     return p;
 }
@@ -443,28 +490,30 @@ hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* 
                            int r, float s, uint16_t* dx, float* dA, void* ws, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
     // without dx only the LoRA part runs: one workgroup per tile, no contraction steps
-    const int splits = dx ? p.splits : 1;
-    const dim3 grid(unsigned(p.ktiles), unsigned(p.mtiles), unsigned(splits));
-    float* partial = splits > 1 ? reinterpret_cast<float*>(w + p.off_dx) : nullptr;
+    BwdTiles tl{p.full, p.tail, p.pieces, p.steps_per_piece, p.mtiles};
+    if (!dx) tl = BwdTiles{p.mtiles * p.ktiles, 0, 1, 0, p.mtiles};
+    const dim3 grid(unsigned(tl.full + tl.tail * tl.pieces));
+    float* partial = tl.tail > 0 ? reinterpret_cast<float*>(w + p.off_dx) : nullptr;
     float* dapart = reinterpret_cast<float*>(w + p.off_dapart);
     const BwdLora lora{reinterpret_cast<const float*>(w + p.off_gpart), p.gparts, A, x, dapart, r, s};
     if (dx) prof_gemm_begin(stream);
     if (wdense)
         hipLaunchKernelGGL(k_nf4_gemm_bwd_dx<true>, grid, dim3(kThreads), 0, stream, dy,
-                           static_cast<const void*>(wdense), nullptr, int(T), int(N), int(K),
-                           dx ? p.steps_per_split : 0, lora, dx, partial, tables());
+                           static_cast<const void*>(wdense), nullptr, int(T), int(N), int(K), tl, lora, dx, partial,
+                           tables());
     else
         hipLaunchKernelGGL(k_nf4_gemm_bwd_dx<false>, grid, dim3(kThreads), 0, stream, dy,
-                           static_cast<const void*>(codes), absmax, int(T), int(N), int(K),
-                           dx ? p.steps_per_split : 0, lora, dx, partial, tables());
+                           static_cast<const void*>(codes), absmax, int(T), int(N), int(K), tl, lora, dx, partial,
+                           tables());
     if (dx) prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t dx_total = splits > 1 ? T * K : 0, da_total = r > 0 ? int64_t(r) * K : 0;
+    const BwdFinishDx f{partial, tl.full, tl.tail, tl.pieces, p.mtiles, p.bm, p.bn, int(T), int(K)};
+    const int64_t dx_total = int64_t(tl.tail) * p.bm * p.bn, da_total = r > 0 ? int64_t(r) * K : 0;
     const int64_t dx_blocks = cdiv(dx_total / 4, 256), da_blocks = cdiv(da_total / 4, 256);
     if (dx_blocks + da_blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_bwd_finish, dim3(unsigned(dx_blocks + da_blocks)), dim3(256), 0, stream, partial, splits,
-                       dx_total, dx, dx_blocks, dapart, p.mtiles, da_total, dA);
+    hipLaunchKernelGGL(k_bwd_finish, dim3(unsigned(dx_blocks + da_blocks)), dim3(256), 0, stream, f, dx, dx_blocks,
+                       dapart, p.mtiles, da_total, dA);
     return hipGetLastError();
 }
 

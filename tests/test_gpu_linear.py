@@ -66,6 +66,9 @@ def test_single_linear_workload(gpu_lib):
     (513, 160, 192, 16),     # T one past a tile boundary
     (150, 208, 384, 5),      # odd rank: partial 4-rank groups, unaligned rows of u, g, B
     (129, 3584, 640, 12),    # rank 12: B rows not a 16-byte multiple; dX split over N
+    (300, 1104, 8192, 16),   # long K and N: both GEMMs split their contraction, ragged tiles
+    (40, 1040, 8256, 7),     # same with an odd step count over K and an odd rank
+    (300, 640, 22976, 16),   # 540 dX tiles: a whole round of 512, the last 28 (ragged) split over N
 ])
 def test_shapes(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
