@@ -55,11 +55,15 @@ SkinnyPlan plan_skinny_bwd(int64_t T, int64_t N, int64_t K);
 
 // Forward plan: how the kernels are split for a shape (a pure function of the shape,
 // so repeated calls - streamed or resident - launch identical grids). Workspace:
-// [u partials | split-K partials of y].
+// [u partials | fp32 partial tiles of the split y tiles].
+// y tiles (token tile fastest) 0 .. full-1 run whole; the last `tail` tiles are split
+// over K into `pieces` ranges of steps_per_piece 64-wide steps, one workgroup each
+// (all tiles when there are too few to fill the CUs, else the last partial round).
 struct FwdPlan {
     int bm, bn;           // GEMM workgroup tile (tokens x out features)
-    int splits;           // GEMM K splits (1: y written by the GEMM tile directly)
-    int steps_per_split;  // 64-wide K steps per split
+    int full, tail;       // whole tiles, split tiles
+    int pieces, steps_per_piece;
+    int mtiles;           // token tiles
     int down_parts;       // K ranges of u = x.A^T (partials summed by the GEMM); 0 if r == 0
     int down_steps;       // 32-wide K steps per range
     size_t off_upart, off_ypart;  // workspace offsets (bytes)

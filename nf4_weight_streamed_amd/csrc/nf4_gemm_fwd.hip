@@ -12,8 +12,9 @@
 //    kernel comment), while the x tile goes through double-buffered LDS;
 //  - LoRA: (s.u) is split into bf16 hi + lo and contracted with B on the same
 //    accumulators (a K-extension of r per part), so y is rounded once;
-//  - split-K (for shapes with too few tiles to fill 256 CUs): fp32 partials in the
-//    caller's workspace (split 0 carries the LoRA term), added in split order and
+//  - split-K, for shapes with too few tiles to fill 256 CUs (every tile) or with a
+//    last, partial round of tiles (those tiles only): fp32 partial tiles in the
+//    caller's workspace (piece 0 carries the LoRA term), added in piece order and
 //    rounded once by k_split_sum_bf16 (a kernel boundary, not in-kernel signalling:
 //    the per-XCD L2 caches are only made coherent by whole-cache maintenance).
 // The same kernel, with kDense, takes a dense bf16 base instead (the experimental
@@ -35,6 +36,7 @@ constexpr int kFwdWaves = 4;   // waves per workgroup (each 128 tokens x 128 / k
 constexpr int kFwdXAhead = 1;  // K steps x is loaded ahead of its use (register sets)
 constexpr int kFwdWAhead = 2;  // K steps the weights are loaded ahead of their dequantisation
 constexpr int kFwdOccupancy = 3;  // waves per SIMD the register budget must allow (3 tiles per CU)
+constexpr int64_t kCUs = 256;
 
 // ------------------------------------------------------------------------------------
 // NW waves split the BN = 128 output features (128 / NW each, FN = 4 / NW fragments of
@@ -58,11 +60,19 @@ struct FwdLora {
     float s;
 };
 
+// Which tile (and K range) each workgroup of the 1-D grid takes: ids 0 .. full-1 are
+// whole tiles, the rest pieces of the last `tail` tiles, piece z of tile full + q at
+// id full + z * tail + q. Both ranges are laid over the XCDs separately (full is 0
+// or a multiple of 256), so every XCD gets the same share of whole tiles and pieces.
+struct FwdTiles {
+    int full, tail, pieces, steps_per_piece;
+    int mtiles;  // token tiles (tile index = token tile + mtiles * column tile)
+};
+
 template <int NW, bool kDense>
 __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
     const uint16_t* __restrict__ x, const void* __restrict__ weights, const float* __restrict__ absmax, int T,
-    int N, int K, int steps_per_split, FwdLora lora, uint16_t* __restrict__ y, float* __restrict__ partial,
-    Tables tab) {
+    int N, int K, FwdTiles tl, FwdLora lora, uint16_t* __restrict__ y, float* __restrict__ partial, Tables tab) {
     constexpr int NT = 64 * NW;
     constexpr int BM = 128, BN = 128, FM = 4, FN = 4 / NW;
     constexpr int A_CHUNKS = BM * (kBK / 8) / NT;
@@ -73,17 +83,25 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    // tile order: token tile fastest, then column tile, then split; per-XCD ranges,
+    // tile order: token tile fastest, then column tile (then piece); per-XCD ranges,
     // so the token tiles sharing one weight slice run together in one L2
-    const uint32_t tile = xcd_tile_order(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
-                                         gridDim.x * gridDim.y * gridDim.z);
-    const int tm = int(tile % gridDim.y), tc = int((tile / gridDim.y) % gridDim.x);
-    const int tz = int(tile / (gridDim.y * gridDim.x));
+    const int ksteps = K / kBK;
+    int tile, tz = 0, kb_begin = 0, kb_end = ksteps;
+    float* ptile = nullptr;  // fp32 partial tile of a split tile
+    if (int(blockIdx.x) < tl.full) {
+        tile = int(xcd_tile_order(blockIdx.x, uint32_t(tl.full)));
+    } else {
+        const int u = int(xcd_tile_order(blockIdx.x - uint32_t(tl.full), uint32_t(tl.tail * tl.pieces)));
+        const int q = u % tl.tail;
+        tz = u / tl.tail;
+        tile = tl.full + q;
+        kb_begin = tz * tl.steps_per_piece;
+        kb_end = min(kb_begin + tl.steps_per_piece, ksteps);
+        ptile = partial + (size_t(tz) * tl.tail + q) * (BM * BN);
+    }
+    const int tm = tile % tl.mtiles, tc = tile / tl.mtiles;
     const int n0 = tc * BN;
     const int m0 = tm * BM;
-    const int ksteps = K / kBK;
-    const int kb_begin = tz * steps_per_split;
-    const int kb_end = min(kb_begin + steps_per_split, ksteps);
     const int frag_row = lane & 31;
     const int half = lane >> 5;
     for (int i = tid; i < 256; i += NT) {  // entry b: the two codes of byte b
@@ -336,7 +354,7 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
         }
     }
 
-    if (!partial) {
+    if (!ptile) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int col = n0 + 32 * (FN * wave + j) + frag_row;
@@ -351,31 +369,43 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
         return;
     }
 
-    // split K: this split's fp32 tile; k_split_sum_bf16 adds the splits in order
-    float* pdst = partial + size_t(tz) * T * N;
+    // a piece of a split tile: the whole fp32 tile [BM][BN] (rows past T and columns
+    // past N included; never read back); k_split_sum_bf16 adds the pieces in order
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        const int col = n0 + 32 * (FN * wave + j) + frag_row;
+        const int col = 32 * (FN * wave + j) + frag_row;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = m0 + 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
-                if (row < T && col < N) pdst[size_t(row) * N + col] = acc[i][j][e];
+                const int row = 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
+                ptile[row * BN + col] = acc[i][j][e];
             }
     }
 }
 
-// y = RNbf(((p0 + p1) + p2) + ...): the split partials added in split order (split 0
-// holds the LoRA term), rounded once; four consecutive outputs per thread.
-__global__ __launch_bounds__(256) void k_split_sum_bf16(const float* __restrict__ partial, int splits,
-                                                        int64_t total, uint16_t* __restrict__ out) {
+// y = RNbf(((p0 + p1) + p2) + ...) of each split tile: its pieces' fp32 tiles added in
+// piece order (piece 0 holds the LoRA term), rounded once; four consecutive outputs
+// per thread.
+struct SplitTiles {
+    const float* part;  // [pieces][tail][BM * BN]
+    int full, tail, pieces, mtiles, bm, bn;
+    int T, N;
+};
+
+__global__ __launch_bounds__(256) void k_split_sum_bf16(SplitTiles f, uint16_t* __restrict__ out) {
+    const int tile_elems = f.bm * f.bn;
+    const int64_t total = int64_t(f.tail) * tile_elems;
     const int64_t idx = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
     if (idx >= total) return;
-    f32x4 a = *reinterpret_cast<const f32x4*>(partial + idx);
-    for (int z = 1; z < splits; ++z) a += *reinterpret_cast<const f32x4*>(partial + size_t(z) * total + idx);
+    const int q = int(idx / tile_elems), loc = int(idx % tile_elems);
+    const int tile = f.full + q;
+    const int row = (tile % f.mtiles) * f.bm + loc / f.bn, col = (tile / f.mtiles) * f.bn + loc % f.bn;
+    if (row >= f.T || col >= f.N) return;  // N % 16 == 0: the four columns are all in or all out
+    f32x4 a = *reinterpret_cast<const f32x4*>(f.part + idx);
+    for (int z = 1; z < f.pieces; ++z) a += *reinterpret_cast<const f32x4*>(f.part + z * total + idx);
     const u32x2 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-    *reinterpret_cast<u32x2*>(out + idx) = o;
+    *reinterpret_cast<u32x2*>(out + size_t(row) * f.N + col) = o;
 }
 
 }  // namespace
@@ -390,17 +420,36 @@ FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     }
     p.bm = 128;
     p.bn = 128;
-    const int64_t tiles = cdiv(T, p.bm) * cdiv(N, p.bn);
+    p.mtiles = int(cdiv(T, p.bm));
+    const int64_t tiles = int64_t(p.mtiles) * cdiv(N, p.bn);
     const int64_t ksteps = K / kBK;
+    // Under 256 tiles: every tile split (about 512 workgroups in all). Many: whole rounds
+    // of 256 tiles (one more per CU each) run whole, and a last round of at most 128
+    // tiles is split into pieces that spread over the CUs: the time of a CU grows with
+    // the tiles it holds, so 2 whole tiles + a third of one beat 3 whole tiles.
+    int64_t tail = 0, pieces = 1;
     const int64_t splits = pick_splits(tiles, ksteps, 4);
-    p.steps_per_split = int(cdiv(ksteps, splits));
-    p.splits = int(cdiv(ksteps, p.steps_per_split));
+    if (splits > 1) {
+        tail = tiles;
+        pieces = splits;
+    } else if (tiles > kCUs) {
+        const int64_t last = tiles % kCUs;
+        const int64_t pc = last > 0 ? std::min<int64_t>(kCUs / last, ksteps / 4) : 1;
+        if (last > 0 && last <= kCUs / 2 && pc >= 2) {
+            tail = last;
+            pieces = pc;
+        }
+    }
+    p.steps_per_piece = int(cdiv(ksteps, pieces));
+    p.pieces = tail > 0 ? int(cdiv(ksteps, p.steps_per_piece)) : 1;
+    p.tail = int(tail);
+    p.full = int(tiles - tail);  // 0 or a multiple of kCUs (a multiple of the XCD count)
     if (r > 0) plan_lora_down(p, K);
     size_t off = 0;
     p.off_upart = off;
     off += align256(size_t(p.down_parts) * size_t(T) * size_t(r) * 4);
     p.off_ypart = off;
-    off += p.splits > 1 ? align256(size_t(p.splits) * size_t(T) * size_t(N) * 4) : 0;
+    off += p.tail > 0 ? align256(size_t(p.pieces) * size_t(p.tail) * size_t(p.bm) * size_t(p.bn) * 4) : 0;
     p.ws_bytes = off;
     return p;
 }
@@ -409,25 +458,26 @@ hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* 
                            const uint16_t* x, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,
                            uint16_t* y, float* u_save, void* ws, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
-    const dim3 grid(unsigned(cdiv(N, p.bn)), unsigned(cdiv(T, p.bm)), unsigned(p.splits));
-    float* partial = p.splits > 1 ? reinterpret_cast<float*>(w + p.off_ypart) : nullptr;
+    const FwdTiles tl{p.full, p.tail, p.pieces, p.steps_per_piece, p.mtiles};
+    const dim3 grid(unsigned(p.full + p.tail * p.pieces));
+    float* partial = p.tail > 0 ? reinterpret_cast<float*>(w + p.off_ypart) : nullptr;
     const FwdLora lora{r > 0 ? reinterpret_cast<const float*>(w + p.off_upart) : nullptr, p.down_parts, u_save, B,
                        r, s};
     prof_gemm_begin(stream);
     if (wdense)
         hipLaunchKernelGGL((k_nf4_gemm_fwd<kFwdWaves, true>), grid, dim3(64 * kFwdWaves), 0, stream, x,
-                           static_cast<const void*>(wdense), nullptr, int(T), int(N), int(K), p.steps_per_split, lora, y,
-                           partial, tables());
+                           static_cast<const void*>(wdense), nullptr, int(T), int(N), int(K), tl, lora, y, partial,
+                           tables());
     else
         hipLaunchKernelGGL((k_nf4_gemm_fwd<kFwdWaves, false>), grid, dim3(64 * kFwdWaves), 0, stream, x,
-                           static_cast<const void*>(codes), absmax, int(T), int(N), int(K), p.steps_per_split, lora, y,
-                           partial, tables());
+                           static_cast<const void*>(codes), absmax, int(T), int(N), int(K), tl, lora, y, partial,
+                           tables());
     prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splits == 1) return e;
-    const int64_t total = T * N;
-    hipLaunchKernelGGL(k_split_sum_bf16, dim3(unsigned(cdiv(total / 4, 256))), dim3(256), 0, stream, partial,
-                       p.splits, total, y);
+    if (e != hipSuccess || p.tail == 0) return e;
+    const SplitTiles f{partial, p.full, p.tail, p.pieces, p.mtiles, p.bm, p.bn, int(T), int(N)};
+    const int64_t total = int64_t(p.tail) * p.bm * p.bn;
+    hipLaunchKernelGGL(k_split_sum_bf16, dim3(unsigned(cdiv(total / 4, 256))), dim3(256), 0, stream, f, y);
     return hipGetLastError();
 }
 
