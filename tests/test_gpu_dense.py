@@ -21,6 +21,8 @@ PROJS = ("q", "k", "v", "o", "gate", "up", "down")
     (17, 3584, 512, 5),      # odd rank
     (129, 512, 3584, 64),    # maximum rank, split contraction
     (64, 256, 512, 0),       # base only
+    (300, 10992, 640, 16),   # 258 y tiles: the last 2 split over K
+    (300, 640, 22976, 16),   # 540 dX tiles: the last 28 split over N
 ])
 def test_dense_linear_matches_oracle(gpu_lib, t, n, k, r):
     case = S.linear_case(t, n, k, r=max(r, 1))

@@ -69,6 +69,7 @@ def test_single_linear_workload(gpu_lib):
     (300, 1104, 8192, 16),   # long K and N: both GEMMs split their contraction, ragged tiles
     (40, 1040, 8256, 7),     # same with an odd step count over K and an odd rank
     (300, 640, 22976, 16),   # 540 dX tiles: a whole round of 512, the last 28 (ragged) split over N
+    (300, 10992, 640, 16),   # 258 y tiles: a whole round of 256, the last 2 (ragged) split over K
 ])
 def test_shapes(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
