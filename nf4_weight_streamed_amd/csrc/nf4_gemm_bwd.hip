@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
         if (nb < nb_end) step(nb, std::integral_constant<int, 0>{});
     }
 
-    // LoRA (split 0 only when split). g = sum of the partials in partial order; (s.g)^T
+    // LoRA (whole tiles and piece 0 of split tiles). g = sum of the partials in partial order; (s.g)^T
     // is staged as bf16 hi/lo [j][t] in the (now free) dY buffers and the x tile as
     // [k][t] in the weight buffers. Then
     //   dX tile += (s.g)_hi . A + (s.g)_lo . A      (K-extension on the accumulators)
