@@ -26,7 +26,7 @@ namespace {
 constexpr int kBN = 64;        // contraction (N) per main-loop step
 constexpr int kLds = kBN + 8;  // LDS pitch in bf16
 constexpr int kThreads = 256;
-constexpr int64_t kBwdSlots = 512;  // resident workgroups: two per CU (LDS), 256 CUs
+constexpr int64_t kCUs = 256;
 
 // Workgroup tile: 128 tokens x 128 input features, 4 waves in a 2x2 grid (64 x 64
 // each, 32x32x16 MFMA), contraction steps of 64 over N. Per step each thread loads
@@ -34,8 +34,12 @@ constexpr int64_t kBwdSlots = 512;  // resident workgroups: two per CU (LDS), 25
 // codes with the 4 row scales, and 4 16-byte chunks of the dY tile, one step ahead;
 // after the current step's MFMAs it dequantises the patch - one 8-byte read of a
 // 256-entry (level[lo], level[hi]) pair table per code byte, fp32 multiply by the
-// row's absmax, bf16 pack pairing rows - and stores the patch transposed into the
-// other LDS buffer. dY and the weight tile are double-buffered: one barrier per step.
+// row's absmax, bf16 pack pairing rows - and, once every wave has read the current
+// tiles, stores it transposed. dY and the weight tile are single-buffered (two
+// barriers per step) so that the LDS block (51 KB, shared with the LoRA epilogue) and
+// 165 VGPRs let three workgroups share a CU; the other workgroups' MFMAs fill each
+// workgroup's store phase.
+
 // Which tile (and contraction range) each workgroup of the 1-D grid takes: ids
 // 0 .. full-1 are whole tiles, the rest pieces of the last `tail` tiles, piece z of
 // tile full + q at id full + z * tail + q. Both ranges are laid over the XCDs
@@ -57,7 +61,7 @@ struct BwdLora {
 };
 
 template <bool kDense>
-__global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
+__global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
     const uint16_t* __restrict__ dy, const void* __restrict__ weights, const float* __restrict__ absmax, int T,
     int N, int K, BwdTiles tl, BwdLora lora, uint16_t* __restrict__ dx, float* __restrict__ partial, Tables tab) {
     constexpr int BM = 128, BK = 128;
@@ -65,9 +69,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     constexpr int FM = WM / 32, FK = WK / 32;
     constexpr int A_CHUNKS = BM * (kBN / 8) / kThreads;  // 4
 
-    __shared__ __align__(16) uint16_t sA[2][BM * kLds];
-    __shared__ __align__(16) uint16_t sWt[2][BK * kLds];
-    __shared__ __align__(16) float sLut[512];
+    // One LDS block (51 KB: three workgroups per CU). Main loop: the dY tile, the
+    // weight tile and the pair table, single-buffered; LoRA epilogue: (s.g)^T hi/lo
+    // for up to 64 ranks and one 64-column half of the x tile, transposed.
+    constexpr int kTP = BM + 8;  // pitch of the epilogue's [.][t] tiles
+    constexpr int kMain = BM * kLds + BK * kLds + 2 * 512;
+    constexpr int kEpi = (2 * 64 + BK / 2) * kTP;
+    __shared__ __align__(16) uint16_t smem[kMain > kEpi ? kMain : kEpi];
+    uint16_t* const sA = smem;
+    uint16_t* const sWt = smem + BM * kLds;
+    float* const sLut = reinterpret_cast<float*>(smem + BM * kLds + BK * kLds);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -141,11 +152,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
         }
     };
     const char* lut = reinterpret_cast<const char*>(sLut);
-    auto sstore = [&](int buf) {
+    auto sstore = [&]() {
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
             const int c = tid + kThreads * i;
-            *reinterpret_cast<u32x4*>(&sA[buf][(c >> 3) * kLds + (c & 7) * 8]) = ra[i];
+            *reinterpret_cast<u32x4*>(&sA[(c >> 3) * kLds + (c & 7) * 8]) = ra[i];
         }
         // row k = 8*pc + e holds n = 4*pr .. 4*pr+3: chunk pr/2 (swizzled by pc), half pr&1
         const int col = (((pr >> 1) ^ (pc & 7)) << 3) + 4 * (pr & 1);
@@ -155,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
                 const int sh = 16 * (e & 1);
                 auto bits = [&](int i) { return (rw[i][e >> 1] >> sh) & 0xFFFFu; };
                 const u32x2 o = {bits(0) | (bits(1) << 16), bits(2) | (bits(3) << 16)};
-                *reinterpret_cast<u32x2*>(&sWt[buf][(8 * pc + e) * kLds + col]) = o;
+                *reinterpret_cast<u32x2*>(&sWt[(8 * pc + e) * kLds + col]) = o;
             }
             return;
         }
@@ -172,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             u32x2 o = {pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e])};
-            *reinterpret_cast<u32x2*>(&sWt[buf][(8 * pc + e) * kLds + col]) = o;
+            *reinterpret_cast<u32x2*>(&sWt[(8 * pc + e) * kLds + col]) = o;
         }
     };
 
@@ -187,13 +198,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     if (nb_begin < nb_end) {
         gload(nb_begin);
         __syncthreads();  // sLut visible
-        sstore(0);
+        sstore();
         __syncthreads();
         // loads are issued unconditionally (a step past the end reads data that is never
-        // used, or zeros): the compiler's wait counts then stay exact
-        auto step = [&](int nb, auto c_) {
-            constexpr int C = decltype(c_)::value;
-            const bool more = nb + 1 < nb_end;
+        // used, or zeros): the compiler's wait counts then stay exact. Two barriers per
+        // step: the single-buffered tiles are rewritten only after every wave has read
+        // them; the other workgroups on the CU keep the MFMAs busy meanwhile.
+        for (int nb = nb_begin; nb < nb_end; ++nb) {
             gload(nb + 1);
             __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
 #pragma unroll
@@ -202,41 +213,37 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
                     af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                        &sA[C][(wm * WM + 32 * i + frag_row) * kLds + kk * 16 + frag_k]));
+                        &sA[(wm * WM + 32 * i + frag_row) * kLds + kk * 16 + frag_k]));
 #pragma unroll
                 for (int j = 0; j < FK; ++j) {
                     const int row = wk * WK + 32 * j + frag_row;
                     const int chunk = (2 * kk + (lane >> 5)) ^ ((row >> 3) & 7);
-                    bw[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sWt[C][row * kLds + chunk * 8]));
+                    bw[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sWt[row * kLds + chunk * 8]));
                 }
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FK; ++j) acc[i][j] = mfma32x32x16(af[i], bw[j], acc[i][j]);
             }
-            if (more) sstore(C ^ 1);  // next step's tiles into the other buffers
-            __syncthreads();
-        };
-        int nb = nb_begin;
-        for (; nb + 1 < nb_end; nb += 2) {
-            step(nb, std::integral_constant<int, 0>{});
-            step(nb + 1, std::integral_constant<int, 1>{});
+            __syncthreads();  // every wave's fragment reads of this step are done
+            if (nb + 1 < nb_end) {
+                sstore();  // the next step's tiles
+                __syncthreads();
+            }
         }
-        if (nb < nb_end) step(nb, std::integral_constant<int, 0>{});
     }
 
-    // LoRA (whole tiles and piece 0 of split tiles). g = sum of the partials in partial order; (s.g)^T
-    // is staged as bf16 hi/lo [j][t] in the (now free) dY buffers and the x tile as
-    // [k][t] in the weight buffers. Then
+    // LoRA (whole tiles and piece 0 of split tiles). g = sum of the partials in partial
+    // order; (s.g)^T is staged as bf16 hi/lo [j][t] and the x tile as [k][t], one
+    // 64-column half at a time, in the (now free) LDS block. Then
     //   dX tile += (s.g)_hi . A + (s.g)_lo . A      (K-extension on the accumulators)
     //   dA share of this token tile = (s.g)^T . x over its tokens (k_bwd_finish adds
     //   the shares in token-tile order: dA = ((d0 + d1) + d2) + ...)
     const int r = lora.r;
     if (tz == 0 && r > 0) {
-        constexpr int kTP = BM + 8;  // pitch of the [.][t] tiles
-        uint16_t* sg_hi = &sA[0][0];           // [64][kTP]
-        uint16_t* sg_lo = sg_hi + 64 * kTP;    // [64][kTP]
-        uint16_t* sxt = &sWt[0][0];            // [BK][kTP]
+        uint16_t* const sg_hi = smem;             // [64][kTP]
+        uint16_t* const sg_lo = smem + 64 * kTP;  // [64][kTP]
+        uint16_t* const sxt = smem + 128 * kTP;   // [BK / 2][kTP]
         const int rp = (r + 15) & ~15;
         // the partials region is padded to 256 bytes: 16-byte loads at 4-byte aligned
         // offsets stay inside it; lanes j >= r are masked below
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
             const int c = tid + kThreads * i, t = c / (BK / 8), k8 = 8 * (c % (BK / 8));
             xv[i] = buf_load16(rx, (uint32_t(t) * uint32_t(K) + uint32_t(k0 + k8)) * 2u);
         }
-        constexpr int GR = 8;  // partials loaded per round
+        constexpr int GR = 2;  // partials loaded per round
         for (int jb = 0; jb < rp / 16; ++jb) {
             f32x4 gsum[GI];
 #pragma unroll
@@ -307,15 +314,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
                 }
             }
         }
+        // x^T of columns 64 h .. 64 h + 63: a thread's chunks all sit in one half (their
+        // column offset is 8 (tid % 16))
+        auto stage_x = [&](int h) {
+            if (((tid & 15) >> 3) != h) return;
 #pragma unroll
-        for (int i = 0; i < XC; ++i) {
-            const int c = tid + kThreads * i, t = c / (BK / 8), k8 = 8 * (c % (BK / 8));
+            for (int i = 0; i < XC; ++i) {
+                const int c = tid + kThreads * i, t = c / (BK / 8), k8 = 8 * (c % (BK / 8)) - 64 * h;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t w = xv[i][e >> 1];
-                sxt[(k8 + e) * kTP + t] = uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF));
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w = xv[i][e >> 1];
+                    sxt[(k8 + e) * kTP + t] = uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF));
+                }
             }
-        }
+        };
+        stage_x(0);
         __syncthreads();
 
         if (dx) {
@@ -346,26 +359,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
             }
         }
 
-        // dA share of this token tile: D[k][j] over t, 16x16x32 MFMAs; wave w owns the
-        // K sub-blocks 2w, 2w+1 (16 columns each)
+        // dA share of this token tile: D[k][j] over t, 16x16x32 MFMAs; per 64-column
+        // half, wave w owns the K sub-block w (16 columns)
         const int l16 = lane & 15, t8 = 8 * (lane >> 4);
         float* dpart = lora.dapart + size_t(tm) * r * K;
-        for (int jb = 0; jb < rp / 16; ++jb) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-                const int kb = 2 * wave + kb2;
+        for (int h = 0; h < 2; ++h) {
+            if (h > 0) {
+                __syncthreads();  // the first half's reads are done
+                stage_x(h);
+                __syncthreads();
+            }
+            for (int jb = 0; jb < rp / 16; ++jb) {
                 f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ts = 0; ts < BM / 32; ++ts) {
                     const int tt = 32 * ts + t8;
-                    const bf16x8 xa = as_bf16x8(*reinterpret_cast<const u32x4*>(&sxt[(16 * kb + l16) * kTP + tt]));
+                    const bf16x8 xa = as_bf16x8(*reinterpret_cast<const u32x4*>(&sxt[(16 * wave + l16) * kTP + tt]));
                     const bf16x8 gh = as_bf16x8(*reinterpret_cast<const u32x4*>(&sg_hi[(16 * jb + l16) * kTP + tt]));
                     const bf16x8 gl = as_bf16x8(*reinterpret_cast<const u32x4*>(&sg_lo[(16 * jb + l16) * kTP + tt]));
                     d = mfma16x16x32(xa, gh, d);
                     d = mfma16x16x32(xa, gl, d);
                 }
-                // lane holds D[k = 16 kb + 4 (lane / 16) + e][j = 16 jb + lane % 16]
-                const int j = 16 * jb + l16, kq = k0 + 16 * kb + 4 * (lane >> 4);
+                // lane holds D[k = 64 h + 16 wave + 4 (lane / 16) + e][j = 16 jb + lane % 16]
+                const int j = 16 * jb + l16, kq = k0 + 64 * h + 16 * wave + 4 * (lane >> 4);
                 if (j < r && kq < K) *reinterpret_cast<f32x4*>(&dpart[size_t(j) * K + kq]) = d;
             }
         }
@@ -453,18 +469,19 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     p.ktiles = int(cdiv(K, p.bn));
     const int64_t tiles = int64_t(p.mtiles) * p.ktiles;
     const int64_t nsteps = cdiv(N, kBN);
-    // Under 256 tiles: every tile split (about 512 workgroups in all). Many: whole
-    // rounds of kSlots tiles (two workgroups per CU, set by LDS) run whole and a last,
-    // partial round of at most half the slots is split to fill them.
+    // Under 256 tiles: every tile split (about 512 workgroups in all). Many: whole rounds
+    // of 256 tiles (one more per CU each) run whole, and a last round of at most 128
+    // tiles is split into pieces that spread over the CUs: the time of a CU grows with
+    // the tiles it holds, so 2 whole tiles + a third of one beat 3 whole tiles.
     int64_t tail = 0, pieces = 1;
     const int64_t splits = pick_splits(tiles, nsteps, 4);
     if (splits > 1) {
         tail = tiles;
         pieces = splits;
-    } else if (tiles > kBwdSlots) {
-        const int64_t last = tiles % kBwdSlots;
-        const int64_t pc = last > 0 ? std::min<int64_t>(kBwdSlots / last, nsteps / 4) : 1;
-        if (last > 0 && last <= kBwdSlots / 2 && pc >= 2) {
+    } else if (tiles > kCUs) {
+        const int64_t last = tiles % kCUs;
+        const int64_t pc = last > 0 ? std::min<int64_t>(kCUs / last, nsteps / 4) : 1;
+        if (last > 0 && last <= kCUs / 2 && pc >= 2) {
             tail = last;
             pieces = pc;
         }
@@ -472,7 +489,7 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     p.steps_per_piece = int(cdiv(nsteps, pieces));
     p.pieces = tail > 0 ? int(cdiv(nsteps, p.steps_per_piece)) : 1;
     p.tail = int(tail);
-    p.full = int(tiles - tail);  // 0 or a multiple of kBwdSlots (a multiple of the XCD count)
+    p.full = int(tiles - tail);  // 0 or a multiple of kCUs (a multiple of the XCD count)
     if (r > 0) plan_lora_bwd_pre(p, N, kMaxGParts);
     size_t off = 0;
     p.off_gpart = off;
