@@ -402,8 +402,10 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
         return;
     }
 
-    // a piece of a split tile: the whole fp32 tile [BM][BK] (rows past T and columns
-    // past K included; never read back); k_bwd_finish adds the pieces in order
+    // a piece of a split tile: its fp32 tile [BM][BK], rows below T only (few tokens
+    // leave most rows empty; columns past K are written but never read); k_bwd_finish
+    // adds the pieces in order
+    const int rlim = T - m0;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
             for (int e = 0; e < 16; ++e) {
                 const int row = wm * WM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 const int col = wk * WK + 32 * j + (lane & 31);
-                ptile[row * BK + col] = acc[i][j][e];
+                if (row < rlim) ptile[row * BK + col] = acc[i][j][e];
             }
 }
 

@@ -369,8 +369,8 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
         return;
     }
 
-    // a piece of a split tile: the whole fp32 tile [BM][BN] (rows past T and columns
-    // past N included; never read back); k_split_sum_bf16 adds the pieces in order
+    // a piece of a split tile: its fp32 tile [BM][BN], rows below T and columns below N
+    // only (the rest is never read); k_split_sum_bf16 adds the pieces in order
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int col = 32 * (FN * wave + j) + frag_row;
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
-                ptile[row * BN + col] = acc[i][j][e];
+                if (m0 + row < T && n0 + col < N) ptile[row * BN + col] = acc[i][j][e];
             }
     }
 }
