@@ -304,12 +304,13 @@ int linear_bwd(const char* fn, const uint8_t* codes, const float* absmax, const 
                           "nf4_lora_linear_bwd (few-token path)");
     if (r > 0) {
         int st = hip_status(launch_lora_bwd_pre(p, dy, B, u_save, T, N, r, scale,
-                                                reinterpret_cast<float*>(w + p.off_gpart), dB, s),
+                                                reinterpret_cast<float*>(w + p.off_gpart), dB,
+                                                reinterpret_cast<float*>(w + p.off_dbpart), s),
                             "nf4_lora_linear_bwd (g, dB)");
         if (st != NF4_OK) return st;
     }
     // dX (when requested) with its LoRA term, and dA
-    return hip_status(launch_gemm_bwd(p, codes, absmax, wdense, dy, x, A, T, N, K, r, scale, dx, dA, ws, s),
+    return hip_status(launch_gemm_bwd(p, codes, absmax, wdense, dy, x, A, T, N, K, r, scale, dx, dA, dB, ws, s),
                       "nf4_lora_linear_bwd (dX, dA)");
 }
 

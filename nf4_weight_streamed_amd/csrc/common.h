@@ -35,6 +35,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t 
 constexpr int kMaxDownParts = 16; // K ranges of u = x.A^T
 constexpr int kMaxGParts = 16;    // N ranges of g = dY.B (128-token path)
 constexpr int kMaxGPartsFew = 64; // N ranges of g = dY.B (few-token path: summed by the finish kernel)
+constexpr int kMaxDbChunks = 8;   // token ranges of dB = s.dY^T.u (shares summed by the finish kernel)
 
 // Few-token path (T <= kSkinnyT; measured faster than the 128-token kernels up to T = 16,
 // slower from T = 32): streaming kernels with 16-token MFMA blocks and fp32
@@ -86,13 +87,15 @@ struct BwdPlan {
     int pieces, steps_per_piece;
     int mtiles, ktiles;    // dX tile grid
     int gparts, gsteps;    // N ranges of g = dY.B (partials summed by the GEMM), 128-feature chunks each
+    int dbchunks, dbtokens;  // token ranges of dB (1: written directly), tokens each
+    size_t off_dbpart;     // dB shares [dbchunks][N][r] when dbchunks > 1
     size_t off_gpart, off_dapart, off_dx;  // workspace offsets (bytes)
     size_t ws_bytes;
     bool skinny;           // few-token path: g partials and dX partials (sk) at off_gpart / off_dx
     SkinnyPlan sk;
 };
 BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense = false);
-void plan_lora_bwd_pre(BwdPlan& p, int64_t N, int max_parts);  // g partials over N ranges
+void plan_lora_bwd_pre(BwdPlan& p, int64_t T, int64_t N, int max_parts);  // g over N ranges, dB over token ranges
 
 hipError_t launch_lora_down(const FwdPlan& p, const uint16_t* x, const uint16_t* A, int64_t T, int64_t K, int r,
                             float* upart, hipStream_t stream);
@@ -101,10 +104,10 @@ hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* 
                            const uint16_t* x, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,
                            uint16_t* y, float* u_save, void* ws, hipStream_t stream);
 hipError_t launch_lora_bwd_pre(const BwdPlan& p, const uint16_t* dy, const uint16_t* B, const float* u, int64_t T,
-                               int64_t N, int r, float s, float* gpart, float* dB, hipStream_t stream);
+                               int64_t N, int r, float s, float* gpart, float* dB, float* dbpart, hipStream_t stream);
 hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* wdense,
                            const uint16_t* dy, const uint16_t* x, const uint16_t* A, int64_t T, int64_t N, int64_t K,
-                           int r, float s, uint16_t* dx, float* dA, void* ws, hipStream_t stream);
+                           int r, float s, uint16_t* dx, float* dA, float* dB, void* ws, hipStream_t stream);
 
 hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* x,
                              const uint16_t* A, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,

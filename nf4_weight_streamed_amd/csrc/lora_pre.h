@@ -19,10 +19,11 @@ constexpr int kThreads = 256;
 //    chunk the B rows are staged transposed in LDS ([j][n], double-buffered, loads
 //    one chunk ahead) and each wave contracts 16 tokens x 64 features straight from
 //    dY in registers; the two waves of a token half add up in fixed order -> gpart[p].
-//  - dB role: 64 features x all tokens in DBT-token sub-chunks (dY
-//    transposed and (s.u) hi/lo staged in LDS, loads one sub-chunk ahead) -> dB;
-//    with many tokens the sub-chunks are long (kDbTLong) so that few of them (one
-//    memory round trip each) run in sequence.
+//  - dB role: 64 features x a token range in DBT-token sub-chunks (dY
+//    transposed and (s.u) hi/lo staged in LDS, loads one sub-chunk ahead) -> dB, or
+//    this range's share of dB (the shares are added in range order after the dX
+//    GEMM); with many tokens the sub-chunks are long (kDbTLong) so that few of them
+//    (one memory round trip each) run in sequence.
 constexpr int kTC = 32;         // tokens per g workgroup; dB sub-chunk for few tokens
 constexpr int kDbTLong = 128;   // dB sub-chunk for many tokens
 constexpr int kGChunk = 128;    // features per g chunk
@@ -116,9 +117,10 @@ __device__ void g_role(const uint16_t* __restrict__ dy, const uint16_t* __restri
     }
 }
 
+// tokens [t_begin, t_end) of features 64 blk .. 64 blk + 63 -> dst [N][r]
 template <int RB, int DBT>
 __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict__ u, int T, int N, int r, float s,
-                        int blk, float* __restrict__ dB, DbSmem<RB, DBT>& sm) {
+                        int blk, int t_begin, int t_end, float* __restrict__ dst, DbSmem<RB, DBT>& sm) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blk * 64;
     const int lt = tid >> 3, ln8 = (tid & 7) * 8;  // 16-byte pieces: tokens lt + 32 i, features ln8 .. ln8 + 7
@@ -132,15 +134,15 @@ __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict
 #pragma unroll
         for (int i = 0; i < DV; ++i) {
             const int t = t0 + lt + 32 * i;
-            const bool ok = t < T && n0 + ln8 < N;
+            const bool ok = t < t_end && n0 + ln8 < N;
             vdy[i] = buf_load16(rdy, ok ? (uint32_t(t) * uint32_t(N) + uint32_t(n0 + ln8)) * 2u : kOutOfRange);
         }
 #pragma unroll
         for (int i = 0; i < UV; ++i) {
             const int o = tid + kThreads * i;  // o = t * 16 RB + j
             const int t = o / (16 * RB), j = o % (16 * RB);
-            uv[i] = buf_load_f32(ru, (t0 + t < T && j < r) ? (uint32_t(t0 + t) * uint32_t(r) + uint32_t(j)) * 4u
-                                                           : kOutOfRange);
+            uv[i] = buf_load_f32(ru, (t0 + t < t_end && j < r) ? (uint32_t(t0 + t) * uint32_t(r) + uint32_t(j)) * 4u
+                                                               : kOutOfRange);
         }
     };
     auto sstore = [&]() {
@@ -165,8 +167,8 @@ __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict
 #pragma unroll
     for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int kof = 8 * (lane >> 4);
-    gload(0);
-    for (int t0 = 0; t0 < T; t0 += DBT) {
+    gload(t_begin);
+    for (int t0 = t_begin; t0 < t_end; t0 += DBT) {
         __syncthreads();  // the previous sub-chunk's reads are done
         sstore();
         __syncthreads();
@@ -189,7 +191,7 @@ __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int n = n0 + 16 * wave + 4 * (lane >> 4) + e, j = 16 * b + (lane & 15);
-            if (n < N && j < r) dB[size_t(n) * r + j] = acc[b][e];
+            if (n < N && j < r) dst[size_t(n) * r + j] = acc[b][e];
         }
 }
 

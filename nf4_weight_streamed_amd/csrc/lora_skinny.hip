@@ -75,7 +75,8 @@ __global__ __launch_bounds__(kThreads) void k_lora_down(const uint16_t* __restri
 
 // ---------------------------------------------------------------- backward pre-pass
 // One launch, the two roles of lora_pre.h: g workgroups [0, gblocks), dB workgroups
-// the rest.
+// the rest (feature block fastest, then token range; with one range dB is written
+// directly, else each range's share goes to dbpart [range][N][r]).
 using pre::db_role;
 using pre::g_role;
 using pre::kGChunk;
@@ -86,13 +87,17 @@ template <int RB>
 __global__ __launch_bounds__(kThreads) void k_lora_bwd_pre(const uint16_t* __restrict__ dy,
                                                            const uint16_t* __restrict__ B,
                                                            const float* __restrict__ u, int T, int N, int r, float s,
-                                                           int gsteps, int gblocks, float* __restrict__ gpart,
-                                                           float* __restrict__ dB) {
+                                                           int gsteps, int gblocks, int dbtokens, float* __restrict__ gpart,
+                                                           float* __restrict__ dB, float* __restrict__ dbpart) {
     __shared__ __align__(16) PreSmem<RB, pre::kDbTLong> sm;
-    if (int(blockIdx.x) < gblocks)
+    if (int(blockIdx.x) < gblocks) {
         g_role<RB>(dy, B, T, N, r, gsteps, blockIdx.x, gpart, sm.g);
-    else
-        db_role<RB, pre::kDbTLong>(dy, u, T, N, r, s, int(blockIdx.x) - gblocks, dB, sm.d);
+        return;
+    }
+    const int nblocks = (N + 63) / 64, d = int(blockIdx.x) - gblocks;
+    const int chunk = d / nblocks, t_begin = chunk * dbtokens;
+    float* dst = dbtokens >= T ? dB : dbpart + size_t(chunk) * N * r;
+    db_role<RB, pre::kDbTLong>(dy, u, T, N, r, s, d % nblocks, t_begin, min(T, t_begin + dbtokens), dst, sm.d);
 }
 
 template <int RB>
@@ -104,11 +109,11 @@ void launch_down_rb(const FwdPlan& p, const uint16_t* x, const uint16_t* A, int6
 
 template <int RB>
 void launch_pre_rb(const BwdPlan& p, const uint16_t* dy, const uint16_t* B, const float* u, int64_t T, int64_t N,
-                   int r, float s, float* gpart, float* dB, hipStream_t stream) {
+                   int r, float s, float* gpart, float* dB, float* dbpart, hipStream_t stream) {
     const int gblocks = int(cdiv(T, kTC)) * p.gparts;
-    const int dblocks = int(cdiv(N, 64));
+    const int dblocks = int(cdiv(N, 64)) * p.dbchunks;
     hipLaunchKernelGGL(k_lora_bwd_pre<RB>, dim3(unsigned(gblocks + dblocks)), dim3(kThreads), 0, stream, dy, B, u,
-                       int(T), int(N), r, s, p.gsteps, gblocks, gpart, dB);
+                       int(T), int(N), r, s, p.gsteps, gblocks, p.dbtokens, gpart, dB, dbpart);
 }
 
 }  // namespace
@@ -122,11 +127,17 @@ void plan_lora_down(FwdPlan& p, int64_t K) {
     p.down_parts = int(cdiv(ks32, p.down_steps));
 }
 
-void plan_lora_bwd_pre(BwdPlan& p, int64_t N, int max_parts) {
+void plan_lora_bwd_pre(BwdPlan& p, int64_t T, int64_t N, int max_parts) {
     const int64_t chunks = cdiv(N, kGChunk);
     const int64_t parts = std::max<int64_t>(1, std::min<int64_t>(max_parts, chunks / 2));
     p.gsteps = int(cdiv(chunks, parts));
     p.gparts = int(cdiv(chunks, p.gsteps));
+    // dB over token ranges of whole 128-token sub-chunks (at most kMaxDbChunks ranges):
+    // each workgroup then waits on one or a few sub-chunk loads instead of all of them
+    const int64_t sub = cdiv(T, pre::kDbTLong);
+    const int64_t ranges = std::min<int64_t>(kMaxDbChunks, sub);
+    p.dbtokens = int(pre::kDbTLong * cdiv(sub, ranges));
+    p.dbchunks = int(cdiv(T, p.dbtokens));
 }
 
 hipError_t launch_lora_down(const FwdPlan& p, const uint16_t* x, const uint16_t* A, int64_t T, int64_t K, int r,
@@ -141,12 +152,12 @@ hipError_t launch_lora_down(const FwdPlan& p, const uint16_t* x, const uint16_t*
 }
 
 hipError_t launch_lora_bwd_pre(const BwdPlan& p, const uint16_t* dy, const uint16_t* B, const float* u, int64_t T,
-                               int64_t N, int r, float s, float* gpart, float* dB, hipStream_t stream) {
+                               int64_t N, int r, float s, float* gpart, float* dB, float* dbpart, hipStream_t stream) {
     switch ((r + 15) / 16) {
-        case 1: launch_pre_rb<1>(p, dy, B, u, T, N, r, s, gpart, dB, stream); break;
-        case 2: launch_pre_rb<2>(p, dy, B, u, T, N, r, s, gpart, dB, stream); break;
-        case 3: launch_pre_rb<3>(p, dy, B, u, T, N, r, s, gpart, dB, stream); break;
-        default: launch_pre_rb<4>(p, dy, B, u, T, N, r, s, gpart, dB, stream); break;
+        case 1: launch_pre_rb<1>(p, dy, B, u, T, N, r, s, gpart, dB, dbpart, stream); break;
+        case 2: launch_pre_rb<2>(p, dy, B, u, T, N, r, s, gpart, dB, dbpart, stream); break;
+        case 3: launch_pre_rb<3>(p, dy, B, u, T, N, r, s, gpart, dB, dbpart, stream); break;
+        default: launch_pre_rb<4>(p, dy, B, u, T, N, r, s, gpart, dB, dbpart, stream); break;
     }
     return hipGetLastError();
 }

@@ -420,20 +420,34 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
 
 // The backward's reductions, in one launch: blocks [0, dx_blocks) form
 // dX = RNbf(((p0 + p1) + p2) + ...) of the split tiles from their pieces' fp32 tiles;
-// the rest form dA = ((d0 + d1) + d2) + ... from the token tiles' shares. Four
-// outputs per thread.
+// the next da_blocks form dA = ((d0 + d1) + d2) + ... from the token tiles' shares and
+// the rest dB from its token ranges' shares, in the same way. Four outputs per thread.
 struct BwdFinishDx {
     const float* part;  // [pieces][tail][BM * BK]
     int full, tail, pieces, mtiles, bm, bk;
     int T, K;
 };
+struct Shares {  // dst[i] = ((src[0][i] + src[1][i]) + src[2][i]) + ...
+    const float* src;
+    int count;
+    int64_t total;
+    float* dst;
+};
+
+__device__ __forceinline__ void sum_shares(const Shares& sh, int64_t block) {
+    const int64_t idx = (block * 256 + threadIdx.x) * 4;
+    if (idx >= sh.total) return;
+    f32x4 a = *reinterpret_cast<const f32x4*>(sh.src + idx);
+    for (int z = 1; z < sh.count; ++z) a += *reinterpret_cast<const f32x4*>(sh.src + size_t(z) * sh.total + idx);
+    *reinterpret_cast<f32x4*>(sh.dst + idx) = a;
+}
 
 __global__ __launch_bounds__(256) void k_bwd_finish(BwdFinishDx f, uint16_t* __restrict__ dx, int64_t dx_blocks,
-                                                    const float* __restrict__ dapart, int shares, int64_t da_total,
-                                                    float* __restrict__ dA) {
-    if (int64_t(blockIdx.x) < dx_blocks) {
+                                                    Shares da, int64_t da_blocks, Shares db) {
+    const int64_t b = blockIdx.x;
+    if (b < dx_blocks) {
         const int64_t tile_elems = int64_t(f.bm) * f.bk, total = int64_t(f.tail) * tile_elems;
-        const int64_t idx = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+        const int64_t idx = (b * 256 + threadIdx.x) * 4;
         if (idx >= total) return;
         const int q = int(idx / tile_elems), loc = int(idx % tile_elems);
         const int tile = f.full + q;
@@ -443,12 +457,10 @@ __global__ __launch_bounds__(256) void k_bwd_finish(BwdFinishDx f, uint16_t* __r
         for (int z = 1; z < f.pieces; ++z) a += *reinterpret_cast<const f32x4*>(f.part + z * total + idx);
         const u32x2 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
         *reinterpret_cast<u32x2*>(dx + size_t(row) * f.K + col) = o;
+    } else if (b < dx_blocks + da_blocks) {
+        sum_shares(da, b - dx_blocks);
     } else {
-        const int64_t idx = ((int64_t(blockIdx.x) - dx_blocks) * 256 + threadIdx.x) * 4;
-        if (idx >= da_total) return;
-        f32x4 a = *reinterpret_cast<const f32x4*>(dapart + idx);
-        for (int z = 1; z < shares; ++z) a += *reinterpret_cast<const f32x4*>(dapart + size_t(z) * da_total + idx);
-        *reinterpret_cast<f32x4*>(dA + idx) = a;
+        sum_shares(db, b - dx_blocks - da_blocks);
     }
 }
 
@@ -459,7 +471,7 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     if (T <= kSkinnyT && !dense) {
         p.skinny = true;
         p.sk = plan_skinny_bwd(T, N, K);
-        if (r > 0) plan_lora_bwd_pre(p, N, kMaxGPartsFew);
+        if (r > 0) plan_lora_bwd_pre(p, T, N, kMaxGPartsFew);
         p.off_gpart = 0;
         p.off_dx = align256(size_t(p.gparts) * size_t(T) * size_t(r) * 4);
         p.ws_bytes = p.off_dx + p.sk.ws_bytes;
@@ -492,12 +504,14 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     p.pieces = tail > 0 ? int(cdiv(nsteps, p.steps_per_piece)) : 1;
     p.tail = int(tail);
     p.full = int(tiles - tail);  // 0 or a multiple of kCUs (a multiple of the XCD count)
-    if (r > 0) plan_lora_bwd_pre(p, N, kMaxGParts);
+    if (r > 0) plan_lora_bwd_pre(p, T, N, kMaxGParts);
     size_t off = 0;
     p.off_gpart = off;
     off += align256(size_t(p.gparts) * size_t(T) * size_t(r) * 4);
     p.off_dapart = off;
     off += r > 0 ? align256(size_t(p.mtiles) * size_t(r) * size_t(K) * 4) : 0;
+    p.off_dbpart = off;
+    off += r > 0 && p.dbchunks > 1 ? align256(size_t(p.dbchunks) * size_t(N) * size_t(r) * 4) : 0;
     p.off_dx = off;
     off += p.tail > 0 ? align256(size_t(p.pieces) * size_t(p.tail) * size_t(p.bm) * size_t(p.bn) * 4) : 0;
     p.ws_bytes = off;
@@ -506,7 +520,7 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
 
 hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* absmax, const uint16_t* wdense,
                            const uint16_t* dy, const uint16_t* x, const uint16_t* A, int64_t T, int64_t N, int64_t K,
-                           int r, float s, uint16_t* dx, float* dA, void* ws, hipStream_t stream) {
+                           int r, float s, uint16_t* dx, float* dA, float* dB, void* ws, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
     // without dx only the LoRA part runs: one workgroup per tile, no contraction steps
     BwdTiles tl{p.full, p.tail, p.pieces, p.steps_per_piece, p.mtiles};
@@ -528,11 +542,16 @@ hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const BwdFinishDx f{partial, tl.full, tl.tail, tl.pieces, p.mtiles, p.bm, p.bn, int(T), int(K)};
-    const int64_t dx_total = int64_t(tl.tail) * p.bm * p.bn, da_total = r > 0 ? int64_t(r) * K : 0;
-    const int64_t dx_blocks = cdiv(dx_total / 4, 256), da_blocks = cdiv(da_total / 4, 256);
-    if (dx_blocks + da_blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_bwd_finish, dim3(unsigned(dx_blocks + da_blocks)), dim3(256), 0, stream, f, dx, dx_blocks,
-                       dapart, p.mtiles, da_total, dA);
+    const int64_t dx_total = int64_t(tl.tail) * p.bm * p.bn;
+    const Shares da{dapart, p.mtiles, r > 0 ? int64_t(r) * K : 0, dA};
+    // dB shares (N * r is a multiple of 4: N % 16 == 0)
+    const Shares db{reinterpret_cast<const float*>(w + p.off_dbpart), p.dbchunks,
+                    r > 0 && p.dbchunks > 1 ? N * r : 0, dB};
+    const int64_t dx_blocks = cdiv(dx_total / 4, 256), da_blocks = cdiv(da.total / 4, 256),
+                  db_blocks = cdiv(db.total / 4, 256);
+    if (dx_blocks + da_blocks + db_blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_bwd_finish, dim3(unsigned(dx_blocks + da_blocks + db_blocks)), dim3(256), 0, stream, f, dx,
+                       dx_blocks, da, da_blocks, db);
     return hipGetLastError();
 }
 

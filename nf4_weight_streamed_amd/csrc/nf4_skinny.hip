@@ -597,7 +597,7 @@ __global__ __launch_bounds__(kThreads, kBOccupancy) void k_skinny_bwd(
     if (blk < gblocks)
         pre::g_role<RB>(dy, B, T, N, r, gsteps, blk, gpart, sm.pre.g);
     else if (blk < gblocks + dblocks)
-        pre::db_role<RB, pre::kTC>(dy, u, T, N, r, s, blk - gblocks, dB, sm.pre.d);
+        pre::db_role<RB, pre::kTC>(dy, u, T, N, r, s, blk - gblocks, 0, T, dB, sm.pre.d);
 }
 
 // Backward finish, two kinds of workgroups in one launch (64 features each, lane =
