@@ -208,6 +208,50 @@ def cpu_baseline(seconds_budget: float = 12.0) -> dict:
     }
 
 
+def quantize_measure(lib, torch, ev: "HipEvents", cpu: bool) -> dict:
+    """Load-time quantisation (not part of the step): the library's nf4_quantize on the
+    gate weight (18944 x 3584 bf16, N(0, 0.02)) in device time, against HBM bytes
+    2 + 0.5625 per parameter (bf16 read, codes + absmax written); with `cpu`, the
+    oracle's quantise on a bounded sample of the same weight beside it."""
+    n, k = INTER, HIDDEN
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    w = (torch.randn(n, k, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    codes = torch.empty(n, k // 2, dtype=torch.uint8, device="cuda")
+    absmax = torch.empty(n, k // 64, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        lib.quantize(w, codes, absmax)
+    reps = 10
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.record(e0, stream)
+    for _ in range(reps):
+        lib.quantize(w, codes, absmax)
+    ev.record(e1, stream)
+    us = ev.elapsed_ms(e0, e1) * 1e3 / reps
+    ev.destroy(e0)
+    ev.destroy(e1)
+    nbytes = n * k * (2 + 0.5625)
+    res = {"shape_NxK": [n, k], "gpu_us": round(us, 2), "gpu_params_per_s": round(n * k / us * 1e6, 1),
+           "hbm_gbs": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    if cpu:
+        import oracle as O
+
+        rows = 1024  # a bounded sample: the first rows of the same weight
+        ws = w[:rows].float().cpu().numpy()
+        t0, cnt = time.perf_counter(), 0
+        while cnt < 2 or time.perf_counter() - t0 < 3.0:
+            O.quantize(ws)
+            cnt += 1
+        dt = (time.perf_counter() - t0) / cnt
+        res["cpu_oracle_params_per_s"] = round(rows * k / dt, 1)
+        res["cpu_sample"] = f"oracle quantise of {rows} x {k} rows of the same weight, {dt * 1e3:.1f} ms per pass"
+    del w, codes, absmax
+    torch.cuda.empty_cache()
+    return res
+
+
 def measured_mfma_tflops(lib, torch, ev: "HipEvents") -> float:
     """bf16 MFMA issue rate with the GEMMs' instruction (v_mfma_f32_32x32x16_bf16): 512
     workgroups x 4 waves, each 8 independent MFMAs per round on registers."""
@@ -529,6 +573,7 @@ def main() -> int:
 
     mfma_meas = measured_mfma_tflops(lib, torch, ev)
     copy_meas = measured_copy_gbs(torch, ev)
+    quant = quantize_measure(lib, torch, ev, cpu=not args.no_cpu_baseline)
     ms = dt * 1000.0 / args.steps
     tokens_per_s = T_TOKENS / (dt / args.steps)
     tflops = step_flops(T_TOKENS, RANK) / (dt / args.steps) / 1e12
@@ -572,6 +617,7 @@ def main() -> int:
             "algorithmic_bytes_per_launch": gate_bytes,
             "hbm_gbs_algorithmic": round(gate_bytes / avg_gemm_s / 1e9, 1),
         },
+        "quantize": quant,
         "denominators": {
             "mfma_bf16_tflops_published": MFMA_BF16_PEAK_TFLOPS,
             "mfma_bf16_tflops_measured": round(mfma_meas, 1),
