@@ -41,10 +41,33 @@ __device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
     }
 }
 
+// code = #{j : q >= thresh[j]} for q = RN32(w / absmax) in [-1, 1], through 65 buckets
+// of width 1/32: bucket i = floor(32 q) + 32 (exact: 32 q is exact and so is the
+// floor) holds the count of thresholds at or below its lower edge and the one
+// threshold strictly inside it, if any (the thresholds are more than 1/32 apart), so a
+// single compare finishes the count.
+constexpr int kBuckets = 65;
+struct Bucket {
+    uint32_t below;  // thresholds <= the bucket's lower edge
+    float inside;    // the threshold inside the bucket, or +inf
+};
+
 template <typename In>
 __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const In* __restrict__ w, int64_t n_blocks,
                                                            uint32_t* __restrict__ codes32,
                                                            float* __restrict__ absmax, Tables tab) {
+    __shared__ Bucket buckets[kBuckets];
+    if (threadIdx.x < kBuckets) {
+        const float lo = float(int(threadIdx.x) - 32) * (1.0f / 32.0f), hi = lo + 1.0f / 32.0f;
+        uint32_t below = 0;
+        float inside = __builtin_inff();
+        for (int j = 0; j < 15; ++j) {
+            below += tab.thresh[j] <= lo ? 1u : 0u;
+            if (tab.thresh[j] > lo && tab.thresh[j] < hi) inside = tab.thresh[j];
+        }
+        buckets[threadIdx.x] = Bucket{below, inside};
+    }
+    __syncthreads();
     const int64_t gid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
     const int64_t blk = gid >> 3;
     const int sub = int(gid & 7);
@@ -69,9 +92,8 @@ __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const In* __restrict_
         uint32_t code = 7;  // all-zero block: every element takes the level 0
         if (m > 0.0f) {
             const float q = __fdiv_rn(v[i], m);  // correctly rounded float32 quotient
-            code = 0;
-#pragma unroll
-            for (int j = 0; j < 15; ++j) code += (q >= tab.thresh[j]) ? 1u : 0u;
+            const Bucket b = buckets[int(__builtin_floorf(q * 32.0f)) + 32];
+            code = b.below + (q >= b.inside ? 1u : 0u);
         }
         packed |= code << (4 * i);
     }
