@@ -44,6 +44,19 @@ def _edge_matrix():
     rows.append(rng.standard_cauchy(size=128))                       # heavy tails
     big = rng.normal(size=128); big[5] = 3.0e38; rows.append(big)    # near float32 max
     rows.append(np.concatenate([t, -t, t * 0.5, t[::-1]] * 2)[:128])  # every level
+    # quotients on and next to every multiple of 1/32 in [-1, 1] (each block holds 1.0,
+    # so its absmax is 1 and the quotient is the value itself), also scaled by 2^-3
+    grid = [k / 32.0 for k in range(-32, 33)]
+    vals = []
+    for g in grid:
+        g32 = np.float32(g)
+        vals += [float(g32), float(np.nextafter(g32, np.float32(2))), float(np.nextafter(g32, np.float32(-2)))]
+    vals = [v for v in vals if abs(v) <= 1.0]
+    blocks = [[1.0] + vals[i:i + 63] for i in range(0, len(vals), 63)]
+    flat = np.concatenate([np.pad(np.array(b), (0, 64 - len(b))) for b in blocks])
+    flat = np.pad(flat, (0, (-len(flat)) % 128))
+    for scale in (1.0, 0.125):
+        rows += list(flat.reshape(-1, 128) * scale)
     for e in (-30, -5, 0, 7):
         rows.append(rng.normal(size=128) * 2.0 ** e)
     return np.stack(rows).astype(np.float32)
