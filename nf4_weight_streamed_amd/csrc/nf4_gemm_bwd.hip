@@ -269,12 +269,14 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
         };
         uint32_t av[FK][8];
         load_a(0, av);
+        // this thread's x chunks: 8 consecutive tokens xt0 .. xt0+7 of columns xk8 .. xk8+7
+        static_assert(XC == 8 && BM == 16 * XC && BK == 16 * 8, "x tile: 16 x 16 chunk blocks of 8 x 8");
+        const int xk8 = 8 * (tid & 15), xt0 = 8 * (tid >> 4);
         u32x4 xv[XC];
 #pragma unroll
         for (int i = 0; i < XC; ++i) {
             // rows past T read zero; columns past K only feed dA columns never stored
-            const int c = tid + kThreads * i, t = c / (BK / 8), k8 = 8 * (c % (BK / 8));
-            xv[i] = buf_load16(rx, (uint32_t(t) * uint32_t(K) + uint32_t(k0 + k8)) * 2u);
+            xv[i] = buf_load16(rx, (uint32_t(xt0 + i) * uint32_t(K) + uint32_t(k0 + xk8)) * 2u);
         }
         constexpr int GR = 2;  // partials loaded per round
         for (int jb = 0; jb < rp / 16; ++jb) {
@@ -315,17 +317,19 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
             }
         }
         // x^T of columns 64 h .. 64 h + 63: a thread's chunks all sit in one half (their
-        // column offset is 8 (tid % 16))
+        // column offset is 8 (tid % 16)); the 8 x 8 block is transposed in registers
+        // (byte permutes pairing tokens) and written as one 16-byte row piece per column
         auto stage_x = [&](int h) {
             if (((tid & 15) >> 3) != h) return;
 #pragma unroll
-            for (int i = 0; i < XC; ++i) {
-                const int c = tid + kThreads * i, t = c / (BK / 8), k8 = 8 * (c % (BK / 8)) - 64 * h;
+            for (int e = 0; e < 8; ++e) {
+                // element e of chunks i and i + 1: low halves (e even) or high halves (e odd)
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                u32x4 col;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t w = xv[i][e >> 1];
-                    sxt[(k8 + e) * kTP + t] = uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF));
-                }
+                for (int p = 0; p < 4; ++p)
+                    col[p] = __builtin_amdgcn_perm(xv[2 * p + 1][e >> 1], xv[2 * p][e >> 1], sel);
+                *reinterpret_cast<u32x4*>(&sxt[(xk8 - 64 * h + e) * kTP + xt0]) = col;
             }
         };
         stage_x(0);
