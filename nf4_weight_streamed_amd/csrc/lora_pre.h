@@ -55,16 +55,32 @@ __device__ void g_role(const uint16_t* __restrict__ dy, const uint16_t* __restri
     const int kof = 8 * (lane >> 4);
     constexpr int BV = kGChunk * 16 * RB / kThreads;  // B values per thread per chunk
 
-    uint32_t bv[BV];
+    // B values of a chunk: with r % 4 == 0 thread (f, q) = (tid % 64, tid / 64) loads
+    // ranks 4 RB q .. 4 RB q + 4 RB - 1 of features 2f and 2f + 1 as 8-byte pieces and
+    // stores them as 4-byte feature pairs of B^T; otherwise one bf16 per load and store.
+    // Ranks past r read the next row's values or zero: they only reach g columns that
+    // are never written.
+    static_assert(BV == 8 * RB, "8 RB B values per thread per chunk");
+    const bool vec = (r & 3) == 0;
+    const int bf = tid & 63, bq = tid >> 6;
+    u32x2 bp[BV / 2];  // vector path: 2 RB pieces of 4 ranks; scalar path: one bf16 per dword
     u32x4 dv[2];
     auto gload = [&](int c) {
         const int n0 = c * kGChunk;
+        if (vec) {
 #pragma unroll
-        for (int i = 0; i < BV; ++i) {
-            const int o = tid + kThreads * i;  // o = n * 16 RB + j
-            const int n = o / (16 * RB), j = o % (16 * RB);
-            bv[i] = __builtin_amdgcn_raw_buffer_load_b16(
-                rb, int(j < r ? (uint32_t(n0 + n) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0);
+            for (int i = 0; i < 2 * RB; ++i) {  // piece i: feature 2 bf + (i & 1), ranks 4 RB bq + 4 (i / 2)
+                const int n = n0 + 2 * bf + (i & 1), j = 4 * RB * bq + 4 * (i >> 1);
+                bp[i] = buf_load8(rb, j < r ? (uint32_t(n) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < BV; ++i) {
+                const int o = tid + kThreads * i;  // o = n * 16 RB + j
+                const int n = o / (16 * RB), j = o % (16 * RB);
+                bp[i >> 1][i & 1] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rb, int(j < r ? (uint32_t(n0 + n) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0);
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -73,10 +89,24 @@ __device__ void g_role(const uint16_t* __restrict__ dy, const uint16_t* __restri
         }
     };
     auto bstore = [&](int buf) {
+        if (vec) {
+            // piece 2 i + f (rank quad i, feature 2 bf + f) holds ranks j, j + 1 in its
+            // first dword and j + 2, j + 3 in its second, j = 4 RB bq + 4 i
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = bp[2 * i][e >> 1], hi = bp[2 * i + 1][e >> 1];
+                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                    *reinterpret_cast<uint32_t*>(&sm.bt[buf][4 * RB * bq + 4 * i + e][2 * bf]) =
+                        __builtin_amdgcn_perm(hi, lo, sel);
+                }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < BV; ++i) {
             const int o = tid + kThreads * i;
-            sm.bt[buf][o % (16 * RB)][o / (16 * RB)] = uint16_t(bv[i]);
+            sm.bt[buf][o % (16 * RB)][o / (16 * RB)] = uint16_t(bp[i >> 1][i & 1]);
         }
     };
 
@@ -123,9 +153,16 @@ __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict
                         int blk, int t_begin, int t_end, float* __restrict__ dst, DbSmem<RB, DBT>& sm) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blk * 64;
-    const int lt = tid >> 3, ln8 = (tid & 7) * 8;  // 16-byte pieces: tokens lt + 32 i, features ln8 .. ln8 + 7
+    // dY: 16-byte pieces of tokens DV lt .. DV lt + DV - 1, features ln8 .. ln8 + 7 per
+    // thread, transposed in registers (byte permutes pairing tokens) into [n][t] rows
+    const int lt = tid >> 3, ln8 = (tid & 7) * 8;
     constexpr int DV = DBT / 32;                   // dY pieces per thread per sub-chunk
     constexpr int UV = DBT * 16 * RB / kThreads;   // u values per thread per sub-chunk
+    static_assert(DV == 1 || DV % 2 == 0, "dY pieces: one, or token pairs");
+    static_assert(UV % 2 == 0, "u values: token pairs");
+    // u: pair q of the thread is rank (tid + kThreads q) % 16 RB of tokens 2 tp, 2 tp + 1,
+    // tp = (tid + kThreads q) / 16 RB
+
     const auto rdy = make_rsrc(dy, uint32_t(T) * uint32_t(N) * 2u);
     const auto ru = make_rsrc(u, uint32_t(T) * uint32_t(r) * 4u);
     u32x4 vdy[DV];
@@ -133,34 +170,53 @@ __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict
     auto gload = [&](int t0) {
 #pragma unroll
         for (int i = 0; i < DV; ++i) {
-            const int t = t0 + lt + 32 * i;
+            const int t = t0 + DV * lt + i;
             const bool ok = t < t_end && n0 + ln8 < N;
             vdy[i] = buf_load16(rdy, ok ? (uint32_t(t) * uint32_t(N) + uint32_t(n0 + ln8)) * 2u : kOutOfRange);
         }
 #pragma unroll
         for (int i = 0; i < UV; ++i) {
-            const int o = tid + kThreads * i;  // o = t * 16 RB + j
-            const int t = o / (16 * RB), j = o % (16 * RB);
-            uv[i] = buf_load_f32(ru, (t0 + t < t_end && j < r) ? (uint32_t(t0 + t) * uint32_t(r) + uint32_t(j)) * 4u
-                                                               : kOutOfRange);
+            const int o = tid + kThreads * (i >> 1), j = o % (16 * RB), tp = o / (16 * RB);
+            const int t = t0 + 2 * tp + (i & 1);
+            uv[i] = buf_load_f32(ru, (t < t_end && j < r) ? (uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u
+                                                          : kOutOfRange);
         }
     };
     auto sstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < DV; ++i)
+        if constexpr (DV == 1) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t w = vdy[i][e >> 1];
-                sm.dyt[ln8 + e][lt + 32 * i] = uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF));
+                const uint32_t w = vdy[0][e >> 1];
+                sm.dyt[ln8 + e][lt] = uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF));
             }
+        } else {
 #pragma unroll
-        for (int i = 0; i < UV; ++i) {
-            const int o = tid + kThreads * i;
-            const int t = o / (16 * RB), j = o % (16 * RB);
-            __bf16 h, l;
-            split_bf16(s * uv[i], h, l);
-            sm.uh[j][t] = __builtin_bit_cast(uint16_t, h);
-            sm.ul[j][t] = __builtin_bit_cast(uint16_t, l);
+            for (int e = 0; e < 8; ++e) {
+                // element e of tokens 2p, 2p + 1: low halves (e even) or high halves (e odd)
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                uint32_t col[DV / 2];
+#pragma unroll
+                for (int p = 0; p < DV / 2; ++p)
+                    col[p] = __builtin_amdgcn_perm(vdy[2 * p + 1][e >> 1], vdy[2 * p][e >> 1], sel);
+                if constexpr (DV == 4)
+                    *reinterpret_cast<u32x2*>(&sm.dyt[ln8 + e][DV * lt]) = u32x2{col[0], col[1]};
+                else
+#pragma unroll
+                    for (int p = 0; p < DV / 2; ++p)
+                        *reinterpret_cast<uint32_t*>(&sm.dyt[ln8 + e][DV * lt + 2 * p]) = col[p];
+            }
+        }
+        // (s.u)^T hi / lo as bf16 token pairs
+#pragma unroll
+        for (int q = 0; q < UV / 2; ++q) {
+            const int o = tid + kThreads * q, j = o % (16 * RB), tp = o / (16 * RB);
+            __bf16 h0, l0, h1, l1;
+            split_bf16(s * uv[2 * q], h0, l0);
+            split_bf16(s * uv[2 * q + 1], h1, l1);
+            *reinterpret_cast<uint32_t*>(&sm.uh[j][2 * tp]) =
+                uint32_t(__builtin_bit_cast(uint16_t, h0)) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+            *reinterpret_cast<uint32_t*>(&sm.ul[j][2 * tp]) =
+                uint32_t(__builtin_bit_cast(uint16_t, l0)) | (uint32_t(__builtin_bit_cast(uint16_t, l1)) << 16);
         }
     };
     f32x4 acc[RB];
