@@ -6,6 +6,8 @@
 // Device functions for 256-thread workgroups, shared by the stand-alone pre-pass
 // kernel and the few-token backward kernel, which runs them beside its dX workgroups.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 #include "device.h"
 
@@ -40,9 +42,11 @@ struct DbSmem {
     uint16_t ul[16 * RB][DBT + 8];   // lo
 };
 
-template <int RB>
+// GRING chunks of loads in flight (1 or 2; 2 where the registers allow it)
+template <int RB, int GRING>
 __device__ void g_role(const uint16_t* __restrict__ dy, const uint16_t* __restrict__ B, int T, int N, int r,
                        int steps_per_part, int blk, float* __restrict__ gpart, GSmem<RB>& sm) {
+    static_assert(GRING == 1 || GRING == 2, "one or two chunks in flight");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tblocks = (T + kTC - 1) / kTC;
     const int t0 = (blk % tblocks) * kTC, part = blk / tblocks;
@@ -63,9 +67,14 @@ __device__ void g_role(const uint16_t* __restrict__ dy, const uint16_t* __restri
     static_assert(BV == 8 * RB, "8 RB B values per thread per chunk");
     const bool vec = (r & 3) == 0;
     const int bf = tid & 63, bq = tid >> 6;
-    u32x2 bp[BV / 2];  // vector path: 2 RB pieces of 4 ranks; scalar path: one bf16 per dword
-    u32x4 dv[2];
-    auto gload = [&](int c) {
+    struct Set {
+        u32x2 bp[BV / 2];  // vector path: 2 RB pieces of 4 ranks; scalar path: one bf16 per dword
+        u32x4 dv[2];
+    };
+    Set ring[GRING];
+    auto gload = [&](int c, Set& st) {
+        u32x2(&bp)[BV / 2] = st.bp;
+        u32x4(&dv)[2] = st.dv;
         const int n0 = c * kGChunk;
         if (vec) {
 #pragma unroll
@@ -88,7 +97,8 @@ __device__ void g_role(const uint16_t* __restrict__ dy, const uint16_t* __restri
             dv[kk] = buf_load16(rdy, n < N ? dyrow + uint32_t(n) * 2u : kOutOfRange);
         }
     };
-    auto bstore = [&](int buf) {
+    auto bstore = [&](int buf, const Set& st) {
+        const u32x2(&bp)[BV / 2] = st.bp;
         if (vec) {
             // piece 2 i + f (rank quad i, feature 2 bf + f) holds ranks j, j + 1 in its
             // first dword and j + 2, j + 3 in its second, j = 4 RB bq + 4 i
@@ -114,21 +124,36 @@ __device__ void g_role(const uint16_t* __restrict__ dy, const uint16_t* __restri
 #pragma unroll
     for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (c_begin < c_end) {
-        gload(c_begin);
-        bstore(0);
+#pragma unroll
+        for (int i = 0; i < GRING; ++i) gload(c_begin + i, ring[i]);  // past the range: unused data or zeros
+        bstore(0, ring[0]);
         __syncthreads();
-        for (int c = c_begin; c < c_end; ++c) {
+        // chunk c sits in ring slot S = (c - c_begin) % GRING (compile-time: the loop is
+        // unrolled by GRING); its loads are replaced by those of chunk c + GRING, and the
+        // next chunk's B^T (slot (S + 1) % GRING) goes to the other LDS buffer
+        auto step = [&](int c, auto s_) {
+            constexpr int S = decltype(s_)::value;
             const int buf = (c - c_begin) & 1;
-            const u32x4 d0 = dv[0], d1 = dv[1];
-            gload(c + 1);  // one chunk ahead; past the range: unused data or zeros
+            const u32x4 d0 = ring[S].dv[0], d1 = ring[S].dv[1];
+            gload(c + GRING, ring[S]);
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
                 const uint16_t* row = &sm.bt[buf][16 * b + (lane & 15)][64 * nh + kof];
                 acc[b] = mfma16x16x32(as_bf16x8(d0), as_bf16x8(*reinterpret_cast<const u32x4*>(row)), acc[b]);
                 acc[b] = mfma16x16x32(as_bf16x8(d1), as_bf16x8(*reinterpret_cast<const u32x4*>(row + 32)), acc[b]);
             }
-            bstore(buf ^ 1);
+            bstore(buf ^ 1, ring[(S + 1) % GRING]);
             __syncthreads();
+        };
+        int c = c_begin;
+        if constexpr (GRING == 2) {
+            for (; c + 1 < c_end; c += 2) {
+                step(c, std::integral_constant<int, 0>{});
+                step(c + 1, std::integral_constant<int, 1>{});
+            }
+            if (c < c_end) step(c, std::integral_constant<int, 0>{});
+        } else {
+            for (; c < c_end; ++c) step(c, std::integral_constant<int, 0>{});
         }
     }
 #pragma unroll

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void k_lora_bwd_pre(const uint16_t* __res
                                                            float* __restrict__ dB, float* __restrict__ dbpart) {
     __shared__ __align__(16) PreSmem<RB, pre::kDbTLong> sm;
     if (int(blockIdx.x) < gblocks) {
-        g_role<RB>(dy, B, T, N, r, gsteps, blockIdx.x, gpart, sm.g);
+        g_role<RB, (RB <= 2 ? 2 : 1)>(dy, B, T, N, r, gsteps, blockIdx.x, gpart, sm.g);  // two chunks in flight where the registers allow
         return;
     }
     const int nblocks = (N + 63) / 64, d = int(blockIdx.x) - gblocks;

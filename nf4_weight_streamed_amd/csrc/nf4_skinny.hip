@@ -595,7 +595,7 @@ __global__ __launch_bounds__(kThreads, kBOccupancy) void k_skinny_bwd(
     }
     const int blk = int(blockIdx.x) - dx_cols + pre_cols * int(blockIdx.y);
     if (blk < gblocks)
-        pre::g_role<RB>(dy, B, T, N, r, gsteps, blk, gpart, sm.pre.g);
+        pre::g_role<RB, 1>(dy, B, T, N, r, gsteps, blk, gpart, sm.pre.g);
     else if (blk < gblocks + dblocks)
         pre::db_role<RB, pre::kTC>(dy, u, T, N, r, s, blk - gblocks, 0, T, dB, sm.pre.d);
 }
