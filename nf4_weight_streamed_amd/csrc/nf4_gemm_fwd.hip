@@ -161,13 +161,16 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
         }
     };
     const char* lut = reinterpret_cast<const char*>(sLut);
+    // weight fragments of the current step; sub-step q of the next step is dequantised
+    // into wf[.][q] right after the MFMAs of sub-step q have read it (only its final
+    // packs wait for those MFMAs: the table reads and multiplies can run under them)
     bf16x8 wf[FN][4];
     // weight fragments of sub-step q (all FN fragments) from a register set
-    auto dequant_q = [&](const u32x4 (&cw)[FN][WP], const float (&sc)[FN], int q) {
+    auto dequant_q = [&](const u32x4 (&cw)[FN][WP], const float (&sc)[FN], int q, bf16x8 (&wo)[FN][4]) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             if constexpr (kDense) {
-                wf[j][q] = as_bf16x8(cw[j][q]);
+                wo[j][q] = as_bf16x8(cw[j][q]);
                 continue;
             }
             const uint32_t w = cw[j][0][q];
@@ -178,12 +181,8 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
                 // level * absmax in fp32, then RNbf: the format's two roundings
                 o[b] = pack_bf16x2(lv.x * sc[j], lv.y * sc[j]);
             }
-            wf[j][q] = as_bf16x8(o);
+            wo[j][q] = as_bf16x8(o);
         }
-    };
-    auto dequant = [&](const u32x4 (&cw)[FN][WP], const float (&sc)[FN]) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dequant_q(cw, sc, q);
     };
 
     f32x16 acc[FM][FN];
@@ -201,16 +200,21 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
         for (int i = 0; i < PW; ++i) gload_w(kb_begin + i, rc[i], rs[i]);
         store_x(ra[0], 0);
         __syncthreads();  // sLut and x tile 0 visible
-        dequant(rc[0], rs[0]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dequant_q(rc[0], rs[0], q, wf);
         // one K step; C = (kb - kb_begin) mod U at compile time (the loop is unrolled by U
-        // so that no register array is indexed at run time): LDS buffer C mod 2, x set
-        // C mod PX, weight set C mod PW. Loads are issued unconditionally (a step past the
-        // end reads data that is never used, or zeros beyond the buffer): with a fixed
-        // issue pattern the compiler's wait counts stay exact and never drain later loads.
+        // so that no register array is indexed at run time): LDS buffer C mod 2, x set C mod PX, weight set C mod PW. The body has no branch, so the
+        // scheduler can interleave the next step's dequantisation with the MFMAs: loads,
+        // the next step's dequantisation and its x store are all unconditional (a step
+        // past the end reads data that is never used, or zeros beyond the buffer, and
+        // writes the idle LDS buffer); with a fixed issue pattern the compiler's wait
+        // counts also stay exact and never drain later loads.
         auto step = [&](int kb, auto c_) {
             constexpr int C = decltype(c_)::value;
-            const bool more = kb + 1 < kb_end;
             gload_x(kb + PX, ra[C % PX]);               // that set was stored into LDS last step
+            // x first: the x store at the end of the step waits on the in-order load
+            // counter, which must not also drain the weights loaded PW steps ahead
+            __builtin_amdgcn_sched_barrier(0);
             gload_w(kb + PW, rc[C % PW], rs[C % PW]);   // that set is this step's, already dequantised
             // keep the loads here, ahead of the MFMAs: sinking them next to their use
             // would expose their full latency
@@ -225,11 +229,15 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
 #pragma unroll
                     for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(af, wf[j][kk], acc[i][j]);
                 }
+                // sub-step kk of the next step's weights, independent of the MFMAs
+                dequant_q(rc[(C + 1) % PW], rs[(C + 1) % PW], kk, wf);
             }
-            if (more) {
-                dequant(rc[(C + 1) % PW], rs[(C + 1) % PW]);  // next step's weights, independent of the MFMAs
-                store_x(ra[(C + 1) % PX], (C + 1) & 1);
-            }
+            // interleave the fragment and table reads, multiplies and MFMAs of the step
+            // (the scheduler's small-GEMM strategy keeps several LDS reads in flight under
+            // the MFMAs; without it each read waits for the previous one). NF4 only: the
+            // dense variant's larger weight registers would spill under it.
+            if constexpr (!kDense) __builtin_amdgcn_iglp_opt(0);
+            store_x(ra[(C + 1) % PX], (C + 1) & 1);
             __syncthreads();
         };
         int kb = kb_begin;
