@@ -381,18 +381,21 @@ SMALL_T_SHAPES = [  # (model, projection, N, K)
 ]
 
 
-def small_t_sweep(lib, torch, ev: "HipEvents", reps: int = 8) -> dict:
+def small_t_sweep(lib, torch, ev: "HipEvents", reps: int = 8, shapes=None, tokens=None) -> dict:
     """Device time of one projection's forward and backward at T in {1, 8, 16, 32, 64}
     against HBM bytes = 1.125NK + T(6K + 4N + 8r) + 8r(N + K) (the base is read once in
     the forward and once in the backward). Four weight sets (>= 512 MB for the large
     shapes) are cycled so that the 256 MB last-level cache cannot serve repeated reads.
     Device time comes from replaying the calls captured in one graph; the eager loop's
-    time (host launches included) is reported beside it."""
+    time (host launches included) is reported beside it. `shapes` ("model:proj" names)
+    and `tokens` restrict the sweep (e.g. for a short profiled run)."""
     g = torch.Generator(device="cuda")
     g.manual_seed(42)
     stream = torch.cuda.current_stream().cuda_stream
     rows = []
     for model, proj, n, k in SMALL_T_SHAPES:
+        if shapes and f"{model}:{proj}" not in shapes:
+            continue
         nsets = 4 if n * k * 0.5625 * 4 >= 512e6 else max(4, int(512e6 // (n * k * 0.5625)) + 1)
         sets = []
         for _ in range(nsets):
@@ -402,6 +405,8 @@ def small_t_sweep(lib, torch, ev: "HipEvents", reps: int = 8) -> dict:
         a = ((torch.rand(RANK, k, generator=g, device="cuda") * 2 - 1) / k ** 0.5).to(torch.bfloat16)
         b = (torch.randn(n, RANK, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
         for t in SMALL_T:
+            if tokens and t not in tokens:
+                continue
             x = torch.randn(t, k, generator=g, device="cuda").to(torch.bfloat16)
             dy = torch.randn(t, n, generator=g, device="cuda").to(torch.bfloat16)
             y = torch.empty(t, n, dtype=torch.bfloat16, device="cuda")
@@ -513,6 +518,9 @@ def main() -> int:
     ap.add_argument("--stack-steps", type=int, default=3)
     ap.add_argument("--small-t-sweep", action="store_true",
                     help="instead of the layer step: per-projection fwd/bwd device time at T = 1..64 vs HBM bytes")
+    ap.add_argument("--sweep-shapes", default="",
+                    help="comma-separated model:projection names the small-T sweep is restricted to (e.g. 72b:gate)")
+    ap.add_argument("--sweep-tokens", default="", help="comma-separated token counts the small-T sweep is restricted to")
     ap.add_argument("--merge", action="store_true",
                     help="instead of the layer step: merge_and_unload (dense W + s.B.A) device time vs HBM bytes")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -528,9 +536,13 @@ def main() -> int:
     from nf4_weight_streamed_amd import lib
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
     if args.small_t_sweep:
         ev = HipEvents()
-        sweep = small_t_sweep(lib, torch, ev)
+        shapes = [v for v in args.sweep_shapes.split(",") if v]
+        tokens = [int(v) for v in args.sweep_tokens.split(",") if v]
+        sweep = small_t_sweep(lib, torch, ev, shapes=shapes, tokens=tokens)
         copy_meas = measured_copy_gbs(torch, ev)
         for row in sweep["rows"]:
             row["hbm_frac_vs_measured_copy"] = round(row["hbm_gbs"] / copy_meas, 4)
@@ -549,8 +561,6 @@ def main() -> int:
         print(json.dumps({"metric": "merge_and_unload device time; % of HBM roofline", "n_gpus": 1, "dtype": "bf16",
                           "data": "synthetic", "merge": res}), flush=True)
         return 0
-    if args.copy_calibration:
-        copy_calibration(torch)
     layer = build_layer(lib, torch)
     ev = HipEvents()
     for _ in range(args.warmup):

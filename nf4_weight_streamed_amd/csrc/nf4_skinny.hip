@@ -140,7 +140,7 @@ __device__ __forceinline__ void skinny_fwd_weights(const uint16_t* __restrict__ 
             const int buf = (kb - kb_begin) & 1;
             gload(kb + R - 1, ring[(C + R - 1) % R]);  // R - 1 steps ahead; past the range: unused or zeros
             __builtin_amdgcn_sched_barrier(0);
-            const Set& cur = ring[C];
+            const Set& cur = ring[C % R];
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 bf16x8 bw[2];
@@ -445,17 +445,17 @@ struct BwdSmem {
 
 __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes,
                                               const float* __restrict__ absmax, int T, int N, int K,
-                                              int steps_per_split, float* __restrict__ dxpart, const Tables& tab,
-                                              BwdSmem& sm) {
+                                              int steps_per_split, int col, int split, float* __restrict__ dxpart,
+                                              const Tables& tab, BwdSmem& sm) {
     float* sLut = sm.lut;
     auto& sSc = sm.sc;
     auto& sRed = sm.red;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q = lane >> 4;
-    const int k0 = int(blockIdx.x) * kBCols;
+    const int k0 = col * kBCols;
     const int nsteps = (N + kBRows - 1) / kBRows;
-    const int s_begin = int(blockIdx.y) * steps_per_split;
+    const int s_begin = split * steps_per_split;
     const int s_end = min(s_begin + steps_per_split, nsteps);
     const int nw = max(0, (s_end - s_begin - wave + 3) / 4);  // this wave's steps
     sLut[2 * tid] = tab.level[tid & 15];
@@ -503,7 +503,7 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
             constexpr int C = decltype(c_)::value;
             gload(i + R - 1, ring[(C + R - 1) % R]);  // R - 1 steps ahead; past the range: unused or zeros
             __builtin_amdgcn_sched_barrier(0);
-            const Set& cur = ring[C];
+            const Set& cur = ring[C % R];
             // the wave's LDS slice: written and read by this wave only, in program order
             ssc[(lane & 3) * kBRows + (lane >> 2)] = cur.sc[0];
             ssc[(lane & 3) * kBRows + 16 + (lane >> 2)] = cur.sc[1];
@@ -569,31 +569,34 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
     __syncthreads();
     const int k = k0 + tid;
     if (k < K) {
-        float* dst = dxpart + size_t(blockIdx.y) * T * K + k;
+        float* dst = dxpart + size_t(split) * T * K + k;
         for (int t = 0; t < T; ++t) dst[size_t(t) * K] = sRed[0][t][tid] + sRed[1][t][tid];
     }
 }
 
-// The backward launch: grid (dx_cols + pre_cols, splits). Columns below dx_cols are dX
-// workgroups (column block x split); the rest run the LoRA pre-pass roles, numbered
-// (x - dx_cols) + pre_cols . y: g workgroups [0, gblocks), dB workgroups
-// [gblocks, gblocks + dblocks), the remainder exit. The roles share no data inside the
-// launch (g is summed by the finish kernel, dB is final).
+// The backward launch: a 1-D grid of dx_total = dx_cols x splits dX workgroups (one
+// column block and split each), then the LoRA pre-pass roles, numbered from dx_total:
+// g workgroups [0, gblocks), dB workgroups [gblocks, gblocks + dblocks). The roles share
+// no data inside the launch (g is summed by the finish kernel, dB is final).
 template <int RB>
 __global__ __launch_bounds__(kThreads, kBOccupancy) void k_skinny_bwd(
     const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
     const uint16_t* __restrict__ B, const float* __restrict__ u, int T, int N, int K, int r, float s,
-    int steps_per_split, int dx_cols, int pre_cols, int gsteps, int gblocks, int dblocks, float* __restrict__ dxpart,
+    int steps_per_split, int dx_cols, int dx_total, int gsteps, int gblocks, int dblocks, float* __restrict__ dxpart,
     float* __restrict__ gpart, float* __restrict__ dB, Tables tab) {
     __shared__ __align__(16) union {
         BwdSmem dx;
         pre::PreSmem<RB, pre::kTC> pre;
     } sm;
-    if (int(blockIdx.x) < dx_cols) {
-        skinny_bwd_dx(dy, codes, absmax, T, N, K, steps_per_split, dxpart, tab, sm.dx);
+    // dX workgroups in an XCD-aware order (each XCD runs a contiguous range of (column
+    // block, split) pairs, column block fastest): the eight column blocks whose scales
+    // share one 128-byte line of a row then read it through one L2
+    if (int(blockIdx.x) < dx_total) {
+        const int t = int(xcd_tile_order(blockIdx.x, uint32_t(dx_total)));
+        skinny_bwd_dx(dy, codes, absmax, T, N, K, steps_per_split, t % dx_cols, t / dx_cols, dxpart, tab, sm.dx);
         return;
     }
-    const int blk = int(blockIdx.x) - dx_cols + pre_cols * int(blockIdx.y);
+    const int blk = int(blockIdx.x) - dx_total;
     if (blk < gblocks)
         pre::g_role<RB, 1>(dy, B, T, N, r, gsteps, blk, gpart, sm.pre.g);
     else if (blk < gblocks + dblocks)
@@ -753,19 +756,19 @@ hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8
     const int splits = dx ? p.splits : 1;
     const int gblocks = r > 0 ? int(cdiv(T, pre::kTC)) * bp.gparts : 0;
     const int dblocks = r > 0 ? int(cdiv(N, 64)) : 0;
-    const int pre_cols = int(cdiv(gblocks + dblocks, splits));
-    if (dx_cols + pre_cols > 0) {
-        const dim3 grid(unsigned(dx_cols + pre_cols), unsigned(splits));
+    const int dx_total = dx_cols * splits;
+    if (dx_total + gblocks + dblocks > 0) {
+        const dim3 grid(unsigned(dx_total + gblocks + dblocks));
         if (dx) prof_gemm_begin(stream);
         switch (std::max(1, (r + 15) / 16)) {
             case 1: hipLaunchKernelGGL(k_skinny_bwd<1>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
-                                       p.steps_per_split, dx_cols, pre_cols, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
+                                       p.steps_per_split, dx_cols, dx_total, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
             case 2: hipLaunchKernelGGL(k_skinny_bwd<2>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
-                                       p.steps_per_split, dx_cols, pre_cols, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
+                                       p.steps_per_split, dx_cols, dx_total, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
             case 3: hipLaunchKernelGGL(k_skinny_bwd<3>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
-                                       p.steps_per_split, dx_cols, pre_cols, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
+                                       p.steps_per_split, dx_cols, dx_total, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
             default: hipLaunchKernelGGL(k_skinny_bwd<4>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
-                                        p.steps_per_split, dx_cols, pre_cols, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
+                                        p.steps_per_split, dx_cols, dx_total, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
         }
         if (dx) prof_gemm_end(stream);
         hipError_t e = hipGetLastError();
