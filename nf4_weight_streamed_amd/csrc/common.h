@@ -64,6 +64,7 @@ struct FwdPlan {
     int bm, bn;           // GEMM workgroup tile (tokens x out features)
     int full, tail;       // whole tiles, split tiles
     int pieces, steps_per_piece;
+    int bal_a, bal_pa;    // balanced split: the first bal_a split tiles in bal_pa pieces, the rest in pieces (0: off)
     int mtiles;           // token tiles
     int down_parts;       // K ranges of u = x.A^T (partials summed by the GEMM); 0 if r == 0
     int down_steps;       // 32-wide K steps per range
@@ -85,6 +86,7 @@ struct BwdPlan {
     int bm, bn;            // dX tile (tokens x in features)
     int full, tail;        // whole tiles, split tiles
     int pieces, steps_per_piece;
+    int bal_a, bal_pa;     // balanced split (as in FwdPlan)
     int mtiles, ktiles;    // dX tile grid
     int gparts, gsteps;    // N ranges of g = dY.B (partials summed by the GEMM), 128-feature chunks each
     int dbchunks, dbtokens;  // token ranges of dB (1: written directly), tokens each
@@ -140,5 +142,22 @@ inline int64_t pick_splits(int64_t tiles, int64_t steps, int64_t min_steps) {
     return std::max<int64_t>(1, s);
 }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Balanced split for fewer tiles than CUs: 2 x cus workgroups, `a` tiles cut into pa
+// pieces and the other tiles - cut into pa + 1, with every piece at least min_steps
+// long. The dispatcher gives linear workgroup ids L and L + cus the same CU, so with
+// the a * pa longer pieces (at most cus of them) in the first round and only shorter
+// ones in the second, every CU runs one longer and one shorter piece or two shorter
+// ones: tiles = 112 gives at most 74 + 60 K steps per CU for 296 steps per tile,
+// against 2 x 74 for four pieces each (448 workgroups, 192 CUs with two). False when
+// it does not apply (then the uniform split stands).
+inline bool pick_balanced(int64_t tiles, int64_t steps, int64_t min_steps, int64_t cus, int64_t& a, int64_t& pa) {
+    if (tiles <= 0 || tiles >= cus) return false;
+    const int64_t p = 2 * cus / tiles, b = 2 * cus - p * tiles, aa = tiles - b;
+    if (b <= 0 || aa <= 0 || aa * p > cus || (p + 1) * min_steps > steps) return false;
+    a = aa;
+    pa = p;
+    return true;
+}
 
 }  // namespace nf4

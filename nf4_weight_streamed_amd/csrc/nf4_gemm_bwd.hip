@@ -48,6 +48,7 @@ constexpr int64_t kCUs = 256;
 struct BwdTiles {
     int full, tail, pieces, steps_per_piece;
     int mtiles;  // token tiles (tile index = token tile + mtiles * column tile)
+    int bal_a, bal_pa;  // balanced split of all tiles (balanced_piece), 0: off
 };
 
 struct BwdLora {
@@ -92,6 +93,11 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
     float* ptile = nullptr;  // fp32 partial tile of a split tile
     if (int(blockIdx.x) < tl.full) {
         tile = int(xcd_tile_order(blockIdx.x, uint32_t(tl.full)));
+    } else if (tl.bal_a > 0) {
+        int q;
+        balanced_piece(blockIdx.x - uint32_t(tl.full), tl.tail, tl.bal_a, tl.bal_pa, nsteps, q, tz, nb_begin, nb_end);
+        tile = tl.full + q;
+        ptile = partial + (size_t(tz) * tl.tail + q) * (BM * BK);
     } else {
         const int u = int(xcd_tile_order(blockIdx.x - uint32_t(tl.full), uint32_t(tl.tail * tl.pieces)));
         const int q = u % tl.tail;
@@ -430,6 +436,7 @@ struct BwdFinishDx {
     const float* part;  // [pieces][tail][BM * BK]
     int full, tail, pieces, mtiles, bm, bk;
     int T, K;
+    int bal_a, bal_pa;  // balanced split: tiles below bal_a have bal_pa pieces
 };
 struct Shares {  // dst[i] = ((src[0][i] + src[1][i]) + src[2][i]) + ...
     const float* src;
@@ -458,7 +465,8 @@ __global__ __launch_bounds__(256) void k_bwd_finish(BwdFinishDx f, uint16_t* __r
         const int row = (tile % f.mtiles) * f.bm + loc / f.bk, col = (tile / f.mtiles) * f.bk + loc % f.bk;
         if (row >= f.T || col >= f.K) return;  // K % 64 == 0: the four columns are all in or all out
         f32x4 a = *reinterpret_cast<const f32x4*>(f.part + idx);
-        for (int z = 1; z < f.pieces; ++z) a += *reinterpret_cast<const f32x4*>(f.part + z * total + idx);
+        const int np = q < f.bal_a ? f.bal_pa : f.pieces;
+        for (int z = 1; z < np; ++z) a += *reinterpret_cast<const f32x4*>(f.part + z * total + idx);
         const u32x2 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
         *reinterpret_cast<u32x2*>(dx + size_t(row) * f.K + col) = o;
     } else if (b < dx_blocks + da_blocks) {
@@ -491,9 +499,12 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     // of 256 tiles (one more per CU each) run whole, and a last round of at most 128
     // tiles is split into pieces that spread over the CUs: the time of a CU grows with
     // the tiles it holds, so 2 whole tiles + a third of one beat 3 whole tiles.
-    int64_t tail = 0, pieces = 1;
+    int64_t tail = 0, pieces = 1, bal_a = 0, bal_pa = 0;
     const int64_t splits = pick_splits(tiles, nsteps, 4);
-    if (splits > 1) {
+    if (pick_balanced(tiles, nsteps, 4, kCUs, bal_a, bal_pa)) {
+        tail = tiles;
+        pieces = bal_pa + 1;
+    } else if (splits > 1) {
         tail = tiles;
         pieces = splits;
     } else if (tiles > kCUs) {
@@ -506,6 +517,12 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     }
     p.steps_per_piece = int(cdiv(nsteps, pieces));
     p.pieces = tail > 0 ? int(cdiv(nsteps, p.steps_per_piece)) : 1;
+    p.bal_a = int(bal_a);
+    p.bal_pa = int(bal_pa);
+    if (bal_a > 0) {  // piece bounds come from balanced_piece; the slot count is bal_pa + 1
+        p.pieces = int(pieces);
+        p.steps_per_piece = 0;
+    }
     p.tail = int(tail);
     p.full = int(tiles - tail);  // 0 or a multiple of kCUs (a multiple of the XCD count)
     if (r > 0) plan_lora_bwd_pre(p, T, N, kMaxGParts);
@@ -527,9 +544,9 @@ hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* 
                            int r, float s, uint16_t* dx, float* dA, float* dB, void* ws, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
     // without dx only the LoRA part runs: one workgroup per tile, no contraction steps
-    BwdTiles tl{p.full, p.tail, p.pieces, p.steps_per_piece, p.mtiles};
-    if (!dx) tl = BwdTiles{p.mtiles * p.ktiles, 0, 1, 0, p.mtiles};
-    const dim3 grid(unsigned(tl.full + tl.tail * tl.pieces));
+    BwdTiles tl{p.full, p.tail, p.pieces, p.steps_per_piece, p.mtiles, p.bal_a, p.bal_pa};
+    if (!dx) tl = BwdTiles{p.mtiles * p.ktiles, 0, 1, 0, p.mtiles, 0, 0};
+    const dim3 grid(unsigned(tl.full + (tl.bal_a > 0 ? 2 * kCUs : int64_t(tl.tail) * tl.pieces)));
     float* partial = tl.tail > 0 ? reinterpret_cast<float*>(w + p.off_dx) : nullptr;
     float* dapart = reinterpret_cast<float*>(w + p.off_dapart);
     const BwdLora lora{reinterpret_cast<const float*>(w + p.off_gpart), p.gparts, A, x, dapart, r, s};
@@ -545,7 +562,7 @@ hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* 
     if (dx) prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const BwdFinishDx f{partial, tl.full, tl.tail, tl.pieces, p.mtiles, p.bm, p.bn, int(T), int(K)};
+    const BwdFinishDx f{partial, tl.full, tl.tail, tl.pieces, p.mtiles, p.bm, p.bn, int(T), int(K), tl.bal_a, tl.bal_pa};
     const int64_t dx_total = int64_t(tl.tail) * p.bm * p.bn;
     const Shares da{dapart, p.mtiles, r > 0 ? int64_t(r) * K : 0, dA};
     // dB shares (N * r is a multiple of 4: N % 16 == 0)

@@ -67,6 +67,7 @@ struct FwdLora {
 struct FwdTiles {
     int full, tail, pieces, steps_per_piece;
     int mtiles;  // token tiles (tile index = token tile + mtiles * column tile)
+    int bal_a, bal_pa;  // balanced split of all tiles (balanced_piece), 0: off
 };
 
 template <int NW, bool kDense>
@@ -90,6 +91,11 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
     float* ptile = nullptr;  // fp32 partial tile of a split tile
     if (int(blockIdx.x) < tl.full) {
         tile = int(xcd_tile_order(blockIdx.x, uint32_t(tl.full)));
+    } else if (tl.bal_a > 0) {
+        int q;
+        balanced_piece(blockIdx.x - uint32_t(tl.full), tl.tail, tl.bal_a, tl.bal_pa, ksteps, q, tz, kb_begin, kb_end);
+        tile = tl.full + q;
+        ptile = partial + (size_t(tz) * tl.tail + q) * (BM * BN);
     } else {
         const int u = int(xcd_tile_order(blockIdx.x - uint32_t(tl.full), uint32_t(tl.tail * tl.pieces)));
         const int q = u % tl.tail;
@@ -399,6 +405,7 @@ struct SplitTiles {
     const float* part;  // [pieces][tail][BM * BN]
     int full, tail, pieces, mtiles, bm, bn;
     int T, N;
+    int bal_a, bal_pa;  // balanced split: tiles below bal_a have bal_pa pieces
 };
 
 __global__ __launch_bounds__(256) void k_split_sum_bf16(SplitTiles f, uint16_t* __restrict__ out) {
@@ -411,7 +418,8 @@ __global__ __launch_bounds__(256) void k_split_sum_bf16(SplitTiles f, uint16_t* 
     const int row = (tile % f.mtiles) * f.bm + loc / f.bn, col = (tile / f.mtiles) * f.bn + loc % f.bn;
     if (row >= f.T || col >= f.N) return;  // N % 16 == 0: the four columns are all in or all out
     f32x4 a = *reinterpret_cast<const f32x4*>(f.part + idx);
-    for (int z = 1; z < f.pieces; ++z) a += *reinterpret_cast<const f32x4*>(f.part + z * total + idx);
+    const int np = q < f.bal_a ? f.bal_pa : f.pieces;
+    for (int z = 1; z < np; ++z) a += *reinterpret_cast<const f32x4*>(f.part + z * total + idx);
     const u32x2 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
     *reinterpret_cast<u32x2*>(out + size_t(row) * f.N + col) = o;
 }
@@ -435,9 +443,12 @@ FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     // of 256 tiles (one more per CU each) run whole, and a last round of at most 128
     // tiles is split into pieces that spread over the CUs: the time of a CU grows with
     // the tiles it holds, so 2 whole tiles + a third of one beat 3 whole tiles.
-    int64_t tail = 0, pieces = 1;
+    int64_t tail = 0, pieces = 1, bal_a = 0, bal_pa = 0;
     const int64_t splits = pick_splits(tiles, ksteps, 4);
-    if (splits > 1) {
+    if (pick_balanced(tiles, ksteps, 4, kCUs, bal_a, bal_pa)) {
+        tail = tiles;
+        pieces = bal_pa + 1;
+    } else if (splits > 1) {
         tail = tiles;
         pieces = splits;
     } else if (tiles > kCUs) {
@@ -450,6 +461,12 @@ FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     }
     p.steps_per_piece = int(cdiv(ksteps, pieces));
     p.pieces = tail > 0 ? int(cdiv(ksteps, p.steps_per_piece)) : 1;
+    p.bal_a = int(bal_a);
+    p.bal_pa = int(bal_pa);
+    if (bal_a > 0) {  // piece bounds come from balanced_piece; the slot count is bal_pa + 1
+        p.pieces = int(pieces);
+        p.steps_per_piece = 0;
+    }
     p.tail = int(tail);
     p.full = int(tiles - tail);  // 0 or a multiple of kCUs (a multiple of the XCD count)
     if (r > 0) plan_lora_down(p, K);
@@ -466,8 +483,8 @@ hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* 
                            const uint16_t* x, const uint16_t* B, int64_t T, int64_t N, int64_t K, int r, float s,
                            uint16_t* y, float* u_save, void* ws, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
-    const FwdTiles tl{p.full, p.tail, p.pieces, p.steps_per_piece, p.mtiles};
-    const dim3 grid(unsigned(p.full + p.tail * p.pieces));
+    const FwdTiles tl{p.full, p.tail, p.pieces, p.steps_per_piece, p.mtiles, p.bal_a, p.bal_pa};
+    const dim3 grid(unsigned(p.full + (p.bal_a > 0 ? 2 * kCUs : int64_t(p.tail) * p.pieces)));
     float* partial = p.tail > 0 ? reinterpret_cast<float*>(w + p.off_ypart) : nullptr;
     const FwdLora lora{r > 0 ? reinterpret_cast<const float*>(w + p.off_upart) : nullptr, p.down_parts, u_save, B,
                        r, s};
@@ -483,7 +500,7 @@ hipError_t launch_gemm_fwd(const FwdPlan& p, const uint8_t* codes, const float* 
     prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.tail == 0) return e;
-    const SplitTiles f{partial, p.full, p.tail, p.pieces, p.mtiles, p.bm, p.bn, int(T), int(N)};
+    const SplitTiles f{partial, p.full, p.tail, p.pieces, p.mtiles, p.bm, p.bn, int(T), int(N), p.bal_a, p.bal_pa};
     const int64_t total = int64_t(p.tail) * p.bm * p.bn;
     hipLaunchKernelGGL(k_split_sum_bf16, dim3(unsigned(cdiv(total / 4, 256))), dim3(256), 0, stream, f, y);
     return hipGetLastError();

@@ -70,6 +70,8 @@ def test_single_linear_workload(gpu_lib):
     (40, 1040, 8256, 7),     # same with an odd step count over K and an odd rank
     (300, 640, 22976, 16),   # 540 dX tiles: a whole round of 512, the last 28 (ragged) split over N
     (300, 10992, 640, 16),   # 258 y tiles: a whole round of 256, the last 2 (ragged) split over K
+    (512, 3584, 3584, 16),   # q-shaped at 512 tokens: 112 tiles, balanced two-round split in both GEMMs
+    (200, 7040, 1600, 16),   # balanced split with ragged tokens and K: 110 y tiles (25 K steps), 26 dX tiles
 ])
 def test_shapes(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
