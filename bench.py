@@ -306,10 +306,11 @@ def pinned_h2d_gbs(torch, nbytes: int = 1 << 30) -> float:
 
 
 def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2d_gbs: float,
-                 base_kind: str = "nf4") -> dict:
+                 base_kind: str = "nf4", n_slots: int = 2) -> dict:
     """Streamed vs resident step time of a Qwen2.5-shaped identity-mixing stack, with
     the bitwise check, H2D traffic and copy/compute overlap. base_kind "bf16" streams a
-    dense bf16 base (the experimental bf16_bitwise mode) instead of NF4."""
+    dense bf16 base (the experimental bf16_bitwise mode) instead of NF4. n_slots = device
+    pool slots of one block each (the streamed runs; the resident run holds every block)."""
     from nf4_weight_streamed_amd import stack as ST
 
     dims, n_layers = ST.QWEN25[model]
@@ -327,7 +328,7 @@ def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2
     # each block's forward recomputed in its backward visit)
     for mode, remat, key in (("resident", False, "resident"), ("streamed", False, "streamed"),
                              ("streamed", True, "remat")):
-        st = ST.NF4Stack(base, lora, tokens, ALPHA, mode=mode, remat=remat)
+        st = ST.NF4Stack(base, lora, tokens, ALPHA, mode=mode, remat=remat, n_slots=n_slots)
         y, dx = st.step(h0, dh)                       # warmup (and the parity sample)
         torch.cuda.synchronize()
         out[key + "_y"], out[key + "_dx"] = y.clone(), dx.clone()
@@ -344,7 +345,8 @@ def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2
     copy_s = nbytes / (h2d_gbs * 1e9)
     overlap = (r_s + copy_s - s_s) / min(r_s, copy_s) if min(r_s, copy_s) > 0 else None
     return {
-        "workload": f"qwen2.5-{model}-shaped stack, {n_layers} layers, block_size {block_size}, {tokens} tokens, "
+        "workload": f"qwen2.5-{model}-shaped stack, {n_layers} layers, block_size {block_size}, {n_slots} pool slots, "
+                    f"{tokens} tokens, "
                     f"{'dense bf16' if base_kind == 'bf16' else 'NF4'} in pinned host, identity attention mixing, fwd+bwd",
         "bitwise_equal_to_resident": bool(torch.equal(out["resident_y"], out["streamed_y"])
                                           and torch.equal(out["resident_dx"], out["streamed_dx"])),
@@ -512,6 +514,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--streamed", default="7b", help="stack for the streamed measurement: 7b, 32b, 72b or none")
     ap.add_argument("--block-size", type=int, default=4)
+    ap.add_argument("--slots", type=int, default=2, help="device pool slots (blocks) of the streamed stack")
     ap.add_argument("--stream-base", default="nf4", choices=("nf4", "bf16"),
                     help="format of the streamed base: nf4, or dense bf16 (the bf16_bitwise mode)")
     ap.add_argument("--stack-tokens", type=int, default=512)
@@ -640,7 +643,7 @@ def main() -> int:
         torch.cuda.empty_cache()
         h2d = pinned_h2d_gbs(torch)
         out["streamed"] = stream_bench(torch, args.streamed, args.block_size, args.stack_tokens, args.stack_steps, h2d,
-                                       args.stream_base)
+                                       args.stream_base, args.slots)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
