@@ -319,6 +319,7 @@ def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2
     base = host_cls(dims, n_layers, block_size, ST.qwen_weight_fn())
     lora = ST.LoraParams(dims, n_layers, RANK, ST.qwen_lora_fn())
     build_s = time.perf_counter() - t0
+    print(f"[stream_bench] {model}: host base built in {build_s:.1f} s", file=sys.stderr, flush=True)
     g = torch.Generator(device="cuda")
     g.manual_seed(42)
     h0 = torch.randn(tokens, dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
@@ -340,6 +341,7 @@ def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2
         st.close()
         del st
         torch.cuda.empty_cache()
+        print(f"[stream_bench] {model}: {key} {secs * 1e3:.1f} ms per step", file=sys.stderr, flush=True)
     flops = n_layers * sum(4 * tokens * n * k + 6 * tokens * RANK * (n + k) for n, k in dims.shapes().values())
     r_s, s_s, nbytes = out["resident_s"], out["streamed_s"], out["streamed_bytes"]
     copy_s = nbytes / (h2d_gbs * 1e9)
