@@ -72,6 +72,8 @@ def test_single_linear_workload(gpu_lib):
     (300, 10992, 640, 16),   # 258 y tiles: a whole round of 256, the last 2 (ragged) split over K
     (512, 3584, 3584, 16),   # q-shaped at 512 tokens: 112 tiles, balanced two-round split in both GEMMs
     (200, 7040, 1600, 16),   # balanced split with ragged tokens and K: 110 y tiles (25 K steps), 26 dX tiles
+    (512, 8192, 1024, 16),   # exactly 256 y tiles: split in two over K
+    (512, 1024, 8192, 16),   # exactly 256 dX tiles: split in two over N
 ])
 def test_shapes(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
