@@ -145,6 +145,28 @@ inline int64_t pick_splits(int64_t tiles, int64_t steps, int64_t min_steps) {
 }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Pieces per tile for the `last` tiles of a final, partial round of `cus` tiles (one
+// workgroup per tile otherwise). At most half a round: one piece per CU (cus / last
+// pieces each). More than half: the piece count (2..4) that puts the least work on the
+// busiest CU, ceil(last * pc / cus) / pc tiles' worth, if that beats one whole tile;
+// these tiles run after the earlier rounds (e.g. 924 tiles: three workgroups per CU
+// fill 768 slots, and 156 tiles left whole would each run alone on a CU, at the slow
+// single-workgroup rate). 1: no split.
+inline int64_t pick_tail_pieces(int64_t last, int64_t max_pieces, int64_t cus) {
+    if (last <= 0 || max_pieces < 2) return 1;
+    if (last <= cus / 2) return std::max<int64_t>(1, std::min<int64_t>(cus / last, max_pieces));
+    int64_t best = 1, best_num = 1, best_den = 1;  // busiest CU's load best_num / best_den tiles
+    for (int64_t pc = 2; pc <= std::min<int64_t>(4, max_pieces); ++pc) {
+        const int64_t num = cdiv(last * pc, cus);
+        if (num * best_den < best_num * pc) {
+            best = pc;
+            best_num = num;
+            best_den = pc;
+        }
+    }
+    return best;
+}
+
 // Balanced split for fewer tiles than CUs: 2 x cus workgroups, `a` tiles cut into pa
 // pieces and the other tiles - cut into pa + 1, with every piece at least min_steps
 // long. The dispatcher gives linear workgroup ids L and L + cus the same CU, so with

@@ -509,8 +509,8 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
         pieces = splits;
     } else if (tiles > kCUs) {
         const int64_t last = tiles % kCUs;
-        const int64_t pc = last > 0 ? std::min<int64_t>(kCUs / last, nsteps / 4) : 1;
-        if (last > 0 && last <= kCUs / 2 && pc >= 2) {
+        const int64_t pc = pick_tail_pieces(last, nsteps / 4, kCUs);
+        if (pc >= 2) {
             tail = last;
             pieces = pc;
         }

@@ -74,6 +74,8 @@ def test_single_linear_workload(gpu_lib):
     (200, 7040, 1600, 16),   # balanced split with ragged tokens and K: 110 y tiles (25 K steps), 26 dX tiles
     (512, 8192, 1024, 16),   # exactly 256 y tiles: split in two over K
     (512, 1024, 8192, 16),   # exactly 256 dX tiles: split in two over N
+    (512, 12800, 1536, 16),  # 400 y tiles: a whole round, the last 144 split in three over K
+    (512, 1536, 12800, 16),  # 400 dX tiles: a whole round, the last 144 split in three over N
 ])
 def test_shapes(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
