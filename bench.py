@@ -547,6 +547,12 @@ def main() -> int:
         ev = HipEvents()
         shapes = [v for v in args.sweep_shapes.split(",") if v]
         tokens = [int(v) for v in args.sweep_tokens.split(",") if v]
+        known = {f"{m}:{p}" for m, p, _, _ in SMALL_T_SHAPES}
+        bad = [v for v in shapes if v not in known] + [str(t) for t in tokens if t not in SMALL_T]
+        if bad:
+            print(f"unknown --sweep-shapes / --sweep-tokens values {bad}; shapes: {sorted(known)}, tokens: {SMALL_T}",
+                  file=sys.stderr)
+            return 2
         sweep = small_t_sweep(lib, torch, ev, shapes=shapes, tokens=tokens)
         copy_meas = measured_copy_gbs(torch, ev)
         for row in sweep["rows"]:

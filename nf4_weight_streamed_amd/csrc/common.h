@@ -130,6 +130,10 @@ void prof_gemm_end(hipStream_t stream);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Compute units of one MI355X (gfx950): the round size of the GEMM grids (the
+// dispatcher gives linear workgroup ids L, L + 256, L + 512 the same CU).
+constexpr int64_t kChipCUs = 256;
+
 // Split count for a GEMM with `tiles` output tiles and `steps` reduction steps: the
 // GEMM kernels run two workgroups per CU, so up to 2 * 256 workgroups run in one
 // round; a grid just above that leaves a nearly empty second round. Split only

@@ -63,25 +63,25 @@ __device__ __forceinline__ uint32_t xcd_tile_order(uint32_t L, uint32_t total) {
     return xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
 }
 
-// Balanced two-round split (pick_balanced on the host): workgroups [0, 2 x 256) of the
-// split tiles; linear ids L and L + 256 run on one CU. Round 0 (L < 256) holds the
+// Balanced two-round split (pick_balanced on the host): workgroups [0, 2 x round) of
+// the split tiles, round = the CU count; linear ids L and L + round run on one CU.
+// Round 0 (L < round) holds the
 // a * pa pieces of tiles [0, a) (pa pieces each) and then pieces of the other tiles
 // (pa + 1 each), round 1 only the latter; within a round the logical order is
 // XCD-aware (xcd_tile_order), so neighbouring tiles - the token tiles of one weight
 // slice - meet in one L2. Piece z of P covers steps [z S / P, (z + 1) S / P): all
 // pieces of a tile are non-empty and differ by at most one step.
-__device__ __forceinline__ void balanced_piece(uint32_t L, int tail, int a, int pa, int steps, int& q, int& z,
-                                               int& s0, int& s1) {
-    constexpr uint32_t kRound = 256;
-    const int l = int(xcd_tile_order(L % kRound, kRound));
+__device__ __forceinline__ void balanced_piece(uint32_t L, uint32_t round, int tail, int a, int pa, int steps, int& q,
+                                               int& z, int& s0, int& s1) {
+    const int l = int(xcd_tile_order(L % round, round));
     const int na = a * pa, b = tail - a;
     int P;
-    if (L < kRound && l < na) {
+    if (L < round && l < na) {
         q = l % a;
         z = l / a;
         P = pa;
     } else {
-        const int v = L < kRound ? l - na : int(kRound) - na + l;
+        const int v = L < round ? l - na : int(round) - na + l;
         q = a + v % b;
         z = v / b;
         P = pa + 1;

@@ -26,7 +26,7 @@ namespace {
 constexpr int kBN = 64;        // contraction (N) per main-loop step
 constexpr int kLds = kBN + 8;  // LDS pitch in bf16
 constexpr int kThreads = 256;
-constexpr int64_t kCUs = 256;
+constexpr int64_t kCUs = kChipCUs;
 
 // Workgroup tile: 128 tokens x 128 input features, 4 waves in a 2x2 grid (64 x 64
 // each, 32x32x16 MFMA), contraction steps of 64 over N. Per step each thread loads
@@ -95,7 +95,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
         tile = int(xcd_tile_order(blockIdx.x, uint32_t(tl.full)));
     } else if (tl.bal_a > 0) {
         int q;
-        balanced_piece(blockIdx.x - uint32_t(tl.full), tl.tail, tl.bal_a, tl.bal_pa, nsteps, q, tz, nb_begin, nb_end);
+        balanced_piece(blockIdx.x - uint32_t(tl.full), uint32_t(kCUs), tl.tail, tl.bal_a, tl.bal_pa, nsteps, q, tz,
+                       nb_begin, nb_end);
         tile = tl.full + q;
         ptile = partial + (size_t(tz) * tl.tail + q) * (BM * BK);
     } else {

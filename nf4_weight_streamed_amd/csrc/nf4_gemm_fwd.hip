@@ -36,7 +36,7 @@ constexpr int kFwdWaves = 4;   // waves per workgroup (each 128 tokens x 128 / k
 constexpr int kFwdXAhead = 1;  // K steps x is loaded ahead of its use (register sets)
 constexpr int kFwdWAhead = 2;  // K steps the weights are loaded ahead of their dequantisation
 constexpr int kFwdOccupancy = 3;  // waves per SIMD the register budget must allow (3 tiles per CU)
-constexpr int64_t kCUs = 256;
+constexpr int64_t kCUs = kChipCUs;
 
 // ------------------------------------------------------------------------------------
 // NW waves split the BN = 128 output features (128 / NW each, FN = 4 / NW fragments of
@@ -93,7 +93,8 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
         tile = int(xcd_tile_order(blockIdx.x, uint32_t(tl.full)));
     } else if (tl.bal_a > 0) {
         int q;
-        balanced_piece(blockIdx.x - uint32_t(tl.full), tl.tail, tl.bal_a, tl.bal_pa, ksteps, q, tz, kb_begin, kb_end);
+        balanced_piece(blockIdx.x - uint32_t(tl.full), uint32_t(kCUs), tl.tail, tl.bal_a, tl.bal_pa, ksteps, q, tz,
+                       kb_begin, kb_end);
         tile = tl.full + q;
         ptile = partial + (size_t(tz) * tl.tail + q) * (BM * BN);
     } else {
