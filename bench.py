@@ -288,6 +288,26 @@ def measured_copy_gbs(torch, ev: "HipEvents", nbytes: int = 1 << 30) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def measured_read_gbs(torch, ev: "HipEvents", nbytes: int = 2 << 30) -> float:
+    """Read-only reference: a PyTorch fp32 sum over 2 GiB (best of 5 launches), the rate a
+    plain read-bound kernel reaches on this device."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    a.sum()
+    stream = torch.cuda.current_stream().cuda_stream
+    best = 0.0
+    for _ in range(5):
+        e0, e1 = ev.create(), ev.create()
+        ev.record(e0, stream)
+        a.sum()
+        ev.record(e1, stream)
+        best = max(best, nbytes / (ev.elapsed_ms(e0, e1) * 1e-3) / 1e9)
+        ev.destroy(e0)
+        ev.destroy(e1)
+    del a
+    torch.cuda.empty_cache()
+    return best
+
+
 def pinned_h2d_gbs(torch, nbytes: int = 1 << 30) -> float:
     """Pinned host -> device hipMemcpyAsync bandwidth on a side stream (best of 3)."""
     h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
@@ -555,9 +575,11 @@ def main() -> int:
             return 2
         sweep = small_t_sweep(lib, torch, ev, shapes=shapes, tokens=tokens)
         copy_meas = measured_copy_gbs(torch, ev)
+        read_meas = measured_read_gbs(torch, ev)
         for row in sweep["rows"]:
             row["hbm_frac_vs_measured_copy"] = round(row["hbm_gbs"] / copy_meas, 4)
         sweep["hbm_copy_gbs_measured"] = round(copy_meas, 1)
+        sweep["hbm_read_gbs_measured"] = round(read_meas, 1)
         out = {"metric": "NF4-LoRA linear fwd+bwd device time at small T; % of HBM roofline", "n_gpus": 1,
                "dtype": "bf16", "data": "synthetic", "small_t": sweep}
         print(json.dumps(out), flush=True)
@@ -594,6 +616,7 @@ def main() -> int:
 
     mfma_meas = measured_mfma_tflops(lib, torch, ev)
     copy_meas = measured_copy_gbs(torch, ev)
+    read_meas = measured_read_gbs(torch, ev)
     quant = quantize_measure(lib, torch, ev, cpu=not args.no_cpu_baseline)
     ms = dt * 1000.0 / args.steps
     tokens_per_s = T_TOKENS / (dt / args.steps)
@@ -644,6 +667,7 @@ def main() -> int:
             "mfma_bf16_tflops_measured": round(mfma_meas, 1),
             "hbm_gbs_published": HBM_PEAK_GBS,
             "hbm_copy_gbs_measured": round(copy_meas, 1),
+            "hbm_read_gbs_measured": round(read_meas, 1),
         },
     }
     if args.streamed != "none":
