@@ -288,22 +288,26 @@ def measured_copy_gbs(torch, ev: "HipEvents", nbytes: int = 1 << 30) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def measured_read_gbs(torch, ev: "HipEvents", nbytes: int = 2 << 30) -> float:
-    """Read-only reference: a PyTorch fp32 sum over 2 GiB (best of 5 launches), the rate a
-    plain read-bound kernel reaches on this device."""
-    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
-    a.sum()
+def measured_read_gbs(lib, torch, ev: "HipEvents", nbytes: int = 2 << 30) -> float:
+    """Read-only reference: the library's read probe (coalesced 16-byte loads, grid-stride)
+    over 2 GiB, best over a few grid sizes and launches: the rate a plain read-bound kernel
+    reaches on this device."""
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     best = 0.0
-    for _ in range(5):
-        e0, e1 = ev.create(), ev.create()
-        ev.record(e0, stream)
-        a.sum()
-        ev.record(e1, stream)
-        best = max(best, nbytes / (ev.elapsed_ms(e0, e1) * 1e-3) / 1e9)
-        ev.destroy(e0)
-        ev.destroy(e1)
-    del a
+    for wg in (1024, 2048, 4096):
+        out = torch.empty(256 * wg, dtype=torch.int32, device="cuda")
+        lib.probe_read(src, out, wg)
+        for _ in range(3):
+            e0, e1 = ev.create(), ev.create()
+            ev.record(e0, stream)
+            lib.probe_read(src, out, wg)
+            ev.record(e1, stream)
+            best = max(best, nbytes / (ev.elapsed_ms(e0, e1) * 1e-3) / 1e9)
+            ev.destroy(e0)
+            ev.destroy(e1)
+        del out
+    del src
     torch.cuda.empty_cache()
     return best
 
@@ -575,7 +579,7 @@ def main() -> int:
             return 2
         sweep = small_t_sweep(lib, torch, ev, shapes=shapes, tokens=tokens)
         copy_meas = measured_copy_gbs(torch, ev)
-        read_meas = measured_read_gbs(torch, ev)
+        read_meas = measured_read_gbs(lib, torch, ev)
         for row in sweep["rows"]:
             row["hbm_frac_vs_measured_copy"] = round(row["hbm_gbs"] / copy_meas, 4)
         sweep["hbm_copy_gbs_measured"] = round(copy_meas, 1)
@@ -616,7 +620,7 @@ def main() -> int:
 
     mfma_meas = measured_mfma_tflops(lib, torch, ev)
     copy_meas = measured_copy_gbs(torch, ev)
-    read_meas = measured_read_gbs(torch, ev)
+    read_meas = measured_read_gbs(lib, torch, ev)
     quant = quantize_measure(lib, torch, ev, cpu=not args.no_cpu_baseline)
     ms = dt * 1000.0 / args.steps
     tokens_per_s = T_TOKENS / (dt / args.steps)

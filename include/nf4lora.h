@@ -247,6 +247,19 @@ int nf4_profile_next_gemm(void* start_event, void* stop_event);
  */
 int nf4_probe_mfma(float* out, int workgroups, int iters, nf4_stream stream);
 
+/*
+ * Instrumentation: the HBM read rate of a plain streaming kernel, for reporting the
+ * few-token kernels' bytes against a measured read ceiling beside the published one.
+ * Launches `workgroups` workgroups of 256 threads on `stream` that read `bytes` bytes
+ * of the device buffer `src` (16-byte aligned, bytes a positive multiple of 16) with
+ * coalesced 16-byte loads in a grid-stride loop and write the XOR of each thread's
+ * 32-bit words to out[256 * workgroup + thread] (device uint32, 256 * workgroups
+ * entries, caller-owned; the XOR of all of out is the XOR of all words of src). Time it
+ * with events on the same stream. NF4_E_ARG for NULL pointers, misalignment, a size
+ * that is not a positive multiple of 16 or workgroups < 1.
+ */
+int nf4_probe_read(const void* src, size_t bytes, uint32_t* out, int workgroups, nf4_stream stream);
+
 /* ------------------------------------------------------------------ stream pool
  * Blockwise residency of the frozen base ([hn] main comment; [api]
  * "patch_hf_model" Behavior 5-6; [consumer] "What you need besides VRAM",

@@ -162,6 +162,14 @@ int nf4_probe_mfma(float* out, int workgroups, int iters, nf4_stream stream) {
     return hip_status(launch_probe_mfma(out, workgroups, iters, static_cast<hipStream_t>(stream)), "nf4_probe_mfma");
 }
 
+int nf4_probe_read(const void* src, size_t bytes, uint32_t* out, int workgroups, nf4_stream stream) {
+    if (!src || !out || workgroups < 1 || bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0)
+        return fail(NF4_E_ARG, "nf4_probe_read: need src != NULL (16-byte aligned), bytes a positive multiple of 16 "
+                               "(got %zu), out != NULL, workgroups >= 1 (got %d)", bytes, workgroups);
+    return hip_status(nf4::launch_probe_read(src, uint64_t(bytes), out, workgroups, static_cast<hipStream_t>(stream)),
+                      "nf4_probe_read");
+}
+
 int nf4_profile_next_gemm(void* start_event, void* stop_event) {
     if ((start_event == nullptr) != (stop_event == nullptr))
         return fail(NF4_E_ARG, "nf4_profile_next_gemm: pass both events or neither");

@@ -63,6 +63,7 @@ def _load() -> C.CDLL:
         "nf4_lora_linear_bwd": (i32, [vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "nf4_profile_next_gemm": (i32, [vp, vp]),
         "nf4_probe_mfma": (i32, [vp, i32, i32, vp]),
+        "nf4_probe_read": (i32, [vp, C.c_size_t, vp, i32, vp]),
         "nf4_rmsnorm_fwd": (i32, [vp, i64, i64, f32, vp, vp, vp]),
         "nf4_rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, vp, vp]),
         "nf4_add_bf16": (i32, [vp, vp, vp, i64, vp, vp]),
@@ -140,6 +141,15 @@ def probe_mfma(out, workgroups: int, iters: int, stream=None) -> None:
     if out.dtype != torch.float32 or not out.is_cuda or out.numel() < 4 * workgroups:
         raise ValueError("probe_mfma: out must be a device fp32 tensor of >= 4 * workgroups entries")
     _check(_lib.nf4_probe_mfma(_ptr(out), int(workgroups), int(iters), _stream(stream)))
+
+
+def probe_read(src, out, workgroups: int, stream=None) -> None:
+    """Launch the HBM read-rate probe over the device tensor `src` (its bytes, a multiple
+    of 16); `out` = device int32 tensor of >= 256 * workgroups entries."""
+    nbytes = src.numel() * src.element_size()
+    if not src.is_cuda or not out.is_cuda or out.dtype != torch.int32 or out.numel() < 256 * workgroups:
+        raise ValueError("probe_read: src and out must be device tensors, out int32 with >= 256 * workgroups entries")
+    _check(_lib.nf4_probe_read(_ptr(src), C.c_size_t(nbytes), _ptr(out), int(workgroups), _stream(stream)))
 
 
 def codebook() -> list:
