@@ -57,7 +57,7 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
 // [0, total) for any total.
 constexpr uint32_t kXcds = 8;
 
-__device__ __forceinline__ uint32_t xcd_tile_order(uint32_t L, uint32_t total) {
+__host__ __device__ __forceinline__ uint32_t xcd_tile_order(uint32_t L, uint32_t total) {
     const uint32_t q = total / kXcds, rem = total % kXcds;
     const uint32_t xcd = L % kXcds, local = L / kXcds;
     return xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
@@ -71,8 +71,8 @@ __device__ __forceinline__ uint32_t xcd_tile_order(uint32_t L, uint32_t total) {
 // XCD-aware (xcd_tile_order), so neighbouring tiles - the token tiles of one weight
 // slice - meet in one L2. Piece z of P covers steps [z S / P, (z + 1) S / P): all
 // pieces of a tile are non-empty and differ by at most one step.
-__device__ __forceinline__ void balanced_piece(uint32_t L, uint32_t round, int tail, int a, int pa, int steps, int& q,
-                                               int& z, int& s0, int& s1) {
+__host__ __device__ __forceinline__ void balanced_piece(uint32_t L, uint32_t round, int tail, int a, int pa, int steps,
+                                                        int& q, int& z, int& s0, int& s1) {
     const int l = int(xcd_tile_order(L % round, round));
     const int na = a * pa, b = tail - a;
     int P;
