@@ -105,42 +105,89 @@ def build_layer(lib, torch, seed: int = 42):
 
 
 def run_step(lib, layer, prof=None):
-    """Forward of all 7 projections, then backward in reverse order. `prof` =
-    (name, start, stop) records events around that projection's forward GEMM."""
+    """Forward of all 7 projections, then backward in reverse order. `prof` maps
+    ("fwd" | "bwd", projection) to a (start, stop) pair of hipEvent_t handles that the
+    library records immediately around that call's fused GEMM launch, on its stream."""
+    prof = prof or {}
     for name, *_ in PROJ:
         p = layer[name]
-        if prof is not None and prof[0] == name:
-            lib.profile_next_gemm(prof[1], prof[2])
+        if ("fwd", name) in prof:
+            lib.profile_next_gemm(*prof[("fwd", name)])
         lib.lora_linear_fwd(p["codes"], p["absmax"], p["x"], p["A"], p["B"], ALPHA, y=p["y"], u=p["u"], ws=p["wsf"])
     for name, *_ in reversed(PROJ):
         p = layer[name]
+        if ("bwd", name) in prof:
+            lib.profile_next_gemm(*prof[("bwd", name)])
         lib.lora_linear_bwd(p["codes"], p["absmax"], p["x"], p["u"], p["dy"], p["A"], p["B"], ALPHA, dx=p["dx"],
                             dA=p["dA"], dB=p["dB"], ws=p["wsb"])
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_nf4_gemm_fwd_gate_qwen7b_t512_traffic.md")
-# sources whose change invalidates the HBM traffic taken with the counters
-TRAFFIC_SOURCES = [os.path.join(ROOT, "nf4_weight_streamed_amd", "csrc", f)
-                   for f in ("nf4_gemm_fwd.hip", "device.h", "common.h")]
+def gemm_flops(kind: str, t: int, n: int, k: int, r: int) -> float:
+    """Algorithmic FLOPs of one fused GEMM launch: forward 2TNK + 2TNr (base + LoRA
+    epilogue); backward 2TNK + 2TKr + 2TKr (dX base, dX LoRA term, dA share)."""
+    return 2.0 * t * n * k + (2.0 * t * n * r if kind == "fwd" else 4.0 * t * k * r)
+
+
+def gemm_bytes(kind: str, t: int, n: int, k: int, r: int) -> float:
+    """Algorithmic HBM bytes of one fused GEMM launch: the NF4 base (0.5625 B a weight)
+    once, each operand read once and each output written once. Forward: x, u, B in,
+    y out. Backward: dY, g, A and x (for dA) in, dX and dA out."""
+    w = n * k * 0.5 + n * (k // 64) * 4
+    if kind == "fwd":
+        return w + 2 * t * k + 4 * t * r + 2 * n * r + 2 * t * n
+    return w + 2 * t * n + 4 * t * r + 2 * r * k + 2 * t * k + 2 * t * k + 4 * r * k
+
+
+def gemm_attribution(lib, torch, layer, ev: "HipEvents", steps: int = 3) -> dict:
+    """Device time of every fused GEMM launch of the step (HIP events recorded by the
+    library around each launch, on its stream), averaged over `steps` untimed steps:
+    which kernel holds the most device time per step."""
+    names = [n for n, *_ in PROJ]
+    keys = [(kind, n) for kind in ("fwd", "bwd") for n in names]
+    acc = {key: 0.0 for key in keys}
+    for _ in range(steps):
+        prof = {key: (ev.create(), ev.create()) for key in keys}
+        run_step(lib, layer, prof)
+        torch.cuda.synchronize()
+        for key, (a, b) in prof.items():
+            acc[key] += ev.elapsed_ms(a, b) * 1e3 / steps
+            ev.destroy(a)
+            ev.destroy(b)
+    per = {kind: {n: round(acc[(kind, n)], 2) for n in names} for kind in ("fwd", "bwd")}
+    totals = {"k_nf4_gemm_fwd": round(sum(per["fwd"].values()), 1),
+              "k_nf4_gemm_bwd_dx": round(sum(per["bwd"].values()), 1)}
+    return {"us_per_launch": per, "us_per_step": totals,
+            "dominant": max(totals, key=totals.get)}
+
+
+# committed counter summaries of the fused GEMMs, and the sources whose change
+# invalidates the HBM traffic they report
+_CSRC = os.path.join(ROOT, "nf4_weight_streamed_amd", "csrc")
+TRAFFIC = {
+    "k_nf4_gemm_fwd": (os.path.join(ROOT, "profiles", "k_nf4_gemm_fwd_gate_qwen7b_t512_traffic.md"),
+                       [os.path.join(_CSRC, f) for f in ("nf4_gemm_fwd.hip", "device.h", "common.h")]),
+    "k_nf4_gemm_bwd_dx": (os.path.join(ROOT, "profiles", "k_nf4_gemm_bwd_dx_gate_qwen7b_t512_traffic.md"),
+                          [os.path.join(_CSRC, f) for f in ("nf4_gemm_bwd.hip", "device.h", "common.h")]),
+}
 COPY_CALIBRATION_BYTES = 1 << 30
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(kernel: str = "k_nf4_gemm_fwd") -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in TRAFFIC[kernel][1]:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic() -> int | None:
-    """HBM bytes per launch of the dominant kernel from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, each scaled by the copy calibration), or None when that
-    summary is missing or was taken on different kernel sources."""
+def measured_traffic(kernel: str) -> int | None:
+    """HBM bytes per launch of `kernel` (gate projection) from its committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the copy calibration), or None when
+    that summary is missing or was taken on different kernel sources."""
     try:
-        with open(TRAFFIC_PROFILE) as fh:
+        with open(TRAFFIC[kernel][0]) as fh:
             text = fh.read()
     except OSError:
         return None
@@ -149,7 +196,7 @@ def measured_traffic() -> int | None:
         if line.startswith("- ") and ": " in line:
             key, val = line[2:].split(": ", 1)
             fields[key.strip("` ")] = val.strip("` ")
-    if fields.get("source_sha256") != kernel_source_digest():
+    if fields.get("source_sha256") != kernel_source_digest(kernel):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -169,43 +216,133 @@ def copy_calibration(torch) -> None:
     torch.cuda.empty_cache()
 
 
-def cpu_baseline(seconds_budget: float = 12.0) -> dict:
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
-    the q projection (3584 x 3584) of the layer with all 512 tokens - dequantise
-    + forward + backward - repeated for about `seconds_budget` seconds, scaled
-    to the whole layer by the algorithmic-FLOP ratio. Quantisation (load time)
-    is outside the timed region, as on the GPU."""
+def _blas_info() -> dict:
+    """numpy's BLAS build and the host cores the oracle may use."""
     import numpy as np
 
+    info = {"cores_affinity": len(os.sched_getaffinity(0)), "numpy": np.__version__}
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        info["blas"] = f"{blas.get('name')} {blas.get('version')}"
+        info["blas_config"] = blas.get("openblas configuration", "")
+    except Exception as e:  # pragma: no cover - numpy builds without the dict form
+        info["blas"] = f"unknown ({e})"
+    return info
+
+
+def _blas_threads(n: int):
+    """Pin the BLAS pool to n threads for the oracle's timing; returns (context, threads in use)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    ctx = threadpool_limits(limits=n, user_api="blas")
+    used = max([i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"] or [0])
+    return ctx, used
+
+
+def _oracle_linear_seconds(case: dict, budget: float) -> tuple[float, int]:
+    """Mean seconds of one oracle pass (dequantise + fwd + bwd) over at least 3 passes
+    and about `budget` seconds; the NF4 storage is made once, outside the timing."""
     import oracle as O
     import synthetic_inputs as S
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = 1
-    n, k = QW, HIDDEN
-    case = S.linear_case(T_TOKENS, n, k, r=RANK, proj="q")
     codes, absmax = O.quantize(S.bf16_bits_to_f32(case["W"]))
     reps = 0
     t0 = time.perf_counter()
-    while reps < 3 or time.perf_counter() - t0 < seconds_budget:
+    while reps < 3 or time.perf_counter() - t0 < budget:
         wq = O.dequantize(codes, absmax)
         O.lora_linear_fwd(case["x"], wq, case["A"], case["B"], ALPHA)
         O.lora_linear_bwd(case["x"], wq, case["A"], case["B"], ALPHA, case["dY"])
         reps += 1
-    dt = (time.perf_counter() - t0) / reps
-    sample_flops = 4 * T_TOKENS * n * k + 6 * T_TOKENS * RANK * (n + k)
-    layer_seconds = dt * step_flops(T_TOKENS, RANK) / sample_flops
+    return (time.perf_counter() - t0) / reps, reps
+
+
+def linear_flops(t: int, n: int, k: int, r: int) -> float:
+    return 4.0 * t * n * k + 6.0 * t * r * (n + k)
+
+
+def cpu_baseline(seconds_budget: float = 12.0) -> dict:
+    """The fp64 oracle, as it stands, on the GPU machine's host cores (BLAS pinned to the
+    cores of this process's affinity mask), on a bounded sample of the same workload:
+    the q projection (3584 x 3584) of the layer with all 512 tokens - dequantise +
+    forward + backward - repeated for about `seconds_budget` seconds, scaled to the
+    whole layer by the algorithmic-FLOP ratio. Beside it: the single 1024 x 1024 linear
+    at 256 tokens timed whole, and the streamed stacks' step time extrapolated from the
+    sample's FLOP rate (one layer x the layer count; labelled extrapolated).
+    Quantisation (load time) is outside the timed region, as on the GPU."""
+    import synthetic_inputs as S
+    from nf4_weight_streamed_amd import stack as ST
+
+    info = _blas_info()
+    ctx, threads = _blas_threads(info["cores_affinity"])
+    with ctx:
+        n, k = QW, HIDDEN
+        dt, reps = _oracle_linear_seconds(S.linear_case(T_TOKENS, n, k, r=RANK, proj="q"), seconds_budget)
+        c0_dt, c0_reps = _oracle_linear_seconds(S.linear_case(256, 1024, 1024, r=RANK), 2.0)
+    sample_flops = linear_flops(T_TOKENS, n, k, RANK)
+    rate = sample_flops / dt
+    layer_seconds = step_flops(T_TOKENS, RANK) / rate
+    stacks = {}
+    for model, (dims, n_layers) in ST.QWEN25.items():
+        f = n_layers * sum(linear_flops(T_TOKENS, n_, k_, RANK) for n_, k_ in dims.shapes().values())
+        stacks[model] = {"seconds_per_step": round(f / rate, 1), "tokens_per_s": round(T_TOKENS * rate / f, 3),
+                         "layers": n_layers, "kind": "extrapolated: sample FLOP rate x the stack's algorithmic FLOPs"}
     return {
         "value": round(T_TOKENS / layer_seconds, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
         "sample": (f"q projection 3584x3584, 512 tokens, r16: dequantise + fwd + bwd in fp64 numpy, "
                    f"{dt:.2f} s per pass (mean of {reps}); "
                    f"scaled to the 7-projection layer by algorithmic FLOPs ({step_flops(T_TOKENS, RANK) / sample_flops:.2f}x)"),
-        "gflops": round(sample_flops / dt / 1e9, 3),
+        "gflops": round(rate / 1e9, 3),
+        "host": info,
+        "single_linear_1024": {"seconds_per_fwd_bwd": round(c0_dt, 4), "passes": c0_reps,
+                               "tokens_per_s": round(256 / c0_dt, 1),
+                               "gflops": round(linear_flops(256, 1024, 1024, RANK) / c0_dt / 1e9, 3)},
+        "stacks_t512": stacks,
     }
+
+
+def config0_measure(lib, torch, ev: "HipEvents", reps: int = 200) -> dict:
+    """The single NF4-LoRA linear, in = out = 1024, 256 tokens, r 16, alpha 32: forward +
+    backward (dX, dA, dB) device time over `reps` back-to-back calls (events on the
+    stream), against its algorithmic FLOPs and bytes. The working set (about 3 MB) stays
+    in the caches: the figure is latency-bound, reported for completeness."""
+    import synthetic_inputs as S
+
+    t, n, k = 256, 1024, 1024
+    case = S.linear_case(t, n, k, r=RANK)
+    dev = {key: torch.from_numpy(case[key].view("int16")).view(torch.bfloat16).cuda() for key in ("W", "x", "A", "B", "dY")}
+    codes, absmax = lib.quantize(dev["W"])
+    y = torch.empty(t, n, dtype=torch.bfloat16, device="cuda")
+    u = torch.empty(t, RANK, dtype=torch.float32, device="cuda")
+    dx = torch.empty(t, k, dtype=torch.bfloat16, device="cuda")
+    da = torch.empty(RANK, k, dtype=torch.float32, device="cuda")
+    db = torch.empty(n, RANK, dtype=torch.float32, device="cuda")
+    wsf = lib.workspace(lib.fwd_workspace_bytes(t, n, k, RANK))
+    wsb = lib.workspace(lib.bwd_workspace_bytes(t, n, k, RANK))
+
+    def one():
+        lib.lora_linear_fwd(codes, absmax, dev["x"], dev["A"], dev["B"], ALPHA, y=y, u=u, ws=wsf)
+        lib.lora_linear_bwd(codes, absmax, dev["x"], u, dev["dY"], dev["A"], dev["B"], ALPHA, dx=dx, dA=da, dB=db,
+                            ws=wsb)
+
+    for _ in range(10):
+        one()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.record(e0, stream)
+    for _ in range(reps):
+        one()
+    ev.record(e1, stream)
+    us = ev.elapsed_ms(e0, e1) * 1e3 / reps
+    ev.destroy(e0)
+    ev.destroy(e1)
+    flops = linear_flops(t, n, k, RANK)
+    nbytes = 2 * (n * k * 0.5625) + t * (6 * k + 4 * n + 8 * RANK) + 8 * RANK * (n + k)
+    return {"workload": "single NF4-LoRA linear 1024x1024, 256 tokens, r16, fwd+bwd", "us_per_fwd_bwd": round(us, 2),
+            "tokens_per_s": round(t / us * 1e6, 1), "tflops": round(flops / us / 1e6, 2),
+            "mfma_frac": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 5),
+            "hbm_gbs_algorithmic": round(nbytes / us / 1e3, 1), "algorithmic_flops": flops,
+            "algorithmic_bytes": nbytes}
 
 
 def quantize_measure(lib, torch, ev: "HipEvents", cpu: bool) -> dict:
@@ -329,77 +466,131 @@ def pinned_h2d_gbs(torch, nbytes: int = 1 << 30) -> float:
     return best
 
 
-def stream_bench(torch, model: str, block_size: int, tokens: int, steps: int, h2d_gbs: float,
-                 base_kind: str = "nf4", n_slots: int = 2) -> dict:
-    """Streamed vs resident step time of a Qwen2.5-shaped identity-mixing stack, with
-    the bitwise check, H2D traffic and copy/compute overlap. base_kind "bf16" streams a
-    dense bf16 base (the experimental bf16_bitwise mode) instead of NF4. n_slots = device
-    pool slots of one block each (the streamed runs; the resident run holds every block)."""
-    from nf4_weight_streamed_amd import stack as ST
-
-    dims, n_layers = ST.QWEN25[model]
-    t0 = time.perf_counter()
-    host_cls = ST.HostBF16Base if base_kind == "bf16" else ST.HostNF4Base
-    base = host_cls(dims, n_layers, block_size, ST.qwen_weight_fn())
-    lora = ST.LoraParams(dims, n_layers, RANK, ST.qwen_lora_fn())
-    build_s = time.perf_counter() - t0
-    print(f"[stream_bench] {model}: host base built in {build_s:.1f} s", file=sys.stderr, flush=True)
+def _stack_inputs(torch, tokens: int, hidden: int):
     g = torch.Generator(device="cuda")
     g.manual_seed(42)
-    h0 = torch.randn(tokens, dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
-    dh = torch.randn(tokens, dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
-    out = {}
-    # resident, streamed, and streamed with rematerialisation (block-boundary states kept,
-    # each block's forward recomputed in its backward visit)
-    for mode, remat, key in (("resident", False, "resident"), ("streamed", False, "streamed"),
-                             ("streamed", True, "remat")):
-        st = ST.NF4Stack(base, lora, tokens, ALPHA, mode=mode, remat=remat, n_slots=n_slots)
-        y, dx = st.step(h0, dh)                       # warmup (and the parity sample)
+    h0 = torch.randn(tokens, hidden, generator=g, device="cuda").to(torch.bfloat16)
+    dh = torch.randn(tokens, hidden, generator=g, device="cuda").to(torch.bfloat16)
+    return h0, dh
+
+
+def _stack_run(torch, ST, base, lora, tokens, h0, dh, steps, **kw) -> dict:
+    """One stack configuration: a first step (its outputs kept for the bitwise check),
+    then `steps` timed steps with the pool's copy and acquire-stall spans recorded."""
+    st = ST.NF4Stack(base, lora, tokens, ALPHA, **kw)
+    try:
+        y, dx = st.step(h0, dh)
         torch.cuda.synchronize()
-        out[key + "_y"], out[key + "_dx"] = y.clone(), dx.clone()
-        out[key + "_act"] = st.activation_bytes()
+        res = {"y": y.clone(), "dx": dx.clone(), "act": st.activation_bytes()}
         c0 = st.pool.stats()["bytes_copied"]
-        secs = ST.timed_steps(st, h0, dh, steps, warmup=0)
-        out[key + "_s"] = secs
-        out[key + "_bytes"] = (st.pool.stats()["bytes_copied"] - c0) / steps
+        st.pool.timing_enable(True)
+        res["s"] = ST.timed_steps(st, h0, dh, steps, warmup=0)
+        tm = st.pool.timing_collect()
+        res["bytes"] = (st.pool.stats()["bytes_copied"] - c0) / steps
+        res["copy_ms"] = tm["copy_ms"] / steps
+        res["stall_ms"] = tm["stall_ms"] / steps
+        return res
+    finally:
         st.close()
         del st
         torch.cuda.empty_cache()
-        print(f"[stream_bench] {model}: {key} {secs * 1e3:.1f} ms per step", file=sys.stderr, flush=True)
-    flops = n_layers * sum(4 * tokens * n * k + 6 * tokens * RANK * (n + k) for n, k in dims.shapes().values())
-    r_s, s_s, nbytes = out["resident_s"], out["streamed_s"], out["streamed_bytes"]
-    copy_s = nbytes / (h2d_gbs * 1e9)
-    overlap = (r_s + copy_s - s_s) / min(r_s, copy_s) if min(r_s, copy_s) > 0 else None
-    return {
-        "workload": f"qwen2.5-{model}-shaped stack, {n_layers} layers, block_size {block_size}, {n_slots} pool slots, "
-                    f"{tokens} tokens, "
-                    f"{'dense bf16' if base_kind == 'bf16' else 'NF4'} in pinned host, identity attention mixing, fwd+bwd",
-        "bitwise_equal_to_resident": bool(torch.equal(out["resident_y"], out["streamed_y"])
-                                          and torch.equal(out["resident_dx"], out["streamed_dx"])),
-        "resident_ms_per_step": round(r_s * 1e3, 3),
-        "streamed_ms_per_step": round(s_s * 1e3, 3),
-        "streamed_over_resident": round(s_s / r_s, 3),
-        "streamed_tokens_per_s": round(tokens / s_s, 2),
-        "streamed_tflops": round(flops / s_s / 1e12, 2),
-        "resident_tflops": round(flops / r_s / 1e12, 2),
-        "h2d_gb_per_step": round(nbytes / 1e9, 3),
-        "h2d_gbs_achieved_over_step": round(nbytes / s_s / 1e9, 2),
-        "h2d_gbs_pinned_peak_measured": round(h2d_gbs, 2),
-        "pcie_frac": round(nbytes / s_s / 1e9 / h2d_gbs, 4),
-        "pcie_floor_ratio": round(max(r_s, copy_s) / r_s, 3),
-        "copy_compute_overlap": None if overlap is None else round(overlap, 3),
-        "host_base_gb": round(base.total_bytes() / 1e9, 3),
-        "build_s": round(build_s, 1),
-        "remat": {
-            "bitwise_equal_to_resident": bool(torch.equal(out["resident_y"], out["remat_y"])
-                                              and torch.equal(out["resident_dx"], out["remat_dx"])),
-            "streamed_ms_per_step": round(out["remat_s"] * 1e3, 3),
-            "over_streamed": round(out["remat_s"] / s_s, 3),
-            "activation_gb": round(out["remat_act"] / 1e9, 3),
-            "activation_gb_stored": round(out["streamed_act"] / 1e9, 3),
-            "h2d_gb_per_step": round(out["remat_bytes"] / 1e9, 3),
-        },
-    }
+
+
+def stream_bench(torch, model: str, block_sizes, tokens_list, steps: int, h2d_gbs: float, base_kind: str = "nf4",
+                 n_slots: int = 2, remat: bool = True, layer_parts: bool = False) -> dict:
+    """Streamed vs resident step time of a Qwen2.5-shaped identity-mixing stack for each
+    (tokens, block size), with the bitwise check, H2D traffic, and the copy/compute
+    overlap measured by the pool's own events: copy_ms = device time of the H2D copies
+    per step, stall_ms = time the compute stream stood waiting for a copy per step;
+    copy time hidden under compute = copy_ms - stall_ms. base_kind "bf16" streams a dense
+    bf16 base (the experimental bf16_bitwise mode) instead of NF4. n_slots = device pool
+    slots of one block each (the resident run holds every block). One pinned host copy
+    of the base serves every block size (regroup). With `remat`, the first block size is
+    also run with rematerialisation (block-boundary states kept, each block's forward
+    recomputed in its backward visit). layer_parts: the pool copies and releases each
+    layer of a block on its own instead of one copy per block."""
+    from nf4_weight_streamed_amd import stack as ST
+
+    dims, n_layers = ST.QWEN25[model]
+    host_cls = ST.HostBF16Base if base_kind == "bf16" else ST.HostNF4Base
+    base = host_cls(dims, n_layers, block_sizes[0], ST.qwen_weight_fn())
+    lora = ST.LoraParams(dims, n_layers, RANK, ST.qwen_lora_fn())
+    load = {k: round(v, 3) if isinstance(v, float) else v for k, v in base.load_stats.items()}
+    print(f"[stream_bench] {model}: host base loaded in {load['seconds']:.1f} s", file=sys.stderr, flush=True)
+    fmt = "dense bf16" if base_kind == "bf16" else "NF4"
+    rows = []
+    for tokens in tokens_list:
+        h0, dh = _stack_inputs(torch, tokens, dims.hidden)
+        flops = n_layers * sum(4 * tokens * n * k + 6 * tokens * RANK * (n + k) for n, k in dims.shapes().values())
+        res = _stack_run(torch, ST, base, lora, tokens, h0, dh, steps, mode="resident")
+        print(f"[stream_bench] {model} T={tokens}: resident {res['s'] * 1e3:.1f} ms per step", file=sys.stderr,
+              flush=True)
+        for i, bs in enumerate(block_sizes):
+            b = base.regroup(bs)
+            got = _stack_run(torch, ST, b, lora, tokens, h0, dh, steps, mode="streamed", n_slots=n_slots,
+                             layer_parts=layer_parts)
+            r_s, s_s, nbytes = res["s"], got["s"], got["bytes"]
+            print(f"[stream_bench] {model} T={tokens} bs={bs}: streamed {s_s * 1e3:.1f} ms per step", file=sys.stderr,
+                  flush=True)
+            copy_s = nbytes / (h2d_gbs * 1e9)
+            c_ms, st_ms = got["copy_ms"], got["stall_ms"]
+            row = {
+                "workload": f"qwen2.5-{model}-shaped stack, {n_layers} layers, block_size {bs}, {n_slots} pool slots, "
+                            f"{tokens} tokens, {fmt} in pinned host, identity attention mixing, fwd+bwd",
+                "copies": "one per layer" if (layer_parts or not b.contiguous) else "one per block",
+                "tokens": tokens, "block_size": bs,
+                "bitwise_equal_to_resident": bool(torch.equal(res["y"], got["y"]) and torch.equal(res["dx"], got["dx"])),
+                "resident_ms_per_step": round(r_s * 1e3, 3),
+                "streamed_ms_per_step": round(s_s * 1e3, 3),
+                "streamed_over_resident": round(s_s / r_s, 3),
+                "streamed_tokens_per_s": round(tokens / s_s, 2),
+                "streamed_tflops": round(flops / s_s / 1e12, 2),
+                "resident_tflops": round(flops / r_s / 1e12, 2),
+                "h2d_gb_per_step": round(nbytes / 1e9, 3),
+                "h2d_gbs_achieved_over_step": round(nbytes / s_s / 1e9, 2),
+                "h2d_gbs_while_copying": round(nbytes / (c_ms * 1e-3) / 1e9, 2) if c_ms > 0 else None,
+                "h2d_gbs_pinned_peak_measured": round(h2d_gbs, 2),
+                "pcie_frac": round(nbytes / s_s / 1e9 / h2d_gbs, 4),
+                "pcie_floor_ratio": round(max(r_s, copy_s) / r_s, 3),
+                "copy_engine_busy_ms_per_step": round(c_ms, 3),
+                "compute_stall_ms_per_step": round(st_ms, 3),
+                "compute_busy_ms_per_step": round(s_s * 1e3 - st_ms, 3),
+                "copy_time_hidden_frac": round((c_ms - st_ms) / c_ms, 4) if c_ms > 0 else None,
+                "overlap_source": "HIP events of the pool: copy spans on the copy stream, acquire-wait spans on the "
+                                  "compute stream",
+                "host_base_gb": round(base.total_bytes() / 1e9, 3),
+            }
+            if remat and i == 0:
+                rm = _stack_run(torch, ST, b, lora, tokens, h0, dh, steps, mode="streamed", n_slots=n_slots,
+                                remat=True, layer_parts=layer_parts)
+                row["remat"] = {
+                    "bitwise_equal_to_resident": bool(torch.equal(res["y"], rm["y"]) and torch.equal(res["dx"], rm["dx"])),
+                    "streamed_ms_per_step": round(rm["s"] * 1e3, 3),
+                    "over_streamed": round(rm["s"] / s_s, 3),
+                    "activation_gb": round(rm["act"] / 1e9, 3),
+                    "activation_gb_stored": round(got["act"] / 1e9, 3),
+                    "h2d_gb_per_step": round(rm["bytes"] / 1e9, 3),
+                }
+                del rm
+            rows.append(row)
+            del got
+        del res, h0, dh
+    del base, lora
+    release_memory(torch)
+    return {"model": model, "load": load, "rows": rows}
+
+
+def release_memory(torch) -> None:
+    """Free cached device memory and cached pinned host blocks while the runtime is up
+    (not left to interpreter-exit destructors)."""
+    import gc
+
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    host_empty = getattr(torch._C, "_host_emptyCache", None)
+    if host_empty is not None:
+        host_empty()
 
 
 SMALL_T = (1, 8, 16, 32, 64)
@@ -538,12 +729,16 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--streamed", default="7b", help="stack for the streamed measurement: 7b, 32b, 72b or none")
-    ap.add_argument("--block-size", type=int, default=4)
+    ap.add_argument("--streamed", default="7b",
+                    help="comma-separated stacks for the streamed measurement (7b, 32b, 72b) or none")
+    ap.add_argument("--block-sizes", default="4", help="comma-separated block sizes of the streamed stacks")
     ap.add_argument("--slots", type=int, default=2, help="device pool slots (blocks) of the streamed stack")
     ap.add_argument("--stream-base", default="nf4", choices=("nf4", "bf16"),
                     help="format of the streamed base: nf4, or dense bf16 (the bf16_bitwise mode)")
-    ap.add_argument("--stack-tokens", type=int, default=512)
+    ap.add_argument("--stack-tokens", default="512", help="comma-separated token counts of the streamed stacks")
+    ap.add_argument("--no-remat", action="store_true", help="skip the rematerialisation run of the streamed stacks")
+    ap.add_argument("--layer-parts", action="store_true",
+                    help="streamed stacks: copy and release each layer of a block on its own")
     ap.add_argument("--stack-steps", type=int, default=3)
     ap.add_argument("--small-t-sweep", action="store_true",
                     help="instead of the layer step: per-projection fwd/bwd device time at T = 1..64 vs HBM bytes")
@@ -558,6 +753,12 @@ def main() -> int:
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
               "GPU; sharding across GPUs is not built)", file=sys.stderr)
+        return 2
+    models = [m for m in args.streamed.split(",") if m and m != "none"]
+    block_sizes = [int(v) for v in args.block_sizes.split(",") if v]
+    stack_tokens = [int(v) for v in args.stack_tokens.split(",") if v]
+    if any(m not in ("7b", "32b", "72b") for m in models) or not block_sizes or not stack_tokens:
+        print(f"--streamed takes 7b, 32b, 72b or none; --block-sizes and --stack-tokens need values", file=sys.stderr)
         return 2
 
     import torch
@@ -603,33 +804,58 @@ def main() -> int:
     for _ in range(args.warmup):
         run_step(lib, layer)
     torch.cuda.synchronize()
+    attribution = gemm_attribution(lib, torch, layer, ev)
 
-    # timed region: exactly `steps` steps, synchronized on both sides; the gate forward
-    # GEMM of every step is bracketed by HIP events on the stream it runs on
-    starts = [ev.create() for _ in range(args.steps)]
-    stops = [ev.create() for _ in range(args.steps)]
+    # timed region: exactly `steps` steps, synchronized on both sides; the gate
+    # projection's forward and backward GEMMs of every step are bracketed by HIP events
+    # recorded by the library on the stream they run on
+    prof = [{("fwd", "gate"): (ev.create(), ev.create()), ("bwd", "gate"): (ev.create(), ev.create())}
+            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_step(lib, layer, prof=("gate", starts[i], stops[i]))
+        run_step(lib, layer, prof=prof[i])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    gemm_ms = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
-    for e in starts + stops:
-        ev.destroy(e)
+    launch_s = {kind: sum(ev.elapsed_ms(*p[(kind, "gate")]) for p in prof) / len(prof) / 1e3 for kind in ("fwd", "bwd")}
+    for p in prof:
+        for a, b in p.values():
+            ev.destroy(a)
+            ev.destroy(b)
 
     mfma_meas = measured_mfma_tflops(lib, torch, ev)
     copy_meas = measured_copy_gbs(torch, ev)
     read_meas = measured_read_gbs(lib, torch, ev)
     quant = quantize_measure(lib, torch, ev, cpu=not args.no_cpu_baseline)
+    config0 = config0_measure(lib, torch, ev)
     ms = dt * 1000.0 / args.steps
     tokens_per_s = T_TOKENS / (dt / args.steps)
     tflops = step_flops(T_TOKENS, RANK) / (dt / args.steps) / 1e12
     n, k = INTER, HIDDEN
-    gate_flops = 2.0 * T_TOKENS * n * k + 2.0 * T_TOKENS * n * RANK
-    gate_bytes = n * k * 0.5 + n * (k // 64) * 4 + T_TOKENS * k * 2 + T_TOKENS * n * 2 + T_TOKENS * RANK * 4 + n * RANK * 2
-    avg_gemm_s = sum(gemm_ms) / len(gemm_ms) / 1000.0
-    achieved = gate_flops / avg_gemm_s / 1e12
+
+    def roofline(kind: str) -> dict:
+        kernel = "k_nf4_gemm_fwd" if kind == "fwd" else "k_nf4_gemm_bwd_dx"
+        f, b, sec = gemm_flops(kind, T_TOKENS, n, k, RANK), gemm_bytes(kind, T_TOKENS, n, k, RANK), launch_s[kind]
+        achieved = f / sec / 1e12
+        what = "y = x.W^T + LoRA epilogue" if kind == "fwd" else "dX = dY.W + LoRA term, dA share"
+        return {
+            "kernel": f"{kernel} (gate projection 18944x3584, 512 tokens: {what})",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(kernel),
+            "peak_measured": round(mfma_meas, 1),
+            "frac_vs_measured": round(achieved / mfma_meas, 4),
+            "avg_launch_us": round(sec * 1e6, 2),
+            "algorithmic_flops_per_launch": f,
+            "algorithmic_bytes_per_launch": b,
+            "hbm_gbs_algorithmic": round(b / sec / 1e9, 1),
+            "device_us_per_step_all_projections": attribution["us_per_step"][kernel],
+        }
+
+    dominant = "bwd" if attribution["dominant"] == "k_nf4_gemm_bwd_dx" else "fwd"
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
@@ -650,21 +876,10 @@ def main() -> int:
         },
         "tflops": round(tflops, 2),
         "mfma_frac_step": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-        "roofline": {
-            "kernel": "k_nf4_gemm_fwd (gate projection 18944x3584, 512 tokens, LoRA epilogue)",
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "peak_measured": round(mfma_meas, 1),
-            "frac_vs_measured": round(achieved / mfma_meas, 4),
-            "traffic": measured_traffic(),
-            "avg_launch_us": round(avg_gemm_s * 1e6, 2),
-            "algorithmic_flops_per_launch": gate_flops,
-            "algorithmic_bytes_per_launch": gate_bytes,
-            "hbm_gbs_algorithmic": round(gate_bytes / avg_gemm_s / 1e9, 1),
-        },
+        "roofline": roofline(dominant),
+        "roofline_other_gemm": roofline("fwd" if dominant == "bwd" else "bwd"),
+        "gemm_device_time": attribution,
+        "config0": config0,
         "quantize": quant,
         "denominators": {
             "mfma_bf16_tflops_published": MFMA_BF16_PEAK_TFLOPS,
@@ -674,14 +889,18 @@ def main() -> int:
             "hbm_read_gbs_measured": round(read_meas, 1),
         },
     }
-    if args.streamed != "none":
-        del layer
-        torch.cuda.empty_cache()
+    del layer
+    release_memory(torch)
+    if models:
         h2d = pinned_h2d_gbs(torch)
-        out["streamed"] = stream_bench(torch, args.streamed, args.block_size, args.stack_tokens, args.stack_steps, h2d,
-                                       args.stream_base, args.slots)
+        out["denominators"]["h2d_pinned_gbs_measured"] = round(h2d, 2)
+        runs = [stream_bench(torch, m, block_sizes, stack_tokens, args.stack_steps, h2d, args.stream_base, args.slots,
+                             remat=not args.no_remat, layer_parts=args.layer_parts) for m in models]
+        out["streamed"] = dict(runs[0]["rows"][0], load=runs[0]["load"])
+        out["streamed_all"] = runs
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
+    release_memory(torch)
     print(json.dumps(out), flush=True)
     return 0
 

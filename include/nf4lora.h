@@ -133,7 +133,7 @@ size_t nf4_lora_linear_fwd_workspace(int64_t T, int64_t N, int64_t K, int r);
  *                 contents on entry are ignored
  * r == 0 computes the base only (A, B, u_save may be NULL). T == 0 is a no-op.
  * Device pointers must be 16-byte aligned. Size limits (NF4_E_SHAPE beyond them,
- * here and in nf4_lora_linear_bwd): N, K <= 2^21, N*K <= 2^31, T <= 2^30.
+ * here and in nf4_lora_linear_bwd): N, K <= 2^21, N*K <= 2^31, T <= 2^23.
  */
 int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, int64_t K,
                         const uint16_t* x, int64_t T,
@@ -170,7 +170,7 @@ int nf4_lora_linear_bwd(const uint8_t* codes, const float* absmax, int64_t N, in
  * "bf16_bitwise": an experimental dense-BF16 base streamed blockwise with bitwise resident
  * parity). Same computation, arguments, workspace rules, limits and errors as
  * nf4_lora_linear_fwd / nf4_lora_linear_bwd, with the frozen base given directly as
- *   w   device bf16 [N][K], 16-byte aligned, N*K <= 2^30
+ *   w   device bf16 [N][K], 16-byte aligned, N*K < 2^30
  * in place of codes + absmax. Every T runs the 128-token kernels (no few-token path).
  */
 size_t nf4_lora_linear_fwd_bf16_workspace(int64_t T, int64_t N, int64_t K, int r);
@@ -302,6 +302,33 @@ int stream_pool_create(const nf4_host_block* blocks, int n_blocks, void* device_
                        size_t slot_bytes, int n_slots, nf4_stream copy_stream, nf4_pool** out);
 
 /*
+ * Create a pool whose blocks are made of parts, e.g. one pinned host range per layer
+ * (a block of block_size layers need not be one contiguous host allocation; [api]
+ * "patch_hf_model" Behavior 4: layers regrouped into blocks). Block b is the parts
+ * parts[part_begin[b]] .. parts[part_begin[b + 1] - 1], copied back to back into its
+ * slot (one hipMemcpyAsync each), so part i starts at the sum of the earlier parts'
+ * bytes; every part but a block's last must be a multiple of 256 bytes.
+ *   parts       HOST array of part_begin[n_blocks] descriptors (copied; the pinned
+ *               ranges must outlive the pool)
+ *   part_begin  HOST array of n_blocks + 1 increasing indices, part_begin[0] == 0
+ * Other arguments and errors as stream_pool_create (which is this call with one part
+ * per block). Each part of a held block can be released on its own
+ * (stream_pool_release_part): a later copy into the slot waits only for the release
+ * of the parts whose bytes it overwrites.
+ */
+int stream_pool_create_parts(const nf4_host_block* parts, const int* part_begin, int n_blocks,
+                             void* device_slab, size_t slot_bytes, int n_slots, nf4_stream copy_stream,
+                             nf4_pool** out);
+
+/*
+ * Order in which the parts of a block are copied from now on: ascending (0, the
+ * default) or descending (non-zero). A pass that uses a block's parts last to first
+ * (a backward pass over layers) sets descending, so that each copy starts with the
+ * part whose previous occupant was released first.
+ */
+int stream_pool_set_order(nf4_pool* pool, int descending);
+
+/*
  * Issue the H2D copy of `block` on the copy stream if it is not already in a
  * slot (no-op then). The victim slot is the least recently used slot not held
  * between acquire and release; the copy first waits for that slot's last
@@ -317,11 +344,20 @@ int stream_pool_prefetch(nf4_pool* pool, int block);
 int stream_pool_acquire(nf4_pool* pool, int block, nf4_stream compute, const void** dev);
 
 /*
- * End the use of `block` on `compute`: record the slot's last-use event there.
- * The slot stays valid (a later acquire of the same block is a hit) until a
- * prefetch/acquire of another block reuses it. NF4_E_STATE if not held.
+ * End the use of `block` on `compute`: record the last-use events of its parts
+ * (those not released by stream_pool_release_part) there. The slot stays valid (a
+ * later acquire of the same block is a hit) until a prefetch/acquire of another
+ * block reuses it. NF4_E_STATE if not held.
  */
 int stream_pool_release(nf4_pool* pool, int block, nf4_stream compute);
+
+/*
+ * End the use of one part of a held block on `compute`: record that part's last-use
+ * event there. The block stays held; stream_pool_release later records the parts not
+ * released this way. NF4_E_STATE if the block is not held or the part was already
+ * released during this hold; NF4_E_ARG for a part outside the block.
+ */
+int stream_pool_release_part(nf4_pool* pool, int block, int part, nf4_stream compute);
 
 /* Counters since creation (HOST struct). */
 int stream_pool_stats(const nf4_pool* pool, nf4_pool_stats* out);
@@ -331,6 +367,48 @@ int stream_pool_slot_block(const nf4_pool* pool, int slot, int* block_out);
 
 /* Wait for the copy stream to drain, then free the pool's events and state. */
 int stream_pool_destroy(nf4_pool* pool);
+
+/*
+ * Instrumentation of the copy/compute overlap ([hn]: blocks are prefetched one
+ * ahead on a dedicated stream so that copies overlap compute). While enabled, the
+ * pool records a pair of timing events around every H2D copy it issues (on the copy
+ * stream, after the copy's wait for the slot's last use: the pair spans the copy
+ * alone) and around every acquire's wait for a block's copy (on the compute stream:
+ * the pair spans the time that stream stood still for the copy; about zero when the
+ * prefetch had landed). stream_pool_timing_collect blocks until the recorded spans
+ * have completed, returns their sums in *out and forgets them. Enabling adds event
+ * records to the streams; it changes no result.
+ */
+typedef struct {
+    double copy_ms;    /* device time of the H2D copies issued while enabled */
+    double stall_ms;   /* time the compute streams waited at acquire for a copy */
+    uint64_t copies;   /* copies timed */
+    uint64_t acquires; /* acquires timed */
+} nf4_pool_timing;
+
+int stream_pool_timing_enable(nf4_pool* pool, int enable);
+int stream_pool_timing_collect(nf4_pool* pool, nf4_pool_timing* out);
+
+/*
+ * Byte layout of one block slab of the streamed base (the slab a pool slot holds;
+ * [api] "patch_hf_model" Behavior 4-6: layers regrouped into blocks of block_size;
+ * [consumer] "What you need besides VRAM": one slab per block in pinned host
+ * memory). For each of `layers` layers in turn and each of the n_proj projections
+ * in the order given: NF4 (dense == 0) codes [N][K/2] then absmax [N][K/64] fp32;
+ * dense (dense != 0) the bf16 weight [N][K]. Every piece starts at a 256-byte
+ * aligned offset, so a layer's bytes are a multiple of 256 and the slab of a block of
+ * L layers is the concatenation of L one-layer slabs; streamed and resident runs use
+ * the same offsets.
+ *   shapes       HOST int64 array of n_proj (N, K) pairs
+ *   offsets_out  HOST array of layers * n_proj * 2 size_t, or NULL: entry
+ *                [layer][proj][0] = codes (dense: weight) offset, [1] = absmax
+ *                offset (0 for dense)
+ *   bytes_out    HOST: the slab size
+ * NF4_E_ARG for NULL shapes/bytes_out or non-positive counts; NF4_E_SHAPE for an N or
+ * K outside 1..2^21 or a K that is not a multiple of 64.
+ */
+int nf4_block_layout(const int64_t* shapes, int n_proj, int layers, int dense, size_t* offsets_out,
+                     size_t* bytes_out);
 
 #ifdef __cplusplus
 }

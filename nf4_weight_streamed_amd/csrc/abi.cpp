@@ -115,10 +115,11 @@ int check_linear_common(const char* fn, const uint8_t* codes, const float* absma
     if (K % NF4_BLOCK != 0)
         return fail(NF4_E_SHAPE, "%s: K=%lld is not a multiple of %d", fn, (long long)K, NF4_BLOCK);
     if (N % 16 != 0) return fail(NF4_E_SHAPE, "%s: N=%lld is not a multiple of 16", fn, (long long)N);
-    // The kernels address one weight matrix, and 128-row tiles of x / dy, with 32-bit
-    // byte offsets: keep each such operand within 2^30 bytes.
-    if (N > (int64_t(1) << 21) || K > (int64_t(1) << 21) || N * K > (int64_t(1) << 31) || T > (int64_t(1) << 30))
-        return fail(NF4_E_SHAPE, "%s: sizes beyond the limits N, K <= 2^21, N*K <= 2^31, T <= 2^30 (N=%lld K=%lld T=%lld)",
+    // The kernels address one weight matrix with 32-bit byte offsets (within 2^30
+    // bytes) and every activation or partial through descriptors over at most one
+    // 128-row tile; T <= 2^23 keeps the tile counts of the 1-D grids below 2^31.
+    if (N > (int64_t(1) << 21) || K > (int64_t(1) << 21) || N * K > (int64_t(1) << 31) || T > (int64_t(1) << 23))
+        return fail(NF4_E_SHAPE, "%s: sizes beyond the limits N, K <= 2^21, N*K <= 2^31, T <= 2^23 (N=%lld K=%lld T=%lld)",
                     fn, (long long)N, (long long)K, (long long)T);
     if (r < 0 || r > NF4_MAX_RANK) return fail(NF4_E_ARG, "%s: rank r=%d outside 0..%d", fn, r, NF4_MAX_RANK);
     if (!std::isfinite(alpha)) return fail(NF4_E_ARG, "%s: alpha is not finite", fn);
@@ -136,8 +137,9 @@ int check_linear_dense(const char* fn, const uint16_t* w, int64_t N, int64_t K, 
     int st = check_linear_common(fn, kStandIn, reinterpret_cast<const float*>(kStandIn), N, K, T, r, alpha);
     if (st != NF4_OK) return st;
     if (!w) return fail(NF4_E_ARG, "%s: the bf16 base must not be NULL", fn);
-    if (N * K > (int64_t(1) << 30))
-        return fail(NF4_E_SHAPE, "%s: dense base beyond N*K <= 2^30 (N=%lld K=%lld)", fn, (long long)N, (long long)K);
+    // 2 bytes a weight in one descriptor, below the out-of-range offset the kernels use
+    if (N * K >= (int64_t(1) << 30))
+        return fail(NF4_E_SHAPE, "%s: dense base beyond N*K < 2^30 (N=%lld K=%lld)", fn, (long long)N, (long long)K);
     if (!aligned(w, 16)) return fail(NF4_E_ARG, "%s: the bf16 base must be 16-byte aligned", fn);
     return NF4_OK;
 }

@@ -188,23 +188,26 @@ __device__ void db_role(const uint16_t* __restrict__ dy, const float* __restrict
     // u: pair q of the thread is rank (tid + kThreads q) % 16 RB of tokens 2 tp, 2 tp + 1,
     // tp = (tid + kThreads q) / 16 RB
 
-    const auto rdy = make_rsrc(dy, uint32_t(T) * uint32_t(N) * 2u);
-    const auto ru = make_rsrc(u, uint32_t(T) * uint32_t(r) * 4u);
     u32x4 vdy[DV];
     float uv[UV];
+    // the descriptors cover one sub-chunk (at most DBT rows of dY and u): their byte
+    // sizes and offsets stay far inside 32 bits for any token count
     auto gload = [&](int t0) {
+        const uint32_t rows = uint32_t(max(0, min(DBT, t_end - t0)));
+        const auto rdy = make_rsrc(dy + size_t(t0) * N, rows * uint32_t(N) * 2u);
+        const auto ru = make_rsrc(u + size_t(t0) * r, rows * uint32_t(r) * 4u);
 #pragma unroll
         for (int i = 0; i < DV; ++i) {
-            const int t = t0 + DV * lt + i;
-            const bool ok = t < t_end && n0 + ln8 < N;
+            const int t = DV * lt + i;
+            const bool ok = t0 + t < t_end && n0 + ln8 < N;
             vdy[i] = buf_load16(rdy, ok ? (uint32_t(t) * uint32_t(N) + uint32_t(n0 + ln8)) * 2u : kOutOfRange);
         }
 #pragma unroll
         for (int i = 0; i < UV; ++i) {
             const int o = tid + kThreads * (i >> 1), j = o % (16 * RB), tp = o / (16 * RB);
-            const int t = t0 + 2 * tp + (i & 1);
-            uv[i] = buf_load_f32(ru, (t < t_end && j < r) ? (uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u
-                                                          : kOutOfRange);
+            const int t = 2 * tp + (i & 1);
+            uv[i] = buf_load_f32(ru, (t0 + t < t_end && j < r) ? (uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u
+                                                               : kOutOfRange);
         }
     };
     auto sstore = [&]() {

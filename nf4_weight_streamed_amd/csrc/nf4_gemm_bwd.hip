@@ -248,13 +248,21 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
     //   the shares in token-tile order: dA = ((d0 + d1) + d2) + ...)
     const int r = lora.r;
     if (tz == 0 && r > 0) {
+        // without contraction steps (no dX, or an empty piece) no barrier has run since
+        // the pair-table fill, which shares bytes with the epilogue's tiles
+        if (nb_begin >= nb_end) __syncthreads();
         uint16_t* const sg_hi = smem;             // [64][kTP]
         uint16_t* const sg_lo = smem + 64 * kTP;  // [64][kTP]
         uint16_t* const sxt = smem + 128 * kTP;   // [BK / 2][kTP]
         const int rp = (r + 15) & ~15;
-        // the partials region is padded to 256 bytes: 16-byte loads at 4-byte aligned
-        // offsets stay inside it; lanes j >= r are masked below
-        const auto rgp = make_rsrc(lora.gpart, (uint32_t(lora.parts) * uint32_t(T) * uint32_t(r) * 4u + 255u) & ~255u);
+        // one descriptor per partial over this tile's rows, so sizes and offsets stay
+        // small for any token count; 12 bytes of slack keep the last 16-byte load (4-byte
+        // aligned, lanes j >= r masked below) inside it, and inside the allocation: the
+        // partials region is padded to 256 bytes
+        const uint32_t gbytes = trows * uint32_t(r) * 4u + 12u;
+        auto gpart_rsrc = [&](int p) {
+            return make_rsrc(lora.gpart + (size_t(min(p, lora.parts - 1)) * T + m0) * r, gbytes);
+        };
         const auto rx = make_rsrc(lora.x + size_t(m0) * K, trows * uint32_t(K) * 2u);
         // every load of the staging is issued before the first is consumed (one memory
         // round trip at the end of the kernel, not one per loop trip)
@@ -292,17 +300,18 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
             for (int i = 0; i < GI; ++i) gsum[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             for (int p0 = 0; p0 < lora.parts; p0 += GR) {  // partials in partial order
                 f32x4 pv[GI][GR];
+                __amdgpu_buffer_rsrc_t rgp[GR];
+#pragma unroll
+                for (int pp = 0; pp < GR; ++pp) rgp[pp] = gpart_rsrc(p0 + pp);
 #pragma unroll
                 for (int i = 0; i < GI; ++i) {
                     const int o = tid + kThreads * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
                     const bool ok = m0 + t < T && j < r;
-                    const uint32_t off = (uint32_t(m0 + t) * uint32_t(r) + uint32_t(j)) * 4u;
+                    const uint32_t off = (uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u;
 #pragma unroll
                     for (int pp = 0; pp < GR; ++pp)
                         pv[i][pp] = __builtin_bit_cast(
-                            f32x4, buf_load16(rgp, ok && p0 + pp < lora.parts
-                                                       ? off + uint32_t(p0 + pp) * uint32_t(T) * uint32_t(r) * 4u
-                                                       : kOutOfRange));
+                            f32x4, buf_load16(rgp[pp], ok && p0 + pp < lora.parts ? off : kOutOfRange));
                 }
 #pragma unroll
                 for (int i = 0; i < GI; ++i)

@@ -276,10 +276,14 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
         uint16_t* su_hi = &sA[0][0];
         uint16_t* su_lo = &sA[1][0];
         const int rp = (r + 15) & ~15;
-        // the partials region is padded to 256 bytes: 16-byte loads at 4-byte aligned
-        // offsets stay inside it; lanes j >= r are masked below
-        const uint32_t ubytes = (uint32_t(lora.parts) * uint32_t(T) * uint32_t(r) * 4u + 255u) & ~255u;
-        const auto rup = make_rsrc(lora.upart, ubytes);
+        // one descriptor per partial over this tile's rows, so sizes and offsets stay
+        // small for any token count; 12 bytes of slack keep the last 16-byte load (4-byte
+        // aligned, lanes j >= r masked below) inside it, and inside the allocation: the
+        // partials region is padded to 256 bytes
+        const uint32_t ubytes = uint32_t(max(0, min(BM, T - m0))) * uint32_t(r) * 4u + 12u;
+        auto upart_rsrc = [&](int p) {
+            return make_rsrc(lora.upart + (size_t(min(p, lora.parts - 1)) * T + m0) * r, ubytes);
+        };
         const auto rb = make_rsrc(lora.B, uint32_t(N) * uint32_t(r) * 2u);
         const bool write_u = tc == 0;
         // B values of one 16-rank slice for this lane's fragments (lane: column n, ranks
@@ -312,17 +316,18 @@ __global__ __launch_bounds__(64 * NW, kFwdOccupancy) void k_nf4_gemm_fwd(
             for (int i = 0; i < UI; ++i) usum[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             for (int p0 = 0; p0 < lora.parts; p0 += UR) {  // partials in partial order
                 f32x4 pv[UI][UR];
+                __amdgpu_buffer_rsrc_t rup[UR];
+#pragma unroll
+                for (int pp = 0; pp < UR; ++pp) rup[pp] = upart_rsrc(p0 + pp);
 #pragma unroll
                 for (int i = 0; i < UI; ++i) {
                     const int o = tid + NT * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
                     const bool ok = m0 + t < T && j < r;
-                    const uint32_t off = (uint32_t(m0 + t) * uint32_t(r) + uint32_t(j)) * 4u;
+                    const uint32_t off = (uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u;
 #pragma unroll
                     for (int pp = 0; pp < UR; ++pp)
                         pv[i][pp] = __builtin_bit_cast(
-                            f32x4, buf_load16(rup, ok && p0 + pp < lora.parts
-                                                       ? off + uint32_t(p0 + pp) * uint32_t(T) * uint32_t(r) * 4u
-                                                       : kOutOfRange));
+                            f32x4, buf_load16(rup[pp], ok && p0 + pp < lora.parts ? off : kOutOfRange));
                 }
 #pragma unroll
                 for (int i = 0; i < UI; ++i)

@@ -1,44 +1,17 @@
-// Blockwise residency of the frozen NF4 base: a pool of pre-allocated device
-// slots fed from pinned host slabs on a dedicated copy stream.
-//
-// HN comment thread on streaming the frozen base (main comment): the base sits
-// in host RAM and streams into a small pool of pre-allocated device buffers,
-// prefetched one ahead on a dedicated stream. Poros API reference,
-// "patch_hf_model" Behavior 5-6: layers regrouped into blocks; a block manager
-// with cross-stream safety. "Poros on consumer GPUs", "What you need besides
-// VRAM": the streamed base lives in pinned host memory, needed for async copies.
-//
-// Ordering is carried entirely by HIP events on the two streams:
-//   ready[slot]    recorded on the copy stream after the block's H2D copy;
-//                  acquire makes the compute stream wait on it;
-//   last_use[slot] recorded on the compute stream at release; the copy that
-//                  later overwrites the slot waits on it first.
-// The host never blocks (except in destroy), and a slot is never overwritten
-// while a kernel enqueued before its release may still read it.
+// Blockwise residency of the frozen NF4 base on HIP: the pool state machine of
+// pool_core.h driven by a HIP engine (hipMemcpyAsync on the dedicated copy stream,
+// hipEventRecord / hipStreamWaitEvent between the copy and compute streams), plus
+// optional timing spans for the copy/compute overlap. See pool_core.h for the ordering
+// rules; the pages behind them: HN comment thread on streaming the frozen base (main
+// comment); Poros API reference, "patch_hf_model" Behavior 4-6; "Poros on consumer
+// GPUs", "What you need besides VRAM" (the streamed base lives in pinned host memory,
+// needed for asynchronous copies).
 #include <cstdint>
 #include <vector>
 
 #include "../../include/nf4lora.h"
 #include "common.h"
-
-struct nf4_pool {
-    struct Slot {
-        int block = -1;
-        bool held = false;
-        bool has_last_use = false;
-        uint64_t stamp = 0;
-        hipEvent_t ready = nullptr;
-        hipEvent_t last_use = nullptr;
-    };
-    std::vector<nf4_host_block> blocks;
-    std::vector<int> where;  // block -> slot, or -1
-    std::vector<Slot> slots;
-    char* slab = nullptr;
-    size_t slot_bytes = 0;
-    hipStream_t copy = nullptr;
-    uint64_t clock = 0;
-    nf4_pool_stats stats{};
-};
+#include "pool_core.h"
 
 using nf4::fail;
 
@@ -49,50 +22,105 @@ int hip_ok(hipError_t e, const char* what) {
     return NF4_OK;
 }
 
-int check_block(const nf4_pool* p, int block, const char* fn) {
-    if (!p) return fail(NF4_E_ARG, "%s: NULL pool", fn);
-    if (block < 0 || block >= int(p->blocks.size()))
-        return fail(NF4_E_ARG, "%s: block %d outside 0..%d", fn, block, int(p->blocks.size()) - 1);
-    return NF4_OK;
-}
+struct HipEngine {
+    using Event = hipEvent_t;
+    using Stream = hipStream_t;
+    struct Span {  // two timing events around one interval on one stream
+        hipEvent_t a = nullptr, b = nullptr;
+    };
+    // timing (stream_pool_timing_enable): copy spans on the copy stream, stall spans
+    // around each acquire's wait on the compute stream, and recycled events
+    bool timing = false;
+    std::vector<Span> copy_spans, stall_spans;
+    std::vector<hipEvent_t> spare;
 
-// Issue the copy of `block` into a victim slot; returns the slot or a negative status.
-int issue_copy(nf4_pool* p, int block) {
-    int victim = -1;
-    for (int i = 0; i < int(p->slots.size()); ++i) {
-        const auto& s = p->slots[i];
-        if (s.held) continue;
-        if (s.block < 0) {  // an empty slot is always the first choice
-            victim = i;
-            break;
+    int create_event(hipEvent_t* e) {
+        return hip_ok(hipEventCreateWithFlags(e, hipEventDisableTiming), "stream_pool: hipEventCreate");
+    }
+    void destroy_event(hipEvent_t e) {
+        if (e) (void)hipEventDestroy(e);
+    }
+    int record(hipEvent_t e, hipStream_t s) { return hip_ok(hipEventRecord(e, s), "stream_pool: record event"); }
+    int wait(hipStream_t s, hipEvent_t e) { return hip_ok(hipStreamWaitEvent(s, e, 0), "stream_pool: wait event"); }
+
+    hipEvent_t timing_event() {
+        if (!spare.empty()) {
+            hipEvent_t e = spare.back();
+            spare.pop_back();
+            return e;
         }
-        if (victim < 0 || s.stamp < p->slots[victim].stamp) victim = i;
+        hipEvent_t e = nullptr;
+        return hipEventCreate(&e) == hipSuccess ? e : nullptr;
     }
-    if (victim < 0)
-        return fail(NF4_E_BUSY, "stream_pool: all %d slots are held; release a block before prefetching block %d",
-                    int(p->slots.size()), block);
-    auto& s = p->slots[victim];
-    if (s.has_last_use) {
-        int st = hip_ok(hipStreamWaitEvent(p->copy, s.last_use, 0), "stream_pool: wait for last use");
-        if (st != NF4_OK) return st;
+    int span_begin(Span& sp, hipStream_t stream) {
+        if (!timing) return NF4_OK;
+        sp.a = timing_event();
+        sp.b = timing_event();
+        if (!sp.a || !sp.b) return fail(NF4_E_HIP, "stream_pool: hipEventCreate failed (timing)");
+        return hip_ok(hipEventRecord(sp.a, stream), "stream_pool: record timing event");
     }
-    const nf4_host_block& hb = p->blocks[block];
-    int st = hip_ok(hipMemcpyAsync(p->slab + size_t(victim) * p->slot_bytes, hb.host, hb.bytes,
-                                   hipMemcpyHostToDevice, p->copy),
-                    "stream_pool: H2D copy");
-    if (st != NF4_OK) return st;
-    st = hip_ok(hipEventRecord(s.ready, p->copy), "stream_pool: record ready");
-    if (st != NF4_OK) return st;
-    if (s.block >= 0) {
-        p->where[s.block] = -1;
-        p->stats.evictions++;
+    int span_end(Span& sp, hipStream_t stream, std::vector<Span>& into) {
+        if (!timing) return NF4_OK;
+        int st = hip_ok(hipEventRecord(sp.b, stream), "stream_pool: record timing event");
+        if (st == NF4_OK) into.push_back(sp);
+        return st;
     }
-    s.block = block;
-    s.stamp = ++p->clock;
-    p->where[block] = victim;
-    p->stats.copies++;
-    p->stats.bytes_copied += hb.bytes;
-    return victim;
+
+    // one part's H2D copy (after its waits: the span is the copy alone)
+    int copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+        Span sp;
+        int st = span_begin(sp, s);
+        if (st == NF4_OK)
+            st = hip_ok(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s), "stream_pool: H2D copy");
+        if (st == NF4_OK) st = span_end(sp, s, copy_spans);
+        return st;
+    }
+    // the compute stream's wait for a block's copy (the span is the time it stood still)
+    int acquire_wait(hipStream_t compute, hipEvent_t ready) {
+        Span sp;
+        int st = span_begin(sp, compute);
+        if (st == NF4_OK) st = wait(compute, ready);
+        if (st == NF4_OK) st = span_end(sp, compute, stall_spans);
+        return st;
+    }
+
+    void destroy_spans() {
+        for (auto* v : {&copy_spans, &stall_spans})
+            for (auto& sp : *v) {
+                (void)hipEventSynchronize(sp.b);  // their work is already enqueued
+                (void)hipEventDestroy(sp.a);
+                (void)hipEventDestroy(sp.b);
+            }
+        for (hipEvent_t e : spare) (void)hipEventDestroy(e);
+        copy_spans.clear();
+        stall_spans.clear();
+        spare.clear();
+    }
+};
+
+}  // namespace
+
+struct nf4_pool {
+    HipEngine eng;
+    nf4::PoolCore<HipEngine> core;
+};
+
+namespace {
+
+int create(const nf4_host_block* parts, const int* part_begin, int n_blocks, void* device_slab, size_t slot_bytes,
+           int n_slots, nf4_stream copy_stream, nf4_pool** out) {
+    if (!out) return fail(NF4_E_ARG, "stream_pool_create: NULL out");
+    *out = nullptr;
+    auto* p = new nf4_pool;
+    const int st = p->core.init(&p->eng, parts, part_begin, n_blocks, device_slab, slot_bytes, n_slots,
+                                static_cast<hipStream_t>(copy_stream), copy_stream != nullptr);
+    if (st != NF4_OK) {
+        p->core.destroy_events();
+        delete p;
+        return st;
+    }
+    *out = p;
+    return NF4_OK;
 }
 
 }  // namespace
@@ -101,109 +129,123 @@ extern "C" {
 
 int stream_pool_create(const nf4_host_block* blocks, int n_blocks, void* device_slab, size_t slot_bytes, int n_slots,
                        nf4_stream copy_stream, nf4_pool** out) {
-    if (!out) return fail(NF4_E_ARG, "stream_pool_create: NULL out");
-    *out = nullptr;
-    if (!blocks || n_blocks <= 0 || n_slots <= 0 || !device_slab || !copy_stream)
-        return fail(NF4_E_ARG, "stream_pool_create: need blocks, n_blocks > 0, n_slots > 0, a device slab and a copy "
-                               "stream (got n_blocks=%d n_slots=%d)", n_blocks, n_slots);
-    if (slot_bytes == 0 || slot_bytes % 256 != 0 || reinterpret_cast<uintptr_t>(device_slab) % 256 != 0)
-        return fail(NF4_E_ARG, "stream_pool_create: slot_bytes (%zu) and the slab address must be multiples of 256",
-                    slot_bytes);
-    for (int b = 0; b < n_blocks; ++b) {
-        if (!blocks[b].host) return fail(NF4_E_ARG, "stream_pool_create: block %d has a NULL host pointer", b);
-        if (blocks[b].bytes > slot_bytes)
-            return fail(NF4_E_OOM, "stream_pool_create: block %d needs %zu bytes but a slot holds %zu (%d slots, %zu "
-                                   "bytes of device slab requested)", b, blocks[b].bytes, slot_bytes, n_slots,
-                        slot_bytes * size_t(n_slots));
-    }
-    auto* p = new nf4_pool;
-    p->blocks.assign(blocks, blocks + n_blocks);
-    p->where.assign(n_blocks, -1);
-    p->slots.resize(n_slots);
-    p->slab = static_cast<char*>(device_slab);
-    p->slot_bytes = slot_bytes;
-    p->copy = static_cast<hipStream_t>(copy_stream);
-    for (auto& s : p->slots) {
-        if (hipEventCreateWithFlags(&s.ready, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&s.last_use, hipEventDisableTiming) != hipSuccess) {
-            stream_pool_destroy(p);
-            return fail(NF4_E_HIP, "stream_pool_create: hipEventCreate failed");
-        }
-    }
-    *out = p;
+    if (n_blocks <= 0 || !blocks) return create(blocks, nullptr, n_blocks, device_slab, slot_bytes, n_slots, copy_stream, out);
+    std::vector<int> begin(size_t(n_blocks) + 1);
+    for (int b = 0; b <= n_blocks; ++b) begin[b] = b;  // one part per block
+    return create(blocks, begin.data(), n_blocks, device_slab, slot_bytes, n_slots, copy_stream, out);
+}
+
+int stream_pool_create_parts(const nf4_host_block* parts, const int* part_begin, int n_blocks, void* device_slab,
+                             size_t slot_bytes, int n_slots, nf4_stream copy_stream, nf4_pool** out) {
+    return create(parts, part_begin, n_blocks, device_slab, slot_bytes, n_slots, copy_stream, out);
+}
+
+int stream_pool_set_order(nf4_pool* p, int descending) {
+    if (!p) return fail(NF4_E_ARG, "stream_pool_set_order: NULL pool");
+    p->core.descending = descending != 0;
     return NF4_OK;
 }
 
 int stream_pool_prefetch(nf4_pool* p, int block) {
-    int st = check_block(p, block, "stream_pool_prefetch");
-    if (st != NF4_OK) return st;
-    if (p->where[block] >= 0) return NF4_OK;  // already issued or resident
-    st = issue_copy(p, block);
-    return st < 0 ? st : NF4_OK;
+    if (!p) return fail(NF4_E_ARG, "stream_pool_prefetch: NULL pool");
+    return p->core.prefetch(block);
 }
 
 int stream_pool_acquire(nf4_pool* p, int block, nf4_stream compute, const void** dev) {
-    int st = check_block(p, block, "stream_pool_acquire");
-    if (st != NF4_OK) return st;
-    if (!dev) return fail(NF4_E_ARG, "stream_pool_acquire: NULL dev");
-    int slot = p->where[block];
-    if (slot >= 0 && p->slots[slot].held)
-        return fail(NF4_E_STATE, "stream_pool_acquire: block %d is already held", block);
-    if (slot < 0) {
-        slot = issue_copy(p, block);
-        if (slot < 0) return slot;
-        p->stats.misses++;
-    } else {
-        p->stats.hits++;
-    }
-    auto& s = p->slots[slot];
-    st = hip_ok(hipStreamWaitEvent(static_cast<hipStream_t>(compute), s.ready, 0), "stream_pool_acquire: wait");
-    if (st != NF4_OK) return st;
-    s.held = true;
-    s.stamp = ++p->clock;
-    *dev = p->slab + size_t(slot) * p->slot_bytes;
-    return NF4_OK;
+    if (!p) return fail(NF4_E_ARG, "stream_pool_acquire: NULL pool");
+    return p->core.acquire(block, static_cast<hipStream_t>(compute), dev);
+}
+
+int stream_pool_release_part(nf4_pool* p, int block, int part, nf4_stream compute) {
+    if (!p) return fail(NF4_E_ARG, "stream_pool_release_part: NULL pool");
+    return p->core.release_part(block, part, static_cast<hipStream_t>(compute));
 }
 
 int stream_pool_release(nf4_pool* p, int block, nf4_stream compute) {
-    int st = check_block(p, block, "stream_pool_release");
-    if (st != NF4_OK) return st;
-    const int slot = p->where[block];
-    if (slot < 0 || !p->slots[slot].held)
-        return fail(NF4_E_STATE, "stream_pool_release: block %d is not held", block);
-    auto& s = p->slots[slot];
-    st = hip_ok(hipEventRecord(s.last_use, static_cast<hipStream_t>(compute)), "stream_pool_release: record");
-    if (st != NF4_OK) return st;
-    s.held = false;
-    s.has_last_use = true;
-    s.stamp = ++p->clock;
-    return NF4_OK;
+    if (!p) return fail(NF4_E_ARG, "stream_pool_release: NULL pool");
+    return p->core.release(block, static_cast<hipStream_t>(compute));
 }
 
 int stream_pool_stats(const nf4_pool* p, nf4_pool_stats* out) {
     if (!p || !out) return fail(NF4_E_ARG, "stream_pool_stats: NULL argument");
-    *out = p->stats;
+    *out = p->core.stats;
     return NF4_OK;
 }
 
 int stream_pool_slot_block(const nf4_pool* p, int slot, int* block_out) {
     if (!p || !block_out) return fail(NF4_E_ARG, "stream_pool_slot_block: NULL argument");
-    if (slot < 0 || slot >= int(p->slots.size()))
-        return fail(NF4_E_ARG, "stream_pool_slot_block: slot %d outside 0..%d", slot, int(p->slots.size()) - 1);
-    *block_out = p->slots[slot].block;
+    if (slot < 0 || slot >= int(p->core.slots.size()))
+        return fail(NF4_E_ARG, "stream_pool_slot_block: slot %d outside 0..%d", slot, int(p->core.slots.size()) - 1);
+    *block_out = p->core.slots[slot].block;
     return NF4_OK;
+}
+
+int stream_pool_timing_enable(nf4_pool* p, int enable) {
+    if (!p) return fail(NF4_E_ARG, "stream_pool_timing_enable: NULL pool");
+    p->eng.timing = enable != 0;
+    return NF4_OK;
+}
+
+int stream_pool_timing_collect(nf4_pool* p, nf4_pool_timing* out) {
+    if (!p || !out) return fail(NF4_E_ARG, "stream_pool_timing_collect: NULL argument");
+    *out = nf4_pool_timing{};
+    int st = NF4_OK;
+    auto sum = [&](std::vector<HipEngine::Span>& spans, double& ms, uint64_t& count) {
+        for (auto& sp : spans) {
+            float v = 0.0f;
+            if (st == NF4_OK) st = hip_ok(hipEventSynchronize(sp.b), "stream_pool_timing_collect: wait");
+            if (st == NF4_OK) st = hip_ok(hipEventElapsedTime(&v, sp.a, sp.b), "stream_pool_timing_collect: elapsed");
+            ms += v;
+            count++;
+            p->eng.spare.push_back(sp.a);
+            p->eng.spare.push_back(sp.b);
+        }
+        spans.clear();
+    };
+    sum(p->eng.copy_spans, out->copy_ms, out->copies);
+    sum(p->eng.stall_spans, out->stall_ms, out->acquires);
+    return st;
 }
 
 int stream_pool_destroy(nf4_pool* p) {
     if (!p) return NF4_OK;
     int st = NF4_OK;
-    if (p->copy) st = hip_ok(hipStreamSynchronize(p->copy), "stream_pool_destroy: drain copy stream");
-    for (auto& s : p->slots) {
-        if (s.ready) (void)hipEventDestroy(s.ready);
-        if (s.last_use) (void)hipEventDestroy(s.last_use);
-    }
+    if (p->core.copy) st = hip_ok(hipStreamSynchronize(p->core.copy), "stream_pool_destroy: drain copy stream");
+    p->core.destroy_events();
+    p->eng.destroy_spans();
     delete p;
     return st;
 }
 
 }  // extern "C"
+
+extern "C" int nf4_block_layout(const int64_t* shapes, int n_proj, int layers, int dense, size_t* offsets_out,
+                                size_t* bytes_out) {
+    if (!shapes || !bytes_out || n_proj <= 0 || layers <= 0)
+        return fail(NF4_E_ARG, "nf4_block_layout: need shapes, bytes_out, n_proj > 0 and layers > 0 (got n_proj=%d "
+                               "layers=%d)", n_proj, layers);
+    for (int j = 0; j < n_proj; ++j) {
+        const int64_t n = shapes[2 * j], k = shapes[2 * j + 1];
+        if (n <= 0 || k <= 0 || k % NF4_BLOCK != 0 || n > (int64_t(1) << 21) || k > (int64_t(1) << 21))
+            return fail(NF4_E_SHAPE, "nf4_block_layout: projection %d has N=%lld K=%lld (need N, K in 1..2^21, K %% %d "
+                                     "== 0)", j, (long long)n, (long long)k, NF4_BLOCK);
+    }
+    auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
+    size_t off = 0;
+    for (int l = 0; l < layers; ++l)
+        for (int j = 0; j < n_proj; ++j) {
+            const size_t n = size_t(shapes[2 * j]), k = size_t(shapes[2 * j + 1]);
+            size_t* o = offsets_out ? offsets_out + (size_t(l) * n_proj + j) * 2 : nullptr;
+            if (dense) {
+                if (o) o[0] = off, o[1] = 0;
+                off = align(off + n * k * 2);
+            } else {
+                if (o) o[0] = off;
+                off = align(off + n * k / 2);
+                if (o) o[1] = off;
+                off = align(off + n * (k / NF4_BLOCK) * 4);
+            }
+        }
+    *bytes_out = off;
+    return NF4_OK;
+}

@@ -35,6 +35,11 @@ class HostBlock(C.Structure):
     _fields_ = [("host", C.c_void_p), ("bytes", C.c_size_t)]
 
 
+class PoolTiming(C.Structure):
+    _fields_ = [("copy_ms", C.c_double), ("stall_ms", C.c_double), ("copies", C.c_uint64),
+                ("acquires", C.c_uint64)]
+
+
 class PoolStats(C.Structure):
     _fields_ = [("bytes_copied", C.c_uint64), ("copies", C.c_uint64), ("hits", C.c_uint64),
                 ("misses", C.c_uint64), ("evictions", C.c_uint64)]
@@ -78,6 +83,14 @@ def _load() -> C.CDLL:
         "stream_pool_stats": (i32, [vp, C.POINTER(PoolStats)]),
         "stream_pool_slot_block": (i32, [vp, i32, C.POINTER(i32)]),
         "stream_pool_destroy": (i32, [vp]),
+        "stream_pool_create_parts": (i32, [C.POINTER(HostBlock), C.POINTER(i32), i32, vp, sz, i32, vp,
+                                           C.POINTER(vp)]),
+        "stream_pool_set_order": (i32, [vp, i32]),
+        "stream_pool_release_part": (i32, [vp, i32, i32, vp]),
+        "stream_pool_timing_enable": (i32, [vp, i32]),
+        "stream_pool_timing_collect": (i32, [vp, C.POINTER(PoolTiming)]),
+        "nf4_block_layout": (i32, [C.POINTER(C.c_int64), i32, i32, i32, C.POINTER(C.c_size_t),
+                                   C.POINTER(C.c_size_t)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -426,22 +439,77 @@ def repeat_kv_bwd(da, kv: int, head_dim: int, out=None, stream=None):
     return out
 
 
-class StreamPool:
-    """Thin handle over stream_pool_*: pinned host blocks -> device slots on a copy stream."""
+def block_layout(shapes, layers: int, dense: bool = False):
+    """nf4_block_layout: ([layer][proj] = (codes or weight offset, absmax offset)), slab bytes)
+    for the projections' (N, K) `shapes` in order."""
+    n_proj = len(shapes)
+    arr = (C.c_int64 * (2 * n_proj))(*[int(v) for nk in shapes for v in nk])
+    offs = (C.c_size_t * (2 * n_proj * layers))()
+    total = C.c_size_t()
+    _check(_lib.nf4_block_layout(arr, n_proj, int(layers), int(bool(dense)), offs, C.byref(total)))
+    table = [[(offs[(l * n_proj + j) * 2], offs[(l * n_proj + j) * 2 + 1]) for j in range(n_proj)]
+             for l in range(layers)]
+    return table, total.value
 
-    def __init__(self, host_blocks, device_slab: torch.Tensor, slot_bytes: int, n_slots: int, copy_stream):
+
+_HIP = None
+
+
+def _hip_runtime() -> C.CDLL:
+    """The HIP runtime torch has loaded (same soname): for page-locked host memory."""
+    global _HIP
+    if _HIP is None:
+        _HIP = C.CDLL("libamdhip64.so.7")
+        _HIP.hipHostMalloc.argtypes = [C.POINTER(C.c_void_p), C.c_size_t, C.c_uint]
+        _HIP.hipHostFree.argtypes = [C.c_void_p]
+    return _HIP
+
+
+def pinned_empty(nbytes: int) -> torch.Tensor:
+    """A uint8 CPU tensor over page-locked host memory of exactly `nbytes` bytes
+    (hipHostMalloc; torch's pinned allocator rounds every request up to a power of
+    two). The memory belongs to the buffer object the tensor wraps and is freed
+    (hipHostFree, which waits for the device) once the last view of it is gone."""
+    hip = _hip_runtime()
+    p = C.c_void_p()
+    nbytes = max(int(nbytes), 1)
+    rc = hip.hipHostMalloc(C.byref(p), C.c_size_t(nbytes), 0)
+    if rc != 0 or not p.value:
+        raise Nf4Error(NF4_E_OOM, f"hipHostMalloc of {nbytes} bytes of pinned host memory failed (hipError {rc})")
+    addr = p.value
+
+    class _PinnedOwner(C.c_uint8 * nbytes):
+        def __del__(self):
+            hip.hipHostFree(C.c_void_p(addr))
+
+    return torch.frombuffer(_PinnedOwner.from_address(addr), dtype=torch.uint8)
+
+
+class StreamPool:
+    """Thin handle over stream_pool_*: pinned host blocks -> device slots on a copy stream.
+
+    host_blocks: one pinned uint8 tensor per block, or (with part_begin) one per part,
+    block b being parts part_begin[b] .. part_begin[b + 1] - 1 (stream_pool_create_parts)."""
+
+    def __init__(self, host_blocks, device_slab: torch.Tensor, slot_bytes: int, n_slots: int, copy_stream,
+                 part_begin=None):
         arr = (HostBlock * len(host_blocks))()
         for i, hb in enumerate(host_blocks):
             if hb.device.type != "cpu" or not hb.is_pinned():
-                raise ValueError(f"host block {i} must be pinned host memory")
+                raise ValueError(f"host range {i} must be pinned host memory")
             arr[i].host = hb.data_ptr()
             arr[i].bytes = hb.numel() * hb.element_size()
-        self._blocks = list(host_blocks)     # keep the slabs alive
+        self._blocks = list(host_blocks)     # keep the ranges alive
         self._slab = device_slab
         self._copy = copy_stream
         h = C.c_void_p()
-        _check(_lib.stream_pool_create(arr, len(host_blocks), _ptr(device_slab), slot_bytes, n_slots,
-                                       _stream(copy_stream), C.byref(h)))
+        if part_begin is None:
+            _check(_lib.stream_pool_create(arr, len(host_blocks), _ptr(device_slab), slot_bytes, n_slots,
+                                           _stream(copy_stream), C.byref(h)))
+        else:
+            pb = (C.c_int * len(part_begin))(*[int(v) for v in part_begin])
+            _check(_lib.stream_pool_create_parts(arr, pb, len(part_begin) - 1, _ptr(device_slab), slot_bytes, n_slots,
+                                                 _stream(copy_stream), C.byref(h)))
         self._h = h
         self.slot_bytes = slot_bytes
         self.n_slots = n_slots
@@ -449,10 +517,16 @@ class StreamPool:
     def prefetch(self, block: int) -> None:
         _check(_lib.stream_pool_prefetch(self._h, block))
 
+    def set_order(self, descending: bool) -> None:
+        _check(_lib.stream_pool_set_order(self._h, int(bool(descending))))
+
     def acquire(self, block: int, stream=None) -> int:
         dev = C.c_void_p()
         _check(_lib.stream_pool_acquire(self._h, block, _stream(stream), C.byref(dev)))
         return dev.value
+
+    def release_part(self, block: int, part: int, stream=None) -> None:
+        _check(_lib.stream_pool_release_part(self._h, block, part, _stream(stream)))
 
     def release(self, block: int, stream=None) -> None:
         _check(_lib.stream_pool_release(self._h, block, _stream(stream)))
@@ -461,6 +535,16 @@ class StreamPool:
         s = PoolStats()
         _check(_lib.stream_pool_stats(self._h, C.byref(s)))
         return {f: getattr(s, f) for f, _ in PoolStats._fields_}
+
+    def timing_enable(self, enable: bool = True) -> None:
+        """Record copy and acquire-stall spans (stream_pool_timing_enable)."""
+        _check(_lib.stream_pool_timing_enable(self._h, int(bool(enable))))
+
+    def timing_collect(self) -> dict:
+        """Sums of the spans recorded since the last collect (waits for them to complete)."""
+        t = PoolTiming()
+        _check(_lib.stream_pool_timing_collect(self._h, C.byref(t)))
+        return {f: getattr(t, f) for f, _ in PoolTiming._fields_}
 
     def slot_block(self, slot: int) -> int:
         b = C.c_int()

@@ -1,10 +1,11 @@
 """Blockwise weight-streamed stack of NF4-LoRA decoder layers on one GPU.
 
-The frozen NF4 base of `block_size` layers at a time lives in one pinned host
-slab per block ("Poros on consumer GPUs", "What you need besides VRAM": the
-streamed base is pinned host memory; Poros API reference, "patch_hf_model"
-Behavior 4-6: layers regrouped into blocks of block_size, default 4, under a
-block manager). In streamed mode the slabs pass through a pool of device slots:
+The frozen NF4 base lives in one pinned host buffer, layer after layer; a block
+of `block_size` layers is the contiguous slab of its layers ("Poros on consumer
+GPUs", "What you need besides VRAM": the streamed base is pinned host memory;
+Poros API reference, "patch_hf_model" Behavior 4-6: layers regrouped into blocks
+of block_size, default 4, under a block manager). In streamed mode the slabs pass
+through a pool of device slots:
 block b is acquired on the compute stream while block b+1 is prefetched on a
 dedicated copy stream (HN comment thread on streaming the frozen base, main
 comment: prefetched one ahead on a dedicated stream). In resident mode every
@@ -70,120 +71,176 @@ QWEN25 = {
 }
 
 
-def _align(v: int, a: int = 256) -> int:
-    return (v + a - 1) // a * a
-
-
-def block_layout(dims: StackDims, layers: int):
-    """Offsets of every (layer-in-block, projection) piece of a block slab:
-    [{proj: (codes_off, absmax_off)}] and the slab size. Pieces are 256-byte aligned."""
-    off = 0
+def block_layout(dims: StackDims, layers: int, dense: bool = False):
+    """Offsets of every (layer-in-block, projection) piece of a block slab and the slab
+    size, from the library's nf4_block_layout: per layer, projections in the order q, k,
+    v, o, gate, up, down, each codes then absmax (dense: the bf16 weight), every piece at
+    a 256-byte aligned offset. Returns ([{proj: (codes_off, absmax_off)} or
+    [{proj: (w_off,)}] per layer], block bytes)."""
+    shapes = [dims.shapes()[name] for name in PROJS]
+    offs, total = lib.block_layout(shapes, layers, dense)
     table = []
-    for _ in range(layers):
-        entry = {}
-        for name in PROJS:
-            n, k = dims.shapes()[name]
-            c_off = off
-            off = _align(off + n * k // 2)
-            a_off = off
-            off = _align(off + n * (k // 64) * 4)
-            entry[name] = (c_off, a_off)
-        table.append(entry)
-    return table, off
-
-
-class HostNF4Base:
-    """The frozen NF4 base in pinned host memory, one slab per block.
-
-    weight_fn(layer, proj, n, k) -> bf16 device tensor [n, k]; it is quantised by
-    nf4_quantize on the GPU into a staging slab that is copied into the block's
-    pinned slab (block by block, so device residency stays at one block)."""
-
-    dense = False
-
-    def __init__(self, dims: StackDims, n_layers: int, block_size: int, weight_fn):
-        if block_size < 1:
-            raise ValueError("block_size must be >= 1")
-        self.dims, self.n_layers, self.block_size = dims, n_layers, block_size
-        self.n_blocks = (n_layers + block_size - 1) // block_size
-        self.layout, self.slot_bytes = block_layout(dims, block_size)
-        self.blocks = []
-        self.block_bytes = []
-        staging = torch.empty(self.slot_bytes, dtype=torch.uint8, device="cuda")
-        for b in range(self.n_blocks):
-            nl = min(block_size, n_layers - b * block_size)
-            used = block_layout(dims, nl)[1]
-            for li in range(nl):
-                layer = b * block_size + li
-                for name in PROJS:
-                    n, k = dims.shapes()[name]
-                    c_off, a_off = self.layout[li][name]
-                    w = weight_fn(layer, name, n, k)
-                    codes = staging[c_off:c_off + n * k // 2].view(n, k // 2)
-                    absmax = staging[a_off:a_off + n * (k // 64) * 4].view(torch.float32).view(n, k // 64)
-                    lib.quantize(w, codes=codes, absmax=absmax)
-                    del w
-            host = torch.empty(used, dtype=torch.uint8, pin_memory=True)
-            host.copy_(staging[:used])           # D2H into pinned memory (synchronous)
-            self.blocks.append(host)
-            self.block_bytes.append(used)
-        torch.cuda.synchronize()
-
-    def total_bytes(self) -> int:
-        return sum(self.block_bytes)
+    for li in range(layers):
+        if dense:
+            table.append({name: (offs[li][j][0],) for j, name in enumerate(PROJS)})
+        else:
+            table.append({name: tuple(offs[li][j]) for j, name in enumerate(PROJS)})
+    return table, total
 
 
 def block_layout_bf16(dims: StackDims, layers: int):
     """Dense-bf16 slabs: [{proj: (w_off,)}] and the slab size, pieces 256-byte aligned."""
-    off = 0
-    table = []
-    for _ in range(layers):
-        entry = {}
-        for name in PROJS:
-            n, k = dims.shapes()[name]
-            entry[name] = (off,)
-            off = _align(off + n * k * 2)
-        table.append(entry)
-    return table, off
+    return block_layout(dims, layers, dense=True)
 
 
-class HostBF16Base:
-    """The frozen base as dense bf16 in pinned host memory, one slab per block (the
-    experimental "bf16_bitwise" mode of the Poros API reference,
-    "PorosTrainer.from_pretrained": a dense-BF16 base streamed blockwise, bitwise equal
-    to a resident run; 2 bytes a weight against NF4's 0.5625).
+class _HostBase:
+    """The frozen base of a stack in pinned host memory: one page-locked buffer of
+    exactly the stack's size, layer after layer with the block layout of a one-layer
+    block (every layer's bytes are a multiple of 256), or, if so large an allocation is
+    refused, one buffer per layer. A block of block_size layers is its layers' slabs
+    back to back - with one buffer, a contiguous host range copied in one piece - and
+    the slot then holds exactly the slab that nf4_block_layout describes for that many
+    layers; regroup(block_size) re-groups the same host bytes for another block size.
 
-    weight_fn(layer, proj, n, k) -> bf16 device tensor [n, k], staged on the device
-    and copied into the block's pinned slab block by block."""
+    Loading ("Poros on consumer GPUs", "OOM playbook": the streamed loader keeps GPU
+    residency bounded at any model size and gives bytes identical to the standard
+    load): weight_fn(layer, proj, n, k) returns the projection's bf16 weight [n, k],
+    either host-resident (a CPU tensor: copied to the device) or already on the device.
+    Each projection is converted on the device on its own (`_convert`) and copied into
+    its place in the layer's pinned buffer before the next one is read, so the device
+    holds at most one projection's bf16 weight plus its converted bytes; load_stats
+    records the peak and the throughput. The pinned buffers live as long as a view of
+    them does (this base, a regrouped view, a pool); close() drops this base's views."""
 
-    dense = True
+    dense = False
 
-    def __init__(self, dims: StackDims, n_layers: int, block_size: int, weight_fn):
+    def __init__(self, dims: StackDims, n_layers: int, block_size: int, weight_fn=None, _shared=None):
         if block_size < 1:
             raise ValueError("block_size must be >= 1")
         self.dims, self.n_layers, self.block_size = dims, n_layers, block_size
+        self.layer_layout, self.layer_bytes = block_layout(dims, 1, self.dense)
+        self.layout, self.slot_bytes = block_layout(dims, block_size, self.dense)
+        for li in range(block_size):   # a block's layout is its layers' layouts, back to back
+            for name, offs in self.layout[li].items():
+                assert offs == tuple(o + li * self.layer_bytes for o in self.layer_layout[0][name])
         self.n_blocks = (n_layers + block_size - 1) // block_size
-        self.layout, self.slot_bytes = block_layout_bf16(dims, block_size)
-        self.blocks = []
-        self.block_bytes = []
-        staging = torch.empty(self.slot_bytes, dtype=torch.uint8, device="cuda")
-        for b in range(self.n_blocks):
-            nl = min(block_size, n_layers - b * block_size)
-            used = block_layout_bf16(dims, nl)[1]
-            for li in range(nl):
-                layer = b * block_size + li
-                for name in PROJS:
-                    n, k = dims.shapes()[name]
-                    (w_off,) = self.layout[li][name]
-                    staging[w_off:w_off + n * k * 2].view(torch.bfloat16).view(n, k).copy_(weight_fn(layer, name, n, k))
-            host = torch.empty(used, dtype=torch.uint8, pin_memory=True)
-            host.copy_(staging[:used])           # D2H into pinned memory (synchronous)
-            self.blocks.append(host)
-            self.block_bytes.append(used)
-        torch.cuda.synchronize()
+        self._shared = _shared if _shared is not None else self._load(weight_fn)
+        self.load_stats = self._shared["stats"]
+        self.layers = list(self._shared["bufs"])
+        self.contiguous = self._shared["whole"] is not None
+        self.part_begin = [b * block_size for b in range(self.n_blocks)] + [n_layers]
+        self.block_bytes = [(self.part_begin[b + 1] - self.part_begin[b]) * self.layer_bytes
+                            for b in range(self.n_blocks)]
+
+    def pool_ranges(self, layer_parts: bool):
+        """Host ranges and part_begin for stream_pool_create_parts: one part per layer,
+        or (contiguous base only) one part per block."""
+        if layer_parts or not self.contiguous:
+            return self.layers, self.part_begin
+        whole, lb = self._shared["whole"], self.layer_bytes
+        ranges = [whole[self.part_begin[b] * lb:self.part_begin[b + 1] * lb] for b in range(self.n_blocks)]
+        return ranges, list(range(self.n_blocks + 1))
+
+    def regroup(self, block_size: int):
+        """The same host bytes grouped in blocks of `block_size` layers."""
+        return type(self)(self.dims, self.n_layers, block_size, _shared=self._shared)
 
     def total_bytes(self) -> int:
-        return sum(self.block_bytes)
+        return self.n_layers * self.layer_bytes
+
+    def layer_bytes_of(self, layer: int) -> torch.Tensor:
+        """The pinned bytes of one layer (its one-layer slab)."""
+        return self.layers[layer]
+
+    def close(self) -> None:
+        """Drop this base's references to the pinned buffers (they are freed when no
+        regrouped view or pool holds them any more)."""
+        self.layers = []
+        self._shared = {"bufs": [], "whole": None, "stats": self.load_stats}
+
+    def _load(self, weight_fn):
+        shapes = self.dims.shapes()
+        max_w = max(n * k for n, k in shapes.values())
+        try:
+            whole = lib.pinned_empty(self.n_layers * self.layer_bytes)
+            bufs = [whole[l * self.layer_bytes:(l + 1) * self.layer_bytes] for l in range(self.n_layers)]
+        except lib.Nf4Error:
+            whole = None
+            bufs = [lib.pinned_empty(self.layer_bytes) for _ in range(self.n_layers)]
+        base_alloc = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        staging_w = None          # device bf16 staging for host-resident weights
+        staging = torch.empty(self._converted_bytes(max_w), dtype=torch.uint8, device="cuda")
+        t0 = time.perf_counter()
+        read = 0
+        for layer in range(self.n_layers):
+            dst = bufs[layer]
+            for name in PROJS:
+                n, k = shapes[name]
+                w = weight_fn(layer, name, n, k)
+                if w.dtype != torch.bfloat16 or tuple(w.shape) != (n, k):
+                    raise ValueError(f"weight_fn({layer}, {name}) must give a bf16 [{n}, {k}] tensor")
+                if w.device.type == "cpu":
+                    if staging_w is None:
+                        staging_w = torch.empty(max_w, dtype=torch.bfloat16, device="cuda")
+                    wd = staging_w[:n * k].view(n, k)
+                    wd.copy_(w)                          # H2D of one projection
+                else:
+                    wd = w
+                read += n * k * 2
+                self._convert(wd, name, self.layer_layout[0][name], dst, staging)
+                del w, wd
+        torch.cuda.synchronize()
+        secs = time.perf_counter() - t0
+        stats = {"seconds": secs, "bf16_gb_read": read / 1e9, "host_gb_written": self.total_bytes() / 1e9,
+                 "bf16_gbs": read / secs / 1e9,
+                 "peak_device_bytes": torch.cuda.max_memory_allocated() - base_alloc}
+        stats["one_pinned_buffer"] = whole is not None
+        del staging, staging_w
+        return {"bufs": bufs, "whole": whole, "stats": stats}
+
+
+class HostNF4Base(_HostBase):
+    """The frozen NF4 base in pinned host memory: each projection quantised by
+    nf4_quantize on the GPU and its codes and absmax copied into the pinned buffer."""
+
+    dense = False
+
+    @staticmethod
+    def _converted_bytes(max_w: int) -> int:
+        return _align(max_w // 2) + _align(max_w // 64 * 4)
+
+    def _convert(self, wd, name, offs, dst, staging):
+        n, k = wd.shape
+        c_off, a_off = offs
+        codes = staging[:n * k // 2].view(n, k // 2)
+        a0 = _align(n * k // 2)
+        absmax = staging[a0:a0 + n * (k // 64) * 4].view(torch.float32).view(n, k // 64)
+        lib.quantize(wd, codes=codes, absmax=absmax)
+        dst[c_off:c_off + n * k // 2].copy_(staging[:n * k // 2])      # D2H (synchronous)
+        dst[a_off:a_off + n * (k // 64) * 4].copy_(staging[a0:a0 + n * (k // 64) * 4])
+
+
+class HostBF16Base(_HostBase):
+    """The frozen base as dense bf16 in pinned host memory (the experimental
+    "bf16_bitwise" mode of the Poros API reference, "PorosTrainer.from_pretrained": a
+    dense-BF16 base streamed blockwise, bitwise equal to a resident run; 2 bytes a
+    weight against NF4's 0.5625)."""
+
+    dense = True
+
+    @staticmethod
+    def _converted_bytes(max_w: int) -> int:
+        return 256
+
+    def _convert(self, wd, name, offs, dst, staging):
+        n, k = wd.shape
+        (w_off,) = offs
+        dst[w_off:w_off + n * k * 2].copy_(wd.contiguous().view(torch.uint8).view(-1))   # D2H (synchronous)
+
+
+def _align(v: int, a: int = 256) -> int:
+    return (v + a - 1) // a * a
 
 
 class LoraParams:
@@ -199,18 +256,26 @@ class NF4Stack:
     """Forward + backward over the stack, streamed through a slot pool or resident."""
 
     def __init__(self, base: HostNF4Base, lora: LoraParams, tokens: int, alpha: float = 32.0,
-                 mode: str = "streamed", n_slots: int = 2, prefetch: bool = True, remat: bool = False):
+                 mode: str = "streamed", n_slots: int = 2, prefetch: bool = True, remat: bool = False,
+                 layer_parts: bool = False):
         if mode not in ("streamed", "resident"):
             raise ValueError("mode must be 'streamed' or 'resident'")
         self.base, self.lora, self.T, self.alpha = base, lora, tokens, alpha
         self.mode, self.prefetch, self.remat = mode, prefetch, remat
+        # layer_parts: each layer of a block is a part of its own (copied separately,
+        # released as soon as the layer is done, so a copy into the slot can start
+        # before the whole block is done); else a block is one part when the base is
+        # one contiguous host buffer (one copy per block)
+        self.layer_parts = layer_parts or not base.contiguous
         d = base.dims
         self.dims = d
         nb = base.n_blocks
         self.n_slots = nb if mode == "resident" else max(1, n_slots)
         self.slab = torch.empty(self.n_slots * base.slot_bytes, dtype=torch.uint8, device="cuda")
         self.copy_stream = torch.cuda.Stream()
-        self.pool = lib.StreamPool(base.blocks, self.slab, base.slot_bytes, self.n_slots, self.copy_stream)
+        ranges, part_begin = base.pool_ranges(self.layer_parts)
+        self.pool = lib.StreamPool(ranges, self.slab, base.slot_bytes, self.n_slots, self.copy_stream,
+                                   part_begin=part_begin)
         self._views = [self._slot_views(s) for s in range(self.n_slots)]
         T, r = tokens, lora.rank
         shapes = d.shapes()
@@ -373,12 +438,18 @@ class NF4Stack:
 
     def forward(self, h0: torch.Tensor) -> torch.Tensor:
         (self.boundary[0] if self.remat else self.acts[0]["h"]).copy_(h0)
-        nb = self.base.n_blocks
+        nb, bs = self.base.n_blocks, self.base.block_size
+        self.pool.set_order(False)            # layers of a block used first to last
         for b in range(nb):
             w = self._acquire(b)
             if self.prefetch and self.n_slots > 1 and b + 1 < nb:
                 self.pool.prefetch(b + 1)
-            self._block_forward(b, w)
+            if self.remat:
+                self.acts[0]["h"].copy_(self.boundary[b])
+            for li in self._layers_of(b):
+                self._layer_forward(li, w[li - b * bs])
+                if self.layer_parts:
+                    self.pool.release_part(b, li - b * bs)   # the layer's bytes may be overwritten after this
             self.pool.release(b)
         return self.boundary[nb] if self.remat else self.acts[-1]["h"]
 
@@ -387,6 +458,7 @@ class NF4Stack:
         cur = self.dh[0]
         cur.copy_(dh)
         k = 1
+        self.pool.set_order(True)             # layers of a block used last to first
         for b in range(nb - 1, -1, -1):
             w = self._acquire(b)
             if self.prefetch and self.n_slots > 1 and b - 1 >= 0:
@@ -398,6 +470,8 @@ class NF4Stack:
             for li in reversed(self._layers_of(b)):
                 nxt = self.dh[k]
                 self._layer_backward(li, w[li - b * self.base.block_size], cur, nxt)
+                if self.layer_parts:
+                    self.pool.release_part(b, li - b * self.base.block_size)
                 cur, k = nxt, 1 - k
             self.pool.release(b)
         return cur

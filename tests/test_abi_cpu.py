@@ -75,6 +75,8 @@ def test_linear_fwd_validation(L):
     _err(L, _fwd(raw, N=100), L.NF4_E_SHAPE, "N=100")
     _err(L, _fwd(raw, N=1 << 22), L.NF4_E_SHAPE, "limits")                 # 32-bit tile offsets
     _err(L, _fwd(raw, N=1 << 21, K=1 << 11), L.NF4_E_SHAPE, "limits")      # N*K > 2^31
+    _err(L, _fwd(raw, T=(1 << 23) + 1), L.NF4_E_SHAPE, "T <= 2^23")       # tile counts of the 1-D grids
+    _err(L, _fwd(raw, N=29568, K=8192, T=1 << 23, ws_bytes=0), L.NF4_E_ARG, "workspace")  # T = 2^23 passes the shape check
     _err(L, _fwd(raw, r=65), L.NF4_E_ARG, "r=65")
     _err(L, _fwd(raw, r=-1), L.NF4_E_ARG)
     _err(L, _fwd(raw, alpha=float("inf")), L.NF4_E_ARG, "alpha")
@@ -112,6 +114,7 @@ def test_dense_linear_validation(L):
     _err(L, fwd(w=C.c_void_p(0x10008)), L.NF4_E_ARG, "16-byte")
     _err(L, fwd(K=100), L.NF4_E_SHAPE, "K=100")
     _err(L, fwd(N=1 << 20, K=1 << 11), L.NF4_E_SHAPE, "2^30")      # N*K = 2^31: beyond the dense limit
+    _err(L, fwd(N=1 << 16, K=1 << 14), L.NF4_E_SHAPE, "2^30")      # N*K = 2^30: 2^31 bytes, not below 2^31 - 16
     _err(L, fwd(r=65), L.NF4_E_ARG, "r=65")
     assert fwd(T=0) == 0
     rc = raw.nf4_lora_linear_bwd_bf16(None, 128, 128, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 16, 32.0, FAKE, FAKE, FAKE,
@@ -156,3 +159,29 @@ def test_pool_validation(L):
     _err(L, rc, L.NF4_E_ARG, "copy")
     rc = raw.stream_pool_prefetch(None, 0)
     _err(L, rc, L.NF4_E_ARG, "NULL pool")
+
+
+def test_block_layout(L):
+    """nf4_block_layout: pieces in layer, projection, codes-then-absmax order, each
+    256-byte aligned and exactly as long as its tensor; L layers = L one-layer slabs."""
+    shapes = [(3584, 3584), (512, 3584), (512, 3584), (3584, 3584), (18944, 3584), (18944, 3584), (3584, 18944)]
+    one, one_bytes = L.block_layout(shapes, 1)
+    four, four_bytes = L.block_layout(shapes, 4)
+    assert one_bytes % 256 == 0 and four_bytes == 4 * one_bytes
+    for li in range(4):
+        assert [tuple(o - li * one_bytes for o in p) for p in four[li]] == one[0]
+    end = 0
+    for (n, k), (c, a) in zip(shapes, one[0]):
+        assert c % 256 == 0 and a % 256 == 0 and c >= end
+        assert a >= c + n * k // 2 and a - (c + n * k // 2) < 256
+        end = a + n * (k // 64) * 4
+    assert one_bytes - end < 256
+    assert one_bytes == sum(-(-n * k // 2 // 256) * 256 + -(-n * (k // 64) * 4 // 256) * 256 for n, k in shapes)
+    dense, dense_bytes = L.block_layout(shapes, 2, dense=True)
+    assert dense_bytes == 2 * sum(-(-n * k * 2 // 256) * 256 for n, k in shapes)
+    assert all(p[1] == 0 for layer in dense for p in layer)
+    raw = L.raw()
+    bad = (C.c_int64 * 2)(128, 100)
+    out = C.c_size_t()
+    _err(L, raw.nf4_block_layout(bad, 1, 1, 0, None, C.byref(out)), L.NF4_E_SHAPE, "K=100")
+    _err(L, raw.nf4_block_layout(bad, 1, 0, 0, None, C.byref(out)), L.NF4_E_ARG, "layers")

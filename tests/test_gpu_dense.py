@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 import synthetic_inputs as S
-from helpers import bits_of, check_bf16_output, check_f32_output, f32_of, to_dev_bf16
+from helpers import bits_of, check_linear, f32_of, linear_mags, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 PROJS = ("q", "k", "v", "o", "gate", "up", "down")
@@ -36,12 +36,12 @@ def test_dense_linear_matches_oracle(gpu_lib, t, n, k, r):
     torch.cuda.synchronize()
     y_ref, u_ref = O.lora_linear_fwd(case["x"], case["W"], case["A"], case["B"], 32.0)
     dx_ref, da_ref, db_ref = O.lora_linear_bwd(case["x"], case["W"], case["A"], case["B"], 32.0, case["dY"])
-    check_bf16_output(bits_of(y), y_ref, f"dense y {t}x{n}x{k} r{r}")
-    check_bf16_output(bits_of(dx), dx_ref, f"dense dX {t}x{n}x{k} r{r}")
+    refs = {"y": y_ref, "u": u_ref, "dx": dx_ref, "dA": da_ref, "dB": db_ref}
+    mags = linear_mags(case["x"], case["W"], case["A"], case["B"], 32.0, case["dY"])
+    outs = {"y": bits_of(y), "dx": bits_of(dx)}
     if r:
-        check_f32_output(f32_of(u), u_ref, "u")
-        check_f32_output(f32_of(da), da_ref, "dA")
-        check_f32_output(f32_of(db), db_ref, "dB")
+        outs.update(u=f32_of(u), dA=f32_of(da), dB=f32_of(db))
+    check_linear(outs, refs, mags, t, n, k, r, f"dense {t}x{n}x{k} r{r}")
 
 
 def test_dense_equals_nf4_on_the_dequantised_base(gpu_lib):

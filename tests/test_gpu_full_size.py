@@ -50,21 +50,26 @@ def test_full_size_projection_sampled(gpu_lib, t, n, k, proj):
 
     s = O.lora_scale(alpha, r)
     xf, dyf, af, bf = (O.bf16_bits_to_f64(v) for v in (x, dy, a, b))
+    ax, ady, aa, ab = (np.abs(v) for v in (xf, dyf, af, bf))
     u_ref = xf @ af.T
     g_ref = dyf @ bf
-    check_f32_output(u, u_ref, "u")
-    check_f32_output(dA, s * (g_ref.T @ xf), "dA")
-    check_f32_output(dB, s * (dyf.T @ u_ref), "dB")
+    u_mag, g_mag = ax @ aa.T, ady @ ab
+    check_f32_output(u, u_ref, "u", mag=u_mag, terms=k)
+    check_f32_output(dA, s * (g_ref.T @ xf), "dA", mag=s * (g_mag.T @ ax), terms=n + t)
+    check_f32_output(dB, s * (dyf.T @ u_ref), "dB", mag=s * (ady.T @ u_mag), terms=k + t)
 
     # every token of the sampled rows / columns: at least ~2000 bf16 outputs each, so that
     # the rounding floor the check compares against is itself well estimated
     samples = max(SAMPLES, 2048 // t)
     rng = np.random.default_rng(7)
     rows = np.unique(np.concatenate([rng.choice(n, samples, replace=False), [0, n - 1]]))
-    y_ref = xf @ _w_rows(codes, absmax, rows).T + s * (u_ref @ bf[rows].T)
-    check_bf16_output(y[:, rows], y_ref, f"y sampled T={t}")
+    wr = _w_rows(codes, absmax, rows)
+    y_ref = xf @ wr.T + s * (u_ref @ bf[rows].T)
+    y_mag = ax @ np.abs(wr).T + s * (u_mag @ ab[rows].T)
+    check_bf16_output(y[:, rows], y_ref, f"y sampled T={t}", mag=y_mag, terms=k + r)
 
     cols = np.unique(np.concatenate([rng.choice(k, samples, replace=False), [0, k - 1]]))
     wc = np.stack([_w_col(codes, absmax, kk) for kk in cols], axis=1)
     dx_ref = dyf @ wc + s * (g_ref @ af[:, cols])
-    check_bf16_output(dx[:, cols], dx_ref, f"dX sampled T={t}")
+    dx_mag = ady @ np.abs(wc) + s * (g_mag @ aa[:, cols])
+    check_bf16_output(dx[:, cols], dx_ref, f"dX sampled T={t}", mag=dx_mag, terms=n + r)

@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 import synthetic_inputs as S
-from helpers import bits_of, check_bf16_output, check_f32_output, f32_of, to_dev_bf16
+from helpers import bits_of, check_f32_output, check_linear, f32_of, linear_mags, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -41,12 +41,12 @@ def _check_case(lib, t, n, k, r, alpha=32.0, seed=42, b_std=0.01):
     y, u, dx, da, db = _run(lib, dev, alpha)
     y_ref, u_ref = O.lora_linear_fwd(case["x"], wq, case["A"], case["B"], alpha)
     dx_ref, da_ref, db_ref = O.lora_linear_bwd(case["x"], wq, case["A"], case["B"], alpha, case["dY"])
-    check_bf16_output(bits_of(y), y_ref, f"y {t}x{n}x{k} r{r}")
-    check_bf16_output(bits_of(dx), dx_ref, f"dX {t}x{n}x{k} r{r}")
+    refs = {"y": y_ref, "u": u_ref, "dx": dx_ref, "dA": da_ref, "dB": db_ref}
+    mags = linear_mags(case["x"], wq, case["A"], case["B"], alpha, case["dY"])
+    outs = {"y": bits_of(y), "dx": bits_of(dx)}
     if r:
-        check_f32_output(f32_of(u), u_ref, "u")
-        check_f32_output(f32_of(da), da_ref, "dA")
-        check_f32_output(f32_of(db), db_ref, "dB")
+        outs.update(u=f32_of(u), dA=f32_of(da), dB=f32_of(db))
+    check_linear(outs, refs, mags, t, n, k, r, f"{t}x{n}x{k} r{r}")
     return y, dx, da, db
 
 
@@ -102,8 +102,10 @@ def test_few_token_dx_skipped(gpu_lib):
     torch.cuda.synchronize()
     assert dx is None
     _, da_ref, db_ref = O.lora_linear_bwd(case["x"], wq, case["A"], case["B"], 32.0, case["dY"])
-    check_f32_output(f32_of(da), da_ref, "dA")
-    check_f32_output(f32_of(db), db_ref, "dB")
+    mags = linear_mags(case["x"], wq, case["A"], case["B"], 32.0, case["dY"])
+    t, n, k = case["x"].shape[0], case["W"].shape[0], case["W"].shape[1]
+    check_f32_output(f32_of(da), da_ref, "dA", mag=mags["dA"], terms=n + t)
+    check_f32_output(f32_of(db), db_ref, "dB", mag=mags["dB"], terms=k + t)
 
 
 def test_few_token_repeat_is_bitwise_identical(gpu_lib):
@@ -176,5 +178,7 @@ def test_dx_can_be_skipped(gpu_lib):
     torch.cuda.synchronize()
     assert dx is None
     _, da_ref, db_ref = O.lora_linear_bwd(case["x"], wq, case["A"], case["B"], 32.0, case["dY"])
-    check_f32_output(f32_of(da), da_ref, "dA")
-    check_f32_output(f32_of(db), db_ref, "dB")
+    mags = linear_mags(case["x"], wq, case["A"], case["B"], 32.0, case["dY"])
+    t, n, k = case["x"].shape[0], case["W"].shape[0], case["W"].shape[1]
+    check_f32_output(f32_of(da), da_ref, "dA", mag=mags["dA"], terms=n + t)
+    check_f32_output(f32_of(db), db_ref, "dB", mag=mags["dB"], terms=k + t)

@@ -101,3 +101,50 @@ def test_pool_reuse_waits_for_compute(gpu_lib):
         assert torch.equal(after.cpu(), blocks[1])
     finally:
         pool.close()
+
+
+def test_pool_parts_land_back_to_back_and_wait_per_part(gpu_lib):
+    """Blocks of two parts in one slot: each part lands at its offset; the copy of a
+    part waits for the release of the part it overwrites: reads of part 1 enqueued
+    before its release all see the old block although part 0 was released first."""
+    L = gpu_lib
+    n = 1 << 22
+    parts = _blocks(4, n)                       # blocks (0: parts 0, 1) and (1: parts 2, 3)
+    slab = torch.empty(2 * n, dtype=torch.uint8, device="cuda")
+    pool = L.StreamPool(parts, slab, 2 * n, 1, torch.cuda.Stream(), part_begin=[0, 2, 4])
+    try:
+        ptr = pool.acquire(0)
+        assert ptr == slab.data_ptr()
+        pool.release_part(0, 0)                 # part 0 done early
+        sums = [slab[n:].to(torch.int64).sum() for _ in range(50)]   # long reads of part 1
+        pool.release_part(0, 1)
+        with pytest.raises(L.Nf4Error) as e:
+            pool.release_part(0, 1)
+        assert e.value.code == L.NF4_E_STATE
+        pool.release(0)
+        for descending in (True, False):
+            pool.set_order(descending)
+            pool.prefetch(1)                    # the only slot: overwrites block 0 part by part
+            pool.acquire(1)
+            after = slab.clone()
+            pool.release(1)
+            pool.prefetch(0)
+            pool.acquire(0)
+            back = slab.clone()
+            pool.release(0)
+            torch.cuda.synchronize()
+            assert torch.equal(after[:n].cpu(), parts[2]) and torch.equal(after[n:].cpu(), parts[3])
+            assert torch.equal(back[:n].cpu(), parts[0]) and torch.equal(back[n:].cpu(), parts[1])
+        want = int(parts[1].to(torch.int64).sum())
+        assert all(int(s) == want for s in sums)
+    finally:
+        pool.close()
+
+
+def test_pinned_empty_is_exact_and_pinned(gpu_lib):
+    t = gpu_lib.pinned_empty(1000)
+    assert t.numel() == 1000 and t.is_pinned() and t.dtype == torch.uint8
+    t.fill_(7)
+    d = t.cuda(non_blocking=True)
+    torch.cuda.synchronize()
+    assert int(d.sum()) == 7000

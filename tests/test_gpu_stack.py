@@ -82,27 +82,37 @@ def test_tiny_stack_matches_oracle(ST):
 
 
 def _run(ST, base, lora, T, mode, **kw):
+    """Two steps; the outputs and gradients of each are cloned as soon as it ends (the
+    stack reuses its buffers), so step 1 - the one that starts from an empty pool - and
+    step 2 - slots reused across steps - are both compared."""
     st = ST.NF4Stack(base, lora, T, 32.0, mode=mode, **kw)
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
     h0 = torch.randn(T, base.dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
     dh = torch.randn(T, base.dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
-    out, dh0 = st.step(h0, dh)
-    out2, dh02 = st.step(h0, dh)                     # second step: slot reuse across steps
+    res = {"steps": []}
+    for _ in range(2):
+        out, dh0 = st.step(h0, dh)
+        res["steps"].append({"out": out.clone(), "dh0": dh0.clone(),
+                             "grads": [{p: (a.clone(), b.clone()) for p, (a, b) in gl.items()} for gl in st.grads]})
     torch.cuda.synchronize()
-    res = {"out": out.clone(), "dh0": dh0.clone(), "out2": out2.clone(),
-           "grads": [{p: (a.clone(), b.clone()) for p, (a, b) in gl.items()} for gl in st.grads],
-           "stats": st.pool.stats()}
+    res["stats"] = st.pool.stats()
+    res["out"], res["dh0"] = res["steps"][0]["out"], res["steps"][0]["dh0"]
     st.close()
     return res
 
 
 def _same(a, b):
-    assert torch.equal(a["out"], b["out"]) and torch.equal(a["dh0"], b["dh0"])
-    assert torch.equal(a["out2"], a["out"])
-    for ga, gb in zip(a["grads"], b["grads"]):
-        for p in PROJS:
-            assert torch.equal(ga[p][0], gb[p][0]) and torch.equal(ga[p][1], gb[p][1])
+    """Both steps of run a equal those of run b bit for bit, and each run's two steps
+    equal each other."""
+    for sa, sb in zip(a["steps"], b["steps"]):
+        assert torch.equal(sa["out"], sb["out"]) and torch.equal(sa["dh0"], sb["dh0"])
+        for ga, gb in zip(sa["grads"], sb["grads"]):
+            for p in PROJS:
+                assert torch.equal(ga[p][0], gb[p][0]) and torch.equal(ga[p][1], gb[p][1])
+    for run in (a, b):
+        s1, s2 = run["steps"]
+        assert torch.equal(s1["out"], s2["out"]) and torch.equal(s1["dh0"], s2["dh0"])
 
 
 @pytest.mark.parametrize("block_size", [1, 2, 3])
@@ -112,7 +122,8 @@ def test_streamed_equals_resident_tiny(ST, block_size):
     ref = _run(ST, base, lora, T, "resident")
     assert ref["stats"]["copies"] == base.n_blocks and ref["stats"]["misses"] == 0
     for kw in ({"prefetch": True, "n_slots": 2}, {"prefetch": False, "n_slots": 2}, {"prefetch": True, "n_slots": 3},
-               {"prefetch": False, "n_slots": 1}):
+               {"prefetch": False, "n_slots": 1}, {"prefetch": True, "n_slots": 2, "layer_parts": True},
+               {"prefetch": True, "n_slots": 3, "layer_parts": True}, {"prefetch": False, "n_slots": 1, "layer_parts": True}):
         got = _run(ST, base, lora, T, "streamed", **kw)
         _same(got, ref)
         if kw["prefetch"] and base.n_blocks > 2:
@@ -147,6 +158,29 @@ def test_block_size_never_changes_results(ST):
         _same(r, runs[0])
 
 
+def test_regrouped_blocks_share_the_host_bytes(ST):
+    """regroup(block_size) groups the same pinned layer buffers: block b is layers
+    [b bs, (b + 1) bs), copied back to back into a slot, which then holds the slab
+    nf4_block_layout gives for that many layers; results do not depend on the grouping."""
+    _, _, base, lora = _tiny_stack(ST, 5, 1)
+    for bs in (2, 3, 5):
+        g = base.regroup(bs)
+        assert [t.data_ptr() for t in g.layers] == [t.data_ptr() for t in base.layers]
+        assert g.n_blocks == (5 + bs - 1) // bs and g.part_begin[-1] == 5
+        assert g.block_bytes == [min(bs, 5 - b * bs) * base.layer_bytes for b in range(g.n_blocks)]
+    ref = _run(ST, base, lora, 24, "resident")
+    _same(_run(ST, base.regroup(2), lora, 24, "streamed"), ref)
+    st = ST.NF4Stack(base.regroup(3), lora, 24, 32.0, mode="resident")
+    for b in range(2):                       # each slot holds its block's layers back to back
+        ptr = st.pool.acquire(b)
+        off = ptr - st.slab.data_ptr()
+        for i in range(min(3, 5 - 3 * b)):
+            got = st.slab[off + i * base.layer_bytes: off + (i + 1) * base.layer_bytes].cpu()
+            assert torch.equal(got, base.layers[3 * b + i])
+        st.pool.release(b)
+    st.close()
+
+
 def test_qwen7b_stack_streamed_equals_resident(ST):
     """28 Qwen2.5-7B-shaped layers, block_size 4, 512 tokens: streamed (2 slots,
     prefetch one ahead), with stored and with recomputed activations, vs fully
@@ -159,5 +193,46 @@ def test_qwen7b_stack_streamed_equals_resident(ST):
     _same(got, ref)
     got = _run(ST, base, lora, 512, "streamed", remat=True)
     _same(got, ref)
+    _same(_run(ST, base, lora, 512, "streamed", layer_parts=True), ref)   # one copy and release per layer
     assert torch.isfinite(ref["out"].float()).all() and torch.isfinite(ref["dh0"].float()).all()
     assert got["stats"]["bytes_copied"] > 2 * base.total_bytes()
+
+
+def _big_stack_parity(ST, model, cases):
+    """Streamed (two slots, prefetch one ahead) vs fully resident, bitwise, on one
+    host copy of the base regrouped for each block size; `cases` = [(tokens,
+    [block sizes])]. The resident result does not depend on the block size either."""
+    dims, L = ST.QWEN25[model]
+    print(f"{model} stack: loading {L} layers", flush=True)
+    base = ST.HostNF4Base(dims, L, 4, ST.qwen_weight_fn())
+    lora = ST.LoraParams(dims, L, 16, ST.qwen_lora_fn())
+    for T, sizes in cases:
+        print(f"{model} stack T={T}: resident", flush=True)
+        ref = _run(ST, base, lora, T, "resident")
+        assert torch.isfinite(ref["out"].float()).all() and torch.isfinite(ref["dh0"].float()).all()
+        for bs in sizes:
+            print(f"{model} stack T={T}: streamed block_size {bs}", flush=True)
+            b = base.regroup(bs)
+            got = _run(ST, b, lora, T, "streamed", n_slots=2, prefetch=True)
+            _same(got, ref)
+            assert got["stats"]["misses"] == 1 and got["stats"]["copies"] >= 2 * (b.n_blocks - 2)
+            del got
+            if bs == 4 and T == 512:        # layers copied and released one by one
+                _same(_run(ST, b, lora, T, "streamed", n_slots=2, layer_parts=True), ref)
+            torch.cuda.empty_cache()
+        del ref
+    base.close()
+    del base, lora
+    torch.cuda.empty_cache()
+
+
+def test_qwen32b_stack_streamed_equals_resident(ST):
+    """64 Qwen2.5-32B-shaped layers, 512 tokens, block sizes 4 and 1."""
+    _big_stack_parity(ST, "32b", [(512, [4, 1])])
+
+
+def test_qwen72b_stack_streamed_equals_resident(ST):
+    """80 Qwen2.5-72B-shaped layers: block sizes 1, 2 and 4 at 512 tokens, and 4 at 256
+    ("Poros on consumer GPUs", "OOM playbook": block_size 4 -> 2 -> 1 and a shorter
+    sequence never change the results)."""
+    _big_stack_parity(ST, "72b", [(512, [1, 2, 4]), (256, [4])])
