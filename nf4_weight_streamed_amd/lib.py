@@ -479,8 +479,10 @@ def pinned_empty(nbytes: int) -> torch.Tensor:
     addr = p.value
 
     class _PinnedOwner(C.c_uint8 * nbytes):
-        def __del__(self):
-            hip.hipHostFree(C.c_void_p(addr))
+        # the free function and address are bound now: at interpreter exit the module's
+        # globals may already be gone when the last view dies
+        def __del__(self, _free=hip.hipHostFree, _addr=C.c_void_p(addr)):
+            _free(_addr)
 
     return torch.frombuffer(_PinnedOwner.from_address(addr), dtype=torch.uint8)
 
