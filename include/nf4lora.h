@@ -140,6 +140,27 @@ int nf4_lora_linear_fwd(const uint8_t* codes, const float* absmax, int64_t N, in
                         const uint16_t* A, const uint16_t* B, int r, float alpha,
                         uint16_t* y, float* u_save, void* ws, size_t ws_bytes, nf4_stream stream);
 
+/*
+ * nf4_lora_linear_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * computation, arguments, limits and errors as nf4_lora_linear_fwd, without the
+ * workspace arguments: the workspace is a library-owned device array of
+ * NF4_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held from the library's first use on
+ * that GPU until the process ends. This call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine) and issues no memset; the array keeps the
+ * last call's contents, which no call reads before writing.
+ * NF4_E_SHAPE when the sizes need more workspace than the array holds
+ * (nf4_lora_linear_fwd_workspace() > NF4_NOALLOC_SCRATCH_BYTES; the Qwen2.5
+ * 7B/32B/72B projections need at most about 53 MB up to 2048 tokens).
+ * Calls that overlap on one GPU (on different streams, or from different host
+ * threads) share the array and race: order them on one stream.
+ */
+#define NF4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int nf4_lora_linear_fwd_noalloc(const uint8_t* codes, const float* absmax, int64_t N, int64_t K,
+                                const uint16_t* x, int64_t T,
+                                const uint16_t* A, const uint16_t* B, int r, float alpha,
+                                uint16_t* y, float* u_save, nf4_stream stream);
+
 /* Bytes of device workspace nf4_lora_linear_bwd needs for these sizes. */
 size_t nf4_lora_linear_bwd_workspace(int64_t T, int64_t N, int64_t K, int r);
 

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libnf4lora.so")
 
 SOURCES = ["abi.cpp", "stream_pool.cpp", "nf4_codec.hip", "nf4_gemm_fwd.hip", "nf4_gemm_bwd.hip",
            "lora_skinny.hip", "nf4_skinny.hip", "stack_glue.hip",
-           "probe.hip", "nf4_merge.hip"]
+           "probe.hip", "nf4_merge.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

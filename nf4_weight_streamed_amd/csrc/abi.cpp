@@ -148,6 +148,11 @@ float lora_scale(float alpha, int r) { return r > 0 ? alpha / float(r) : 0.0f; }
 
 }  // namespace
 
+int check_linear_args(const char* fn, const uint8_t* codes, const float* absmax, int64_t N, int64_t K, int64_t T, int r,
+                      float alpha) {
+    return check_linear_common(fn, codes, absmax, N, K, T, r, alpha);
+}
+
 }  // namespace nf4
 
 using namespace nf4;
@@ -257,7 +262,6 @@ size_t nf4_lora_linear_bwd_bf16_workspace(int64_t T, int64_t N, int64_t K, int r
 }  // extern "C"
 
 namespace nf4 {
-namespace {
 
 // The forward after the base-specific checks; the base is NF4 (codes, absmax) or dense
 // bf16 (wdense not NULL).
@@ -286,6 +290,8 @@ int linear_fwd(const char* fn, const uint8_t* codes, const float* absmax, const 
     return hip_status(launch_gemm_fwd(p, codes, absmax, wdense, x, B, T, N, K, r, scale, y, u_save, ws, s),
                       "nf4_lora_linear_fwd (gemm)");
 }
+
+namespace {
 
 int linear_bwd(const char* fn, const uint8_t* codes, const float* absmax, const uint16_t* wdense, int64_t N, int64_t K,
                const uint16_t* x, const float* u_save, const uint16_t* dy, int64_t T, const uint16_t* A,

@@ -125,6 +125,14 @@ hipError_t launch_probe_read(const void* src, uint64_t bytes, uint32_t* out, int
 hipError_t launch_merge_lora(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, const uint16_t* A,
                              const uint16_t* B, int r, float s, uint16_t* w_out, hipStream_t stream);
 
+// The forward entry point's shape/rank/pointer checks and its body after them (abi.cpp);
+// ws is the workspace of ws_bytes bytes (NULL allowed when the plan needs none).
+int check_linear_args(const char* fn, const uint8_t* codes, const float* absmax, int64_t N, int64_t K, int64_t T, int r,
+                      float alpha);
+int linear_fwd(const char* fn, const uint8_t* codes, const float* absmax, const uint16_t* wdense, int64_t N, int64_t K,
+               const uint16_t* x, int64_t T, const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* y,
+               float* u_save, void* ws, size_t ws_bytes, void* stream);
+
 // Instrumentation events around the next fused GEMM launch (abi.cpp); no-ops unless requested.
 void prof_gemm_begin(hipStream_t stream);
 void prof_gemm_end(hipStream_t stream);

@@ -61,6 +61,7 @@ def _load() -> C.CDLL:
         "nf4_lora_linear_fwd_workspace": (sz, [i64, i64, i64, i32]),
         "nf4_lora_linear_fwd": (i32, [vp, vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "nf4_lora_linear_bwd_workspace": (sz, [i64, i64, i64, i32]),
+        "nf4_lora_linear_fwd_noalloc": (i32, [vp, vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, vp]),
         "nf4_lora_linear_fwd_bf16_workspace": (sz, [i64, i64, i64, i32]),
         "nf4_lora_linear_fwd_bf16": (i32, [vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "nf4_lora_linear_bwd_bf16_workspace": (sz, [i64, i64, i64, i32]),
@@ -259,6 +260,29 @@ def lora_linear_fwd(codes, absmax, x, A, B, alpha: float, y=None, u=None, ws=Non
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.nf4_lora_linear_fwd(_ptr(codes), _ptr(absmax), n, k, _ptr(x), t, _ptr(A), _ptr(B), r,
                                     float(alpha), _ptr(y), _ptr(u), _ptr(ws), ws_bytes, _stream(stream)))
+    return y, u
+
+
+NF4_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def lora_linear_fwd_noalloc(codes, absmax, x, A, B, alpha: float, y, u=None, stream=None):
+    """The forward with the library's own device scratch as workspace
+    (nf4_lora_linear_fwd_noalloc): y and u are caller-provided; nothing is allocated."""
+    n, kh = codes.shape
+    k = kh * 2
+    t = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(codes, "codes", torch.uint8, (n, kh))
+    _need(absmax, "absmax", torch.float32, (n, k // NF4_BLOCK))
+    _need(x, "x", torch.bfloat16, (t, k))
+    _need(y, "y", torch.bfloat16, (t, n))
+    if r:
+        _need(A, "A", torch.bfloat16, (r, k))
+        _need(B, "B", torch.bfloat16, (n, r))
+        _need(u, "u", torch.float32, (t, r))
+    _check(_lib.nf4_lora_linear_fwd_noalloc(_ptr(codes), _ptr(absmax), n, k, _ptr(x), t, _ptr(A), _ptr(B), r,
+                                            float(alpha), _ptr(y), _ptr(u), _stream(stream)))
     return y, u
 
 
