@@ -138,6 +138,33 @@ def gemm_bytes(kind: str, t: int, n: int, k: int, r: int) -> float:
     return w + 2 * t * n + 4 * t * r + 2 * r * k + 2 * t * k + 2 * t * k + 4 * r * k
 
 
+def gemm_only(lib, torch, layer, ev: "HipEvents", name: str, steps: int, warmup: int) -> dict:
+    """One projection's forward and backward, alone, `steps` times after `warmup`: the
+    fused GEMMs' device times (events around each launch) for short profiled runs."""
+    p = layer[name]
+    fwd_us, bwd_us = [], []
+    for i in range(warmup + steps):
+        pr = {("fwd", name): (ev.create(), ev.create()), ("bwd", name): (ev.create(), ev.create())}
+        lib.profile_next_gemm(*pr[("fwd", name)])
+        lib.lora_linear_fwd(p["codes"], p["absmax"], p["x"], p["A"], p["B"], ALPHA, y=p["y"], u=p["u"], ws=p["wsf"])
+        lib.profile_next_gemm(*pr[("bwd", name)])
+        lib.lora_linear_bwd(p["codes"], p["absmax"], p["x"], p["u"], p["dy"], p["A"], p["B"], ALPHA, dx=p["dx"],
+                            dA=p["dA"], dB=p["dB"], ws=p["wsb"])
+        torch.cuda.synchronize()
+        if i >= warmup:
+            fwd_us.append(ev.elapsed_ms(*pr[("fwd", name)]) * 1e3)
+            bwd_us.append(ev.elapsed_ms(*pr[("bwd", name)]) * 1e3)
+        for a, b in pr.values():
+            ev.destroy(a)
+            ev.destroy(b)
+    n, k = p["n"], p["k"]
+    out = {"projection": name, "N": n, "K": k, "tokens": T_TOKENS}
+    for kind, us in (("fwd", fwd_us), ("bwd", bwd_us)):
+        avg = sum(us) / len(us)
+        out[kind] = {"us": round(avg, 2), "tflops": round(gemm_flops(kind, T_TOKENS, n, k, RANK) / avg / 1e6, 1)}
+    return out
+
+
 def gemm_attribution(lib, torch, layer, ev: "HipEvents", steps: int = 3) -> dict:
     """Device time of every fused GEMM launch of the step (HIP events recorded by the
     library around each launch, on its stream), averaged over `steps` untimed steps:
@@ -476,19 +503,22 @@ def _stack_inputs(torch, tokens: int, hidden: int):
 
 def _stack_run(torch, ST, base, lora, tokens, h0, dh, steps, **kw) -> dict:
     """One stack configuration: a first step (its outputs kept for the bitwise check),
-    then `steps` timed steps with the pool's copy and acquire-stall spans recorded."""
+    then `steps` timed steps, then one more step with the pool's copy and acquire-stall
+    spans recorded (kept out of the timed steps: the timing events can slow some pool
+    configurations down)."""
     st = ST.NF4Stack(base, lora, tokens, ALPHA, **kw)
     try:
         y, dx = st.step(h0, dh)
         torch.cuda.synchronize()
         res = {"y": y.clone(), "dx": dx.clone(), "act": st.activation_bytes()}
         c0 = st.pool.stats()["bytes_copied"]
-        st.pool.timing_enable(True)
         res["s"] = ST.timed_steps(st, h0, dh, steps, warmup=0)
-        tm = st.pool.timing_collect()
         res["bytes"] = (st.pool.stats()["bytes_copied"] - c0) / steps
-        res["copy_ms"] = tm["copy_ms"] / steps
-        res["stall_ms"] = tm["stall_ms"] / steps
+        st.pool.timing_enable(True)
+        res["s_instrumented"] = ST.timed_steps(st, h0, dh, 1, warmup=0)
+        tm = st.pool.timing_collect()
+        res["copy_ms"] = tm["copy_ms"]
+        res["stall_ms"] = tm["stall_ms"]
         return res
     finally:
         st.close()
@@ -497,14 +527,15 @@ def _stack_run(torch, ST, base, lora, tokens, h0, dh, steps, **kw) -> dict:
 
 
 def stream_bench(torch, model: str, block_sizes, tokens_list, steps: int, h2d_gbs: float, base_kind: str = "nf4",
-                 n_slots: int = 2, remat: bool = True, layer_parts: bool = False) -> dict:
+                 slot_counts=(2,), remat: bool = True, layer_parts: bool = False) -> dict:
     """Streamed vs resident step time of a Qwen2.5-shaped identity-mixing stack for each
     (tokens, block size), with the bitwise check, H2D traffic, and the copy/compute
     overlap measured by the pool's own events: copy_ms = device time of the H2D copies
     per step, stall_ms = time the compute stream stood waiting for a copy per step;
     copy time hidden under compute = copy_ms - stall_ms. base_kind "bf16" streams a dense
-    bf16 base (the experimental bf16_bitwise mode) instead of NF4. n_slots = device pool
-    slots of one block each (the resident run holds every block). One pinned host copy
+    bf16 base (the experimental bf16_bitwise mode) instead of NF4. slot_counts = device
+    pool sizes in blocks (the resident run holds every block); a pool of k slots copies
+    about 2(nb - k) blocks a step. One pinned host copy
     of the base serves every block size (regroup). With `remat`, the first block size is
     also run with rematerialisation (block-boundary states kept, each block's forward
     recomputed in its backward visit). layer_parts: the pool copies and releases each
@@ -525,20 +556,23 @@ def stream_bench(torch, model: str, block_sizes, tokens_list, steps: int, h2d_gb
         res = _stack_run(torch, ST, base, lora, tokens, h0, dh, steps, mode="resident")
         print(f"[stream_bench] {model} T={tokens}: resident {res['s'] * 1e3:.1f} ms per step", file=sys.stderr,
               flush=True)
-        for i, bs in enumerate(block_sizes):
+        for i, (bs, n_slots) in enumerate((bs, k) for bs in block_sizes for k in slot_counts):
             b = base.regroup(bs)
+            if n_slots >= b.n_blocks:
+                continue
             got = _stack_run(torch, ST, b, lora, tokens, h0, dh, steps, mode="streamed", n_slots=n_slots,
                              layer_parts=layer_parts)
             r_s, s_s, nbytes = res["s"], got["s"], got["bytes"]
-            print(f"[stream_bench] {model} T={tokens} bs={bs}: streamed {s_s * 1e3:.1f} ms per step", file=sys.stderr,
-                  flush=True)
+            print(f"[stream_bench] {model} T={tokens} bs={bs} slots={n_slots}: streamed {s_s * 1e3:.1f} ms per step",
+                  file=sys.stderr, flush=True)
             copy_s = nbytes / (h2d_gbs * 1e9)
             c_ms, st_ms = got["copy_ms"], got["stall_ms"]
             row = {
                 "workload": f"qwen2.5-{model}-shaped stack, {n_layers} layers, block_size {bs}, {n_slots} pool slots, "
                             f"{tokens} tokens, {fmt} in pinned host, identity attention mixing, fwd+bwd",
                 "copies": "one per layer" if (layer_parts or not b.contiguous) else "one per block",
-                "tokens": tokens, "block_size": bs,
+                "tokens": tokens, "block_size": bs, "slots": n_slots,
+                "device_pool_gb": round(n_slots * b.slot_bytes / 1e9, 3),
                 "bitwise_equal_to_resident": bool(torch.equal(res["y"], got["y"]) and torch.equal(res["dx"], got["dx"])),
                 "resident_ms_per_step": round(r_s * 1e3, 3),
                 "streamed_ms_per_step": round(s_s * 1e3, 3),
@@ -554,10 +588,11 @@ def stream_bench(torch, model: str, block_sizes, tokens_list, steps: int, h2d_gb
                 "pcie_floor_ratio": round(max(r_s, copy_s) / r_s, 3),
                 "copy_engine_busy_ms_per_step": round(c_ms, 3),
                 "compute_stall_ms_per_step": round(st_ms, 3),
-                "compute_busy_ms_per_step": round(s_s * 1e3 - st_ms, 3),
+                "compute_busy_ms_per_step": round(got["s_instrumented"] * 1e3 - st_ms, 3),
                 "copy_time_hidden_frac": round((c_ms - st_ms) / c_ms, 4) if c_ms > 0 else None,
-                "overlap_source": "HIP events of the pool: copy spans on the copy stream, acquire-wait spans on the "
-                                  "compute stream",
+                "instrumented_step_ms": round(got["s_instrumented"] * 1e3, 3),
+                "overlap_source": "HIP events of the pool over one extra step: copy spans on the copy stream, "
+                                  "acquire-wait spans on the compute stream",
                 "host_base_gb": round(base.total_bytes() / 1e9, 3),
             }
             if remat and i == 0:
@@ -684,6 +719,99 @@ def small_t_sweep(lib, torch, ev: "HipEvents", reps: int = 8, shapes=None, token
             "weight_sets_cycled": ">= 4, >= 512 MB", "r": RANK}
 
 
+def small_t_layer(lib, torch, ev: "HipEvents", model: str, tokens, reps: int = 4) -> list:
+    """Device time of one whole layer's projections - the forward of q, k, v, o, gate, up,
+    down, then their backward in reverse order, as in a training step - at each T in
+    `tokens`, against the HBM bytes of the seven projections (per projection
+    1.125NK + T(6K + 4N + 8r) + 8r(N + K)). Weight sets of the whole layer are cycled
+    (>= 512 MB of distinct NF4 bases) so that the last-level cache cannot serve them;
+    device time from a graph replay of reps x sets layer steps."""
+    from nf4_weight_streamed_amd import stack as ST
+
+    dims, _ = ST.QWEN25[model]
+    shapes = dims.shapes()
+    layer_nf4 = dims.layer_nf4_bytes()
+    nsets = max(2, -(-int(512e6) // layer_nf4))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(42)
+    stream = torch.cuda.current_stream().cuda_stream
+    sets = []
+    for _ in range(nsets):
+        ws = {}
+        for name in ST.PROJS:
+            n, k = shapes[name]
+            w = (torch.randn(n, k, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+            ws[name] = lib.quantize(w)
+            del w
+        sets.append(ws)
+    lora = {}
+    for name in ST.PROJS:
+        n, k = shapes[name]
+        lora[name] = (((torch.rand(RANK, k, generator=g, device="cuda") * 2 - 1) / k ** 0.5).to(torch.bfloat16),
+                      (torch.randn(n, RANK, generator=g, device="cuda") * 0.01).to(torch.bfloat16))
+    rows = []
+    for t in tokens:
+        bufs = {}
+        for name in ST.PROJS:
+            n, k = shapes[name]
+            bufs[name] = {
+                "x": torch.randn(t, k, generator=g, device="cuda").to(torch.bfloat16),
+                "dy": torch.randn(t, n, generator=g, device="cuda").to(torch.bfloat16),
+                "y": torch.empty(t, n, dtype=torch.bfloat16, device="cuda"),
+                "u": torch.empty(t, RANK, dtype=torch.float32, device="cuda"),
+                "dx": torch.empty(t, k, dtype=torch.bfloat16, device="cuda"),
+                "dA": torch.empty(RANK, k, dtype=torch.float32, device="cuda"),
+                "dB": torch.empty(n, RANK, dtype=torch.float32, device="cuda"),
+                "wsf": lib.workspace(lib.fwd_workspace_bytes(t, n, k, RANK)),
+                "wsb": lib.workspace(lib.bwd_workspace_bytes(t, n, k, RANK)),
+            }
+
+        def layer_step(i):
+            ws = sets[i % nsets]
+            for name in ST.PROJS:
+                b, (A, Bm) = bufs[name], lora[name]
+                lib.lora_linear_fwd(*ws[name], b["x"], A, Bm, ALPHA, y=b["y"], u=b["u"], ws=b["wsf"])
+            for name in reversed(ST.PROJS):
+                b, (A, Bm) = bufs[name], lora[name]
+                lib.lora_linear_bwd(*ws[name], b["x"], b["u"], b["dy"], A, Bm, ALPHA, dx=b["dx"], dA=b["dA"],
+                                    dB=b["dB"], ws=b["wsb"])
+
+        calls = reps * nsets
+        for i in range(nsets):
+            layer_step(i)
+        e0, e1 = ev.create(), ev.create()
+        ev.record(e0, stream)
+        for i in range(calls):
+            layer_step(i)
+        ev.record(e1, stream)
+        eager = ev.elapsed_ms(e0, e1) * 1e3 / calls
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(calls):
+                layer_step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev.record(e0, stream)
+        graph.replay()
+        ev.record(e1, stream)
+        us = ev.elapsed_ms(e0, e1) * 1e3 / calls
+        ev.destroy(e0)
+        ev.destroy(e1)
+        del graph, bufs
+        nbytes = sum(1.125 * n * k + t * (6 * k + 4 * n + 8 * RANK) + 8 * RANK * (n + k) for n, k in shapes.values())
+        rows.append({"model": model, "T": t, "layer_us": round(us, 2), "layer_us_eager": round(eager, 2),
+                     "bytes": int(nbytes), "hbm_gbs": round(nbytes / us / 1e3, 1),
+                     "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                     "us_at_8tbs": round(nbytes / 8e12 * 1e6, 2),
+                     "weight_sets_cycled": nsets})
+        print(f"[small_t_layer] {model} T={t}: {us:.1f} us per layer fwd+bwd ({nbytes / us / 1e3:.0f} GB/s)",
+              file=sys.stderr, flush=True)
+    del sets, lora
+    torch.cuda.empty_cache()
+    return rows
+
+
 MERGE_SHAPES = [("7b", "gate", 18944, 3584), ("72b", "gate", 29568, 8192)]
 
 
@@ -732,7 +860,8 @@ def main() -> int:
     ap.add_argument("--streamed", default="7b",
                     help="comma-separated stacks for the streamed measurement (7b, 32b, 72b) or none")
     ap.add_argument("--block-sizes", default="4", help="comma-separated block sizes of the streamed stacks")
-    ap.add_argument("--slots", type=int, default=2, help="device pool slots (blocks) of the streamed stack")
+    ap.add_argument("--slots", default="2", help="comma-separated device pool sizes (slots of one block) of the "
+                                                  "streamed stacks")
     ap.add_argument("--stream-base", default="nf4", choices=("nf4", "bf16"),
                     help="format of the streamed base: nf4, or dense bf16 (the bf16_bitwise mode)")
     ap.add_argument("--stack-tokens", default="512", help="comma-separated token counts of the streamed stacks")
@@ -747,6 +876,9 @@ def main() -> int:
     ap.add_argument("--sweep-tokens", default="", help="comma-separated token counts the small-T sweep is restricted to")
     ap.add_argument("--merge", action="store_true",
                     help="instead of the layer step: merge_and_unload (dense W + s.B.A) device time vs HBM bytes")
+    ap.add_argument("--gemm-only", default="", choices=["", "q", "k", "v", "o", "gate", "up", "down"],
+                    help="instead of the layer step: only this projection's forward and backward, --steps times "
+                         "(short runs for counters and traces of its kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="launch one 1 GiB read + 1 GiB write elementwise kernel first (counter calibration)")
     args = ap.parse_args()
@@ -756,6 +888,7 @@ def main() -> int:
         return 2
     models = [m for m in args.streamed.split(",") if m and m != "none"]
     block_sizes = [int(v) for v in args.block_sizes.split(",") if v]
+    slot_counts = [int(v) for v in args.slots.split(",") if v]
     stack_tokens = [int(v) for v in args.stack_tokens.split(",") if v]
     if any(m not in ("7b", "32b", "72b") for m in models) or not block_sizes or not stack_tokens:
         print(f"--streamed takes 7b, 32b, 72b or none; --block-sizes and --stack-tokens need values", file=sys.stderr)
@@ -779,9 +912,12 @@ def main() -> int:
                   file=sys.stderr)
             return 2
         sweep = small_t_sweep(lib, torch, ev, shapes=shapes, tokens=tokens)
+        if not shapes:
+            sweep["layer_rows"] = [row for m in ("7b", "72b")
+                                   for row in small_t_layer(lib, torch, ev, m, tokens or SMALL_T)]
         copy_meas = measured_copy_gbs(torch, ev)
         read_meas = measured_read_gbs(lib, torch, ev)
-        for row in sweep["rows"]:
+        for row in sweep["rows"] + sweep.get("layer_rows", []):
             row["hbm_frac_vs_measured_copy"] = round(row["hbm_gbs"] / copy_meas, 4)
         sweep["hbm_copy_gbs_measured"] = round(copy_meas, 1)
         sweep["hbm_read_gbs_measured"] = round(read_meas, 1)
@@ -801,6 +937,11 @@ def main() -> int:
         return 0
     layer = build_layer(lib, torch)
     ev = HipEvents()
+    if args.gemm_only:
+        print(json.dumps(gemm_only(lib, torch, layer, ev, args.gemm_only, args.steps, args.warmup)), flush=True)
+        del layer
+        release_memory(torch)
+        return 0
     for _ in range(args.warmup):
         run_step(lib, layer)
     torch.cuda.synchronize()
@@ -894,7 +1035,7 @@ def main() -> int:
     if models:
         h2d = pinned_h2d_gbs(torch)
         out["denominators"]["h2d_pinned_gbs_measured"] = round(h2d, 2)
-        runs = [stream_bench(torch, m, block_sizes, stack_tokens, args.stack_steps, h2d, args.stream_base, args.slots,
+        runs = [stream_bench(torch, m, block_sizes, stack_tokens, args.stack_steps, h2d, args.stream_base, slot_counts,
                              remat=not args.no_remat, layer_parts=args.layer_parts) for m in models]
         out["streamed"] = dict(runs[0]["rows"][0], load=runs[0]["load"])
         out["streamed_all"] = runs
