@@ -231,14 +231,20 @@ def measured_traffic(kernel: str) -> int | None:
         return None
 
 
-def copy_calibration(torch) -> None:
-    """One plain streaming kernel of known traffic for the counter calibration: an
-    elementwise negation of a 1 GiB fp32 tensor (reads 1 GiB, writes 1 GiB)."""
+def copy_calibration(torch, lib=None) -> None:
+    """Plain streaming kernels of known traffic for the counter calibration: an
+    elementwise negation of a 1 GiB fp32 tensor (reads 1 GiB, writes 1 GiB) and, with
+    `lib`, the library's read probe over the same 1 GiB (reads 1 GiB, writes 1 MiB)."""
     src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     torch.neg(src, out=dst)
     torch.cuda.synchronize()
+    if lib is not None:
+        out = torch.empty(256 * 1024, dtype=torch.int32, device="cuda")
+        lib.probe_read(src, out, 1024)
+        torch.cuda.synchronize()
+        del out
     del src, dst
     torch.cuda.empty_cache()
 
@@ -900,7 +906,7 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     if args.copy_calibration:
-        copy_calibration(torch)
+        copy_calibration(torch, lib)
     if args.small_t_sweep:
         ev = HipEvents()
         shapes = [v for v in args.sweep_shapes.split(",") if v]
