@@ -518,13 +518,29 @@ def _stack_run(torch, ST, base, lora, tokens, h0, dh, steps, **kw) -> dict:
         torch.cuda.synchronize()
         res = {"y": y.clone(), "dx": dx.clone(), "act": st.activation_bytes()}
         c0 = st.pool.stats()["bytes_copied"]
-        res["s"] = ST.timed_steps(st, h0, dh, steps, warmup=0)
+        st.pool.timing_collect()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            st.step(h0, dh)
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        res["s"] = (time.perf_counter() - t0) / steps
+        res["timed_issue_s"] = (t1 - t0) / steps
+        tm = st.pool.timing_collect()
+        res["timed_host_ms"], res["timed_host_max_ms"] = tm["host_ms"] / steps, tm["host_max_ms"]
         res["bytes"] = (st.pool.stats()["bytes_copied"] - c0) / steps
         st.pool.timing_enable(True)
-        res["s_instrumented"] = ST.timed_steps(st, h0, dh, 1, warmup=0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        st.step(h0, dh)
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        res["s_instrumented"] = time.perf_counter() - t0
+        res["issue_s"] = t1 - t0
         tm = st.pool.timing_collect()
-        res["copy_ms"] = tm["copy_ms"]
-        res["stall_ms"] = tm["stall_ms"]
+        for k in ("copy_ms", "stall_ms", "host_ms", "host_max_ms"):
+            res[k] = tm[k]
         return res
     finally:
         st.close()
@@ -597,6 +613,12 @@ def stream_bench(torch, model: str, block_sizes, tokens_list, steps: int, h2d_gb
                 "compute_busy_ms_per_step": round(got["s_instrumented"] * 1e3 - st_ms, 3),
                 "copy_time_hidden_frac": round((c_ms - st_ms) / c_ms, 4) if c_ms > 0 else None,
                 "instrumented_step_ms": round(got["s_instrumented"] * 1e3, 3),
+                "instrumented_host_issue_ms": round(got["issue_s"] * 1e3, 3),
+                "host_ms_in_pool_hip_calls": round(got["host_ms"], 3),
+                "host_longest_pool_hip_call_ms": round(got["host_max_ms"], 3),
+                "timed_host_issue_ms_per_step": round(got["timed_issue_s"] * 1e3, 3),
+                "timed_host_ms_in_pool_hip_calls_per_step": round(got["timed_host_ms"], 3),
+                "timed_host_longest_pool_hip_call_ms": round(got["timed_host_max_ms"], 3),
                 "overlap_source": "HIP events of the pool over one extra step: copy spans on the copy stream, "
                                   "acquire-wait spans on the compute stream",
                 "host_base_gb": round(base.total_bytes() / 1e9, 3),

@@ -323,6 +323,22 @@ int stream_pool_create(const nf4_host_block* blocks, int n_blocks, void* device_
                        size_t slot_bytes, int n_slots, nf4_stream copy_stream, nf4_pool** out);
 
 /*
+ * The current device's pair of streams for a streamed pass ([hn]: blocks are copied
+ * on a dedicated stream so that the copies overlap compute): *compute_out for the
+ * kernels and the pool's acquire/release, *copy_out for the pool's H2D copies. HIP
+ * places a process's streams on a few hardware queues (4 by default), handing them
+ * out in creation order; a copy stream that shares the compute stream's queue turns
+ * the pool's cross-stream waits into head-of-line blocking there, and copy and
+ * compute then run one after the other (measured: 66 ms against 41 ms for 8 blocks
+ * of 256 MiB, for every fourth stream created). The two streams are created one right
+ * after the other, non-blocking, at the default priority, on the first call for a
+ * device, so they take different queues, and are kept until the process ends; later
+ * calls return the same pair. Errors: NF4_E_ARG for NULL arguments, NF4_E_HIP if a
+ * stream cannot be created.
+ */
+int stream_pool_streams(nf4_stream* compute_out, nf4_stream* copy_out);
+
+/*
  * Create a pool whose blocks are made of parts, e.g. one pinned host range per layer
  * (a block of block_size layers need not be one contiguous host allocation; [api]
  * "patch_hf_model" Behavior 4: layers regrouped into blocks). Block b is the parts
@@ -396,15 +412,20 @@ int stream_pool_destroy(nf4_pool* pool);
  * stream, after the copy's wait for the slot's last use: the pair spans the copy
  * alone) and around every acquire's wait for a block's copy (on the compute stream:
  * the pair spans the time that stream stood still for the copy; about zero when the
- * prefetch had landed). stream_pool_timing_collect blocks until the recorded spans
- * have completed, returns their sums in *out and forgets them. Enabling adds event
- * records to the streams; it changes no result.
+ * prefetch had landed). Whether enabled or not, the pool clocks on the host the time
+ * spent inside its own HIP calls (copy issue, event records and waits: a call that
+ * blocks the host thread shows there, not in the device spans).
+ * stream_pool_timing_collect blocks until the recorded spans have completed, returns
+ * their sums and the host clock since the last collect in *out and forgets them.
+ * Enabling adds event records to the streams; it changes no result.
  */
 typedef struct {
     double copy_ms;    /* device time of the H2D copies issued while enabled */
     double stall_ms;   /* time the compute streams waited at acquire for a copy */
     uint64_t copies;   /* copies timed */
     uint64_t acquires; /* acquires timed */
+    double host_ms;    /* host wall time inside the pool's HIP calls since the last collect */
+    double host_max_ms; /* the longest single such call */
 } nf4_pool_timing;
 
 int stream_pool_timing_enable(nf4_pool* pool, int enable);

@@ -6,7 +6,9 @@
 // comment); Poros API reference, "patch_hf_model" Behavior 4-6; "Poros on consumer
 // GPUs", "What you need besides VRAM" (the streamed base lives in pinned host memory,
 // needed for asynchronous copies).
+#include <chrono>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "../../include/nf4lora.h"
@@ -33,6 +35,19 @@ struct HipEngine {
     bool timing = false;
     std::vector<Span> copy_spans, stall_spans;
     std::vector<hipEvent_t> spare;
+    // host time spent inside the pool's HIP calls, whether or not the device spans are
+    // recorded (a call that blocks the host shows here, not in the device spans)
+    double host_ms = 0.0, host_max_ms = 0.0;
+
+    template <class F>
+    hipError_t host_timed(F&& call) {
+        const auto t0 = std::chrono::steady_clock::now();
+        const hipError_t e = call();
+        const double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+        host_ms += ms;
+        if (ms > host_max_ms) host_max_ms = ms;
+        return e;
+    }
 
     int create_event(hipEvent_t* e) {
         return hip_ok(hipEventCreateWithFlags(e, hipEventDisableTiming), "stream_pool: hipEventCreate");
@@ -40,8 +55,12 @@ struct HipEngine {
     void destroy_event(hipEvent_t e) {
         if (e) (void)hipEventDestroy(e);
     }
-    int record(hipEvent_t e, hipStream_t s) { return hip_ok(hipEventRecord(e, s), "stream_pool: record event"); }
-    int wait(hipStream_t s, hipEvent_t e) { return hip_ok(hipStreamWaitEvent(s, e, 0), "stream_pool: wait event"); }
+    int record(hipEvent_t e, hipStream_t s) {
+        return hip_ok(host_timed([&] { return hipEventRecord(e, s); }), "stream_pool: record event");
+    }
+    int wait(hipStream_t s, hipEvent_t e) {
+        return hip_ok(host_timed([&] { return hipStreamWaitEvent(s, e, 0); }), "stream_pool: wait event");
+    }
 
     hipEvent_t timing_event() {
         if (!spare.empty()) {
@@ -71,7 +90,8 @@ struct HipEngine {
         Span sp;
         int st = span_begin(sp, s);
         if (st == NF4_OK)
-            st = hip_ok(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s), "stream_pool: H2D copy");
+            st = hip_ok(host_timed([&] { return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s); }),
+                        "stream_pool: H2D copy");
         if (st == NF4_OK) st = span_end(sp, s, copy_spans);
         return st;
     }
@@ -180,6 +200,35 @@ int stream_pool_slot_block(const nf4_pool* p, int slot, int* block_out) {
     return NF4_OK;
 }
 
+int stream_pool_streams(nf4_stream* compute_out, nf4_stream* copy_out) {
+    if (!compute_out || !copy_out) return fail(NF4_E_ARG, "stream_pool_streams: NULL argument");
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static hipStream_t pairs[kMaxDevices][2] = {};
+    int dev = 0;
+    int st = hip_ok(hipGetDevice(&dev), "stream_pool_streams: hipGetDevice");
+    if (st != NF4_OK) return st;
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(NF4_E_ARG, "stream_pool_streams: device %d beyond the %d the library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pairs[dev][0]) {
+        // back to back, so that HIP gives them different hardware queues
+        hipStream_t c = nullptr, k = nullptr;
+        st = hip_ok(hipStreamCreateWithFlags(&c, hipStreamNonBlocking), "stream_pool_streams: create compute stream");
+        if (st == NF4_OK)
+            st = hip_ok(hipStreamCreateWithFlags(&k, hipStreamNonBlocking), "stream_pool_streams: create copy stream");
+        if (st != NF4_OK) {
+            if (c) (void)hipStreamDestroy(c);
+            return st;
+        }
+        pairs[dev][0] = c;
+        pairs[dev][1] = k;
+    }
+    *compute_out = pairs[dev][0];
+    *copy_out = pairs[dev][1];
+    return NF4_OK;
+}
+
 int stream_pool_timing_enable(nf4_pool* p, int enable) {
     if (!p) return fail(NF4_E_ARG, "stream_pool_timing_enable: NULL pool");
     p->eng.timing = enable != 0;
@@ -204,6 +253,9 @@ int stream_pool_timing_collect(nf4_pool* p, nf4_pool_timing* out) {
     };
     sum(p->eng.copy_spans, out->copy_ms, out->copies);
     sum(p->eng.stall_spans, out->stall_ms, out->acquires);
+    out->host_ms = p->eng.host_ms;
+    out->host_max_ms = p->eng.host_max_ms;
+    p->eng.host_ms = p->eng.host_max_ms = 0.0;
     return st;
 }
 

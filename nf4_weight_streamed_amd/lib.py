@@ -37,7 +37,7 @@ class HostBlock(C.Structure):
 
 class PoolTiming(C.Structure):
     _fields_ = [("copy_ms", C.c_double), ("stall_ms", C.c_double), ("copies", C.c_uint64),
-                ("acquires", C.c_uint64)]
+                ("acquires", C.c_uint64), ("host_ms", C.c_double), ("host_max_ms", C.c_double)]
 
 
 class PoolStats(C.Structure):
@@ -89,6 +89,7 @@ def _load() -> C.CDLL:
         "stream_pool_set_order": (i32, [vp, i32]),
         "stream_pool_release_part": (i32, [vp, i32, i32, vp]),
         "stream_pool_timing_enable": (i32, [vp, i32]),
+        "stream_pool_streams": (i32, [C.POINTER(vp), C.POINTER(vp)]),
         "stream_pool_timing_collect": (i32, [vp, C.POINTER(PoolTiming)]),
         "nf4_block_layout": (i32, [C.POINTER(C.c_int64), i32, i32, i32, C.POINTER(C.c_size_t),
                                    C.POINTER(C.c_size_t)]),
@@ -509,6 +510,21 @@ def pinned_empty(nbytes: int) -> torch.Tensor:
             _free(_addr)
 
     return torch.frombuffer(_PinnedOwner.from_address(addr), dtype=torch.uint8)
+
+
+_POOL_STREAMS: dict = {}
+
+
+def pool_streams():
+    """The current device's (compute, copy) stream pair for streamed passes
+    (stream_pool_streams): created back to back so that they sit on different
+    hardware queues, kept for the life of the process."""
+    dev = torch.cuda.current_device()
+    if dev not in _POOL_STREAMS:
+        c, k = C.c_void_p(), C.c_void_p()
+        _check(_lib.stream_pool_streams(C.byref(c), C.byref(k)))
+        _POOL_STREAMS[dev] = (torch.cuda.ExternalStream(c.value), torch.cuda.ExternalStream(k.value))
+    return _POOL_STREAMS[dev]
 
 
 class StreamPool:

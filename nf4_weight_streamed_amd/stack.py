@@ -36,6 +36,7 @@ receive a zero gradient.
 
 from __future__ import annotations
 
+import contextlib
 import time
 from dataclasses import dataclass
 
@@ -272,7 +273,9 @@ class NF4Stack:
         nb = base.n_blocks
         self.n_slots = nb if mode == "resident" else max(1, n_slots)
         self.slab = torch.empty(self.n_slots * base.slot_bytes, dtype=torch.uint8, device="cuda")
-        self.copy_stream = torch.cuda.Stream()
+        # the library's compute/copy stream pair: on different hardware queues, so the
+        # pool's waits between them never serialise copies behind kernels
+        self.compute_stream, self.copy_stream = lib.pool_streams()
         ranges, part_begin = base.pool_ranges(self.layer_parts)
         self.pool = lib.StreamPool(ranges, self.slab, base.slot_bytes, self.n_slots, self.copy_stream,
                                    part_begin=part_begin)
@@ -436,7 +439,28 @@ class NF4Stack:
         for li in self._layers_of(b):
             self._layer_forward(li, w[li - b * self.base.block_size])
 
+    @contextlib.contextmanager
+    def _on_compute(self):
+        """Run the enclosed work on the stack's compute stream, ordered after the
+        caller's stream's earlier work and before its later work."""
+        caller = torch.cuda.current_stream()
+        if caller == self.compute_stream:
+            yield
+            return
+        self.compute_stream.wait_stream(caller)
+        with torch.cuda.stream(self.compute_stream):
+            yield
+        caller.wait_stream(self.compute_stream)
+
     def forward(self, h0: torch.Tensor) -> torch.Tensor:
+        with self._on_compute():
+            return self._forward(h0)
+
+    def backward(self, dh: torch.Tensor) -> torch.Tensor:
+        with self._on_compute():
+            return self._backward(dh)
+
+    def _forward(self, h0: torch.Tensor) -> torch.Tensor:
         (self.boundary[0] if self.remat else self.acts[0]["h"]).copy_(h0)
         nb, bs = self.base.n_blocks, self.base.block_size
         self.pool.set_order(False)            # layers of a block used first to last
@@ -453,7 +477,7 @@ class NF4Stack:
             self.pool.release(b)
         return self.boundary[nb] if self.remat else self.acts[-1]["h"]
 
-    def backward(self, dh: torch.Tensor) -> torch.Tensor:
+    def _backward(self, dh: torch.Tensor) -> torch.Tensor:
         nb = self.base.n_blocks
         cur = self.dh[0]
         cur.copy_(dh)
@@ -482,6 +506,7 @@ class NF4Stack:
         return out, dh0
 
     def close(self):
+        self.compute_stream.synchronize()   # the stack's buffers may be reused once freed
         self.pool.close()
 
 

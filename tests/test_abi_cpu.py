@@ -159,6 +159,8 @@ def test_pool_validation(L):
     _err(L, rc, L.NF4_E_ARG, "copy")
     rc = raw.stream_pool_prefetch(None, 0)
     _err(L, rc, L.NF4_E_ARG, "NULL pool")
+    rc = raw.stream_pool_streams(None, None)
+    _err(L, rc, L.NF4_E_ARG, "NULL")
 
 
 def test_block_layout(L):

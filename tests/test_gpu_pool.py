@@ -1,5 +1,7 @@
 """The stream pool on the GPU: copies land intact, reuse is ordered, states are checked."""
 
+import time
+
 import pytest
 import torch
 
@@ -148,3 +150,64 @@ def test_pinned_empty_is_exact_and_pinned(gpu_lib):
     d = t.cuda(non_blocking=True)
     torch.cuda.synchronize()
     assert int(d.sum()) == 7000
+
+
+def test_pool_streams_pair_overlaps_copies_with_compute(gpu_lib):
+    """The library's compute/copy stream pair (stream_pool_streams): the same two
+    streams on every call, and a 2-slot pass over 8 blocks on them overlaps each copy
+    with the previous block's compute: its time stays near that of the copies alone,
+    well below copies plus compute (which a copy stream on the compute stream's
+    hardware queue would give)."""
+    L = gpu_lib
+    comp, copy = L.pool_streams()
+    again = L.pool_streams()
+    assert again[0].cuda_stream == comp.cuda_stream and again[1].cuda_stream == copy.cuda_stream
+    assert comp.cuda_stream != copy.cuda_stream
+    nb, nbytes = 8, 128 << 20
+    host = L.pinned_empty(nb * nbytes)
+    blocks = [host[i * nbytes:(i + 1) * nbytes] for i in range(nb)]
+    slab = torch.empty(2 * nbytes, dtype=torch.uint8, device="cuda")
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty_like(a)
+    pool = L.StreamPool(blocks, slab, nbytes, 2, copy)
+
+    def work():
+        for _ in range(2):
+            torch.matmul(a, b, out=c)
+
+    def one_pass(compute: bool):
+        with torch.cuda.stream(comp):
+            for i in range(nb):
+                pool.acquire(i)
+                if i + 1 < nb:
+                    pool.prefetch(i + 1)
+                if compute:
+                    work()
+                pool.release(i)
+
+    def compute_only():
+        with torch.cuda.stream(comp):
+            for _ in range(nb):
+                work()
+
+    def timed(fn, *args):
+        best = float("inf")
+        for _ in range(3):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn(*args)
+            torch.cuda.synchronize()
+            best = min(best, time.perf_counter() - t0)
+        return best
+
+    try:
+        one_pass(True)
+        t_copy = timed(one_pass, False)
+        t_comp = timed(compute_only)
+        t_both = timed(one_pass, True)
+        print(f"copies {t_copy * 1e3:.2f} ms, compute {t_comp * 1e3:.2f} ms, both {t_both * 1e3:.2f} ms", flush=True)
+        assert t_comp > 0.3 * t_copy, "the compute must be long enough for the check to mean something"
+        assert t_both < t_copy + 0.5 * t_comp, (t_copy, t_comp, t_both)
+    finally:
+        pool.close()

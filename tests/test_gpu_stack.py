@@ -115,6 +115,34 @@ def _same(a, b):
         assert torch.equal(s1["out"], s2["out"]) and torch.equal(s1["dh0"], s2["dh0"])
 
 
+def test_stack_is_ordered_with_the_caller_stream(ST):
+    """The stack runs on the library's compute stream, after the caller's stream's
+    earlier work and before its later work: inputs written late on a side stream (behind
+    a bounded spin) are the ones read, and outputs cloned on that stream right after the
+    step are complete - the bits equal those of a step called from the default stream."""
+    _, _, base, lora = _tiny_stack(ST, 5, 2)
+    T = 48
+    st = ST.NF4Stack(base, lora, T, 32.0, mode="streamed")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    h0_src = torch.randn(T, base.dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    dh_src = torch.randn(T, base.dims.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    out, dh0 = st.step(h0_src, dh_src)
+    ref = (out.clone(), dh0.clone())
+    h0, dh = torch.zeros_like(h0_src), torch.zeros_like(dh_src)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(10_000_000)
+        h0.copy_(h0_src)
+        dh.copy_(dh_src)
+        out, dh0 = st.step(h0, dh)
+        got = (out.clone(), dh0.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+    st.close()
+
+
 @pytest.mark.parametrize("block_size", [1, 2, 3])
 def test_streamed_equals_resident_tiny(ST, block_size):
     L, T = 7, 48
