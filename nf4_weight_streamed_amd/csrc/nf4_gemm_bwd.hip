@@ -7,10 +7,13 @@
 // streaming the frozen base, main comment). The contraction runs over N, the
 // rows of W, while the codes are contiguous along K: each thread dequantises a
 // 4 (n) x 8 (k) patch and packs bf16 pairs across rows, so the tile lands in LDS
-// as [k][n] and the MFMA B operand is again a contiguous 16-byte read. The 16-byte
-// chunks of each LDS row are XOR-swizzled by (k / 8) % 8: the 8-byte transposed
-// stores of a wave then spread over all banks, and the fragment reads (8
-// consecutive rows share one swizzle) stay conflict-free. With kDense the base is
+// as [k][n] and the MFMA B operand is again a contiguous 16-byte read. Its rows are
+// 160 bytes apart and their 16-byte chunks XOR-swizzled by (k / 16) % 8: measured on
+// the MI355X's 64-bank LDS, the fragment reads (16 aligned rows share one swizzle)
+// are then conflict-free and the 8-byte transposed stores as cheap as any layout
+// measured (the former 144-byte pitch with a (k / 8) % 8 swizzle cost 2.6 times the
+// conflict-free time per fragment read). The dY tile keeps 144-byte rows without a
+// swizzle, conflict-free for its fragment reads. With kDense the base is
 // dense bf16 (the experimental "bf16_bitwise" streaming mode of the Poros API
 // reference, "PorosTrainer.from_pretrained"): the patch is four 16-byte row pieces,
 // paired across rows the same way, with nothing to dequantise.
@@ -24,21 +27,22 @@ namespace nf4 {
 namespace {
 
 constexpr int kBN = 64;        // contraction (N) per main-loop step
-constexpr int kLds = kBN + 8;  // LDS pitch in bf16
+constexpr int kLds = kBN + 8;    // LDS pitch of the dY tile in bf16 (144 bytes)
+constexpr int kLdsW = kBN + 16;  // LDS pitch of the weight tile in bf16 (160 bytes)
 constexpr int kThreads = 256;
 constexpr int64_t kCUs = kChipCUs;
 
 // Workgroup tile: 128 tokens x 128 input features, 4 waves in a 2x2 grid (64 x 64
 // each, 32x32x16 MFMA), contraction steps of 64 over N. Per step each thread loads
 // (raw buffer loads, hardware zero outside the tensors) a 4 (n) x 8 (k) patch of
-// codes with the 4 row scales, and 4 16-byte chunks of the dY tile, one step ahead;
-// after the current step's MFMAs it dequantises the patch - one 8-byte read of a
-// 256-entry (level[lo], level[hi]) pair table per code byte, fp32 multiply by the
-// row's absmax, bf16 pack pairing rows - and, once every wave has read the current
-// tiles, stores it transposed. dY and the weight tile are single-buffered (two
-// barriers per step) so that the LDS block (51 KB, shared with the LoRA epilogue) and
-// 165 VGPRs let three workgroups share a CU; the other workgroups' MFMAs fill each
-// workgroup's store phase.
+// codes with the 4 row scales and 4 16-byte chunks of the dY tile, two steps ahead
+// into a ring of two register sets. dY and the weight tile are double-buffered in
+// LDS: during the MFMAs of step s each thread dequantises its patch of step s + 1 -
+// one 8-byte read of a 256-entry (level[lo], level[hi]) pair table per code byte,
+// fp32 multiply by the row's absmax, bf16 pack pairing rows - and stores it
+// transposed, with its dY chunks, into the other buffer; one barrier per step. The
+// step has no branch, so the scheduler interleaves the dequantisation with the
+// MFMAs. LDS block 78 KB (shared with the LoRA epilogue): two workgroups per CU.
 
 // Which tile (and contraction range) each workgroup of the 1-D grid takes: ids
 // 0 .. full-1 are whole tiles, the rest pieces of the last `tail` tiles, piece z of
@@ -62,7 +66,7 @@ struct BwdLora {
 };
 
 template <bool kDense>
-__global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
+__global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     const uint16_t* __restrict__ dy, const void* __restrict__ weights, const float* __restrict__ absmax, int T,
     int N, int K, BwdTiles tl, BwdLora lora, uint16_t* __restrict__ dx, float* __restrict__ partial, Tables tab) {
     constexpr int BM = 128, BK = 128;
@@ -70,16 +74,15 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
     constexpr int FM = WM / 32, FK = WK / 32;
     constexpr int A_CHUNKS = BM * (kBN / 8) / kThreads;  // 4
 
-    // One LDS block (51 KB: three workgroups per CU). Main loop: the dY tile, the
-    // weight tile and the pair table, single-buffered; LoRA epilogue: (s.g)^T hi/lo
-    // for up to 64 ranks and one 64-column half of the x tile, transposed.
+    // One LDS block (78 KB: two workgroups per CU). Main loop: two buffers of (dY
+    // tile, weight tile) and the pair table; LoRA epilogue: (s.g)^T hi/lo for up to 64
+    // ranks and one 64-column half of the x tile, transposed.
     constexpr int kTP = BM + 8;  // pitch of the epilogue's [.][t] tiles
-    constexpr int kMain = BM * kLds + BK * kLds + 2 * 512;
+    constexpr int kBuf = BM * kLds + BK * kLdsW;  // one buffer: dY tile, then weight tile
+    constexpr int kMain = 2 * kBuf + 2 * 512;
     constexpr int kEpi = (2 * 64 + BK / 2) * kTP;
     __shared__ __align__(16) uint16_t smem[kMain > kEpi ? kMain : kEpi];
-    uint16_t* const sA = smem;
-    uint16_t* const sWt = smem + BM * kLds;
-    float* const sLut = reinterpret_cast<float*>(smem + BM * kLds + BK * kLds);
+    float* const sLut = reinterpret_cast<float*>(smem + 2 * kBuf);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -133,16 +136,18 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
         a_off[i] = (uint32_t(c >> 3) * uint32_t(N) + uint32_t(c & 7) * 8u) * 2u;
     }
 
-    u32x4 ra[A_CHUNKS];
-    uint32_t rc[4];  // NF4: 8 codes of each patch row
-    float rs[4];
-    u32x4 rw[4];     // dense: 8 bf16 of each patch row
-    auto gload = [&](int nb) {
+    struct LSet {             // one step's loads
+        u32x4 ra[A_CHUNKS];   // dY chunks
+        uint32_t rc[4];       // NF4: 8 codes of each patch row
+        float rs[4];          //      and its scale
+        u32x4 rw[4];          // dense: 8 bf16 of each patch row
+    };
+    auto gload = [&](int nb, LSet& l) {
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
-            // dY columns at or beyond N (ragged last step) read as zero
+            // dY columns at or beyond N (ragged last step, steps past the end) read as zero
             const bool ok = nb * kBN + 8 * ((tid + kThreads * i) & 7) < N;
-            ra[i] = buf_load16(rdy, ok ? a_off[i] + uint32_t(nb) * (kBN * 2) : kOutOfRange);
+            l.ra[i] = buf_load16(rdy, ok ? a_off[i] + uint32_t(nb) * (kBN * 2) : kOutOfRange);
         }
         // Rows n >= N lie past the end of both buffers and read as zero (scale 0, so
         // the dequantised row is zero). Columns k >= K of a ragged tile read the next
@@ -151,29 +156,33 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
         for (int i = 0; i < 4; ++i) {
             const uint32_t n = uint32_t(nb * kBN + 4 * pr + i);
             if constexpr (kDense) {
-                rw[i] = buf_load16(rcd, (n * uint32_t(K) + kc) * 2u);
+                l.rw[i] = buf_load16(rcd, (n * uint32_t(K) + kc) * 2u);
             } else {
-                rc[i] = buf_load_u32(rcd, n * uint32_t(K / 2) + kc / 2);
-                rs[i] = buf_load_f32(rsc, n * uint32_t(K / 64) * 4u + (kc / 64) * 4u);
+                l.rc[i] = buf_load_u32(rcd, n * uint32_t(K / 2) + kc / 2);
+                l.rs[i] = buf_load_f32(rsc, n * uint32_t(K / 64) * 4u + (kc / 64) * 4u);
             }
         }
     };
     const char* lut = reinterpret_cast<const char*>(sLut);
-    auto sstore = [&]() {
+    // one step's tiles into LDS buffer b
+    auto sstore = [&](const LSet& l, int b) {
+        uint16_t* const sA = smem + b * kBuf;
+        uint16_t* const sWt = sA + BM * kLds;
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
             const int c = tid + kThreads * i;
-            *reinterpret_cast<u32x4*>(&sA[(c >> 3) * kLds + (c & 7) * 8]) = ra[i];
+            *reinterpret_cast<u32x4*>(&sA[(c >> 3) * kLds + (c & 7) * 8]) = l.ra[i];
         }
-        // row k = 8*pc + e holds n = 4*pr .. 4*pr+3: chunk pr/2 (swizzled by pc), half pr&1
-        const int col = (((pr >> 1) ^ (pc & 7)) << 3) + 4 * (pr & 1);
+        // row k = 8*pc + e holds n = 4*pr .. 4*pr+3: chunk pr/2, swizzled by k / 16 = pc / 2,
+        // half pr&1
+        const int col = (((pr >> 1) ^ ((pc >> 1) & 7)) << 3) + 4 * (pr & 1);
         if constexpr (kDense) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sh = 16 * (e & 1);
-                auto bits = [&](int i) { return (rw[i][e >> 1] >> sh) & 0xFFFFu; };
+                auto bits = [&](int i) { return (l.rw[i][e >> 1] >> sh) & 0xFFFFu; };
                 const u32x2 o = {bits(0) | (bits(1) << 16), bits(2) | (bits(3) << 16)};
-                *reinterpret_cast<u32x2*>(&sWt[(8 * pc + e) * kLds + col]) = o;
+                *reinterpret_cast<u32x2*>(&sWt[(8 * pc + e) * kLdsW + col]) = o;
             }
             return;
         }
@@ -181,16 +190,16 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float2 lv = *reinterpret_cast<const float2*>(lut + (((rc[i] >> (8 * b)) & 0xFFu) << 3));
+            for (int q = 0; q < 4; ++q) {
+                const float2 lv = *reinterpret_cast<const float2*>(lut + (((l.rc[i] >> (8 * q)) & 0xFFu) << 3));
                 // level * absmax in fp32, then RNbf (below): the format's two roundings
-                v[i][2 * b] = lv.x * rs[i];
-                v[i][2 * b + 1] = lv.y * rs[i];
+                v[i][2 * q] = lv.x * l.rs[i];
+                v[i][2 * q + 1] = lv.y * l.rs[i];
             }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             u32x2 o = {pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e])};
-            *reinterpret_cast<u32x2*>(&sWt[(8 * pc + e) * kLds + col]) = o;
+            *reinterpret_cast<u32x2*>(&sWt[(8 * pc + e) * kLdsW + col]) = o;
         }
     };
 
@@ -203,17 +212,27 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     if (nb_begin < nb_end) {
-        gload(nb_begin);
+        LSet ld[2];
+        gload(nb_begin, ld[0]);
+        gload(nb_begin + 1, ld[1]);
         __syncthreads();  // sLut visible
-        sstore();
+        sstore(ld[0], 0);
         __syncthreads();
-        // loads are issued unconditionally (a step past the end reads data that is never
-        // used, or zeros): the compiler's wait counts then stay exact. Two barriers per
-        // step: the single-buffered tiles are rewritten only after every wave has read
-        // them; the other workgroups on the CU keep the MFMAs busy meanwhile.
-        for (int nb = nb_begin; nb < nb_end; ++nb) {
-            gload(nb + 1);
+        // Step nb, C = (nb - nb_begin) mod 2 at compile time (the loop is unrolled by 2,
+        // so no register array is indexed at run time): MFMAs on LDS buffer C, loads of
+        // step nb + 2 into register set C (stored into LDS last step), and the tiles of
+        // step nb + 1 from set C ^ 1 into buffer C ^ 1, which every wave finished
+        // reading before the previous step's barrier. Loads and stores are
+        // unconditional (a step past the end reads zeros or data that is never used and
+        // writes the idle buffer), so the body has no branch and the compiler's wait
+        // counts stay exact: the store waits for set C ^ 1 only, leaving the newest
+        // loads in flight.
+        auto step = [&](int nb, auto c_) {
+            constexpr int C = decltype(c_)::value;
+            gload(nb + 2, ld[C]);
             __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+            const uint16_t* const sA = smem + C * kBuf;
+            const uint16_t* const sWt = sA + BM * kLds;
 #pragma unroll
             for (int kk = 0; kk < kBN / 16; ++kk) {
                 bf16x8 af[FM], bw[FK];
@@ -224,20 +243,27 @@ __global__ __launch_bounds__(kThreads, 3) void k_nf4_gemm_bwd_dx(
 #pragma unroll
                 for (int j = 0; j < FK; ++j) {
                     const int row = wk * WK + 32 * j + frag_row;
-                    const int chunk = (2 * kk + (lane >> 5)) ^ ((row >> 3) & 7);
-                    bw[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sWt[row * kLds + chunk * 8]));
+                    const int chunk = (2 * kk + (lane >> 5)) ^ ((row >> 4) & 7);
+                    bw[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sWt[row * kLdsW + chunk * 8]));
                 }
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FK; ++j) acc[i][j] = mfma32x32x16(af[i], bw[j], acc[i][j]);
             }
-            __syncthreads();  // every wave's fragment reads of this step are done
-            if (nb + 1 < nb_end) {
-                sstore();  // the next step's tiles
-                __syncthreads();
-            }
+            sstore(ld[C ^ 1], C ^ 1);  // the next step's tiles
+            // interleave the table reads, multiplies and stores with the MFMAs (the
+            // scheduler's small-GEMM strategy). NF4 only: the dense variant has no
+            // dequantisation to hide.
+            if constexpr (!kDense) __builtin_amdgcn_iglp_opt(0);
+            __syncthreads();  // this step's reads and the next step's stores are done
+        };
+        int nb = nb_begin;
+        for (; nb + 1 < nb_end; nb += 2) {
+            step(nb, std::integral_constant<int, 0>{});
+            step(nb + 1, std::integral_constant<int, 1>{});
         }
+        if (nb < nb_end) step(nb, std::integral_constant<int, 0>{});
     }
 
     // LoRA (whole tiles and piece 0 of split tiles). g = sum of the partials in partial
