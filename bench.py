@@ -458,26 +458,36 @@ def measured_copy_gbs(torch, ev: "HipEvents", nbytes: int = 1 << 30) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+READ_SWEEP: list = []  # (depth, workgroups, nontemporal, GB/s) of the last measured_read_gbs
+
+
 def measured_read_gbs(lib, torch, ev: "HipEvents", nbytes: int = 2 << 30) -> float:
     """Read-only reference: the library's read probe (coalesced 16-byte loads, grid-stride)
-    over 2 GiB, best over a few grid sizes and launches: the rate a plain read-bound kernel
-    reaches on this device."""
+    over 2 GiB, swept over the loads in flight per thread (4 .. 32), the grid (256 .. 8192
+    workgroups) and plain or non-temporal loads, best of 3 launches each; returns the best
+    rate and keeps the sweep in READ_SWEEP, so that the plateau the best comes from is on
+    record."""
     src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     best = 0.0
-    for wg in (1024, 2048, 4096):
-        out = torch.empty(256 * wg, dtype=torch.int32, device="cuda")
-        lib.probe_read(src, out, wg)
-        for _ in range(3):
-            e0, e1 = ev.create(), ev.create()
-            ev.record(e0, stream)
-            lib.probe_read(src, out, wg)
-            ev.record(e1, stream)
-            best = max(best, nbytes / (ev.elapsed_ms(e0, e1) * 1e-3) / 1e9)
-            ev.destroy(e0)
-            ev.destroy(e1)
-        del out
-    del src
+    READ_SWEEP.clear()
+    out = torch.empty(256 * 8192, dtype=torch.int32, device="cuda")
+    for nt in (False, True):
+        for depth in (4, 8, 16, 32):
+            for wg in (256, 384, 512, 768, 1024, 2048, 4096, 8192):
+                lib.probe_read_depth(src, out, wg, depth, nt)
+                rate = 0.0
+                for _ in range(3):
+                    e0, e1 = ev.create(), ev.create()
+                    ev.record(e0, stream)
+                    lib.probe_read_depth(src, out, wg, depth, nt)
+                    ev.record(e1, stream)
+                    rate = max(rate, nbytes / (ev.elapsed_ms(e0, e1) * 1e-3) / 1e9)
+                    ev.destroy(e0)
+                    ev.destroy(e1)
+                READ_SWEEP.append((depth, wg, int(nt), round(rate, 1)))
+                best = max(best, rate)
+    del out, src
     torch.cuda.empty_cache()
     return best
 
@@ -949,6 +959,8 @@ def main() -> int:
             row["hbm_frac_vs_measured_copy"] = round(row["hbm_gbs"] / copy_meas, 4)
         sweep["hbm_copy_gbs_measured"] = round(copy_meas, 1)
         sweep["hbm_read_gbs_measured"] = round(read_meas, 1)
+        sweep["read_probe_sweep"] = {"columns": ["loads_in_flight_per_thread", "workgroups", "nontemporal", "GB/s"],
+                                     "rows": READ_SWEEP}
         out = {"metric": "NF4-LoRA linear fwd+bwd device time at small T; % of HBM roofline", "n_gpus": 1,
                "dtype": "bf16", "data": "synthetic", "small_t": sweep}
         print(json.dumps(out), flush=True)
@@ -1056,6 +1068,8 @@ def main() -> int:
             "hbm_gbs_published": HBM_PEAK_GBS,
             "hbm_copy_gbs_measured": round(copy_meas, 1),
             "hbm_read_gbs_measured": round(read_meas, 1),
+            "read_probe_sweep": {"columns": ["loads_in_flight_per_thread", "workgroups", "nontemporal", "GB/s"],
+                                 "rows": READ_SWEEP},
         },
     }
     del layer

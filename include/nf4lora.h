@@ -281,6 +281,16 @@ int nf4_probe_mfma(float* out, int workgroups, int iters, nf4_stream stream);
  */
 int nf4_probe_read(const void* src, size_t bytes, uint32_t* out, int workgroups, nf4_stream stream);
 
+/*
+ * The same read probe with `depth` 16-byte loads in flight per thread (4, 8, 16 or 32;
+ * nf4_probe_read is depth 8) and, with nontemporal != 0, the loads marked non-temporal
+ * (streamed past the caches), so that a sweep over depth and workgroups can show where
+ * the read rate stops rising. Arguments and errors as nf4_probe_read, plus NF4_E_ARG for
+ * another depth.
+ */
+int nf4_probe_read_depth(const void* src, size_t bytes, uint32_t* out, int workgroups, int depth,
+                         int nontemporal, nf4_stream stream);
+
 /* ------------------------------------------------------------------ stream pool
  * Blockwise residency of the frozen base ([hn] main comment; [api]
  * "patch_hf_model" Behavior 5-6; [consumer] "What you need besides VRAM",

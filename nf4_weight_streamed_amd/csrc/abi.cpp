@@ -177,6 +177,18 @@ int nf4_probe_read(const void* src, size_t bytes, uint32_t* out, int workgroups,
                       "nf4_probe_read");
 }
 
+int nf4_probe_read_depth(const void* src, size_t bytes, uint32_t* out, int workgroups, int depth, int nontemporal,
+                         nf4_stream stream) {
+    if (!src || !out || workgroups < 1 || bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0 ||
+        (depth != 4 && depth != 8 && depth != 16 && depth != 32))
+        return fail(NF4_E_ARG, "nf4_probe_read_depth: need src != NULL (16-byte aligned), bytes a positive multiple "
+                               "of 16 (got %zu), out != NULL, workgroups >= 1 (got %d), depth 4, 8, 16 or 32 (got %d)",
+                    bytes, workgroups, depth);
+    return hip_status(nf4::launch_probe_read_depth(src, uint64_t(bytes), out, workgroups, depth, nontemporal != 0,
+                                                   static_cast<hipStream_t>(stream)),
+                      "nf4_probe_read_depth");
+}
+
 int nf4_profile_next_gemm(void* start_event, void* stop_event) {
     if ((start_event == nullptr) != (stop_event == nullptr))
         return fail(NF4_E_ARG, "nf4_profile_next_gemm: pass both events or neither");

@@ -122,6 +122,8 @@ hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8
 
 hipError_t launch_probe_mfma(float* out, int workgroups, int iters, hipStream_t stream);
 hipError_t launch_probe_read(const void* src, uint64_t bytes, uint32_t* out, int workgroups, hipStream_t stream);
+hipError_t launch_probe_read_depth(const void* src, uint64_t bytes, uint32_t* out, int workgroups, int depth,
+                                  bool nontemporal, hipStream_t stream);
 hipError_t launch_merge_lora(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, const uint16_t* A,
                              const uint16_t* B, int r, float s, uint16_t* w_out, hipStream_t stream);
 

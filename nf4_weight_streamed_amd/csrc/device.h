@@ -115,6 +115,16 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t of
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, 0));
 }
 
+// Non-temporal variants (the load's nt cache-policy bit): for data each kernel reads once
+// while streaming, such as a weight matrix read by a few-token kernel.
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 2));
+}
+
+__device__ __forceinline__ u32x2 buf_load8_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, 2));
+}
+
 __device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0));
 }

@@ -34,32 +34,55 @@ __global__ __launch_bounds__(256) void k_probe_mfma(float* __restrict__ out, int
     if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
 }
 
-// Read-rate probe: coalesced 16-byte loads of `n16` pieces in a grid-stride loop, kU
-// pieces in flight per thread, folded with XOR into one word per thread (written to
-// out[workgroup * 256 + thread]) so that no load is elided.
-constexpr int kProbeReadU = 8;
+// Read-rate probe: coalesced 16-byte loads of `n16` pieces in a grid-stride loop, U
+// pieces in flight per thread (non-temporal loads with NT), folded with XOR into one
+// word per thread (written to out[workgroup * 256 + thread]) so that no load is elided.
+template <int U, bool NT>
 __global__ __launch_bounds__(256) void k_probe_read(const u32x4* __restrict__ src, uint64_t n16,
                                                     uint32_t* __restrict__ out) {
     const uint64_t stride = uint64_t(gridDim.x) * 256;
     uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x;
     u32x4 acc = {0u, 0u, 0u, 0u};
-    for (; i + (kProbeReadU - 1) * stride < n16; i += kProbeReadU * stride) {
-        u32x4 v[kProbeReadU];
+    auto ld = [&](uint64_t j) { return NT ? __builtin_nontemporal_load(src + j) : src[j]; };
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < kProbeReadU; ++u) v[u] = src[i + u * stride];
+        for (int u = 0; u < U; ++u) v[u] = ld(i + u * stride);
 #pragma unroll
-        for (int u = 0; u < kProbeReadU; ++u) acc ^= v[u];
+        for (int u = 0; u < U; ++u) acc ^= v[u];
     }
-    for (; i < n16; i += stride) acc ^= src[i];
+    for (; i < n16; i += stride) acc ^= ld(i);
     out[uint64_t(blockIdx.x) * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
 }  // namespace
 
-hipError_t launch_probe_read(const void* src, uint64_t bytes, uint32_t* out, int workgroups, hipStream_t stream) {
-    hipLaunchKernelGGL(k_probe_read, dim3(unsigned(workgroups)), dim3(256), 0, stream,
-                       static_cast<const u32x4*>(src), bytes / 16, out);
+hipError_t launch_probe_read_depth(const void* src, uint64_t bytes, uint32_t* out, int workgroups, int depth,
+                                  bool nontemporal, hipStream_t stream) {
+    const auto* s = static_cast<const u32x4*>(src);
+    const dim3 grid = dim3(unsigned(workgroups)), block = dim3(256);
+    const uint64_t n16 = bytes / 16;
+#define NF4_PROBE_CASE(U)                                                                                 \
+    case U:                                                                                               \
+        if (nontemporal)                                                                                  \
+            hipLaunchKernelGGL((k_probe_read<U, true>), grid, block, 0, stream, s, n16, out);             \
+        else                                                                                              \
+            hipLaunchKernelGGL((k_probe_read<U, false>), grid, block, 0, stream, s, n16, out);            \
+        break;
+    switch (depth) {
+        NF4_PROBE_CASE(4)
+        NF4_PROBE_CASE(8)
+        NF4_PROBE_CASE(16)
+        NF4_PROBE_CASE(32)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef NF4_PROBE_CASE
     return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void* src, uint64_t bytes, uint32_t* out, int workgroups, hipStream_t stream) {
+    return launch_probe_read_depth(src, bytes, out, workgroups, 8, false, stream);
 }
 
 hipError_t launch_probe_mfma(float* out, int workgroups, int iters, hipStream_t stream) {

@@ -70,6 +70,7 @@ def _load() -> C.CDLL:
         "nf4_profile_next_gemm": (i32, [vp, vp]),
         "nf4_probe_mfma": (i32, [vp, i32, i32, vp]),
         "nf4_probe_read": (i32, [vp, C.c_size_t, vp, i32, vp]),
+        "nf4_probe_read_depth": (i32, [vp, C.c_size_t, vp, i32, i32, i32, vp]),
         "nf4_rmsnorm_fwd": (i32, [vp, i64, i64, f32, vp, vp, vp]),
         "nf4_rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, vp, vp]),
         "nf4_add_bf16": (i32, [vp, vp, vp, i64, vp, vp]),
@@ -165,6 +166,16 @@ def probe_read(src, out, workgroups: int, stream=None) -> None:
     if not src.is_cuda or not out.is_cuda or out.dtype != torch.int32 or out.numel() < 256 * workgroups:
         raise ValueError("probe_read: src and out must be device tensors, out int32 with >= 256 * workgroups entries")
     _check(_lib.nf4_probe_read(_ptr(src), C.c_size_t(nbytes), _ptr(out), int(workgroups), _stream(stream)))
+
+
+def probe_read_depth(src, out, workgroups: int, depth: int, nontemporal: bool = False, stream=None) -> None:
+    """The read probe with `depth` loads in flight per thread (nf4_probe_read_depth)."""
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_cuda and out.is_cuda and out.dtype == torch.int32 and out.numel() >= 256 * workgroups):
+        raise ValueError("probe_read_depth: src and out must be device tensors, out int32 with >= 256 * workgroups "
+                         "entries")
+    _check(_lib.nf4_probe_read_depth(_ptr(src), C.c_size_t(nbytes), _ptr(out), int(workgroups), int(depth),
+                                     int(bool(nontemporal)), _stream(stream)))
 
 
 def codebook() -> list:
