@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
             // rows past T read zero; columns past K only feed dA columns never stored
             xv[i] = buf_load16(rx, (uint32_t(xt0 + i) * uint32_t(K) + uint32_t(k0 + xk8)) * 2u);
         }
-        constexpr int GR = 2;  // partials loaded per round
+        constexpr int GR = 8;  // partials loaded per round (registers are free after the main loop)
         for (int jb = 0; jb < rp / 16; ++jb) {
             f32x4 gsum[GI];
 #pragma unroll
