@@ -539,6 +539,7 @@ def _stack_run(torch, ST, base, lora, tokens, h0, dh, steps, **kw) -> dict:
         res["timed_issue_s"] = (t1 - t0) / steps
         tm = st.pool.timing_collect()
         res["timed_host_ms"], res["timed_host_max_ms"] = tm["host_ms"] / steps, tm["host_max_ms"]
+        res["timed_host_sync_ms"] = tm["host_sync_ms"] / steps
         res["bytes"] = (st.pool.stats()["bytes_copied"] - c0) / steps
         st.pool.timing_enable(True)
         torch.cuda.synchronize()
@@ -559,7 +560,7 @@ def _stack_run(torch, ST, base, lora, tokens, h0, dh, steps, **kw) -> dict:
 
 
 def stream_bench(torch, model: str, block_sizes, tokens_list, steps: int, h2d_gbs: float, base_kind: str = "nf4",
-                 slot_counts=(2,), remat: bool = True, layer_parts: bool = False) -> dict:
+                 slot_counts=(2,), remat: bool = True, layer_parts: bool = True, max_ahead: int = 2) -> dict:
     """Streamed vs resident step time of a Qwen2.5-shaped identity-mixing stack for each
     (tokens, block size), with the bitwise check, H2D traffic, and the copy/compute
     overlap measured by the pool's own events: copy_ms = device time of the H2D copies
@@ -571,7 +572,9 @@ def stream_bench(torch, model: str, block_sizes, tokens_list, steps: int, h2d_gb
     of the base serves every block size (regroup). With `remat`, the first block size is
     also run with rematerialisation (block-boundary states kept, each block's forward
     recomputed in its backward visit). layer_parts: the pool copies and releases each
-    layer of a block on its own instead of one copy per block."""
+    layer of a block on its own instead of one copy per block, and the compute stream
+    waits for each layer's copy instead of the whole block's. max_ahead: blocks the host
+    may run ahead of the device (stream_pool_set_max_ahead; 0 = no bound)."""
     from nf4_weight_streamed_amd import stack as ST
 
     dims, n_layers = ST.QWEN25[model]
@@ -593,7 +596,7 @@ def stream_bench(torch, model: str, block_sizes, tokens_list, steps: int, h2d_gb
             if n_slots >= b.n_blocks:
                 continue
             got = _stack_run(torch, ST, b, lora, tokens, h0, dh, steps, mode="streamed", n_slots=n_slots,
-                             layer_parts=layer_parts)
+                             layer_parts=layer_parts, max_ahead=max_ahead)
             r_s, s_s, nbytes = res["s"], got["s"], got["bytes"]
             print(f"[stream_bench] {model} T={tokens} bs={bs} slots={n_slots}: streamed {s_s * 1e3:.1f} ms per step",
                   file=sys.stderr, flush=True)
@@ -603,6 +606,8 @@ def stream_bench(torch, model: str, block_sizes, tokens_list, steps: int, h2d_gb
                 "workload": f"qwen2.5-{model}-shaped stack, {n_layers} layers, block_size {bs}, {n_slots} pool slots, "
                             f"{tokens} tokens, {fmt} in pinned host, identity attention mixing, fwd+bwd",
                 "copies": "one per layer" if (layer_parts or not b.contiguous) else "one per block",
+                "compute_waits": "per layer" if (layer_parts or not b.contiguous) else "per block",
+                "host_max_blocks_ahead": max_ahead,
                 "tokens": tokens, "block_size": bs, "slots": n_slots,
                 "device_pool_gb": round(n_slots * b.slot_bytes / 1e9, 3),
                 "bitwise_equal_to_resident": bool(torch.equal(res["y"], got["y"]) and torch.equal(res["dx"], got["dx"])),
@@ -629,13 +634,14 @@ def stream_bench(torch, model: str, block_sizes, tokens_list, steps: int, h2d_gb
                 "timed_host_issue_ms_per_step": round(got["timed_issue_s"] * 1e3, 3),
                 "timed_host_ms_in_pool_hip_calls_per_step": round(got["timed_host_ms"], 3),
                 "timed_host_longest_pool_hip_call_ms": round(got["timed_host_max_ms"], 3),
+                "timed_host_ms_held_by_lead_bound_per_step": round(got["timed_host_sync_ms"], 3),
                 "overlap_source": "HIP events of the pool over one extra step: copy spans on the copy stream, "
                                   "acquire-wait spans on the compute stream",
                 "host_base_gb": round(base.total_bytes() / 1e9, 3),
             }
             if remat and i == 0:
                 rm = _stack_run(torch, ST, b, lora, tokens, h0, dh, steps, mode="streamed", n_slots=n_slots,
-                                remat=True, layer_parts=layer_parts)
+                                remat=True, layer_parts=layer_parts, max_ahead=max_ahead)
                 row["remat"] = {
                     "bitwise_equal_to_resident": bool(torch.equal(res["y"], rm["y"]) and torch.equal(res["dx"], rm["dx"])),
                     "streamed_ms_per_step": round(rm["s"] * 1e3, 3),
@@ -904,8 +910,11 @@ def main() -> int:
                     help="format of the streamed base: nf4, or dense bf16 (the bf16_bitwise mode)")
     ap.add_argument("--stack-tokens", default="512", help="comma-separated token counts of the streamed stacks")
     ap.add_argument("--no-remat", action="store_true", help="skip the rematerialisation run of the streamed stacks")
-    ap.add_argument("--layer-parts", action="store_true",
-                    help="streamed stacks: copy and release each layer of a block on its own")
+    ap.add_argument("--block-copies", action="store_true",
+                    help="streamed stacks: one copy per block and one wait for it (default: each layer of a block "
+                         "copied, waited for and released on its own)")
+    ap.add_argument("--max-ahead", type=int, default=2,
+                    help="streamed stacks: blocks the host may run ahead of the device (0: no bound)")
     ap.add_argument("--stack-steps", type=int, default=3)
     ap.add_argument("--small-t-sweep", action="store_true",
                     help="instead of the layer step: per-projection fwd/bwd device time at T = 1..64 vs HBM bytes")
@@ -1078,7 +1087,9 @@ def main() -> int:
         h2d = pinned_h2d_gbs(torch)
         out["denominators"]["h2d_pinned_gbs_measured"] = round(h2d, 2)
         runs = [stream_bench(torch, m, block_sizes, stack_tokens, args.stack_steps, h2d, args.stream_base, slot_counts,
-                             remat=not args.no_remat, layer_parts=args.layer_parts) for m in models]
+                             remat=not args.no_remat, layer_parts=not args.block_copies,
+                             max_ahead=args.max_ahead)
+                for m in models]
         out["streamed"] = dict(runs[0]["rows"][0], load=runs[0]["load"])
         out["streamed_all"] = runs
     if not args.no_cpu_baseline:

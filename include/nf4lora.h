@@ -299,7 +299,8 @@ int nf4_probe_read_depth(const void* src, size_t bytes, uint32_t* out, int workg
  * allocation) receives blocks by hipMemcpyAsync on a dedicated copy stream.
  * A block is used on a compute stream between acquire and release; release
  * records an event on that stream, and the copy that later reuses the slot
- * waits on it, so reuse is ordered on the streams and never blocks the host.
+ * waits on it, so reuse is ordered on the streams, not on the host (which blocks
+ * only under a bound on its lead, stream_pool_set_max_ahead).
  * The bytes a kernel sees are the same whether the block is streamed or was
  * copied once (resident), so streamed and resident results are bitwise equal.
  * A pool is used from one host thread at a time.
@@ -391,6 +392,37 @@ int stream_pool_prefetch(nf4_pool* pool, int block);
 int stream_pool_acquire(nf4_pool* pool, int block, nf4_stream compute, const void** dev);
 
 /*
+ * As stream_pool_acquire, but `compute` is made to wait for nothing: before a stream
+ * reads part i of the block it must call stream_pool_wait_part(pool, block, i, that
+ * stream). With a block copied as several parts (one per layer), the first layers
+ * of the block then run while its later parts are still landing ([hn]: copies
+ * overlap compute); at the end of a pass, where nothing else is left to overlap,
+ * that is what shortens the wait. Errors as stream_pool_acquire.
+ */
+int stream_pool_acquire_deferred(nf4_pool* pool, int block, nf4_stream compute, const void** dev);
+
+/*
+ * Make `stream` wait for the copy of part `part` of a held block (after a deferred
+ * acquire; harmless after a plain one). The wait is on an event the copy stream
+ * records after that part's copy. NF4_E_STATE if the block is not held; NF4_E_ARG for
+ * a part outside the block.
+ */
+int stream_pool_wait_part(nf4_pool* pool, int block, int part, nf4_stream stream);
+
+/*
+ * Bound how far the host may run ahead of the device: with n > 0, every
+ * stream_pool_release records an event on its stream and blocks the host until the
+ * event recorded n releases earlier has completed (n = 0, the default: no bound).
+ * Without a bound a host that issues a whole training step ahead leaves long queues
+ * of copies waiting on releases, and the H2D copies behind them were measured to run
+ * up to 2x slower (7B stack, 2 slots of 4 layers, one copy per layer: about 2.3 ms per
+ * 131 MB layer at first, 2.6-4.6 ms later in the same run; with n = 2 the copies
+ * keep their rate). Lowering n waits at once for the marks beyond it. NF4_E_ARG for
+ * n < 0.
+ */
+int stream_pool_set_max_ahead(nf4_pool* pool, int n);
+
+/*
  * End the use of `block` on `compute`: record the last-use events of its parts
  * (those not released by stream_pool_release_part) there. The slot stays valid (a
  * later acquire of the same block is a hit) until a prefetch/acquire of another
@@ -427,6 +459,14 @@ int stream_pool_destroy(nf4_pool* pool);
  * blocks the host thread shows there, not in the device spans).
  * stream_pool_timing_collect blocks until the recorded spans have completed, returns
  * their sums and the host clock since the last collect in *out and forgets them.
+ * stream_pool_timing_spans (call it before collect, which forgets the spans) blocks
+ * likewise and writes up to max_spans of them, copies first in issue order, then
+ * acquire waits in issue order, to out (HOST array, caller-owned); *n_out = how many
+ * spans are recorded (may exceed max_spans; max_spans = 0 only counts). Device times
+ * are ms after the earliest recorded span start, host times ms after that span's
+ * issuing call (the two clocks are not synchronised: compare device with device and
+ * host with host). NF4_E_ARG for a NULL pool or n_out, a negative max_spans, or a
+ * NULL out with max_spans > 0.
  * Enabling adds event records to the streams; it changes no result.
  */
 typedef struct {
@@ -436,10 +476,28 @@ typedef struct {
     uint64_t acquires; /* acquires timed */
     double host_ms;    /* host wall time inside the pool's HIP calls since the last collect */
     double host_max_ms; /* the longest single such call */
+    double host_copy_ms;   /* of host_ms: inside hipMemcpyAsync */
+    double host_record_ms; /* of host_ms: inside hipEventRecord */
+    double host_wait_ms;   /* of host_ms: inside hipStreamWaitEvent */
+    double host_sync_ms;   /* of host_ms: blocked in the bound on the host's lead (set_max_ahead) */
 } nf4_pool_timing;
+
+#define NF4_SPAN_COPY 0    /* an H2D copy on the copy stream */
+#define NF4_SPAN_ACQUIRE 1 /* an acquire's or wait_part's wait on a compute stream */
+typedef struct {
+    int kind;            /* NF4_SPAN_COPY or NF4_SPAN_ACQUIRE */
+    int block;           /* the block copied or acquired */
+    int part;            /* the part copied or waited for (index within the block); -1 for an acquire */
+    int reserved;
+    double start_ms;     /* device: the span's start */
+    double end_ms;       /* device: the span's end */
+    double host_at_ms;   /* host: when the issuing HIP call began */
+    double host_call_ms; /* host: how long that call took */
+} nf4_pool_span;
 
 int stream_pool_timing_enable(nf4_pool* pool, int enable);
 int stream_pool_timing_collect(nf4_pool* pool, nf4_pool_timing* out);
+int stream_pool_timing_spans(nf4_pool* pool, nf4_pool_span* out, int max_spans, int* n_out);
 
 /*
  * Byte layout of one block slab of the streamed base (the slab a pool slot holds;

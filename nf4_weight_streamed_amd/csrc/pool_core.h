@@ -13,6 +13,9 @@
 // into its slot. Ordering is carried by events on the streams:
 //   ready[slot]   recorded on the copy stream after the block's last part; acquire
 //                 makes the compute stream wait on it;
+//   part_ready    recorded on the copy stream after each part; a deferred acquire
+//                 makes no wait, and wait_part makes a stream wait for one part,
+//                 so a block's first layers can run while its later parts land;
 //   last uses     when part i of a held block is released (stream_pool_release_part,
 //                 or every part not yet released at stream_pool_release) an event
 //                 is recorded on the compute stream and kept with the slot byte
@@ -24,12 +27,17 @@
 // Parts of a copy are issued in ascending order, or descending after
 // set_order(true) (a backward pass uses the layers of a block last to first), so
 // the first part copied overwrites the first part the previous pass released.
-// The host never blocks, and a slot byte is never overwritten while a kernel
-// enqueued before the release of its part may still read it.
+// A slot byte is never overwritten while a kernel enqueued before the release of its
+// part may still read it. The host blocks only when a lead is set (set_max_ahead):
+// each release records an event on its stream, and the host waits for the one
+// recorded that many releases earlier, so the host runs at most that many blocks
+// ahead of the device (a host far ahead leaves long chains of pending cross-stream
+// waits behind the copies, and H2D copies were measured to slow down then).
 #pragma once
 
 #include <cstddef>
 #include <cstdint>
+#include <deque>
 #include <vector>
 
 #include "../../include/nf4lora.h"
@@ -62,6 +70,7 @@ struct PoolCore {
         bool held = false;
         uint64_t stamp = 0;
         Event ready{};
+        std::vector<Event> part_ready;  // per part of the block copied last
         std::vector<LastUse> pending;
         std::vector<char> released;  // parts released in the current hold
     };
@@ -79,6 +88,8 @@ struct PoolCore {
     int max_parts = 0;
     std::vector<Event> events;  // every last-use event created (destroyed at the end)
     std::vector<Event> spare;   // last-use events free for reuse (their waits are enqueued)
+    int max_ahead = 0;          // 0: the host never waits
+    std::deque<Event> ahead;    // release marks not yet waited for, oldest first
     nf4_pool_stats stats{};
 
     // Validate and take the layout: parts [part_begin[b], part_begin[b + 1]) form block b.
@@ -123,6 +134,12 @@ struct PoolCore {
             s.released.assign(max_parts, 0);
             int st = eng->create_event(&s.ready);
             if (st != NF4_OK) return st;
+            s.part_ready.assign(max_parts, Event{});
+            for (auto& e : s.part_ready) {
+                st = eng->create_event(&e);
+                if (st != NF4_OK) return st;
+                events.push_back(e);  // destroyed with the last-use events
+            }
         }
         return NF4_OK;
     }
@@ -132,21 +149,27 @@ struct PoolCore {
         for (auto& e : events) eng->destroy_event(e);
         events.clear();
         spare.clear();
+        ahead.clear();
+    }
+
+    int take_event(Event* e) {
+        if (!spare.empty()) {
+            *e = spare.back();
+            spare.pop_back();
+            return NF4_OK;
+        }
+        int st = eng->create_event(e);
+        if (st == NF4_OK) events.push_back(*e);
+        return st;
     }
 
     // Record a last use of slot bytes [lo, hi) on `compute`. A kept last use of a
     // range inside this one on the same stream is implied by this one and dropped.
     int record_last_use(Slot& s, size_t lo, size_t hi, Stream compute) {
         Event e{};
-        if (!spare.empty()) {
-            e = spare.back();
-            spare.pop_back();
-        } else {
-            int st = eng->create_event(&e);
-            if (st != NF4_OK) return st;
-            events.push_back(e);
-        }
-        int st = eng->record(e, compute);
+        int st = take_event(&e);
+        if (st != NF4_OK) return st;
+        st = eng->record(e, compute);
         if (st != NF4_OK) {
             spare.push_back(e);
             return st;
@@ -205,7 +228,8 @@ struct PoolCore {
                 s.pending[q] = s.pending.back();
                 s.pending.pop_back();
             }
-            int st = eng->copy(dst + p.off, p.host, p.bytes, copy);
+            int st = eng->copy(dst + p.off, p.host, p.bytes, copy, block, i);
+            if (st == NF4_OK) st = eng->record(s.part_ready[i], copy);
             if (st != NF4_OK) return st;
         }
         int st = eng->record(s.ready, copy);
@@ -230,13 +254,14 @@ struct PoolCore {
         return st < 0 ? st : NF4_OK;
     }
 
-    int acquire(int block, Stream compute, const void** dev) {
-        int st = check_block(block, "stream_pool_acquire");
+    // deferred: make no wait (the caller calls wait_part before it reads a part)
+    int acquire(int block, Stream compute, const void** dev, bool deferred = false) {
+        const char* fn = deferred ? "stream_pool_acquire_deferred" : "stream_pool_acquire";
+        int st = check_block(block, fn);
         if (st != NF4_OK) return st;
-        if (!dev) return fail(NF4_E_ARG, "stream_pool_acquire: NULL dev");
+        if (!dev) return fail(NF4_E_ARG, "%s: NULL dev", fn);
         int slot = where[block];
-        if (slot >= 0 && slots[slot].held)
-            return fail(NF4_E_STATE, "stream_pool_acquire: block %d is already held", block);
+        if (slot >= 0 && slots[slot].held) return fail(NF4_E_STATE, "%s: block %d is already held", fn, block);
         if (slot < 0) {
             slot = issue_copy(block);
             if (slot < 0) return slot;
@@ -245,8 +270,10 @@ struct PoolCore {
             stats.hits++;
         }
         auto& s = slots[slot];
-        st = eng->acquire_wait(compute, s.ready);
-        if (st != NF4_OK) return st;
+        if (!deferred) {
+            st = eng->acquire_wait(compute, s.ready, block, -1);
+            if (st != NF4_OK) return st;
+        }
         s.held = true;
         s.stamp = ++clock;
         for (auto& r : s.released) r = 0;
@@ -260,6 +287,16 @@ struct PoolCore {
         const int slot = where[block];
         if (slot < 0 || !slots[slot].held) return fail(NF4_E_STATE, "%s: block %d is not held", fn, block);
         return slot;
+    }
+
+    // make `stream` wait for the copy of one part of a held block
+    int wait_part(int block, int part, Stream stream) {
+        const int slot = held_slot(block, "stream_pool_wait_part");
+        if (slot < 0) return slot;
+        if (part < 0 || part >= blocks[block].count)
+            return fail(NF4_E_ARG, "stream_pool_wait_part: part %d outside 0..%d of block %d", part,
+                        blocks[block].count - 1, block);
+        return eng->acquire_wait(stream, slots[slot].part_ready[part], block, part);
     }
 
     int release_part(int block, int part, Stream compute) {
@@ -308,6 +345,40 @@ struct PoolCore {
         }
         s.held = false;
         s.stamp = ++clock;
+        return bound_lead(compute);
+    }
+
+    // the host's lead over the device (set_max_ahead): mark this release, then wait
+    // for the mark max_ahead releases back
+    int bound_lead(Stream compute) {
+        if (max_ahead <= 0) return NF4_OK;
+        Event e{};
+        int st = take_event(&e);
+        if (st != NF4_OK) return st;
+        st = eng->record(e, compute);
+        if (st != NF4_OK) {
+            spare.push_back(e);
+            return st;
+        }
+        ahead.push_back(e);
+        while (int(ahead.size()) > max_ahead) {
+            st = eng->host_wait(ahead.front());
+            if (st != NF4_OK) return st;
+            spare.push_back(ahead.front());
+            ahead.pop_front();
+        }
+        return NF4_OK;
+    }
+
+    int set_max_ahead(int n) {
+        if (n < 0) return fail(NF4_E_ARG, "stream_pool_set_max_ahead: n must be >= 0 (got %d)", n);
+        max_ahead = n;
+        while (int(ahead.size()) > (n > 0 ? n : 0)) {  // a lower bound applies at once
+            int st = eng->host_wait(ahead.front());
+            if (st != NF4_OK) return st;
+            spare.push_back(ahead.front());
+            ahead.pop_front();
+        }
         return NF4_OK;
     }
 };

@@ -6,6 +6,7 @@
 // comment); Poros API reference, "patch_hf_model" Behavior 4-6; "Poros on consumer
 // GPUs", "What you need besides VRAM" (the streamed base lives in pinned host memory,
 // needed for asynchronous copies).
+#include <algorithm>
 #include <chrono>
 #include <cstdint>
 #include <mutex>
@@ -29,6 +30,8 @@ struct HipEngine {
     using Stream = hipStream_t;
     struct Span {  // two timing events around one interval on one stream
         hipEvent_t a = nullptr, b = nullptr;
+        int kind = 0, block = -1, part = -1;
+        double host_at_ms = 0.0, host_call_ms = 0.0;  // host clock at the issuing call, its duration
     };
     // timing (stream_pool_timing_enable): copy spans on the copy stream, stall spans
     // around each acquire's wait on the compute stream, and recycled events
@@ -37,15 +40,22 @@ struct HipEngine {
     std::vector<hipEvent_t> spare;
     // host time spent inside the pool's HIP calls, whether or not the device spans are
     // recorded (a call that blocks the host shows here, not in the device spans)
-    double host_ms = 0.0, host_max_ms = 0.0;
+    // per kind of call: 0 copy issue, 1 event record, 2 stream wait, 3 host wait for an event
+    double host_ms = 0.0, host_max_ms = 0.0, host_kind_ms[4] = {0.0, 0.0, 0.0, 0.0};
+    double last_call_ms = 0.0, last_call_at_ms = 0.0;
+    const std::chrono::steady_clock::time_point origin = std::chrono::steady_clock::now();
 
     template <class F>
-    hipError_t host_timed(F&& call) {
+    hipError_t host_timed(int kind, F&& call) {
         const auto t0 = std::chrono::steady_clock::now();
         const hipError_t e = call();
-        const double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+        const auto t1 = std::chrono::steady_clock::now();
+        const double ms = std::chrono::duration<double, std::milli>(t1 - t0).count();
         host_ms += ms;
+        host_kind_ms[kind] += ms;
         if (ms > host_max_ms) host_max_ms = ms;
+        last_call_ms = ms;
+        last_call_at_ms = std::chrono::duration<double, std::milli>(t0 - origin).count();
         return e;
     }
 
@@ -56,10 +66,13 @@ struct HipEngine {
         if (e) (void)hipEventDestroy(e);
     }
     int record(hipEvent_t e, hipStream_t s) {
-        return hip_ok(host_timed([&] { return hipEventRecord(e, s); }), "stream_pool: record event");
+        return hip_ok(host_timed(1, [&] { return hipEventRecord(e, s); }), "stream_pool: record event");
     }
     int wait(hipStream_t s, hipEvent_t e) {
-        return hip_ok(host_timed([&] { return hipStreamWaitEvent(s, e, 0); }), "stream_pool: wait event");
+        return hip_ok(host_timed(2, [&] { return hipStreamWaitEvent(s, e, 0); }), "stream_pool: wait event");
+    }
+    int host_wait(hipEvent_t e) {
+        return hip_ok(host_timed(3, [&] { return hipEventSynchronize(e); }), "stream_pool: host wait for a release");
     }
 
     hipEvent_t timing_event() {
@@ -78,29 +91,36 @@ struct HipEngine {
         if (!sp.a || !sp.b) return fail(NF4_E_HIP, "stream_pool: hipEventCreate failed (timing)");
         return hip_ok(hipEventRecord(sp.a, stream), "stream_pool: record timing event");
     }
-    int span_end(Span& sp, hipStream_t stream, std::vector<Span>& into) {
+    // closes the span and tags it with the call it timed (the engine's last HIP call)
+    int span_end(Span& sp, hipStream_t stream, std::vector<Span>& into, int kind, int block, int part) {
         if (!timing) return NF4_OK;
         int st = hip_ok(hipEventRecord(sp.b, stream), "stream_pool: record timing event");
+        sp.kind = kind;
+        sp.block = block;
+        sp.part = part;
+        sp.host_at_ms = last_call_at_ms;
+        sp.host_call_ms = last_call_ms;
         if (st == NF4_OK) into.push_back(sp);
         return st;
     }
 
     // one part's H2D copy (after its waits: the span is the copy alone)
-    int copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+    int copy(void* dst, const void* src, size_t bytes, hipStream_t s, int block, int part) {
         Span sp;
         int st = span_begin(sp, s);
         if (st == NF4_OK)
-            st = hip_ok(host_timed([&] { return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s); }),
+            st = hip_ok(host_timed(0, [&] { return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s); }),
                         "stream_pool: H2D copy");
-        if (st == NF4_OK) st = span_end(sp, s, copy_spans);
+        if (st == NF4_OK) st = span_end(sp, s, copy_spans, NF4_SPAN_COPY, block, part);
         return st;
     }
-    // the compute stream's wait for a block's copy (the span is the time it stood still)
-    int acquire_wait(hipStream_t compute, hipEvent_t ready) {
+    // a compute stream's wait for a block's (part = -1) or one part's copy (the span is
+    // the time it stood still)
+    int acquire_wait(hipStream_t compute, hipEvent_t ready, int block, int part) {
         Span sp;
         int st = span_begin(sp, compute);
         if (st == NF4_OK) st = wait(compute, ready);
-        if (st == NF4_OK) st = span_end(sp, compute, stall_spans);
+        if (st == NF4_OK) st = span_end(sp, compute, stall_spans, NF4_SPAN_ACQUIRE, block, part);
         return st;
     }
 
@@ -174,6 +194,21 @@ int stream_pool_prefetch(nf4_pool* p, int block) {
 int stream_pool_acquire(nf4_pool* p, int block, nf4_stream compute, const void** dev) {
     if (!p) return fail(NF4_E_ARG, "stream_pool_acquire: NULL pool");
     return p->core.acquire(block, static_cast<hipStream_t>(compute), dev);
+}
+
+int stream_pool_acquire_deferred(nf4_pool* p, int block, nf4_stream compute, const void** dev) {
+    if (!p) return fail(NF4_E_ARG, "stream_pool_acquire_deferred: NULL pool");
+    return p->core.acquire(block, static_cast<hipStream_t>(compute), dev, true);
+}
+
+int stream_pool_wait_part(nf4_pool* p, int block, int part, nf4_stream stream) {
+    if (!p) return fail(NF4_E_ARG, "stream_pool_wait_part: NULL pool");
+    return p->core.wait_part(block, part, static_cast<hipStream_t>(stream));
+}
+
+int stream_pool_set_max_ahead(nf4_pool* p, int blocks) {
+    if (!p) return fail(NF4_E_ARG, "stream_pool_set_max_ahead: NULL pool");
+    return p->core.set_max_ahead(blocks);
 }
 
 int stream_pool_release_part(nf4_pool* p, int block, int part, nf4_stream compute) {
@@ -255,8 +290,46 @@ int stream_pool_timing_collect(nf4_pool* p, nf4_pool_timing* out) {
     sum(p->eng.stall_spans, out->stall_ms, out->acquires);
     out->host_ms = p->eng.host_ms;
     out->host_max_ms = p->eng.host_max_ms;
+    out->host_copy_ms = p->eng.host_kind_ms[0];
+    out->host_record_ms = p->eng.host_kind_ms[1];
+    out->host_wait_ms = p->eng.host_kind_ms[2];
+    out->host_sync_ms = p->eng.host_kind_ms[3];
     p->eng.host_ms = p->eng.host_max_ms = 0.0;
+    for (double& v : p->eng.host_kind_ms) v = 0.0;
     return st;
+}
+
+int stream_pool_timing_spans(nf4_pool* p, nf4_pool_span* out, int max_spans, int* n_out) {
+    if (!p || !n_out || max_spans < 0 || (max_spans > 0 && !out))
+        return fail(NF4_E_ARG, "stream_pool_timing_spans: need pool, n_out, max_spans >= 0 and out when max_spans > 0");
+    std::vector<const HipEngine::Span*> all;
+    for (auto* v : {&p->eng.copy_spans, &p->eng.stall_spans})
+        for (auto& sp : *v) all.push_back(&sp);
+    *n_out = int(all.size());
+    if (all.empty()) return NF4_OK;
+    int st = NF4_OK;
+    for (const auto* sp : all)
+        if (st == NF4_OK) st = hip_ok(hipEventSynchronize(sp->b), "stream_pool_timing_spans: wait");
+    if (st != NF4_OK) return st;
+    // origin: the earliest span start on the device; host times from the same span's call
+    const HipEngine::Span* first = all[0];
+    for (const auto* sp : all) {
+        float d = 0.0f;
+        st = hip_ok(hipEventElapsedTime(&d, first->a, sp->a), "stream_pool_timing_spans: elapsed");
+        if (st != NF4_OK) return st;
+        if (d < 0.0f) first = sp;
+    }
+    const int n = std::min(max_spans, int(all.size()));
+    for (int i = 0; i < n; ++i) {
+        const auto* sp = all[size_t(i)];
+        float a = 0.0f, b = 0.0f;
+        st = hip_ok(hipEventElapsedTime(&a, first->a, sp->a), "stream_pool_timing_spans: elapsed");
+        if (st == NF4_OK) st = hip_ok(hipEventElapsedTime(&b, first->a, sp->b), "stream_pool_timing_spans: elapsed");
+        if (st != NF4_OK) return st;
+        out[i] = nf4_pool_span{sp->kind, sp->block, sp->part, 0, double(a), double(b),
+                               sp->host_at_ms - first->host_at_ms, sp->host_call_ms};
+    }
+    return NF4_OK;
 }
 
 int stream_pool_destroy(nf4_pool* p) {

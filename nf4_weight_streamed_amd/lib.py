@@ -37,7 +37,15 @@ class HostBlock(C.Structure):
 
 class PoolTiming(C.Structure):
     _fields_ = [("copy_ms", C.c_double), ("stall_ms", C.c_double), ("copies", C.c_uint64),
-                ("acquires", C.c_uint64), ("host_ms", C.c_double), ("host_max_ms", C.c_double)]
+                ("acquires", C.c_uint64), ("host_ms", C.c_double), ("host_max_ms", C.c_double),
+                ("host_copy_ms", C.c_double), ("host_record_ms", C.c_double), ("host_wait_ms", C.c_double),
+                ("host_sync_ms", C.c_double)]
+
+
+class PoolSpan(C.Structure):
+    _fields_ = [("kind", C.c_int), ("block", C.c_int), ("part", C.c_int), ("reserved", C.c_int),
+                ("start_ms", C.c_double), ("end_ms", C.c_double), ("host_at_ms", C.c_double),
+                ("host_call_ms", C.c_double)]
 
 
 class PoolStats(C.Structure):
@@ -89,9 +97,13 @@ def _load() -> C.CDLL:
                                            C.POINTER(vp)]),
         "stream_pool_set_order": (i32, [vp, i32]),
         "stream_pool_release_part": (i32, [vp, i32, i32, vp]),
+        "stream_pool_acquire_deferred": (i32, [vp, i32, vp, C.POINTER(vp)]),
+        "stream_pool_wait_part": (i32, [vp, i32, i32, vp]),
+        "stream_pool_set_max_ahead": (i32, [vp, i32]),
         "stream_pool_timing_enable": (i32, [vp, i32]),
         "stream_pool_streams": (i32, [C.POINTER(vp), C.POINTER(vp)]),
         "stream_pool_timing_collect": (i32, [vp, C.POINTER(PoolTiming)]),
+        "stream_pool_timing_spans": (i32, [vp, C.POINTER(PoolSpan), i32, C.POINTER(i32)]),
         "nf4_block_layout": (i32, [C.POINTER(C.c_int64), i32, i32, i32, C.POINTER(C.c_size_t),
                                    C.POINTER(C.c_size_t)]),
     }
@@ -578,6 +590,19 @@ class StreamPool:
         _check(_lib.stream_pool_acquire(self._h, block, _stream(stream), C.byref(dev)))
         return dev.value
 
+    def acquire_deferred(self, block: int, stream=None) -> int:
+        """acquire without the wait for the copy: wait_part before reading each part."""
+        dev = C.c_void_p()
+        _check(_lib.stream_pool_acquire_deferred(self._h, block, _stream(stream), C.byref(dev)))
+        return dev.value
+
+    def wait_part(self, block: int, part: int, stream=None) -> None:
+        _check(_lib.stream_pool_wait_part(self._h, block, part, _stream(stream)))
+
+    def set_max_ahead(self, n: int) -> None:
+        """Host blocks at release until the release n earlier has completed (0: no bound)."""
+        _check(_lib.stream_pool_set_max_ahead(self._h, n))
+
     def release_part(self, block: int, part: int, stream=None) -> None:
         _check(_lib.stream_pool_release_part(self._h, block, part, _stream(stream)))
 
@@ -598,6 +623,17 @@ class StreamPool:
         t = PoolTiming()
         _check(_lib.stream_pool_timing_collect(self._h, C.byref(t)))
         return {f: getattr(t, f) for f, _ in PoolTiming._fields_}
+
+    def timing_spans(self) -> list:
+        """The spans recorded since the last collect, copies then acquire waits, each a dict
+        (stream_pool_timing_spans; call before timing_collect, which forgets them)."""
+        n = C.c_int()
+        _check(_lib.stream_pool_timing_spans(self._h, None, 0, C.byref(n)))
+        arr = (PoolSpan * max(1, n.value))()
+        _check(_lib.stream_pool_timing_spans(self._h, arr, n.value, C.byref(n)))
+        kinds = {0: "copy", 1: "acquire"}
+        return [{"kind": kinds[a.kind], "block": a.block, "part": a.part, "start_ms": a.start_ms, "end_ms": a.end_ms,
+                 "host_at_ms": a.host_at_ms, "host_call_ms": a.host_call_ms} for a in arr[:n.value]]
 
     def slot_block(self, slot: int) -> int:
         b = C.c_int()

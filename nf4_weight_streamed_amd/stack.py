@@ -258,7 +258,7 @@ class NF4Stack:
 
     def __init__(self, base: HostNF4Base, lora: LoraParams, tokens: int, alpha: float = 32.0,
                  mode: str = "streamed", n_slots: int = 2, prefetch: bool = True, remat: bool = False,
-                 layer_parts: bool = False):
+                 layer_parts: bool = True, max_ahead: int = 2):
         if mode not in ("streamed", "resident"):
             raise ValueError("mode must be 'streamed' or 'resident'")
         self.base, self.lora, self.T, self.alpha = base, lora, tokens, alpha
@@ -280,6 +280,15 @@ class NF4Stack:
         self.pool = lib.StreamPool(ranges, self.slab, base.slot_bytes, self.n_slots, self.copy_stream,
                                    part_begin=part_begin)
         self._views = [self._slot_views(s) for s in range(self.n_slots)]
+        # streamed with one part per layer: acquire without the block wait and wait for
+        # each layer's part before its first use, so a block's first layers run while
+        # its later layers land (what is left to overlap at the end of a pass)
+        self.part_waits = mode == "streamed" and self.layer_parts
+        self._waited = set()
+        # bound the host's lead over the device (a host a whole step ahead was measured
+        # to slow the copies down)
+        self.max_ahead = max_ahead if mode == "streamed" else 0
+        self.pool.set_max_ahead(self.max_ahead)
         T, r = tokens, lora.rank
         shapes = d.shapes()
         dev = "cuda"
@@ -348,9 +357,19 @@ class NF4Stack:
         return out
 
     def _acquire(self, b: int):
-        ptr = self.pool.acquire(b)
+        if self.part_waits:
+            ptr = self.pool.acquire_deferred(b)
+            self._waited.clear()
+        else:
+            ptr = self.pool.acquire(b)
         slot = (ptr - self.slab.data_ptr()) // self.base.slot_bytes
         return self._views[slot]
+
+    def _ready(self, b: int, li: int) -> None:
+        """Order the compute stream after the copy of layer li's part (deferred acquires)."""
+        if self.part_waits and li not in self._waited:
+            self.pool.wait_part(b, li - b * self.base.block_size)
+            self._waited.add(li)
 
     # ------------------------------------------------------------------ activation sets
     def _act(self, li: int) -> dict:
@@ -437,6 +456,7 @@ class NF4Stack:
         if self.remat:
             self.acts[0]["h"].copy_(self.boundary[b])
         for li in self._layers_of(b):
+            self._ready(b, li)
             self._layer_forward(li, w[li - b * self.base.block_size])
 
     @contextlib.contextmanager
@@ -471,6 +491,7 @@ class NF4Stack:
             if self.remat:
                 self.acts[0]["h"].copy_(self.boundary[b])
             for li in self._layers_of(b):
+                self._ready(b, li)
                 self._layer_forward(li, w[li - b * bs])
                 if self.layer_parts:
                     self.pool.release_part(b, li - b * bs)   # the layer's bytes may be overwritten after this
@@ -493,6 +514,7 @@ class NF4Stack:
                 self._block_forward(b, w)
             for li in reversed(self._layers_of(b)):
                 nxt = self.dh[k]
+                self._ready(b, li)
                 self._layer_backward(li, w[li - b * self.base.block_size], cur, nxt)
                 if self.layer_parts:
                     self.pool.release_part(b, li - b * self.base.block_size)

@@ -13,6 +13,7 @@
 // message with sizes). Prints "ok" and exits 0, or names the failure and exits 1.
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <random>
 #include <string>
@@ -36,12 +37,15 @@ int fail(int code, const char* fmt, ...) {
 using namespace nf4;
 
 static int g_fail = 0;
+static bool g_quiet = false;  // a negative control expects a failure: do not print it
 #define CHECK(cond, ...)                                  \
     do {                                                  \
         if (!(cond)) {                                    \
-            std::printf("FAIL line %d: ", __LINE__);      \
-            std::printf(__VA_ARGS__);                     \
-            std::printf(" [%s]\n", g_last.c_str());       \
+            if (!g_quiet) {                               \
+                std::printf("FAIL line %d: ", __LINE__);  \
+                std::printf(__VA_ARGS__);                 \
+                std::printf(" [%s]\n", g_last.c_str());   \
+            }                                             \
             g_fail = 1;                                   \
             return 1;                                     \
         }                                                 \
@@ -83,8 +87,13 @@ struct HostEngine {
         tick(s);
         return NF4_OK;
     }
-    int acquire_wait(Stream s, Event e) { return wait(s, e); }
-    int copy(void* dst, const void* src, size_t bytes, Stream s) {
+    int acquire_wait(Stream s, Event e, int /*block*/, int /*part*/) { return wait(s, e); }
+    int host_waits = 0;
+    int host_wait(Event) {
+        ++host_waits;
+        return NF4_OK;
+    }
+    int copy(void* dst, const void* src, size_t bytes, Stream s, int /*block*/, int /*part*/) {
         std::memcpy(dst, src, bytes);
         const long i = tick(s);
         const size_t lo = size_t(static_cast<char*>(dst) - slab);
@@ -152,11 +161,14 @@ struct Fixture {
                          0, true);
     }
     int nparts(int b) const { return begin[b + 1] - begin[b]; }
-    // read every part of a held block on `s` (data must be the block's), releasing each
-    int use_block(int b, const void* dev, bool descending, int s) {
+    // read every part of a held block on `s` (data must be the block's), releasing each;
+    // after a deferred acquire, wait for each part first (unless skip_waits: a
+    // negative control whose reads the order check must reject)
+    int use_block(int b, const void* dev, bool descending, int s, bool deferred = false, bool skip_waits = false) {
         const size_t off = size_t(static_cast<const char*>(dev) - base());
         for (int k = 0; k < nparts(b); ++k) {
             const int i = descending ? nparts(b) - 1 - k : k;
+            if (deferred && !skip_waits) CHECK(pool.wait_part(b, i, s) == NF4_OK, "wait_part(%d, %d)", b, i);
             const size_t lo = off + size_t(i) * part_bytes;
             CHECK(std::memcmp(base() + lo, host[begin[b] + i].data(), part_bytes) == 0,
                   "block %d part %d: slot bytes differ from the host part", b, i);
@@ -168,30 +180,54 @@ struct Fixture {
     }
 };
 
-// The stack's streamed pattern for `steps` steps.
-static int stack_pattern(int n_layers, int ppb, int slots, int steps) {
+// The stack's streamed pattern for `steps` steps; deferred: acquire without the
+// block wait and wait for each part before reading it; max_ahead: the host's lead
+// bound (one host wait per release beyond the first max_ahead).
+static int stack_pattern(int n_layers, int ppb, int slots, int steps, bool deferred = false, int max_ahead = 0) {
     Fixture f(n_layers, ppb, slots, 512);
     CHECK(f.init() == NF4_OK, "init");
+    CHECK(f.pool.set_max_ahead(max_ahead) == NF4_OK, "set_max_ahead");
     const int nb = f.n_blocks;
     for (int step = 0; step < steps; ++step) {
         f.pool.descending = false;
         for (int b = 0; b < nb; ++b) {
             const void* dev = nullptr;
-            CHECK(f.pool.acquire(b, 1, &dev) == NF4_OK, "fwd acquire %d", b);
+            CHECK(f.pool.acquire(b, 1, &dev, deferred) == NF4_OK, "fwd acquire %d", b);
             if (slots > 1 && b + 1 < nb) CHECK(f.pool.prefetch(b + 1) == NF4_OK, "fwd prefetch %d", b + 1);
-            if (f.use_block(b, dev, false, 1)) return 1;
+            if (f.use_block(b, dev, false, 1, deferred)) return 1;
         }
         f.pool.descending = true;
         for (int b = nb - 1; b >= 0; --b) {
             const void* dev = nullptr;
-            CHECK(f.pool.acquire(b, 1, &dev) == NF4_OK, "bwd acquire %d", b);
+            CHECK(f.pool.acquire(b, 1, &dev, deferred) == NF4_OK, "bwd acquire %d", b);
             if (slots > 1 && b > 0) CHECK(f.pool.prefetch(b - 1) == NF4_OK, "bwd prefetch %d", b - 1);
-            if (f.use_block(b, dev, true, 1)) return 1;
+            if (f.use_block(b, dev, true, 1, deferred)) return 1;
         }
     }
     if (check_order(f.eng)) return 1;
     // misses: only block 0 of the first forward when prefetching, every block otherwise
     if (slots > 1 && nb > slots) CHECK(f.pool.stats.misses == 1, "misses %llu", (unsigned long long)f.pool.stats.misses);
+    const int releases = 2 * nb * steps;
+    CHECK(f.eng.host_waits == (max_ahead > 0 ? std::max(0, releases - max_ahead) : 0), "host waits %d",
+          f.eng.host_waits);
+    CHECK(int(f.pool.ahead.size()) == std::min(releases, max_ahead), "marks kept %zu", f.pool.ahead.size());
+    f.pool.destroy_events();
+    return 0;
+}
+
+// Negative control of the order check: a deferred acquire whose parts are read without
+// wait_part must be rejected (reads not ordered after their copies).
+static int deferred_without_waits() {
+    Fixture f(4, 2, 1, 512);
+    CHECK(f.init() == NF4_OK, "init");
+    const void* dev = nullptr;
+    CHECK(f.pool.acquire(0, 1, &dev, true) == NF4_OK, "deferred acquire");
+    if (f.use_block(0, dev, false, 1, true, true)) return 1;
+    g_quiet = true;
+    const int bad = check_order(f.eng);
+    g_quiet = false;
+    g_fail = 0;  // the failure above is the expected outcome
+    CHECK(bad == 1, "reads without wait_part passed the order check");
     f.pool.destroy_events();
     return 0;
 }
@@ -270,6 +306,10 @@ static int errors() {
         CHECK(f.pool.prefetch(2) == NF4_OK && f.pool.where[2] == freed && f.pool.where[0] == -1,
               "prefetch after release reuses the released block's slot");
         CHECK(f.pool.prefetch(9) == NF4_E_ARG, "block out of range");
+        CHECK(f.pool.wait_part(0, 0, 1) == NF4_E_STATE, "wait_part of a block not held");
+        CHECK(f.pool.wait_part(1, 2, 1) == NF4_E_ARG, "wait_part of a part outside the block");
+        CHECK(f.pool.wait_part(1, 1, 1) == NF4_OK, "wait_part of a held block");
+        CHECK(f.pool.set_max_ahead(-1) == NF4_E_ARG, "negative lead");
         f.pool.destroy_events();
     }
     {  // a block larger than a slot: OOM, with the sizes in the message
@@ -296,7 +336,10 @@ static int errors() {
 int main() {
     const int shapes[][3] = {{8, 4, 2}, {7, 4, 2}, {5, 1, 2}, {6, 2, 3}, {9, 3, 2}, {4, 4, 1}, {3, 1, 1}, {12, 4, 3}};
     for (const auto& s : shapes)
-        if (stack_pattern(s[0], s[1], s[2], 3)) return 1;
+        for (int deferred = 0; deferred < 2; ++deferred)
+            for (int ahead : {0, 1, 2, 5})
+                if (stack_pattern(s[0], s[1], s[2], 3, deferred != 0, ahead)) return 1;
+    if (deferred_without_waits()) return 1;
     for (unsigned seed = 1; seed <= 300; ++seed)
         if (random_calls(seed)) return 1;
     if (errors()) return 1;

@@ -161,6 +161,9 @@ def test_pool_validation(L):
     _err(L, rc, L.NF4_E_ARG, "NULL pool")
     rc = raw.stream_pool_streams(None, None)
     _err(L, rc, L.NF4_E_ARG, "NULL")
+    n = C.c_int(-1)
+    rc = raw.stream_pool_timing_spans(None, None, 0, C.byref(n))
+    _err(L, rc, L.NF4_E_ARG, "need pool")
 
 
 def test_block_layout(L):

@@ -211,3 +211,92 @@ def test_pool_streams_pair_overlaps_copies_with_compute(gpu_lib):
         assert t_both < t_copy + 0.5 * t_comp, (t_copy, t_comp, t_both)
     finally:
         pool.close()
+
+
+def test_pool_timing_spans_order_and_tags(gpu_lib):
+    """stream_pool_timing_spans: one copy span per part copied (tagged with its block and
+    part, in issue order, back to back on the copy stream: each starts after the previous
+    one ended) and one acquire span per acquire, all completed, with the sums of
+    timing_collect equal to the spans' durations."""
+    L = gpu_lib
+    n = 1 << 22
+    parts = _blocks(6, n)                       # 3 blocks of two parts
+    slab = torch.empty(2 * 2 * n, dtype=torch.uint8, device="cuda")
+    comp, copy = L.pool_streams()
+    pool = L.StreamPool(parts, slab, 2 * n, 2, copy, part_begin=[0, 2, 4, 6])
+    try:
+        assert pool.timing_spans() == []
+        pool.timing_enable(True)
+        with torch.cuda.stream(comp):
+            for b in range(3):
+                pool.acquire(b)
+                if b + 1 < 3:
+                    pool.prefetch(b + 1)
+                pool.release(b)
+        spans = pool.timing_spans()
+        copies = [s for s in spans if s["kind"] == "copy"]
+        acq = [s for s in spans if s["kind"] == "acquire"]
+        assert [(s["block"], s["part"]) for s in copies] == [(0, 0), (0, 1), (1, 0), (1, 1), (2, 0), (2, 1)]
+        assert [s["block"] for s in acq] == [0, 1, 2] and all(s["part"] == -1 for s in acq)
+        assert min(s["start_ms"] for s in spans) == 0.0
+        for s in spans:
+            assert s["end_ms"] >= s["start_ms"] >= 0.0 and s["host_call_ms"] >= 0.0
+        for a, b in zip(copies, copies[1:]):
+            assert b["start_ms"] >= a["end_ms"] - 1e-3 and b["host_at_ms"] >= a["host_at_ms"]
+        tm = pool.timing_collect()
+        assert tm["copies"] == 6 and tm["acquires"] == 3
+        assert abs(tm["copy_ms"] - sum(s["end_ms"] - s["start_ms"] for s in copies)) < 1e-2
+        assert tm["host_ms"] >= tm["host_copy_ms"] > 0.0
+        assert abs(tm["host_ms"] - tm["host_copy_ms"] - tm["host_record_ms"] - tm["host_wait_ms"]) < 1e-6
+        assert pool.timing_spans() == []        # collect forgot them
+    finally:
+        comp.synchronize()
+        pool.close()
+
+
+def test_pool_deferred_acquire_waits_per_part_and_lead_bound(gpu_lib):
+    """stream_pool_acquire_deferred + stream_pool_wait_part: each part read after its own
+    wait holds that part's bytes, over passes that reuse one slot part by part in both
+    orders; with a lead bound of one block the host never has more than one release
+    outstanding (every release returns after the previous one completed), and the bytes
+    are the same. Misuse: wait_part on a block not held, or a part outside it."""
+    L = gpu_lib
+    n = 1 << 22
+    parts = _blocks(6, n)                       # 3 blocks of two parts
+    slab = torch.empty(2 * n, dtype=torch.uint8, device="cuda")
+    comp, copy = L.pool_streams()
+    pool = L.StreamPool(parts, slab, 2 * n, 1, copy, part_begin=[0, 2, 4, 6])
+    try:
+        with pytest.raises(L.Nf4Error) as e:
+            pool.wait_part(0, 0, comp)
+        assert e.value.code == L.NF4_E_STATE
+        with pytest.raises(L.Nf4Error) as e:
+            pool.set_max_ahead(-1)
+        assert e.value.code == L.NF4_E_ARG
+        for ahead in (0, 1):
+            pool.set_max_ahead(ahead)
+            got = []
+            with torch.cuda.stream(comp):
+                for descending in (False, True):
+                    pool.set_order(descending)
+                    for b in (range(3) if not descending else range(2, -1, -1)):
+                        ptr = pool.acquire_deferred(b, comp)
+                        assert ptr == slab.data_ptr()
+                        order = (1, 0) if descending else (0, 1)
+                        for i in order:
+                            pool.wait_part(b, i, comp)
+                            got.append((b, i, slab[i * n:(i + 1) * n].clone()))
+                            pool.release_part(b, i, comp)
+                        if b == 0 and not descending:
+                            with pytest.raises(L.Nf4Error) as e:
+                                pool.wait_part(0, 2, comp)
+                            assert e.value.code == L.NF4_E_ARG
+                        pool.release(b, comp)
+            comp.synchronize()
+            for b, i, t in got:
+                assert torch.equal(t.cpu(), parts[2 * b + i]), (ahead, b, i)
+        tm = pool.timing_collect()
+        assert tm["host_sync_ms"] >= 0.0
+    finally:
+        comp.synchronize()
+        pool.close()

@@ -150,8 +150,10 @@ def test_streamed_equals_resident_tiny(ST, block_size):
     ref = _run(ST, base, lora, T, "resident")
     assert ref["stats"]["copies"] == base.n_blocks and ref["stats"]["misses"] == 0
     for kw in ({"prefetch": True, "n_slots": 2}, {"prefetch": False, "n_slots": 2}, {"prefetch": True, "n_slots": 3},
-               {"prefetch": False, "n_slots": 1}, {"prefetch": True, "n_slots": 2, "layer_parts": True},
-               {"prefetch": True, "n_slots": 3, "layer_parts": True}, {"prefetch": False, "n_slots": 1, "layer_parts": True}):
+               {"prefetch": False, "n_slots": 1}, {"prefetch": True, "n_slots": 2, "layer_parts": False},
+               {"prefetch": True, "n_slots": 3, "layer_parts": False}, {"prefetch": False, "n_slots": 1, "layer_parts": False},
+               {"prefetch": True, "n_slots": 2, "max_ahead": 0}, {"prefetch": True, "n_slots": 2, "max_ahead": 1},
+               {"prefetch": True, "n_slots": 2, "layer_parts": False, "max_ahead": 0}):
         got = _run(ST, base, lora, T, "streamed", **kw)
         _same(got, ref)
         if kw["prefetch"] and base.n_blocks > 2:
@@ -221,7 +223,7 @@ def test_qwen7b_stack_streamed_equals_resident(ST):
     _same(got, ref)
     got = _run(ST, base, lora, 512, "streamed", remat=True)
     _same(got, ref)
-    _same(_run(ST, base, lora, 512, "streamed", layer_parts=True), ref)   # one copy and release per layer
+    _same(_run(ST, base, lora, 512, "streamed", layer_parts=False), ref)   # one copy and one wait per block
     assert torch.isfinite(ref["out"].float()).all() and torch.isfinite(ref["dh0"].float()).all()
     assert got["stats"]["bytes_copied"] > 2 * base.total_bytes()
 
@@ -245,8 +247,8 @@ def _big_stack_parity(ST, model, cases):
             _same(got, ref)
             assert got["stats"]["misses"] == 1 and got["stats"]["copies"] >= 2 * (b.n_blocks - 2)
             del got
-            if bs == 4 and T == 512:        # layers copied and released one by one
-                _same(_run(ST, b, lora, T, "streamed", n_slots=2, layer_parts=True), ref)
+            if bs == 4 and T == 512:        # one copy and one wait per block
+                _same(_run(ST, b, lora, T, "streamed", n_slots=2, layer_parts=False), ref)
             torch.cuda.empty_cache()
         del ref
     base.close()
