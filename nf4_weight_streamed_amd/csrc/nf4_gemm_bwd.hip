@@ -29,20 +29,27 @@ namespace {
 constexpr int kBN = 64;        // contraction (N) per main-loop step
 constexpr int kLds = kBN + 8;    // LDS pitch of the dY tile in bf16 (144 bytes)
 constexpr int kLdsW = kBN + 16;  // LDS pitch of the weight tile in bf16 (160 bytes)
-constexpr int kThreads = 256;
 constexpr int64_t kCUs = kChipCUs;
 
-// Workgroup tile: 128 tokens x 128 input features, 4 waves in a 2x2 grid (64 x 64
-// each, 32x32x16 MFMA), contraction steps of 64 over N. Per step each thread loads
+// Workgroup tile: BM (128 or 256) tokens x 128 input features, BM / 32 waves in a
+// (BM / 64) x 2 grid (64 x 64 each, 32x32x16 MFMA), contraction steps of 64 over N.
+// With 256 tokens the eight waves share one weight tile, so each weight is
+// dequantised and stored to LDS once per 256 tokens instead of 128: waves 0-3
+// dequantise it (the same 256-thread patch layout), waves 4-7 only stage dY and keep
+// the matrix cores busy meanwhile (measured about 8% faster than spreading 4 x 4
+// patches over all eight waves); the main loop is compiled once per role, so each
+// keeps exact wait counts. Per step each thread loads
 // (raw buffer loads, hardware zero outside the tensors) a 4 (n) x 8 (k) patch of
-// codes with the 4 row scales and 4 16-byte chunks of the dY tile, two steps ahead
+// codes with the 4 row scales (weight waves) and 4 16-byte chunks of the dY tile, two
+// steps ahead
 // into a ring of two register sets. dY and the weight tile are double-buffered in
 // LDS: during the MFMAs of step s each thread dequantises its patch of step s + 1 -
 // one 8-byte read of a 256-entry (level[lo], level[hi]) pair table per code byte,
 // fp32 multiply by the row's absmax, bf16 pack pairing rows - and stores it
 // transposed, with its dY chunks, into the other buffer; one barrier per step. The
 // step has no branch, so the scheduler interleaves the dequantisation with the
-// MFMAs. LDS block 78 KB (shared with the LoRA epilogue): two workgroups per CU.
+// MFMAs. LDS block 78 KB with 128 tokens (shared with the LoRA epilogue): two
+// workgroups per CU; 132 KB with 256 tokens: one.
 
 // Which tile (and contraction range) each workgroup of the 1-D grid takes: ids
 // 0 .. full-1 are whole tiles, the rest pieces of the last `tail` tiles, piece z of
@@ -65,22 +72,28 @@ struct BwdLora {
     float s;
 };
 
-template <bool kDense>
-__global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
+template <int BM, bool kDense>
+__global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void k_nf4_gemm_bwd_dx(
     const uint16_t* __restrict__ dy, const void* __restrict__ weights, const float* __restrict__ absmax, int T,
     int N, int K, BwdTiles tl, BwdLora lora, uint16_t* __restrict__ dx, float* __restrict__ partial, Tables tab) {
-    constexpr int BM = 128, BK = 128;
-    constexpr int WM = BM / 2, WK = BK / 2;
+    static_assert(BM == 128 || BM == 256, "128 or 256 tokens per tile");
+    static_assert(!kDense || BM == 128, "the dense base runs 128-token tiles");
+    constexpr int NT = 2 * BM;  // threads: BM / 32 waves
+    constexpr int BK = 128;
+    constexpr int WM = 64, WK = 64;
     constexpr int FM = WM / 32, FK = WK / 32;
-    constexpr int A_CHUNKS = BM * (kBN / 8) / kThreads;  // 4
+    constexpr int A_CHUNKS = BM * (kBN / 8) / NT;  // 4
+    static_assert(A_CHUNKS == 4, "four 16-byte dY chunks per thread and step");
 
-    // One LDS block (78 KB: two workgroups per CU). Main loop: two buffers of (dY
-    // tile, weight tile) and the pair table; LoRA epilogue: (s.g)^T hi/lo for up to 64
-    // ranks and one 64-column half of the x tile, transposed.
+    // One LDS block. Main loop: two buffers of (dY tile, weight tile) and the pair
+    // table; LoRA epilogue: (s.g)^T hi/lo for up to 64 ranks and the x tile transposed
+    // (one 64-column half at a time with 128 tokens, all 128 columns with 256).
     constexpr int kTP = BM + 8;  // pitch of the epilogue's [.][t] tiles
+    constexpr int kXHalves = BM == 256 ? 1 : 2;
+    constexpr int kXCols = BK / kXHalves;         // x columns staged at once
     constexpr int kBuf = BM * kLds + BK * kLdsW;  // one buffer: dY tile, then weight tile
     constexpr int kMain = 2 * kBuf + 2 * 512;
-    constexpr int kEpi = (2 * 64 + BK / 2) * kTP;
+    constexpr int kEpi = (2 * 64 + kXCols) * kTP;
     __shared__ __align__(16) uint16_t smem[kMain > kEpi ? kMain : kEpi];
     float* const sLut = reinterpret_cast<float*>(smem + 2 * kBuf);
 
@@ -116,11 +129,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     const int m0 = tm * BM;
     const int frag_row = lane & 31;
     const int frag_k = (lane >> 5) * 8;
-    sLut[2 * tid] = tab.level[tid & 15];  // entry b: the two codes of byte b
-    sLut[2 * tid + 1] = tab.level[tid >> 4];
+    if (tid < 256) {
+        sLut[2 * tid] = tab.level[tid & 15];  // entry b: the two codes of byte b
+        sLut[2 * tid + 1] = tab.level[tid >> 4];
+    }
 
-    // this thread's patch: rows 4*pr .. 4*pr+3 of the step, columns 8*pc .. 8*pc+7 of the tile
-    const int pr = tid >> 4, pc = tid & 15;
+    // this thread's patch (threads 0-255, the weight waves): rows 4*pr .. 4*pr+3 of the
+    // step, columns 8*pc .. 8*pc+7 of the tile
+    const int pr = (tid & 255) >> 4, pc = tid & 15;
     const uint32_t trows = uint32_t(max(0, min(BM, T - m0)));
     const auto rdy = make_rsrc(dy + size_t(m0) * N, trows * uint32_t(N) * 2u);
     // codes/absmax of the whole matrix (the entry points keep N*K/2 below 2^30 bytes);
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     uint32_t a_off[A_CHUNKS];
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
-        const int c = tid + kThreads * i;
+        const int c = tid + NT * i;
         a_off[i] = (uint32_t(c >> 3) * uint32_t(N) + uint32_t(c & 7) * 8u) * 2u;
     }
 
@@ -142,13 +158,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
         float rs[4];          //      and its scale
         u32x4 rw[4];          // dense: 8 bf16 of each patch row
     };
-    auto gload = [&](int nb, LSet& l) {
+    // kW (compile time): this wave loads and dequantises the weight patch too
+    auto gload = [&](int nb, LSet& l, auto w_) {
+        constexpr bool kW = decltype(w_)::value;
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
             // dY columns at or beyond N (ragged last step, steps past the end) read as zero
-            const bool ok = nb * kBN + 8 * ((tid + kThreads * i) & 7) < N;
+            const bool ok = nb * kBN + 8 * ((tid + NT * i) & 7) < N;
             l.ra[i] = buf_load16(rdy, ok ? a_off[i] + uint32_t(nb) * (kBN * 2) : kOutOfRange);
         }
+        if constexpr (!kW) return;
         // Rows n >= N lie past the end of both buffers and read as zero (scale 0, so
         // the dequantised row is zero). Columns k >= K of a ragged tile read the next
         // row's data: they only reach dX columns that are never stored.
@@ -165,14 +184,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
     };
     const char* lut = reinterpret_cast<const char*>(sLut);
     // one step's tiles into LDS buffer b
-    auto sstore = [&](const LSet& l, int b) {
+    auto sstore = [&](const LSet& l, int b, auto w_) {
+        constexpr bool kW = decltype(w_)::value;
         uint16_t* const sA = smem + b * kBuf;
         uint16_t* const sWt = sA + BM * kLds;
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
-            const int c = tid + kThreads * i;
+            const int c = tid + NT * i;
             *reinterpret_cast<u32x4*>(&sA[(c >> 3) * kLds + (c & 7) * 8]) = l.ra[i];
         }
+        if constexpr (!kW) return;
         // row k = 8*pc + e holds n = 4*pr .. 4*pr+3: chunk pr/2, swizzled by k / 16 = pc / 2,
         // half pr&1
         const int col = (((pr >> 1) ^ ((pc >> 1) & 7)) << 3) + 4 * (pr & 1);
@@ -211,12 +232,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    if (nb_begin < nb_end) {
+    auto main_loop = [&](auto w_) {
         LSet ld[2];
-        gload(nb_begin, ld[0]);
-        gload(nb_begin + 1, ld[1]);
+        gload(nb_begin, ld[0], w_);
+        gload(nb_begin + 1, ld[1], w_);
         __syncthreads();  // sLut visible
-        sstore(ld[0], 0);
+        sstore(ld[0], 0, w_);
         __syncthreads();
         // Step nb, C = (nb - nb_begin) mod 2 at compile time (the loop is unrolled by 2,
         // so no register array is indexed at run time): MFMAs on LDS buffer C, loads of
@@ -229,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
         // loads in flight.
         auto step = [&](int nb, auto c_) {
             constexpr int C = decltype(c_)::value;
-            gload(nb + 2, ld[C]);
+            gload(nb + 2, ld[C], w_);
             __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
             const uint16_t* const sA = smem + C * kBuf;
             const uint16_t* const sWt = sA + BM * kLds;
@@ -251,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
 #pragma unroll
                     for (int j = 0; j < FK; ++j) acc[i][j] = mfma32x32x16(af[i], bw[j], acc[i][j]);
             }
-            sstore(ld[C ^ 1], C ^ 1);  // the next step's tiles
+            sstore(ld[C ^ 1], C ^ 1, w_);  // the next step's tiles
             // interleave the table reads, multiplies and stores with the MFMAs (the
             // scheduler's small-GEMM strategy). NF4 only: the dense variant has no
             // dequantisation to hide.
@@ -264,6 +285,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
             step(nb + 1, std::integral_constant<int, 1>{});
         }
         if (nb < nb_end) step(nb, std::integral_constant<int, 0>{});
+    };
+    if (nb_begin < nb_end) {
+        // both roles run the same steps, so every wave meets the same barriers
+        if (BM == 128 || wave < 4)
+            main_loop(std::true_type{});
+        else
+            main_loop(std::false_type{});
     }
 
     // LoRA (whole tiles and piece 0 of split tiles). g = sum of the partials in partial
@@ -292,8 +320,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
         const auto rx = make_rsrc(lora.x + size_t(m0) * K, trows * uint32_t(K) * 2u);
         // every load of the staging is issued before the first is consumed (one memory
         // round trip at the end of the kernel, not one per loop trip)
-        constexpr int XC = BM * (BK / 8) / kThreads;  // 16-byte x chunks per thread
-        constexpr int GI = BM * 4 / kThreads;         // (t, 4-rank group) items per thread per 16 ranks
+        constexpr int XC = BM * (BK / 8) / NT;  // 16-byte x chunks per thread
+        constexpr int GI = BM * 4 / NT;         // (t, 4-rank group) items per thread per 16 ranks
         const auto ra = make_rsrc(lora.A, uint32_t(r) * uint32_t(K) * 2u);  // rows j >= r read zero
         // A values of one 16-rank slice for this lane's dX fragments: B operand of the
         // LoRA K-extension (lane: column k, ranks c0 + 8 (lane / 32) .. + 7)
@@ -311,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
         uint32_t av[FK][8];
         load_a(0, av);
         // this thread's x chunks: 8 consecutive tokens xt0 .. xt0+7 of columns xk8 .. xk8+7
-        static_assert(XC == 8 && BM == 16 * XC && BK == 16 * 8, "x tile: 16 x 16 chunk blocks of 8 x 8");
+        static_assert(XC == 8 && BM == 8 * (NT / 16) && BK == 16 * 8, "x tile: chunk blocks of 8 x 8, 16 across");
         const int xk8 = 8 * (tid & 15), xt0 = 8 * (tid >> 4);
         u32x4 xv[XC];
 #pragma unroll
@@ -331,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
                 for (int pp = 0; pp < GR; ++pp) rgp[pp] = gpart_rsrc(p0 + pp);
 #pragma unroll
                 for (int i = 0; i < GI; ++i) {
-                    const int o = tid + kThreads * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
+                    const int o = tid + NT * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
                     const bool ok = m0 + t < T && j < r;
                     const uint32_t off = (uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u;
 #pragma unroll
@@ -347,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
             }
 #pragma unroll
             for (int i = 0; i < GI; ++i) {
-                const int o = tid + kThreads * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
+                const int o = tid + NT * i, t = o / 4, j = 16 * jb + 4 * (o % 4);
                 const f32x4 v = gsum[i];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -358,11 +386,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
                 }
             }
         }
-        // x^T of columns 64 h .. 64 h + 63: a thread's chunks all sit in one half (their
-        // column offset is 8 (tid % 16)); the 8 x 8 block is transposed in registers
-        // (byte permutes pairing tokens) and written as one 16-byte row piece per column
+        // x^T of columns kXCols h .. kXCols (h + 1) - 1 (with two halves a thread's chunks
+        // all sit in one, their column offset being 8 (tid % 16)); the 8 x 8 block is
+        // transposed in registers (byte permutes pairing tokens) and written as one
+        // 16-byte row piece per column
         auto stage_x = [&](int h) {
-            if (((tid & 15) >> 3) != h) return;
+            if (kXHalves == 2 && ((tid & 15) >> 3) != h) return;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 // element e of chunks i and i + 1: low halves (e even) or high halves (e odd)
@@ -371,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
                     col[p] = __builtin_amdgcn_perm(xv[2 * p + 1][e >> 1], xv[2 * p][e >> 1], sel);
-                *reinterpret_cast<u32x4*>(&sxt[(xk8 - 64 * h + e) * kTP + xt0]) = col;
+                *reinterpret_cast<u32x4*>(&sxt[(xk8 - kXCols * h + e) * kTP + xt0]) = col;
             }
         };
         stage_x(0);
@@ -405,11 +434,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
             }
         }
 
-        // dA share of this token tile: D[k][j] over t, 16x16x32 MFMAs; per 64-column
-        // half, wave w owns the K sub-block w (16 columns)
+        // dA share of this token tile: D[k][j] over t, 16x16x32 MFMAs; per staged group
+        // of kXCols columns, wave w owns the K sub-block w (16 columns)
+        static_assert(kXCols == 16 * (NT / 64), "one 16-column K sub-block per wave");
         const int l16 = lane & 15, t8 = 8 * (lane >> 4);
         float* dpart = lora.dapart + size_t(tm) * r * K;
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < kXHalves; ++h) {
             if (h > 0) {
                 __syncthreads();  // the first half's reads are done
                 stage_x(h);
@@ -427,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_nf4_gemm_bwd_dx(
                     d = mfma16x16x32(xa, gl, d);
                 }
                 // lane holds D[k = 64 h + 16 wave + 4 (lane / 16) + e][j = 16 jb + lane % 16]
-                const int j = 16 * jb + l16, kq = k0 + 64 * h + 16 * wave + 4 * (lane >> 4);
+                const int j = 16 * jb + l16, kq = k0 + kXCols * h + 16 * wave + 4 * (lane >> 4);
                 if (j < r && kq < K) *reinterpret_cast<f32x4*>(&dpart[size_t(j) * K + kq]) = d;
             }
         }
@@ -514,6 +544,11 @@ __global__ __launch_bounds__(256) void k_bwd_finish(BwdFinishDx f, uint16_t* __r
 
 }  // namespace
 
+int bwd_tile_tokens(int64_t T, int64_t N, int64_t K, bool dense) {
+    (void)N;
+    return !dense && cdiv(T, 256) * cdiv(K, 128) >= kCUs ? 256 : 128;
+}
+
 BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     BwdPlan p{};
     if (T <= kSkinnyT && !dense) {
@@ -525,7 +560,12 @@ BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
         p.ws_bytes = p.off_dx + p.sk.ws_bytes;
         return p;
     }
-    p.bm = 128;
+    // 256-token tiles (half the dequantisation and weight stores per MFMA) when they
+    // still fill a whole round of CUs without splitting the contraction (the 7B down
+    // projection at 512 tokens: 296 tiles, 107-109 against 114-116 us in the layer
+    // step); with fewer tiles the extra split pieces cost more than that saves (gate and
+    // up: 56 tiles, 113-116 against 106-109 us), so those keep 128-token tiles
+    p.bm = bwd_tile_tokens(T, N, K, dense);
     p.bn = 128;
     p.mtiles = int(cdiv(T, p.bm));
     p.ktiles = int(cdiv(K, p.bn));
@@ -588,11 +628,15 @@ hipError_t launch_gemm_bwd(const BwdPlan& p, const uint8_t* codes, const float* 
     const BwdLora lora{reinterpret_cast<const float*>(w + p.off_gpart), p.gparts, A, x, dapart, r, s};
     if (dx) prof_gemm_begin(stream);
     if (wdense)
-        hipLaunchKernelGGL(k_nf4_gemm_bwd_dx<true>, grid, dim3(kThreads), 0, stream, dy,
+        hipLaunchKernelGGL((k_nf4_gemm_bwd_dx<128, true>), grid, dim3(256), 0, stream, dy,
                            static_cast<const void*>(wdense), nullptr, int(T), int(N), int(K), tl, lora, dx, partial,
                            tables());
+    else if (p.bm == 256)
+        hipLaunchKernelGGL((k_nf4_gemm_bwd_dx<256, false>), grid, dim3(512), 0, stream, dy,
+                           static_cast<const void*>(codes), absmax, int(T), int(N), int(K), tl, lora, dx, partial,
+                           tables());
     else
-        hipLaunchKernelGGL(k_nf4_gemm_bwd_dx<false>, grid, dim3(kThreads), 0, stream, dy,
+        hipLaunchKernelGGL((k_nf4_gemm_bwd_dx<128, false>), grid, dim3(256), 0, stream, dy,
                            static_cast<const void*>(codes), absmax, int(T), int(N), int(K), tl, lora, dx, partial,
                            tables());
     if (dx) prof_gemm_end(stream);

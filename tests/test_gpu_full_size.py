@@ -31,8 +31,8 @@ def _w_col(codes, absmax, k):
     return O.bf16_bits_to_f64(w[:, k % O.NF4_BLOCK])
 
 
-@pytest.mark.parametrize("t,n,k,proj", [(512, 18944, 3584, "gate"), (16, 29568, 8192, "gate"),
-                                        (1, 29568, 8192, "gate")])
+@pytest.mark.parametrize("t,n,k,proj", [(512, 18944, 3584, "gate"), (512, 3584, 18944, "down"),
+                                        (16, 29568, 8192, "gate"), (1, 29568, 8192, "gate")])
 def test_full_size_projection_sampled(gpu_lib, t, n, k, proj):
     r, alpha = S.RANK, S.ALPHA
     print(f"full-size projection T={t} N={n} K={k}", flush=True)

@@ -76,6 +76,9 @@ def test_single_linear_workload(gpu_lib):
     (512, 1024, 8192, 16),   # exactly 256 dX tiles: split in two over N
     (512, 12800, 1536, 16),  # 400 y tiles: a whole round, the last 144 split in three over K
     (512, 1536, 12800, 16),  # 400 dX tiles: a whole round, the last 144 split in three over N
+    (300, 1024, 16448, 5),   # 256-token dX tiles (ragged second tile, ragged last column tile), odd rank
+    (257, 1024, 32768, 64),  # 256-token dX tiles one token past a tile, maximum rank
+    (512, 2048, 18944, 16),  # 256-token dX tiles: 296 tiles, a whole round and a split tail
 ])
 def test_shapes(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
