@@ -254,23 +254,30 @@ __global__ __launch_bounds__(2 * BM, BM == 128 ? 2 : 1) void k_nf4_gemm_bwd_dx(
             __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
             const uint16_t* const sA = smem + C * kBuf;
             const uint16_t* const sWt = sA + BM * kLds;
-#pragma unroll
-            for (int kk = 0; kk < kBN / 16; ++kk) {
-                bf16x8 af[FM], bw[FK];
+            // fragments one sub-step ahead in two register sets (the reads of kk + 1 come
+            // before the MFMAs of kk in the program: gate backward 2%, down 3% faster in
+            // the layer step)
+            bf16x8 af[2][FM], bw[2][FK];
+            auto read_frags = [&](int kk, bf16x8 (&a)[FM], bf16x8 (&b)[FK]) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
-                    af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                    a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
                         &sA[(wm * WM + 32 * i + frag_row) * kLds + kk * 16 + frag_k]));
 #pragma unroll
                 for (int j = 0; j < FK; ++j) {
                     const int row = wk * WK + 32 * j + frag_row;
                     const int chunk = (2 * kk + (lane >> 5)) ^ ((row >> 4) & 7);
-                    bw[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sWt[row * kLdsW + chunk * 8]));
+                    b[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sWt[row * kLdsW + chunk * 8]));
                 }
+            };
+            read_frags(0, af[0], bw[0]);
+#pragma unroll
+            for (int kk = 0; kk < kBN / 16; ++kk) {
+                if (kk + 1 < kBN / 16) read_frags(kk + 1, af[(kk + 1) & 1], bw[(kk + 1) & 1]);
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FK; ++j) acc[i][j] = mfma32x32x16(af[i], bw[j], acc[i][j]);
+                    for (int j = 0; j < FK; ++j) acc[i][j] = mfma32x32x16(af[kk & 1][i], bw[kk & 1][j], acc[i][j]);
             }
             sstore(ld[C ^ 1], C ^ 1, w_);  // the next step's tiles
             // interleave the table reads, multiplies and stores with the MFMAs (the
