@@ -36,11 +36,11 @@ constexpr int kXP = kDK + 8;  // LDS pitch of the x tile (bf16)
 // one K range of 256-wide steps. Within a step the contraction order is permuted
 // identically for both operands: lane quarter q (lane / 16) supplies k = 64q + 8c ..
 // 64q + 8c + 7 at MFMA chunk c (0..7), so a lane's 32 bytes of codes per row block are
-// one whole NF4 block (one scale). Codes, scales and x are loaded kFRing - 1 steps ahead
-// into a ring of kFRing register sets (two, measured: the fewer registers let four
-// workgroups share a CU, which keeps more bytes in flight than a deeper ring would); the
-// x tile of the current step is in double-buffered LDS. Output: fp32 partials
-// ypart[split][T][N].
+// one whole NF4 block (one scale). Codes and scales are loaded kFRing - 1 steps ahead
+// into a ring of kFRing register sets (two, measured: a ring of three, or twice the
+// workgroups, gave nothing), x kFRing steps ahead into a ring of its own; the x tile of
+// the current step is in double-buffered LDS, and the table reads of MFMA chunk c + 1 are
+// issued before the multiplies of chunk c. Output: fp32 partials ypart[split][T][N].
 //
 // u workgroups (blockIdx.x >= row_blocks, kUParts per split): the rows of A (bf16, wave
 // w: ranks 16w .. 16w+15) against the same x for u = x.A^T, each over a quarter of the
@@ -78,10 +78,30 @@ __device__ __forceinline__ void skinny_fwd_weights(const uint16_t* __restrict__ 
     struct Set {
         u32x4 cw[2][2];  // codes [row block][16-byte piece]
         float sc[2];
-        u32x4 xv[XCH];
     };
     constexpr int R = kFRing;
     Set ring[R];
+    // x of a step, loaded R steps ahead into its own ring of R sets (the set of the step
+    // being computed is in LDS already), so that the tile stored at the end of a step was
+    // loaded a step before that step's codes and storing it never waits for code loads
+    // still in flight; only the threads of real tokens load (the padded rows stay zero)
+    u32x4 xr[R][XCH];
+#pragma unroll
+    for (int c = 0; c < R; ++c)
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) xr[c][i] = u32x4{0u, 0u, 0u, 0u};
+    auto gload_x = [&](int kb, u32x4 (&xv)[XCH]) {
+        const uint32_t k0 = uint32_t(kb) * kDK;
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+            const int c = tid + kThreads * i;  // token c / 32, columns 8 (c % 32)
+            const int t = c / (kDK / 8), k8 = 8 * (c % (kDK / 8));
+            if (t < T) {
+                const bool ok = int(k0) + k8 < K;
+                xv[i] = buf_load16(rx, ok ? (uint32_t(t) * uint32_t(K) + k0 + uint32_t(k8)) * 2u : kOutOfRange);
+            }
+        }
+    };
     auto gload = [&](int kb, Set& st) {
         const uint32_t k0 = uint32_t(kb) * kDK;
 #pragma unroll
@@ -90,37 +110,16 @@ __device__ __forceinline__ void skinny_fwd_weights(const uint16_t* __restrict__ 
             for (int p = 0; p < 2; ++p) st.cw[nb][p] = buf_load16(rcd, c_off[nb] + k0 / 2u + uint32_t(p) * 16u);
             st.sc[nb] = buf_load_f32(rsc, s_off[nb] + (k0 / 64u) * 4u);
         }
-        // only the threads of real tokens load (the padded rows stay zero in LDS):
-        // vector-memory instructions, not bytes, limit this kernel
-#pragma unroll
-        for (int i = 0; i < XCH; ++i) {
-            const int c = tid + kThreads * i;  // token c / 32, columns 8 (c % 32)
-            const int t = c / (kDK / 8), k8 = 8 * (c % (kDK / 8));
-            if (t < T) {
-                const bool ok = int(k0) + k8 < K;
-                st.xv[i] = buf_load16(rx, ok ? (uint32_t(t) * uint32_t(K) + k0 + uint32_t(k8)) * 2u : kOutOfRange);
-            }
-        }
     };
     typedef uint16_t XTile[TP * kXP];
     XTile* sX = reinterpret_cast<XTile*>(sXflat);
-    auto store_x = [&](const Set& st, int buf) {
+    auto store_x = [&](const u32x4 (&xv)[XCH], int buf) {
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
             const int c = tid + kThreads * i;
-            if (c / (kDK / 8) < T)
-                *reinterpret_cast<u32x4*>(&sX[buf][(c / (kDK / 8)) * kXP + 8 * (c % (kDK / 8))]) = st.xv[i];
+            *reinterpret_cast<u32x4*>(&sX[buf][(c / (kDK / 8)) * kXP + 8 * (c % (kDK / 8))]) = xv[i];
         }
     };
-    // rows of the padded token block past T are zero in both buffers for the whole loop
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-        const int c = tid + kThreads * i;
-        if (c / (kDK / 8) >= T) {
-            *reinterpret_cast<u32x4*>(&sX[0][(c / (kDK / 8)) * kXP + 8 * (c % (kDK / 8))]) = u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(&sX[1][(c / (kDK / 8)) * kXP + 8 * (c % (kDK / 8))]) = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
     const char* lut = reinterpret_cast<const char*>(sLut);
 
     f32x4 acc[TB][2];
@@ -131,28 +130,45 @@ __device__ __forceinline__ void skinny_fwd_weights(const uint16_t* __restrict__ 
 
     if (kb_begin < kb_end) {
 #pragma unroll
+        for (int c = 0; c < R; ++c) gload_x(kb_begin + c, xr[c]);
+#pragma unroll
         for (int c = 0; c < R - 1; ++c) gload(kb_begin + c, ring[c]);
-        store_x(ring[0], 0);
+        store_x(xr[0], 0);
         __syncthreads();  // sLut and x tile 0
         // one step on ring slot C (compile-time: the loop is unrolled by R)
         auto step = [&](int kb, auto c_) {
             constexpr int C = decltype(c_)::value;
             const int buf = (kb - kb_begin) & 1;
-            gload(kb + R - 1, ring[(C + R - 1) % R]);  // R - 1 steps ahead; past the range: unused or zeros
+            // x R steps ahead into the set whose tile is in LDS already, codes R - 1 steps
+            // ahead; past the range: unused or zeros
+            gload_x(kb + R, xr[C % R]);
+            gload(kb + R - 1, ring[(C + R - 1) % R]);
             __builtin_amdgcn_sched_barrier(0);
             const Set& cur = ring[C % R];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                bf16x8 bw[2];
+            // table reads of chunk c + 1 are issued before the arithmetic of chunk c
+            float2 lv[2][2][4];
+            auto table = [&](int c, float2 (&v)[2][4]) {
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) {
                     const uint32_t w = cur.cw[nb][c >> 2][c & 3];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        v[nb][b] = *reinterpret_cast<const float2*>(lut + (((w >> (8 * b)) & 0xFFu) << 3));
+                }
+            };
+            table(0, lv[0]);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if (c + 1 < 8) table(c + 1, lv[(c + 1) & 1]);
+                bf16x8 bw[2];
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
                     u32x4 o;
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        const float2 lv = *reinterpret_cast<const float2*>(lut + (((w >> (8 * b)) & 0xFFu) << 3));
+                        const float2 v = lv[c & 1][nb][b];
                         // level * absmax in fp32, then RNbf: the format's two roundings
-                        o[b] = pack_bf16x2(lv.x * cur.sc[nb], lv.y * cur.sc[nb]);
+                        o[b] = pack_bf16x2(v.x * cur.sc[nb], v.y * cur.sc[nb]);
                     }
                     bw[nb] = as_bf16x8(o);
                 }
@@ -164,7 +180,7 @@ __device__ __forceinline__ void skinny_fwd_weights(const uint16_t* __restrict__ 
                     for (int nb = 0; nb < 2; ++nb) acc[tb][nb] = mfma16x16x32(xa, bw[nb], acc[tb][nb]);
                 }
             }
-            store_x(ring[(C + 1) % R], buf ^ 1);  // the next step's x (loaded earlier)
+            store_x(xr[(C + 1) % R], buf ^ 1);  // the next step's x (loaded a step before its codes)
             __syncthreads();
         };
         int kb = kb_begin;
@@ -518,13 +534,21 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
             const bf16x8 da = as_bf16x8(cur.dv);
 #pragma unroll
             for (int p = 0; p < 8; ++p) {  // features 2p, 2p + 1 of the lane's 16
-                float v0[8], v1[8];
+                // the eight table reads of the pair are issued together, ahead of their
+                // multiplies (left to the scheduler, each read was waited for before the
+                // next one was issued)
+                float2 lv[8];
 #pragma unroll
                 for (int r8 = 0; r8 < 8; ++r8) {
                     const uint32_t byte = (cur.cw[r8][p >> 2] >> (8 * (p & 3))) & 0xFFu;
-                    const float2 lv = *reinterpret_cast<const float2*>(lut + (byte << 3));
-                    v0[r8] = lv.x * sc[r8];  // level * absmax in fp32, RNbf below
-                    v1[r8] = lv.y * sc[r8];
+                    lv[r8] = *reinterpret_cast<const float2*>(lut + (byte << 3));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                float v0[8], v1[8];
+#pragma unroll
+                for (int r8 = 0; r8 < 8; ++r8) {
+                    v0[r8] = lv[r8].x * sc[r8];  // level * absmax in fp32, RNbf below
+                    v1[r8] = lv[r8].y * sc[r8];
                 }
                 const u32x4 f0 = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v0[4], v0[5]),
                                   pack_bf16x2(v0[6], v0[7])};
