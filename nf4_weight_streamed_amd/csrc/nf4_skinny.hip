@@ -1,4 +1,4 @@
-// NF4-LoRA linear for few tokens (T <= 16, one 16-token MFMA block): the same operations
+// NF4-LoRA linear for few tokens (forward T <= 32, backward T <= 16): the same operations
 // as the 128-token GEMMs, organised for the HBM-bound regime, where every weight byte
 // should be read once and streamed at full rate while MFMA work is cheap.
 //
@@ -9,9 +9,10 @@
 //
 // The frozen NF4 base is only read (HN comment thread on streaming the frozen base,
 // main comment); LoRA rank r and alpha as in the Poros API reference
-// ("PorosTrainer.from_pretrained"). Tokens are padded to one block of 16 for
-// v_mfma_f32_16x16x32_bf16 (the forward's TB template counts such blocks; only TB = 1
-// is launched); both GEMM kernels split their contraction over the grid's y dimension
+// ("PorosTrainer.from_pretrained"). Tokens are padded to blocks of 16 for
+// v_mfma_f32_16x16x32_bf16 (the forward's TB template counts such blocks, one or two,
+// and each dequantised weight fragment feeds both; the backward takes one block);
+// both GEMM kernels split their contraction over the grid's y dimension
 // and write fp32 partials, which the finish kernels add in split order, together with
 // the LoRA terms, and round once.
 #include <type_traits>
@@ -699,7 +700,7 @@ void launch_fwd_tb(const SkinnyPlan& p, const uint8_t* codes, const float* absma
 }
 
 // Split policy of the streaming kernels (measured on the 7B and 72B projection shapes
-// at T = 1..16): about kWGs workgroups of at least kMinSteps main-loop steps each -
+// at T = 1..32): about kWGs workgroups of at least kMinSteps main-loop steps each -
 // longer-running workgroups stream better than more of them - unless that leaves
 // fewer than kFillWGs workgroups, then down to one step each; the fp32 partials
 // (written once and read back once, mostly in the last-level cache) at most
@@ -708,7 +709,7 @@ void launch_fwd_tb(const SkinnyPlan& p, const uint8_t* codes, const float* absma
 constexpr int64_t kFillWGs = 256;
 constexpr int64_t kFwdWGs = 512;
 constexpr int64_t kFwdMinSteps = 4;
-constexpr int64_t kFwdPartialDiv = 2;
+constexpr int64_t kFwdPartialDiv = 1;  // 2 was 20% slower on the 7B q forward at T = 32
 constexpr int64_t kBwdWGs = 768;
 constexpr int64_t kBwdMinSteps = 4;  // one per wave
 constexpr int64_t kBwdPartialDiv = 1;
@@ -759,9 +760,13 @@ hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const fl
     char* w = static_cast<char*>(ws);
     float* ypart = reinterpret_cast<float*>(w + p.off_part);
     float* upart = reinterpret_cast<float*>(w + p.off_upart);
-    if (T > kSkinnyMaxT) return hipErrorInvalidValue;  // one 16-token MFMA block
+    if (T > kSkinnyFwdT) return hipErrorInvalidValue;  // at most two 16-token MFMA blocks
+    static_assert(kSkinnyFwdT <= 32, "one or two token blocks are instantiated");
     prof_gemm_begin(stream);
-    launch_fwd_tb<1>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream);
+    if (T <= 16)
+        launch_fwd_tb<1>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream);
+    else
+        launch_fwd_tb<2>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream);
     prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -96,6 +96,19 @@ def test_few_token_path(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
 
 
+@pytest.mark.parametrize("t,n,k,r", [
+    (17, 208, 384, 5),       # two token blocks, the second with one token; odd rank
+    (32, 3584, 3584, 16),    # two full blocks, q-shaped
+    (25, 4096, 256, 16),     # ragged second block, one K step
+    (31, 1040, 8256, 64),    # maximum rank, ragged rows, odd K step count
+    (33, 208, 384, 16),      # one past the few-token forward: the 128-token kernels
+])
+def test_few_token_forward_blocks(gpu_lib, t, n, k, r):
+    """17 <= T <= 32: the forward runs the streaming kernel with two token blocks (the
+    backward the 128-token kernels)."""
+    _check_case(gpu_lib, t, n, k, r)
+
+
 def test_few_token_dx_skipped(gpu_lib):
     case = S.linear_case(4, 256, 512)
     wq, dev = _prepare(gpu_lib, case, 16)
