@@ -40,14 +40,12 @@ constexpr int kMaxDbChunks = 8;   // token ranges of dB = s.dY^T.u (shares summe
 // Few-token path: streaming kernels with 16-token MFMA blocks and fp32 partials over a
 // split contraction, finished (split sum + LoRA + rounding) by a second kernel.
 // Workspace: [partials | u partials] (forward) / [g partials | dX partials] (backward).
-// The backward handles one token block (T <= kSkinnyT: faster than the 128-token
-// kernels up to T = 16, slower from T = 32); the forward up to kSkinnyFwdT tokens in
-// one or two blocks, which share each dequantised weight fragment (at T = 32 the 7B q,
-// 7B gate, 72B gate and 72B down forward take 13.4, 30.6, 65 and 60 us against 23.3,
-// 35.5, 88 and 90 us on the 128-token kernels; at T = 64, four blocks were slower than
-// those on the 7B shapes).
-constexpr int64_t kSkinnyT = 16;
+// Both take up to 32 tokens in one or two blocks, which share each dequantised weight
+// fragment (at T = 32 the 7B q, 7B gate, 72B gate and 72B down forward take 13.4, 30.6,
+// 65 and 60 us against 23.3, 35.5, 88 and 90 us on the 128-token kernels; at T = 64,
+// four blocks were slower than those on the 7B shapes).
 constexpr int64_t kSkinnyFwdT = 32;
+constexpr int64_t kSkinnyBwdT = 32;
 struct SkinnyPlan {
     int row_blocks;       // forward: 128-row workgroups
     int col_blocks;       // backward: 128-column workgroups

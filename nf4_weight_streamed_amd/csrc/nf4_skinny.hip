@@ -27,7 +27,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxRank = 16 * NF4_MAX_RANK_BLOCKS;
-constexpr int kSkinnyMaxT = int(kSkinnyT);
+constexpr int kSkinnyMaxT = int(kSkinnyBwdT);  // the backward finish kernel's g rows
 constexpr int kRows = 128;    // forward: weight rows per workgroup (4 waves x 2 blocks of 16)
 constexpr int kDK = 256;      // forward: K per main-loop step (four NF4 blocks)
 constexpr int kXP = kDK + 8;  // LDS pitch of the x tile (bf16)
@@ -451,19 +451,23 @@ __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __r
 constexpr int kBCols = 256;  // features per workgroup
 constexpr int kBRows = 32;   // weight rows per wave step
 constexpr int kBRing = 2;    // register sets: loads run kBRing - 1 steps ahead
-constexpr int kBOccupancy = 3;  // waves per SIMD the register budget must allow
+// waves per SIMD the register budget must allow: three with one token block, two with two
+template <int TB>
+constexpr int kBOccupancy = TB == 1 ? 3 : 2;
 static_assert(kBRing == 2 || kBRing == 3, "ring of two or three register sets");
 
+template <int TB>
 struct BwdSmem {
     float lut[512];
     float sc[4][4 * kBRows];    // per wave: scales [block][row]
-    float red[2][16][kBCols];   // cross-wave sums [token][feature]
+    float red[2][16 * TB][kBCols];  // cross-wave sums [token][feature]
 };
 
+template <int TB>
 __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes,
                                               const float* __restrict__ absmax, int T, int N, int K,
                                               int steps_per_split, int col, int split, float* __restrict__ dxpart,
-                                              const Tables& tab, BwdSmem& sm) {
+                                              const Tables& tab, BwdSmem<TB>& sm) {
     float* sLut = sm.lut;
     auto& sSc = sm.sc;
     auto& sRed = sm.red;
@@ -489,12 +493,14 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
     struct Set {
         u32x2 cw[8];  // codes of rows 8q + i, 16 features
         float sc[2];  // scales: row 16h + lane / 4, block lane % 4
-        u32x4 dv;     // dY[t = l16][8q .. 8q + 7]
+        u32x4 dv[TB];  // dY[t = 16 tb + l16][8q .. 8q + 7]
     };
     constexpr int R = kBRing;
     Set ring[R];
 #pragma unroll
-    for (int c = 0; c < R; ++c) ring[c].dv = u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < R; ++c)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) ring[c].dv[tb] = u32x4{0u, 0u, 0u, 0u};
     auto gload = [&](int i, Set& st) {
         const uint32_t n0 = uint32_t(s_begin + wave + 4 * i) * kBRows;
 #pragma unroll
@@ -504,15 +510,21 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
         for (int r8 = 0; r8 < 8; ++r8) st.cw[r8] = buf_load8_nt(rcd, (n0 + uint32_t(r8)) * uint32_t(K / 2) + c_lane);
 #pragma unroll
         for (int h = 0; h < 2; ++h) st.sc[h] = buf_load_f32(rsc, (n0 + 16u * h) * uint32_t(K / 64) * 4u + s_lane);
-        const bool ok = l16 < T && int(n0) + 8 * q < N;
-        st.dv = buf_load16(rdy, ok ? (uint32_t(l16) * uint32_t(N) + n0 + uint32_t(8 * q)) * 2u : kOutOfRange);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int t = 16 * tb + l16;
+            const bool ok = t < T && int(n0) + 8 * q < N;
+            st.dv[tb] = buf_load16(rdy, ok ? (uint32_t(t) * uint32_t(N) + n0 + uint32_t(8 * q)) * 2u : kOutOfRange);
+        }
     };
     const char* lut = reinterpret_cast<const char*>(sLut);
     float* ssc = sSc[wave];
 
-    f32x4 acc[16];
+    f32x4 acc[TB][16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[tb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();  // sLut
 
     if (nw > 0) {
@@ -532,7 +544,6 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
             const f32x4 sb = *reinterpret_cast<const f32x4*>(&ssc[(l16 >> 2) * kBRows + 8 * q + 4]);
             __builtin_amdgcn_wave_barrier();
             const float sc[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-            const bf16x8 da = as_bf16x8(cur.dv);
 #pragma unroll
             for (int p = 0; p < 8; ++p) {  // features 2p, 2p + 1 of the lane's 16
                 // the eight table reads of the pair are issued together, ahead of their
@@ -555,8 +566,12 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
                                   pack_bf16x2(v0[6], v0[7])};
                 const u32x4 f1 = {pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]), pack_bf16x2(v1[4], v1[5]),
                                   pack_bf16x2(v1[6], v1[7])};
-                acc[2 * p] = mfma16x16x32(da, as_bf16x8(f0), acc[2 * p]);
-                acc[2 * p + 1] = mfma16x16x32(da, as_bf16x8(f1), acc[2 * p + 1]);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const bf16x8 da = as_bf16x8(cur.dv[tb]);
+                    acc[tb][2 * p] = mfma16x16x32(da, as_bf16x8(f0), acc[tb][2 * p]);
+                    acc[tb][2 * p + 1] = mfma16x16x32(da, as_bf16x8(f1), acc[tb][2 * p + 1]);
+                }
             }
         };
         int i = 0;
@@ -577,23 +592,29 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
         }
     }
 
-    // lane holds D[t = 4q + e][feature 16 l16 + j] in acc[j][e]; sum (w0 + w2) + (w1 + w3)
+    // lane holds D[t = 16 tb + 4q + e][feature 16 l16 + j] in acc[tb][j][e]; sum
+    // (w0 + w2) + (w1 + w3)
     if (wave >= 2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                *reinterpret_cast<f32x4*>(&sRed[wave - 2][4 * q + e][16 * l16 + 4 * m]) =
-                    f32x4{acc[4 * m][e], acc[4 * m + 1][e], acc[4 * m + 2][e], acc[4 * m + 3][e]};
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    *reinterpret_cast<f32x4*>(&sRed[wave - 2][16 * tb + 4 * q + e][16 * l16 + 4 * m]) =
+                        f32x4{acc[tb][4 * m][e], acc[tb][4 * m + 1][e], acc[tb][4 * m + 2][e], acc[tb][4 * m + 3][e]};
     __syncthreads();
     if (wave < 2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f32x4* o = reinterpret_cast<f32x4*>(&sRed[wave][4 * q + e][16 * l16 + 4 * m]);
-                *o = *o + f32x4{acc[4 * m][e], acc[4 * m + 1][e], acc[4 * m + 2][e], acc[4 * m + 3][e]};
-            }
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    f32x4* o = reinterpret_cast<f32x4*>(&sRed[wave][16 * tb + 4 * q + e][16 * l16 + 4 * m]);
+                    *o = *o + f32x4{acc[tb][4 * m][e], acc[tb][4 * m + 1][e], acc[tb][4 * m + 2][e],
+                                    acc[tb][4 * m + 3][e]};
+                }
     __syncthreads();
     const int k = k0 + tid;
     if (k < K) {
@@ -606,14 +627,14 @@ __device__ __forceinline__ void skinny_bwd_dx(const uint16_t* __restrict__ dy, c
 // column block and split each), then the LoRA pre-pass roles, numbered from dx_total:
 // g workgroups [0, gblocks), dB workgroups [gblocks, gblocks + dblocks). The roles share
 // no data inside the launch (g is summed by the finish kernel, dB is final).
-template <int RB>
-__global__ __launch_bounds__(kThreads, kBOccupancy) void k_skinny_bwd(
+template <int RB, int TB>
+__global__ __launch_bounds__(kThreads, kBOccupancy<TB>) void k_skinny_bwd(
     const uint16_t* __restrict__ dy, const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
     const uint16_t* __restrict__ B, const float* __restrict__ u, int T, int N, int K, int r, float s,
     int steps_per_split, int dx_cols, int dx_total, int gsteps, int gblocks, int dblocks, float* __restrict__ dxpart,
     float* __restrict__ gpart, float* __restrict__ dB, Tables tab) {
     __shared__ __align__(16) union {
-        BwdSmem dx;
+        BwdSmem<TB> dx;
         pre::PreSmem<RB, pre::kTC> pre;
     } sm;
     // dX workgroups in an XCD-aware order (each XCD runs a contiguous range of (column
@@ -621,7 +642,7 @@ __global__ __launch_bounds__(kThreads, kBOccupancy) void k_skinny_bwd(
     // share one 128-byte line of a row then read it through one L2
     if (int(blockIdx.x) < dx_total) {
         const int t = int(xcd_tile_order(blockIdx.x, uint32_t(dx_total)));
-        skinny_bwd_dx(dy, codes, absmax, T, N, K, steps_per_split, t % dx_cols, t / dx_cols, dxpart, tab, sm.dx);
+        skinny_bwd_dx<TB>(dy, codes, absmax, T, N, K, steps_per_split, t % dx_cols, t / dx_cols, dxpart, tab, sm.dx);
         return;
     }
     const int blk = int(blockIdx.x) - dx_total;
@@ -683,9 +704,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny_bwd_finish(
     if (k >= K) return;
     for (int j = wave; j < r; j += 4) {
         float c = 0.0f;
-#pragma unroll
-        for (int t = 0; t < kSkinnyMaxT; ++t)
-            if (t < T) c += sg[t * r + j] * sw[t * kFinF + lane];
+#pragma unroll 4
+        for (int t = 0; t < T; ++t) c += sg[t * r + j] * sw[t * kFinF + lane];
         dA[size_t(j) * K + k] = s * c;
     }
 }
@@ -776,6 +796,27 @@ hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const fl
     return hipGetLastError();
 }
 
+template <int TB>
+void launch_bwd_rb(int rb, dim3 grid, const uint16_t* dy, const uint8_t* codes, const float* absmax,
+                   const uint16_t* B, const float* u, int64_t T, int64_t N, int64_t K, int r, float s,
+                   int steps_per_split, int dx_cols, int dx_total, int gsteps, int gblocks, int dblocks, float* dxpart,
+                   float* gpart, float* dB, hipStream_t stream) {
+    switch (rb) {
+        case 1: hipLaunchKernelGGL((k_skinny_bwd<1, TB>), grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u,
+                                   int(T), int(N), int(K), r, s, steps_per_split, dx_cols, dx_total, gsteps, gblocks,
+                                   dblocks, dxpart, gpart, dB, tables()); break;
+        case 2: hipLaunchKernelGGL((k_skinny_bwd<2, TB>), grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u,
+                                   int(T), int(N), int(K), r, s, steps_per_split, dx_cols, dx_total, gsteps, gblocks,
+                                   dblocks, dxpart, gpart, dB, tables()); break;
+        case 3: hipLaunchKernelGGL((k_skinny_bwd<3, TB>), grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u,
+                                   int(T), int(N), int(K), r, s, steps_per_split, dx_cols, dx_total, gsteps, gblocks,
+                                   dblocks, dxpart, gpart, dB, tables()); break;
+        default: hipLaunchKernelGGL((k_skinny_bwd<4, TB>), grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u,
+                                    int(T), int(N), int(K), r, s, steps_per_split, dx_cols, dx_total, gsteps, gblocks,
+                                    dblocks, dxpart, gpart, dB, tables()); break;
+    }
+}
+
 hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8_t* codes, const float* absmax,
                              const uint16_t* dy, const uint16_t* x, const uint16_t* A, const uint16_t* B,
                              const float* u, int64_t T, int64_t N, int64_t K, int r, float s, uint16_t* dx, float* dA,
@@ -783,7 +824,8 @@ hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8
     char* w = static_cast<char*>(ws);
     float* dxpart = reinterpret_cast<float*>(w + bp.off_dx);
     float* gpart = reinterpret_cast<float*>(w + bp.off_gpart);
-    if (T > kSkinnyMaxT) return hipErrorInvalidValue;  // one 16-token MFMA block
+    if (T > kSkinnyBwdT) return hipErrorInvalidValue;  // at most two 16-token MFMA blocks
+    static_assert(kSkinnyBwdT <= 32, "one or two token blocks are instantiated");
     const int dx_cols = dx ? p.col_blocks : 0;
     const int splits = dx ? p.splits : 1;
     const int gblocks = r > 0 ? int(cdiv(T, pre::kTC)) * bp.gparts : 0;
@@ -792,16 +834,13 @@ hipError_t launch_skinny_bwd(const SkinnyPlan& p, const BwdPlan& bp, const uint8
     if (dx_total + gblocks + dblocks > 0) {
         const dim3 grid(unsigned(dx_total + gblocks + dblocks));
         if (dx) prof_gemm_begin(stream);
-        switch (std::max(1, (r + 15) / 16)) {
-            case 1: hipLaunchKernelGGL(k_skinny_bwd<1>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
-                                       p.steps_per_split, dx_cols, dx_total, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
-            case 2: hipLaunchKernelGGL(k_skinny_bwd<2>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
-                                       p.steps_per_split, dx_cols, dx_total, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
-            case 3: hipLaunchKernelGGL(k_skinny_bwd<3>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
-                                       p.steps_per_split, dx_cols, dx_total, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
-            default: hipLaunchKernelGGL(k_skinny_bwd<4>, grid, dim3(kThreads), 0, stream, dy, codes, absmax, B, u, int(T), int(N), int(K), r, s,
-                                        p.steps_per_split, dx_cols, dx_total, bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, tables()); break;
-        }
+        const int rb = std::max(1, (r + 15) / 16);
+        if (T <= 16)
+            launch_bwd_rb<1>(rb, grid, dy, codes, absmax, B, u, T, N, K, r, s, p.steps_per_split, dx_cols, dx_total,
+                             bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, stream);
+        else
+            launch_bwd_rb<2>(rb, grid, dy, codes, absmax, B, u, T, N, K, r, s, p.steps_per_split, dx_cols, dx_total,
+                             bp.gsteps, gblocks, dblocks, dxpart, gpart, dB, stream);
         if (dx) prof_gemm_end(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -97,15 +97,17 @@ def test_few_token_path(gpu_lib, t, n, k, r):
 
 
 @pytest.mark.parametrize("t,n,k,r", [
-    (17, 208, 384, 5),       # two token blocks, the second with one token; odd rank
+    (17, 208, 384, 5),       # forward: two token blocks, the second with one token (backward: 128-token, narrow)
+    (17, 2064, 640, 5),      # both directions two blocks, odd rank
     (32, 3584, 3584, 16),    # two full blocks, q-shaped
     (25, 4096, 256, 16),     # ragged second block, one K step
-    (31, 1040, 8256, 64),    # maximum rank, ragged rows, odd K step count
-    (33, 208, 384, 16),      # one past the few-token forward: the 128-token kernels
+    (31, 2048, 8256, 64),    # maximum rank, odd K step count
+    (31, 1040, 8256, 64),    # narrow weights: forward two blocks, backward 128-token kernels
+    (33, 208, 384, 16),      # one past the few-token path: the 128-token kernels
 ])
-def test_few_token_forward_blocks(gpu_lib, t, n, k, r):
-    """17 <= T <= 32: the forward runs the streaming kernel with two token blocks (the
-    backward the 128-token kernels)."""
+def test_few_token_two_blocks(gpu_lib, t, n, k, r):
+    """17 <= T <= 32: the forward runs the streaming kernel with two token blocks, and so
+    does the backward for weights of at least 2048 rows."""
     _check_case(gpu_lib, t, n, k, r)
 
 
