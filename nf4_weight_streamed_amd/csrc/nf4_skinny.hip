@@ -315,13 +315,16 @@ constexpr int kFinTk = 4;
 constexpr int kMaxSplits = 32;  // split partials a finish thread loads at once
 
 // Split partials of one output element: v[z] = src[base + z * zstride] for z < splits,
-// 0 (out-of-range read) for the rest; sum_splits adds all kMaxSplits in split order
-// (the zeros past `splits` leave the sum unchanged).
+// 0 for the rest: rp spans exactly `splits` partials, so the offsets of z >= splits lie
+// past it and read as zero with no test of their own (a dead lane starts from
+// kOutOfRange, which stays past any buffer and below 2^32 for every z); sum_splits adds
+// all kMaxSplits in split order (the zeros past `splits` leave the sum unchanged).
 __device__ __forceinline__ void load_splits(float (&v)[kMaxSplits], __amdgpu_buffer_rsrc_t rp, int splits,
                                             uint32_t base, uint32_t zstride, bool live) {
+    (void)splits;
+    const uint32_t b = live ? base : kOutOfRange;
 #pragma unroll
-    for (int z = 0; z < kMaxSplits; ++z)
-        v[z] = buf_load_f32(rp, live && z < splits ? base + uint32_t(z) * zstride : kOutOfRange);
+    for (int z = 0; z < kMaxSplits; ++z) v[z] = buf_load_f32(rp, b + uint32_t(z) * zstride);
 }
 
 __device__ __forceinline__ float sum_splits(const float (&v)[kMaxSplits]) {
@@ -354,10 +357,9 @@ __device__ __forceinline__ void stage_partial_sums(float* dst, float* tmp, const
             for (int p0 = 0; p0 < parts; p0 += 32) {
                 float pv[32];
 #pragma unroll
-                for (int pp = 0; pp < 32; ++pp)
-                    pv[pp] = buf_load_f32(rs, ok && p0 + pp < parts
-                                                  ? (uint32_t(p0 + pp) * stride + uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u
-                                                  : kOutOfRange);
+                for (int pp = 0; pp < 32; ++pp)  // parts past the last read past rs: zero
+                    pv[pp] = buf_load_f32(rs, ok ? (uint32_t(p0 + pp) * stride + uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u
+                                                 : kOutOfRange);
 #pragma unroll
                 for (int pp = 0; pp < 32; ++pp)
                     if (p0 + pp < parts) v += pv[pp];
@@ -376,8 +378,8 @@ __device__ __forceinline__ void stage_partial_sums(float* dst, float* tmp, const
 #pragma unroll
         for (int pp = 0; pp < 8; ++pp) {
             const int p = p0 + pp * G;
-            pv[pp] = buf_load_f32(rs, ok && p < parts ? (uint32_t(p) * stride + uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u
-                                                      : kOutOfRange);
+            // parts past the last read past rs: zero
+            pv[pp] = buf_load_f32(rs, ok ? (uint32_t(p) * stride + uint32_t(t) * uint32_t(r) + uint32_t(j)) * 4u : kOutOfRange);
         }
 #pragma unroll
         for (int pp = 0; pp < 8; ++pp)
@@ -408,10 +410,9 @@ __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __r
     const int n0 = int(blockIdx.x) * kFinF, t0 = int(blockIdx.y) * kFinTk;
     const int n = n0 + lane, t = t0 + wave;
     const bool live = n < N && t < T;
-    float pv[kMaxSplits];
-    load_splits(pv, make_rsrc(ypart, uint32_t(splits) * uint32_t(T) * uint32_t(N) * 4u), splits,
-                (uint32_t(t) * uint32_t(N) + uint32_t(n)) * 4u, uint32_t(T) * uint32_t(N) * 4u, live);
-    // B[n][j] for j = wave + 4i, all loads first (rows past N and ranks past r read 0)
+    // every load is issued before the first is waited for (one memory round trip): B[n][j]
+    // for j = wave + 4i (rows past N and ranks past r read 0), the split partials, then
+    // the u partials inside stage_partial_sums
     const auto rb = make_rsrc(B, uint32_t(N) * uint32_t(r) * 2u);
     constexpr int BV = kMaxRank / kFinTk;
     uint32_t bv[BV];
@@ -421,9 +422,13 @@ __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __r
         bv[i] = __builtin_amdgcn_raw_buffer_load_b16(
             rb, int(j < r ? (uint32_t(n) * uint32_t(r) + uint32_t(j)) * 2u : kOutOfRange), 0, 0);
     }
+    float pv[kMaxSplits];
+    load_splits(pv, make_rsrc(ypart, uint32_t(splits) * uint32_t(T) * uint32_t(N) * 4u), splits,
+                (uint32_t(t) * uint32_t(N) + uint32_t(n)) * 4u, uint32_t(T) * uint32_t(N) * 4u, live);
+    stage_partial_sums(su, stmp, upart, uparts, T, r, t0, kFinTk, 0, r);  // ends with a barrier
 #pragma unroll
     for (int i = 0; i < BV; ++i) sB[(wave + kFinTk * i) * kFinF + lane] = bf16_to_f32(uint16_t(bv[i]));
-    stage_partial_sums(su, stmp, upart, uparts, T, r, t0, kFinTk, 0, r);  // ends with a barrier
+    __syncthreads();
     if (blockIdx.x == 0)
         for (int o = tid; o < min(kFinTk, T - t0) * r; o += kThreads) u_save[size_t(t0) * r + o] = su[o];
     if (!live) return;
@@ -669,7 +674,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny_bwd_finish(
     const bool dx_role = int(blockIdx.x) < dx_blocks;
     const int b = dx_role ? int(blockIdx.x) : int(blockIdx.x) - dx_blocks;
     const int k0 = (b % col_blocks) * kFinF, k = k0 + lane;
-    // A rows (dX role) or x rows (dA role), columns k0 .. k0 + 63: all loads first
+    // A rows (dX role) or x rows (dA role), columns k0 .. k0 + 63; every load of a role is
+    // issued before the first is waited for (one memory round trip)
     const int wrows = dx_role ? r : T;
     const auto rw = dx_role ? make_rsrc(A, uint32_t(r) * uint32_t(K) * 2u) : make_rsrc(x, uint32_t(T) * uint32_t(K) * 2u);
     constexpr int WV = kMaxRank / kFinTk;  // rows wave + 4i
@@ -686,10 +692,12 @@ __global__ __launch_bounds__(kThreads) void k_skinny_bwd_finish(
         float pv[kMaxSplits];
         load_splits(pv, make_rsrc(dxpart, uint32_t(splits) * uint32_t(T) * uint32_t(K) * 4u), splits,
                     (uint32_t(t) * uint32_t(K) + uint32_t(k)) * 4u, uint32_t(T) * uint32_t(K) * 4u, live);
+        const int tb0 = (b / col_blocks) * kFinTk;
+        // the g partials' loads join the ones above before any is waited for
+        stage_partial_sums(sg, stmp, gpart, gparts, T, r, tb0, kFinTk, 0, r);  // ends with a barrier
 #pragma unroll
         for (int i = 0; i < WV; ++i) sw[(wave + kFinTk * i) * kFinF + lane] = bf16_to_f32(uint16_t(wv[i]));
-        const int tb0 = (b / col_blocks) * kFinTk;
-        stage_partial_sums(sg, stmp, gpart, gparts, T, r, tb0, kFinTk, 0, r);  // ends with a barrier
+        __syncthreads();
         if (!live) return;
         const float acc = sum_splits(pv);
         float l = 0.0f;
@@ -698,9 +706,10 @@ __global__ __launch_bounds__(kThreads) void k_skinny_bwd_finish(
         dx[size_t(t) * K + k] = bf16_bits(acc + s * l);
         return;
     }
+    stage_partial_sums(sg, stmp, gpart, gparts, T, r, 0, T, 0, r);  // ends with a barrier
 #pragma unroll
     for (int i = 0; i < WV; ++i) sw[(wave + kFinTk * i) * kFinF + lane] = bf16_to_f32(uint16_t(wv[i]));
-    stage_partial_sums(sg, stmp, gpart, gparts, T, r, 0, T, 0, r);  // ends with a barrier
+    __syncthreads();
     if (k >= K) return;
     for (int j = wave; j < r; j += 4) {
         float c = 0.0f;
