@@ -1,4 +1,5 @@
-// NF4-LoRA linear for few tokens (forward T <= 32, backward T <= 16): the same operations
+// NF4-LoRA linear for few tokens (forward T <= 32; backward T <= 16, or T <= 32 for weights
+// of at least 2048 rows): the same operations
 // as the 128-token GEMMs, organised for the HBM-bound regime, where every weight byte
 // should be read once and streamed at full rate while MFMA work is cheap.
 //
@@ -451,7 +452,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny_fwd_finish(const float* __r
 // Scales: two dwords per lane and step ([row][block] in memory), exchanged through the
 // wave's own LDS slice as [block][row]. Codes, scales and dY are loaded kBRing - 1 steps
 // ahead into a ring of kBRing register sets (two, measured: three workgroups per CU then
-// fit in the registers). T <= 16 (one 16-token MFMA block).
+// fit in the registers). TB 16-token MFMA blocks (T <= 16 TB; TB = 1 or 2): each dequantised
+// fragment feeds TB MFMAs, and the accumulators grow to TB x 16.
 // Output: fp32 partials dxpart[split][T][K].
 constexpr int kBCols = 256;  // features per workgroup
 constexpr int kBRows = 32;   // weight rows per wave step
