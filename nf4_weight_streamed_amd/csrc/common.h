@@ -45,6 +45,13 @@ constexpr int kMaxDbChunks = 8;   // token ranges of dB = s.dY^T.u (shares summe
 // 65 and 60 us against 23.3, 35.5, 88 and 90 us on the 128-token kernels; at T = 64,
 // four blocks were slower than those on the 7B shapes).
 constexpr int64_t kSkinnyFwdT = 32;
+// The forward also takes up to 64 tokens (four blocks) for long, narrow weights, where the
+// 128-token kernels have few tiles to split: at T = 64 the 72B down, q and k forward take
+// 80, 37 and 17.7 us against 97, 39 and 26 us, the 7B down 35.5 against 41 us, while the
+// wide 72B gate keeps the 128-token kernels (97 against 100 us).
+constexpr int64_t kSkinnyFwdLongT = 64;
+constexpr int64_t kSkinnyLongK = 8192;      // K at least this
+constexpr int64_t kSkinnyNarrowN = 8192;    // N at most this
 constexpr int64_t kSkinnyBwdT = 32;
 struct SkinnyPlan {
     int row_blocks;       // forward: 128-row workgroups

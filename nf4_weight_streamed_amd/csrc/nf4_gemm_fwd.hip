@@ -443,7 +443,7 @@ __global__ __launch_bounds__(256) void k_split_sum_bf16(SplitTiles f, uint16_t* 
 
 FwdPlan plan_fwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     FwdPlan p{};
-    if (T <= kSkinnyFwdT && !dense) {
+    if ((T <= kSkinnyFwdT || (T <= kSkinnyFwdLongT && K >= kSkinnyLongK && N <= kSkinnyNarrowN)) && !dense) {
         p.skinny = true;
         p.sk = plan_skinny_fwd(T, N, K, r);
         p.ws_bytes = p.sk.ws_bytes;

@@ -791,13 +791,14 @@ hipError_t launch_skinny_fwd(const SkinnyPlan& p, const uint8_t* codes, const fl
     char* w = static_cast<char*>(ws);
     float* ypart = reinterpret_cast<float*>(w + p.off_part);
     float* upart = reinterpret_cast<float*>(w + p.off_upart);
-    if (T > kSkinnyFwdT) return hipErrorInvalidValue;  // at most two 16-token MFMA blocks
-    static_assert(kSkinnyFwdT <= 32, "one or two token blocks are instantiated");
+    if (T > kSkinnyFwdLongT) return hipErrorInvalidValue;  // at most four 16-token MFMA blocks
     prof_gemm_begin(stream);
-    if (T <= 16)
-        launch_fwd_tb<1>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream);
-    else
-        launch_fwd_tb<2>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream);
+    switch ((T + 15) / 16) {
+        case 1: launch_fwd_tb<1>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream); break;
+        case 2: launch_fwd_tb<2>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream); break;
+        case 3: launch_fwd_tb<3>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream); break;
+        default: launch_fwd_tb<4>(p, codes, absmax, x, A, T, N, K, r, ypart, upart, stream); break;
+    }
     prof_gemm_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

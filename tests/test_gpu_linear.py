@@ -111,6 +111,19 @@ def test_few_token_two_blocks(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
 
 
+@pytest.mark.parametrize("t,n,k,r", [
+    (33, 1040, 8256, 16),    # three token blocks (the third with one token), long K, odd step count
+    (48, 208, 8192, 5),      # three full blocks, odd rank
+    (57, 2048, 8192, 64),    # four blocks (ragged), maximum rank
+    (64, 8192, 1024, 16),    # short K: the 128-token kernels
+    (64, 8208, 8192, 16),    # wide N: the 128-token kernels
+])
+def test_few_token_forward_long_k(gpu_lib, t, n, k, r):
+    """33 <= T <= 64 with K >= 8192 and N <= 8192: the forward runs the streaming kernel
+    with three or four token blocks (the backward the 128-token kernels)."""
+    _check_case(gpu_lib, t, n, k, r)
+
+
 def test_few_token_dx_skipped(gpu_lib):
     case = S.linear_case(4, 256, 512)
     wq, dev = _prepare(gpu_lib, case, 16)
