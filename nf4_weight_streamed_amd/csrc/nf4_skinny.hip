@@ -1,5 +1,5 @@
-// NF4-LoRA linear for few tokens (forward T <= 32; backward T <= 16, or T <= 32 for weights
-// of at least 2048 rows): the same operations
+// NF4-LoRA linear for few tokens (forward T <= 32, or T <= 64 for long, narrow weights;
+// backward T <= 16, or T <= 32 for weights of at least 2048 rows): the same operations
 // as the 128-token GEMMs, organised for the HBM-bound regime, where every weight byte
 // should be read once and streamed at full rate while MFMA work is cheap.
 //
@@ -11,8 +11,8 @@
 // The frozen NF4 base is only read (HN comment thread on streaming the frozen base,
 // main comment); LoRA rank r and alpha as in the Poros API reference
 // ("PorosTrainer.from_pretrained"). Tokens are padded to blocks of 16 for
-// v_mfma_f32_16x16x32_bf16 (the forward's TB template counts such blocks, one or two,
-// and each dequantised weight fragment feeds both; the backward takes one block);
+// v_mfma_f32_16x16x32_bf16 (the forward's TB template counts such blocks, one to four,
+// and each dequantised weight fragment feeds all of them; the backward takes one or two);
 // both GEMM kernels split their contraction over the grid's y dimension
 // and write fp32 partials, which the finish kernels add in split order, together with
 // the LoRA terms, and round once.
