@@ -741,7 +741,7 @@ constexpr int64_t kFillWGs = 256;
 constexpr int64_t kFwdWGs = 512;
 constexpr int64_t kFwdMinSteps = 4;
 constexpr int64_t kFwdPartialDiv = 1;  // 2 was 20% slower on the 7B q forward at T = 32
-constexpr int64_t kBwdWGs = 768;
+constexpr int64_t kBwdWGs = 512;  // 768 was 2-10% slower at 16 and 32 tokens (72B q, 7B down)
 constexpr int64_t kBwdMinSteps = 4;  // one per wave
 constexpr int64_t kBwdPartialDiv = 1;
 
