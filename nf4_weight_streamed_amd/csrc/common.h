@@ -43,7 +43,8 @@ constexpr int kMaxDbChunks = 8;   // token ranges of dB = s.dY^T.u (shares summe
 // Workspace: [partials | u partials] (forward) / [g partials | dX partials] (backward).
 // Both take up to 32 tokens in one or two blocks, which share each dequantised weight
 // fragment (at T = 32 the 7B q, 7B gate, 72B gate and 72B down forward take 13.4, 30.6,
-// 65 and 60 us against 23.3, 35.5, 88 and 90 us on the 128-token kernels; at T = 64,
+// 65 and 60 us against 23.3, 35.5, 88 and 90 us on the 128-token kernels, the backward
+// of the 72B gate 58 against 96 us and of the 7B k 17.3 against 17.6 us; at T = 64,
 // four blocks were slower than those on the 7B shapes).
 constexpr int64_t kSkinnyFwdT = 32;
 // The forward also takes up to 64 tokens (four blocks) for long, narrow weights, where the

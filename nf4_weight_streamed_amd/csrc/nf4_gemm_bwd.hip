@@ -558,10 +558,7 @@ int bwd_tile_tokens(int64_t T, int64_t N, int64_t K, bool dense) {
 
 BwdPlan plan_bwd(int64_t T, int64_t N, int64_t K, int r, bool dense) {
     BwdPlan p{};
-    // two token blocks lose to the 128-token kernels on narrow weights (7B k at T = 32:
-    // 20.3 against 17.6 us) and win on wide ones (7B q 21.6 against 23.4, 72B gate 68.5
-    // against 98 us)
-    if ((T <= 16 || (T <= kSkinnyBwdT && N >= 2048)) && !dense) {
+    if (T <= kSkinnyBwdT && !dense) {
         p.skinny = true;
         p.sk = plan_skinny_bwd(T, N, K);
         if (r > 0) plan_lora_bwd_pre(p, T, N, kMaxGPartsFew);

@@ -1,5 +1,5 @@
 // NF4-LoRA linear for few tokens (forward T <= 32, or T <= 64 for long, narrow weights;
-// backward T <= 16, or T <= 32 for weights of at least 2048 rows): the same operations
+// backward T <= 32): the same operations
 // as the 128-token GEMMs, organised for the HBM-bound regime, where every weight byte
 // should be read once and streamed at full rate while MFMA work is cheap.
 //

@@ -97,17 +97,16 @@ def test_few_token_path(gpu_lib, t, n, k, r):
 
 
 @pytest.mark.parametrize("t,n,k,r", [
-    (17, 208, 384, 5),       # forward: two token blocks, the second with one token (backward: 128-token, narrow)
+    (17, 208, 384, 5),       # two token blocks, the second with one token, narrow weights
     (17, 2064, 640, 5),      # both directions two blocks, odd rank
     (32, 3584, 3584, 16),    # two full blocks, q-shaped
     (25, 4096, 256, 16),     # ragged second block, one K step
     (31, 2048, 8256, 64),    # maximum rank, odd K step count
-    (31, 1040, 8256, 64),    # narrow weights: forward two blocks, backward 128-token kernels
+    (31, 1040, 8256, 64),    # maximum rank, narrow weights
     (33, 208, 384, 16),      # one past the few-token path: the 128-token kernels
 ])
 def test_few_token_two_blocks(gpu_lib, t, n, k, r):
-    """17 <= T <= 32: the forward runs the streaming kernel with two token blocks, and so
-    does the backward for weights of at least 2048 rows."""
+    """17 <= T <= 32: both directions run the streaming kernels with two token blocks."""
     _check_case(gpu_lib, t, n, k, r)
 
 
