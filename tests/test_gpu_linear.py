@@ -123,6 +123,26 @@ def test_few_token_forward_long_k(gpu_lib, t, n, k, r):
     _check_case(gpu_lib, t, n, k, r)
 
 
+@pytest.mark.parametrize("t,n,k,r", [
+    (15, 2048, 9216, 64),    # one block below its edge, maximum rank, long K
+    (1, 1424, 8256, 64),     # one token, odd K step count
+    (18, 176, 9216, 33),     # two blocks, three rank blocks (ragged), narrow N
+    (24, 272, 9216, 1),      # rank 1
+    (40, 2064, 1920, 0),     # base only, short K: both directions on the 128-token kernels
+    (47, 1056, 9216, 5),     # three blocks (forward), odd rank
+    (49, 2128, 8192, 33),    # four blocks (ragged), three rank blocks
+    (49, 8208, 192, 1),      # wide N, short K: 128-token kernels
+    (64, 480, 9216, 33),     # four full blocks at the long-K edge
+    (64, 8208, 320, 64),     # short K: 128-token kernels at the maximum rank
+    (65, 384, 1152, 16),     # one past the few-token forward
+])
+def test_few_token_edges(gpu_lib, t, n, k, r):
+    """Shapes around the few-token limits (T = 16 / 32 / 64, K >= 8192, N <= 8192) with
+    ragged ranks, widths and step counts, each direction on whichever kernel the shape
+    selects."""
+    _check_case(gpu_lib, t, n, k, r)
+
+
 def test_few_token_dx_skipped(gpu_lib):
     case = S.linear_case(4, 256, 512)
     wq, dev = _prepare(gpu_lib, case, 16)
