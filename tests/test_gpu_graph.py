@@ -43,6 +43,8 @@ OUTS = ("y", "u", "dx", "dA", "dB")
     (300, 1104, 8192),    # ragged tiles, contraction split in both GEMMs
     (512, 2048, 18944),   # 256-token backward tiles, a whole round plus a split tail
     (5, 3584, 3584),      # few tokens: streaming kernels with split partials
+    (29, 2048, 3584),     # two token blocks in both streaming kernels
+    (50, 1024, 8192),     # four token blocks in the streaming forward (long, narrow weights)
 ])
 def test_graph_replay_equals_eager(gpu_lib, t, n, k):
     lib = gpu_lib
