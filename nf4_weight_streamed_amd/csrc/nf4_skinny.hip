@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_skinny_fwd(
 // fetched cold - and every independent load issued before the first wait.
 constexpr int kFinF = 64;
 constexpr int kFinTk = 4;
-constexpr int kMaxSplits = 32;  // split partials a finish thread loads at once
+constexpr int kMaxSplits = 16;  // split partials a finish thread loads at once (32: a larger finish kernel, slower)
 
 // Split partials of one output element: v[z] = src[base + z * zstride] for z < splits,
 // 0 for the rest: rp spans exactly `splits` partials, so the offsets of z >= splits lie
@@ -741,7 +741,7 @@ constexpr int64_t kFillWGs = 256;
 constexpr int64_t kFwdWGs = 512;
 constexpr int64_t kFwdMinSteps = 4;
 constexpr int64_t kFwdPartialDiv = 1;  // 2 was 20% slower on the 7B q forward at T = 32
-constexpr int64_t kBwdWGs = 512;  // 768 was 2-10% slower at 16 and 32 tokens (72B q, 7B down)
+constexpr int64_t kBwdWGs = 256;  // one per CU: 512 was 4-17% slower, 384 (1.5 per CU) slower still
 constexpr int64_t kBwdMinSteps = 4;  // one per wave
 constexpr int64_t kBwdPartialDiv = 1;
 
