@@ -294,8 +294,9 @@ def linear_flops(t: int, n: int, k: int, r: int) -> float:
 
 
 def cpu_baseline(seconds_budget: float = 12.0) -> dict:
-    """The fp64 oracle, as it stands, on the GPU machine's host cores (BLAS pinned to the
-    cores of this process's affinity mask), on a bounded sample of the same workload:
+    """The fp64 oracle, as it stands, on the host cores of the machine that runs the
+    benchmark (BLAS pinned to the cores of this process's affinity mask), on a bounded
+    sample of the same workload:
     the q projection (3584 x 3584) of the layer with all 512 tokens - dequantise +
     forward + backward - repeated for about `seconds_budget` seconds, scaled to the
     whole layer by the algorithmic-FLOP ratio. Beside it: the single 1024 x 1024 linear
