@@ -92,7 +92,7 @@ def test_shapes(gpu_lib, t, n, k, r):
     (12, 4096, 256, 16),     # long N, short K (one K step)
 ])
 def test_few_token_path(gpu_lib, t, n, k, r):
-    """T <= 16 runs the streaming kernels (16-token MFMA blocks, split contraction)."""
+    """T <= 16: the streaming kernels with one 16-token MFMA block (split contraction)."""
     _check_case(gpu_lib, t, n, k, r)
 
 
