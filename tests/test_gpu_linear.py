@@ -50,6 +50,31 @@ def _check_case(lib, t, n, k, r, alpha=32.0, seed=42, b_std=0.01):
     return y, dx, da, db
 
 
+def _random_shapes(count=24, seed=20261203):
+    """Seeded shapes over the entry points' domain, half of them in the few-token range:
+    T 1..600, N a multiple of 16 up to 4096, K a multiple of 64 up to 6144, rank 0..64,
+    alpha from {8, 16, 32, 64}; the product T*N*K kept small enough for the fp64 oracle."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        t = int(rng.integers(1, 65)) if len(out) % 2 == 0 else int(rng.integers(65, 601))
+        n = 16 * int(rng.integers(1, 257))
+        k = 64 * int(rng.integers(1, 97))
+        if t * n * k > 3_000_000_000:
+            continue
+        r = int(rng.choice([0, 1, 3, 8, 16, 16, 16, 24, 33, 64]))
+        alpha = float(rng.choice([8.0, 16.0, 32.0, 64.0]))
+        out.append((t, n, k, r, alpha, int(rng.integers(1, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("t,n,k,r,alpha,seed", _random_shapes())
+def test_random_shapes(gpu_lib, t, n, k, r, alpha, seed):
+    """Breadth beyond the hand-picked shapes: each case through both entry points, checked
+    element by element against the oracle."""
+    _check_case(gpu_lib, t, n, k, r, alpha=alpha, seed=seed)
+
+
 def test_single_linear_workload(gpu_lib):
     """in = out = 1024, 256 tokens, r = 16, alpha = 32: fwd + bwd (dX, dA, dB)."""
     _check_case(gpu_lib, 256, 1024, 1024, 16)
