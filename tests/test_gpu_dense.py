@@ -25,19 +25,42 @@ PROJS = ("q", "k", "v", "o", "gate", "up", "down")
     (300, 640, 22976, 16),   # 540 dX tiles: the last 28 split over N
 ])
 def test_dense_linear_matches_oracle(gpu_lib, t, n, k, r):
-    case = S.linear_case(t, n, k, r=max(r, 1))
+    _dense_case(gpu_lib, t, n, k, r)
+
+
+def _dense_shapes(count=10, seed=20261204):
+    """Seeded shapes for the dense variant: T 1..600, N a multiple of 16 up to 4096, K a
+    multiple of 64 up to 4096 (dense weights: N*K*2 bytes), ranks 0..64, alpha 8..64."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        t, n, k = int(rng.integers(1, 601)), 16 * int(rng.integers(1, 257)), 64 * int(rng.integers(1, 65))
+        if t * n * k > 2_000_000_000:
+            continue
+        out.append((t, n, k, int(rng.choice([0, 1, 7, 16, 16, 40, 64])), float(rng.choice([8.0, 32.0, 64.0])),
+                    int(rng.integers(1, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("t,n,k,r,alpha,seed", _dense_shapes())
+def test_dense_random_shapes(gpu_lib, t, n, k, r, alpha, seed):
+    _dense_case(gpu_lib, t, n, k, r, alpha, seed)
+
+
+def _dense_case(gpu_lib, t, n, k, r, alpha=32.0, seed=42):
+    case = S.linear_case(t, n, k, r=max(r, 1), seed=seed)
     if r == 0:
         case["A"], case["B"] = np.zeros((0, k), np.uint16), np.zeros((n, 0), np.uint16)
     w = to_dev_bf16(case["W"])
     A = to_dev_bf16(case["A"]) if r else None
     B = to_dev_bf16(case["B"]) if r else None
-    y, u = gpu_lib.lora_linear_fwd_bf16(w, to_dev_bf16(case["x"]), A, B, 32.0)
-    dx, da, db = gpu_lib.lora_linear_bwd_bf16(w, to_dev_bf16(case["x"]), u, to_dev_bf16(case["dY"]), A, B, 32.0)
+    y, u = gpu_lib.lora_linear_fwd_bf16(w, to_dev_bf16(case["x"]), A, B, alpha)
+    dx, da, db = gpu_lib.lora_linear_bwd_bf16(w, to_dev_bf16(case["x"]), u, to_dev_bf16(case["dY"]), A, B, alpha)
     torch.cuda.synchronize()
-    y_ref, u_ref = O.lora_linear_fwd(case["x"], case["W"], case["A"], case["B"], 32.0)
-    dx_ref, da_ref, db_ref = O.lora_linear_bwd(case["x"], case["W"], case["A"], case["B"], 32.0, case["dY"])
+    y_ref, u_ref = O.lora_linear_fwd(case["x"], case["W"], case["A"], case["B"], alpha)
+    dx_ref, da_ref, db_ref = O.lora_linear_bwd(case["x"], case["W"], case["A"], case["B"], alpha, case["dY"])
     refs = {"y": y_ref, "u": u_ref, "dx": dx_ref, "dA": da_ref, "dB": db_ref}
-    mags = linear_mags(case["x"], case["W"], case["A"], case["B"], 32.0, case["dY"])
+    mags = linear_mags(case["x"], case["W"], case["A"], case["B"], alpha, case["dY"])
     outs = {"y": bits_of(y), "dx": bits_of(dx)}
     if r:
         outs.update(u=f32_of(u), dA=f32_of(da), dB=f32_of(db))
